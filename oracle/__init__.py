@@ -1,0 +1,183 @@
+"""Plain CPU reference ("oracle") for microscaling quantization and the
+block-scaled GEMM, wrapped for numpy.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package. The GPU library never calls it and
+shares no code with it; the product path fails when its HIP library is missing
+instead of falling back here.
+
+The arithmetic lives in mx_oracle.c (see its header for what each routine
+follows and how each is pinned). This module only marshals numpy arrays.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+FMT_BF16, FMT_MXFP4, FMT_MXFP8, FMT_NVFP4 = 0, 1, 2, 3
+OUT_F32, OUT_BF16 = 0, 1
+BLOCK = {FMT_MXFP4: 32, FMT_MXFP8: 32, FMT_NVFP4: 16}
+
+_lib = None
+
+
+def lib():
+    """Load liboracle.so, compiling it first if it is missing or stale."""
+    global _lib
+    if _lib is None:
+        path = _build.build(force=False)
+        L = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        L.mxo_bf16_value.restype = ctypes.c_double
+        L.mxo_bf16_value.argtypes = [ctypes.c_uint16]
+        for n in ("mxo_e2m1_value", "mxo_e4m3_value", "mxo_e8m0_value"):
+            getattr(L, n).restype = ctypes.c_double
+            getattr(L, n).argtypes = [ctypes.c_uint8]
+        for n in ("mxo_encode_e2m1", "mxo_encode_e4m3"):
+            getattr(L, n).restype = ctypes.c_uint8
+            getattr(L, n).argtypes = [ctypes.c_double]
+        L.mxo_f32_to_bf16.restype = ctypes.c_uint16
+        L.mxo_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.mxo_mx_scale_exponent.restype = ctypes.c_int
+        L.mxo_mx_scale_exponent.argtypes = [ctypes.c_double, ctypes.c_double]
+        L.mxo_storage_bytes.restype = i64
+        L.mxo_storage_bytes.argtypes = [ctypes.c_int, i64, i64]
+        L.mxo_quantize.restype = ctypes.c_int
+        L.mxo_quantize.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, P, P, P, P]
+        L.mxo_quantize_nvfp4_exact_quotient.restype = ctypes.c_int
+        L.mxo_quantize_nvfp4_exact_quotient.argtypes = [i64, i64, P, P, P, P]
+        L.mxo_dequantize.restype = ctypes.c_int
+        L.mxo_dequantize.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, P, P,
+                                     ctypes.c_float, ctypes.c_int, P]
+        L.mxo_gemm.restype = ctypes.c_int
+        L.mxo_gemm.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                               P, P, ctypes.c_float, P, P, ctypes.c_float, P, P]
+        L.mxo_gemm_entries.restype = ctypes.c_int
+        L.mxo_gemm_entries.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                                       P, P, ctypes.c_float, P, P, ctypes.c_float,
+                                       i64, P, P, P, P]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (status {rc})")
+
+
+# ---- scalar format helpers -------------------------------------------------
+def bf16_value(bits):
+    return lib().mxo_bf16_value(int(bits))
+
+
+def e2m1_value(code):
+    return lib().mxo_e2m1_value(int(code))
+
+
+def e4m3_value(code):
+    return lib().mxo_e4m3_value(int(code))
+
+
+def e8m0_value(e):
+    return lib().mxo_e8m0_value(int(e))
+
+
+def encode_e2m1(v):
+    return lib().mxo_encode_e2m1(float(v))
+
+
+def encode_e4m3(v):
+    return lib().mxo_encode_e4m3(float(v))
+
+
+def f32_to_bf16(f):
+    return lib().mxo_f32_to_bf16(float(f))
+
+
+def mx_scale_exponent(amax, emax):
+    return lib().mxo_mx_scale_exponent(float(amax), float(emax))
+
+
+def storage_bytes(fmt, rows, cols):
+    return lib().mxo_storage_bytes(fmt, rows, cols)
+
+
+# ---- tensor operations -----------------------------------------------------
+def code_shape(fmt, rows, cols):
+    return (rows, cols) if fmt == FMT_MXFP8 else (rows, cols // 2)
+
+
+def quantize(fmt, x_bits):
+    """x_bits: uint16 [rows][cols] bf16 bit patterns.
+    Returns (codes uint8, scales uint8 [rows][cols/block], tensor_scale float)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    rows, cols = x.shape
+    blk = BLOCK[fmt]
+    codes = np.zeros(code_shape(fmt, rows, cols), np.uint8)
+    scales = np.zeros((rows, cols // blk), np.uint8)
+    ts = np.zeros(1, np.float32)
+    _check(lib().mxo_quantize(fmt, blk, rows, cols, _ptr(x), _ptr(codes),
+                              _ptr(scales), _ptr(ts)), "quantize")
+    return codes, scales, float(ts[0])
+
+
+def quantize_nvfp4_exact_quotient(x_bits):
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    rows, cols = x.shape
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 16), np.uint8)
+    ts = np.zeros(1, np.float32)
+    _check(lib().mxo_quantize_nvfp4_exact_quotient(rows, cols, _ptr(x), _ptr(codes),
+                                                   _ptr(scales), _ptr(ts)), "quantize")
+    return codes, scales, float(ts[0])
+
+
+def dequantize(fmt, codes, scales, tensor_scale, rows, cols, out=OUT_F32):
+    """Returns float32 [rows][cols] (OUT_F32) or uint16 bf16 bits (OUT_BF16)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    y = np.zeros((rows, cols), np.float32 if out == OUT_F32 else np.uint16)
+    _check(lib().mxo_dequantize(fmt, BLOCK[fmt], rows, cols, _ptr(codes), _ptr(scales),
+                                float(tensor_scale), out, _ptr(y)), "dequantize")
+    return y
+
+
+def _gemm_operands(fmt, data, scales):
+    if fmt == FMT_BF16:
+        return np.ascontiguousarray(data, dtype=np.uint16), None
+    return (np.ascontiguousarray(data, dtype=np.uint8),
+            np.ascontiguousarray(scales, dtype=np.uint8))
+
+
+def gemm(fmt_a, fmt_b, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts):
+    """Exact-operand GEMM in double. Returns (C, S), each float64 [M][N], with
+    S = sum_k |a_ik * b_jk|. B is stored N x K."""
+    a, a_scales = _gemm_operands(fmt_a, a, a_scales)
+    b, b_scales = _gemm_operands(fmt_b, b, b_scales)
+    C = np.zeros((M, N), np.float64)
+    S = np.zeros((M, N), np.float64)
+    _check(lib().mxo_gemm(fmt_a, fmt_b, M, N, K, _ptr(a), _ptr(a_scales), float(a_ts),
+                          _ptr(b), _ptr(b_scales), float(b_ts), _ptr(C), _ptr(S)), "gemm")
+    return C, S
+
+
+def gemm_entries(fmt_a, fmt_b, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts, ii, jj):
+    """As gemm(), only for output entries (ii[t], jj[t]). Returns (C, S) 1-D."""
+    a, a_scales = _gemm_operands(fmt_a, a, a_scales)
+    b, b_scales = _gemm_operands(fmt_b, b, b_scales)
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    C = np.zeros(len(ii), np.float64)
+    S = np.zeros(len(ii), np.float64)
+    _check(lib().mxo_gemm_entries(fmt_a, fmt_b, M, N, K, _ptr(a), _ptr(a_scales),
+                                  float(a_ts), _ptr(b), _ptr(b_scales), float(b_ts),
+                                  len(ii), _ptr(ii), _ptr(jj), _ptr(C), _ptr(S)),
+           "gemm_entries")
+    return C, S

@@ -1,0 +1,443 @@
+/*
+ * mx_oracle.c -- plain CPU reference for microscaling quantization and the
+ * block-scaled GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke check and the
+ * benchmark's CPU-baseline leg, never by the GPU library. Shares no code with
+ * it. Written for a reader checking it against the pages by eye: values come
+ * from the formats' bit-field definitions, rounding is a nearest-value search
+ * over the representable set, and sums are plain loops in double.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared.
+ * Contraction must stay off: the NVFP4 sequence is specified in fp32 with one
+ * rounding per operation.
+ *
+ * Parity status, per function (what pins each one is listed in the tests):
+ *  - format decoders, element encoders, MX scale rule, MX quantize,
+ *    dequantize, GEMM: pinned (printed value sets and formulas, invariants,
+ *    brute force, library cross-checks).
+ *  - NVFP4 quantize: the element and scale roundings are pinned, but the
+ *    tensor-scale rule s_t = amax / (6 * 448) and the fp32 operation order are
+ *    a reading; no page prints an NVFP4 worked example, so the composed
+ *    sequence is pinned only by invariants.
+ */
+#include "mx_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Element and scale formats                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* bf16 = the high 16 bits of an IEEE binary32. */
+double mxo_bf16_value(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* E2M1 ("Fundamentos matematicos do formato MXFP4 e E8M0"): 1 sign bit,
+ * 2 exponent bits with bias 1, 1 explicit mantissa bit. Exponent field 0 is
+ * subnormal. */
+double mxo_e2m1_value(uint8_t code) {
+  int s = (code >> 3) & 1;
+  int e = (code >> 1) & 3;
+  int m = code & 1;
+  double v;
+  if (e == 0)
+    v = ldexp(m / 2.0, 1 - 1); /* 2^(1-bias) * 0.m */
+  else
+    v = ldexp(1.0 + m / 2.0, e - 1); /* 2^(e-bias) * 1.m */
+  return s ? -v : v;
+}
+
+/* FP8 E4M3 (OCP "fn" variant: no Inf, S.1111.111 is NaN, max 448 as in the
+ * format table): exponent bias 7, 3 mantissa bits, field 0 is subnormal. */
+double mxo_e4m3_value(uint8_t code) {
+  int s = (code >> 7) & 1;
+  int e = (code >> 3) & 15;
+  int m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, 1 - 7);
+  else
+    v = ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* E8M0: an unsigned power of two, 2^(E-127). E = 255 is the format's NaN
+ * (2^128 is not finite in fp32 either). */
+double mxo_e8m0_value(uint8_t e) {
+  if (e == 255) return NAN;
+  return ldexp(1.0, (int)e - 127);
+}
+
+/* Nearest magnitude in a sorted code table, ties to the code with a clear LSB
+ * (the even mantissa), saturating at the top code. Codes 0..ncodes-1 are the
+ * non-negative values in increasing order. */
+static int nearest_code(double a, double (*value)(uint8_t), int ncodes) {
+  double top = value((uint8_t)(ncodes - 1));
+  if (a >= top) return ncodes - 1; /* includes +Inf: saturate */
+  int best = 0;
+  double bestd = fabs(a - value(0));
+  for (int c = 1; c < ncodes; c++) {
+    double d = fabs(a - value((uint8_t)c));
+    if (d < bestd || (d == bestd && (c & 1) == 0)) {
+      best = c;
+      bestd = d;
+    }
+  }
+  return best;
+}
+
+uint8_t mxo_encode_e2m1(double v) {
+  int neg = signbit(v) ? 1 : 0;
+  int c = nearest_code(fabs(v), mxo_e2m1_value, 8);
+  return (uint8_t)((neg << 3) | c);
+}
+
+uint8_t mxo_encode_e4m3(double v) {
+  int neg = signbit(v) ? 1 : 0;
+  int c = nearest_code(fabs(v), mxo_e4m3_value, 127); /* 0x00..0x7E finite */
+  return (uint8_t)((neg << 7) | c);
+}
+
+/* bf16 nearest-even: keep the high half, adding half an ulp plus the LSB of
+ * the kept part so that exact halves go to the even neighbour. */
+uint16_t mxo_f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+/* Shared-exponent rule (FAQ, "Como o formato E8M0 calcula o expoente"):
+ * E = ceil(log2(amax / emax)) + 127, i.e. 127 + the smallest integer n with
+ * amax <= emax * 2^n, so no element of the block exceeds the element format's
+ * ceiling after scaling. amax = 0 has no such smallest n (log2 -> -inf); the
+ * clamp to the format's range [0, 254] gives E = 0. Evaluated by search, with
+ * exact power-of-two products, not with a logarithm. */
+int mxo_mx_scale_exponent(double amax, double emax) {
+  if (!isfinite(amax)) return 255;
+  if (amax == 0.0) return 0;
+  int n = -300;
+  while (!(amax <= ldexp(emax, n))) n++;
+  int E = n + 127;
+  if (E < 0) E = 0;
+  if (E > 254) E = 254;
+  return E;
+}
+
+static int elem_bits(int fmt) {
+  return (fmt == MXO_FMT_MXFP8) ? 8 : 4;
+}
+
+static int fmt_block(int fmt) {
+  return (fmt == MXO_FMT_NVFP4) ? 16 : 32;
+}
+
+/* 4 bits per element plus 8 bits per 32-element block is the page's
+ * "4 + 8/32 = 4.25 bits per element". */
+int64_t mxo_storage_bytes(int fmt, int64_t rows, int64_t cols) {
+  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_NVFP4) return -1;
+  int64_t n = rows * cols;
+  int64_t code_bytes = n * elem_bits(fmt) / 8;
+  int64_t scale_bytes = n / fmt_block(fmt);
+  return code_bytes + scale_bytes + (fmt == MXO_FMT_NVFP4 ? 4 : 0);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Quantize                                                                   */
+/* ------------------------------------------------------------------------ */
+
+static void put_code(uint8_t* codes, int fmt, int64_t idx, uint8_t code) {
+  if (fmt == MXO_FMT_MXFP8) {
+    codes[idx] = code;
+  } else {
+    uint8_t* byte = &codes[idx / 2];
+    if (idx % 2 == 0)
+      *byte = (uint8_t)((*byte & 0xF0) | (code & 0x0F));
+    else
+      *byte = (uint8_t)((*byte & 0x0F) | ((code & 0x0F) << 4));
+  }
+}
+
+static uint8_t get_code(const uint8_t* codes, int fmt, int64_t idx) {
+  if (fmt == MXO_FMT_MXFP8) return codes[idx];
+  uint8_t byte = codes[idx / 2];
+  return (idx % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+}
+
+static int bf16_is_finite(uint16_t bits) {
+  return ((bits >> 7) & 0xFF) != 0xFF;
+}
+
+/* MXFP4 / MXFP8: per 32-element block, E from the block amax, then each
+ * element divided by 2^(E-127) (exact in double) and rounded to the nearest
+ * element value. A block holding Inf or NaN gets the NaN scale and zero codes. */
+static void quantize_mx(int fmt, int64_t rows, int64_t cols, const uint16_t* x,
+                        uint8_t* codes, uint8_t* scales) {
+  const int B = 32;
+  const double emax = (fmt == MXO_FMT_MXFP4) ? 6.0 : 448.0;
+  for (int64_t r = 0; r < rows; r++) {
+    for (int64_t b = 0; b < cols / B; b++) {
+      const uint16_t* xb = x + r * cols + b * B;
+      int64_t first = r * cols + b * B;
+      int finite = 1;
+      double amax = 0.0;
+      for (int i = 0; i < B; i++) {
+        if (!bf16_is_finite(xb[i])) finite = 0;
+        double a = fabs(mxo_bf16_value(xb[i]));
+        if (a > amax) amax = a;
+      }
+      if (!finite) {
+        scales[r * (cols / B) + b] = 255;
+        for (int i = 0; i < B; i++) put_code(codes, fmt, first + i, 0);
+        continue;
+      }
+      int E = mxo_mx_scale_exponent(amax, emax);
+      scales[r * (cols / B) + b] = (uint8_t)E;
+      for (int i = 0; i < B; i++) {
+        double v = ldexp(mxo_bf16_value(xb[i]), 127 - E); /* x / 2^(E-127) */
+        uint8_t c = (fmt == MXO_FMT_MXFP4) ? mxo_encode_e2m1(v)
+                                           : mxo_encode_e4m3(v);
+        put_code(codes, fmt, first + i, c);
+      }
+    }
+  }
+}
+
+/* Nearest-even E2M1 code of x / D for D > 0 without forming the quotient:
+ * |x| is compared with each midpoint times D, all exact in double. */
+static uint8_t e2m1_nearest_scaled(double x, double D) {
+  double a = fabs(x);
+  int c = 0;
+  for (int k = 0; k < 7; k++) {
+    double mid = (mxo_e2m1_value((uint8_t)k) + mxo_e2m1_value((uint8_t)(k + 1))) / 2.0 * D;
+    if (a > mid || (a == mid && ((k + 1) & 1) == 0))
+      c = k + 1;
+    else
+      break;
+  }
+  return (uint8_t)((signbit(x) ? 8 : 0) | c);
+}
+
+/* NVFP4, fp32 throughout (one rounding per operation):
+ *  1. T = max |x| over the tensor.
+ *  2. s_t = T / 2688 (2688 = 6 * 448 maps T onto the largest E2M1 value times
+ *     the largest E4M3 scale); T = 0 gives s_t = 1.
+ *  3. per 16-block: s_b = E4M3 nearest-even, saturating, of amax_b / (6 s_t).
+ *  4. D = s_b * s_t; D = 0 gives sign-only zero codes.
+ *  5. code = E2M1 nearest-even, saturating, of x * (1 / D); x = +-0 gives +-0.
+ * A non-finite T gives s_t = NaN, NaN block scales and zero codes.
+ * exact_quotient != 0 replaces step 5 by the exact quotient x / (s_b s_t). */
+static void quantize_nvfp4(int64_t rows, int64_t cols, const uint16_t* x,
+                           uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                           int exact_quotient) {
+  const int B = 16;
+  const int64_t n = rows * cols;
+  float T = 0.0f;
+  int finite = 1;
+  for (int64_t i = 0; i < n; i++) {
+    if (!bf16_is_finite(x[i])) finite = 0;
+    float a = fabsf((float)mxo_bf16_value(x[i]));
+    if (a > T) T = a;
+  }
+  if (!finite) {
+    if (tensor_scale) *tensor_scale = NAN;
+    for (int64_t b = 0; b < n / B; b++) scales[b] = 0x7F;
+    for (int64_t i = 0; i < n; i++) put_code(codes, MXO_FMT_NVFP4, i, 0);
+    return;
+  }
+  const float s_t = (T == 0.0f) ? 1.0f : T / 2688.0f;
+  const float d6 = 6.0f * s_t;
+  if (tensor_scale) *tensor_scale = s_t;
+  for (int64_t b = 0; b < n / B; b++) {
+    const uint16_t* xb = x + b * B;
+    float bamax = 0.0f;
+    for (int i = 0; i < B; i++) {
+      float a = fabsf((float)mxo_bf16_value(xb[i]));
+      if (a > bamax) bamax = a;
+    }
+    float r = bamax / d6;
+    uint8_t sb = mxo_encode_e4m3((double)r);
+    scales[b] = sb;
+    float D = (float)mxo_e4m3_value(sb) * s_t;
+    float R = 1.0f / D;
+    for (int i = 0; i < B; i++) {
+      float xi = (float)mxo_bf16_value(xb[i]);
+      uint8_t c;
+      if (D == 0.0f || xi == 0.0f) {
+        c = signbit(xi) ? 0x8 : 0x0;
+      } else if (exact_quotient) {
+        c = e2m1_nearest_scaled((double)xi, (double)mxo_e4m3_value(sb) * (double)s_t);
+      } else {
+        float q = xi * R;
+        c = mxo_encode_e2m1((double)q);
+      }
+      put_code(codes, MXO_FMT_NVFP4, b * B + i, c);
+    }
+  }
+}
+
+int mxo_quantize(int fmt, int block, int64_t rows, int64_t cols,
+                 const uint16_t* x, uint8_t* codes, uint8_t* scales,
+                 float* tensor_scale) {
+  if (rows <= 0 || cols <= 0 || !x || !codes || !scales) return MXO_ERR_ARG;
+  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_NVFP4) return MXO_ERR_ARG;
+  if (block != fmt_block(fmt) || cols % block != 0) return MXO_ERR_ARG;
+  if (fmt == MXO_FMT_MXFP4 || fmt == MXO_FMT_MXFP8) {
+    quantize_mx(fmt, rows, cols, x, codes, scales);
+    if (tensor_scale) *tensor_scale = 1.0f;
+  } else {
+    quantize_nvfp4(rows, cols, x, codes, scales, tensor_scale, 0);
+  }
+  return MXO_OK;
+}
+
+int mxo_quantize_nvfp4_exact_quotient(int64_t rows, int64_t cols,
+                                      const uint16_t* x, uint8_t* codes,
+                                      uint8_t* scales, float* tensor_scale) {
+  if (rows <= 0 || cols <= 0 || cols % 16 != 0 || !x || !codes || !scales)
+    return MXO_ERR_ARG;
+  quantize_nvfp4(rows, cols, x, codes, scales, tensor_scale, 1);
+  return MXO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dequantize                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Exact dequantized value of element idx (row-major), in double.
+ * MX: element value * 2^(E-127) (x_real = S * x_elem). NVFP4: e * s_b * s_t,
+ * which needs at most 2 + 4 + 24 significant bits, so it is exact. */
+static double exact_value(int fmt, const uint8_t* codes, const uint8_t* scales,
+                          float ts, int64_t cols, int64_t idx) {
+  int block = fmt_block(fmt);
+  int64_t r = idx / cols, c = idx % cols;
+  uint8_t sc = scales[r * (cols / block) + c / block];
+  uint8_t code = get_code(codes, fmt, idx);
+  double e = (fmt == MXO_FMT_MXFP8) ? mxo_e4m3_value(code) : mxo_e2m1_value(code);
+  if (fmt == MXO_FMT_NVFP4) return e * mxo_e4m3_value(sc) * (double)ts;
+  return e * mxo_e8m0_value(sc);
+}
+
+int mxo_dequantize(int fmt, int block, int64_t rows, int64_t cols,
+                   const uint8_t* codes, const uint8_t* scales,
+                   float tensor_scale, int out_dtype, void* y) {
+  if (rows <= 0 || cols <= 0 || !codes || !scales || !y) return MXO_ERR_ARG;
+  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_NVFP4) return MXO_ERR_ARG;
+  if (block != fmt_block(fmt) || cols % block != 0) return MXO_ERR_ARG;
+  if (out_dtype != MXO_OUT_F32 && out_dtype != MXO_OUT_BF16) return MXO_ERR_ARG;
+  for (int64_t i = 0; i < rows * cols; i++) {
+    float f;
+    if (fmt == MXO_FMT_NVFP4) {
+      /* y = fl32(fl32(e * s_b) * s_t); the inner product is exact. */
+      int64_t r = i / cols, c = i % cols;
+      uint8_t sc = scales[r * (cols / block) + c / block];
+      float es = (float)(mxo_e2m1_value(get_code(codes, fmt, i)) * mxo_e4m3_value(sc));
+      f = es * tensor_scale;
+    } else {
+      f = (float)exact_value(fmt, codes, scales, 1.0f, cols, i);
+    }
+    if (out_dtype == MXO_OUT_F32)
+      ((float*)y)[i] = f;
+    else
+      ((uint16_t*)y)[i] = mxo_f32_to_bf16(f);
+  }
+  return MXO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* GEMM over exactly dequantized operands                                     */
+/* ------------------------------------------------------------------------ */
+
+static void dequant_row(int fmt, const void* data, const uint8_t* scales,
+                        float ts, int64_t K, int64_t row, double* out) {
+  if (fmt == MXO_FMT_BF16) {
+    const uint16_t* x = (const uint16_t*)data + row * K;
+    for (int64_t k = 0; k < K; k++) out[k] = mxo_bf16_value(x[k]);
+    return;
+  }
+  /* exact_value indexes the whole matrix; pass the row's element index. */
+  for (int64_t k = 0; k < K; k++)
+    out[k] = exact_value(fmt, (const uint8_t*)data, scales, ts, K, row * K + k);
+}
+
+static int gemm_args_ok(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
+                        const void* a, const uint8_t* a_scales, const void* b,
+                        const uint8_t* b_scales) {
+  if (M <= 0 || N <= 0 || K <= 0 || !a || !b) return 0;
+  if (fmt_a < MXO_FMT_BF16 || fmt_a > MXO_FMT_NVFP4) return 0;
+  if (fmt_b < MXO_FMT_MXFP4 || fmt_b > MXO_FMT_NVFP4) return 0;
+  if (fmt_a != MXO_FMT_BF16 && (!a_scales || K % fmt_block(fmt_a) != 0)) return 0;
+  if (!b_scales || K % fmt_block(fmt_b) != 0) return 0;
+  return 1;
+}
+
+static void dot_abs(const double* x, const double* y, int64_t K, double* c,
+                    double* s) {
+  double acc = 0.0, accabs = 0.0;
+  for (int64_t k = 0; k < K; k++) {
+    double p = x[k] * y[k];
+    acc += p;
+    accabs += fabs(p);
+  }
+  *c = acc;
+  *s = accabs;
+}
+
+int mxo_gemm(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
+             const void* a, const uint8_t* a_scales, float a_ts,
+             const void* b, const uint8_t* b_scales, float b_ts,
+             double* C, double* S) {
+  if (!gemm_args_ok(fmt_a, fmt_b, M, N, K, a, a_scales, b, b_scales) || !C || !S)
+    return MXO_ERR_ARG;
+  double* bt = (double*)malloc(sizeof(double) * (size_t)(N * K));
+  double* ar = (double*)malloc(sizeof(double) * (size_t)K);
+  if (!bt || !ar) {
+    free(bt);
+    free(ar);
+    return MXO_ERR_ARG;
+  }
+  for (int64_t j = 0; j < N; j++) dequant_row(fmt_b, b, b_scales, b_ts, K, j, bt + j * K);
+  for (int64_t i = 0; i < M; i++) {
+    dequant_row(fmt_a, a, a_scales, a_ts, K, i, ar);
+    for (int64_t j = 0; j < N; j++) dot_abs(ar, bt + j * K, K, &C[i * N + j], &S[i * N + j]);
+  }
+  free(bt);
+  free(ar);
+  return MXO_OK;
+}
+
+int mxo_gemm_entries(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
+                     const void* a, const uint8_t* a_scales, float a_ts,
+                     const void* b, const uint8_t* b_scales, float b_ts,
+                     int64_t n_entries, const int64_t* ii, const int64_t* jj,
+                     double* C, double* S) {
+  if (!gemm_args_ok(fmt_a, fmt_b, M, N, K, a, a_scales, b, b_scales) || !C || !S ||
+      n_entries < 0 || (n_entries > 0 && (!ii || !jj)))
+    return MXO_ERR_ARG;
+  for (int64_t t = 0; t < n_entries; t++)
+    if (ii[t] < 0 || ii[t] >= M || jj[t] < 0 || jj[t] >= N) return MXO_ERR_ARG;
+  double* ar = (double*)malloc(sizeof(double) * (size_t)K);
+  double* br = (double*)malloc(sizeof(double) * (size_t)K);
+  if (!ar || !br) {
+    free(ar);
+    free(br);
+    return MXO_ERR_ARG;
+  }
+  for (int64_t t = 0; t < n_entries; t++) {
+    dequant_row(fmt_a, a, a_scales, a_ts, K, ii[t], ar);
+    dequant_row(fmt_b, b, b_scales, b_ts, K, jj[t], br);
+    dot_abs(ar, br, K, &C[t], &S[t]);
+  }
+  free(ar);
+  free(br);
+  return MXO_OK;
+}

@@ -1,0 +1,105 @@
+/*
+ * mx_oracle.h -- plain CPU reference ("oracle") for microscaling block
+ * quantization (MXFP4, MXFP8, NVFP4) and the block-scaled GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load or call this library. The GPU
+ * library shares no code, header, table or constant with it, and never calls it.
+ *
+ * Every routine works on host memory, computes in double unless the method
+ * fixes fp32 (the NVFP4 sequence), and is written for clarity, not speed.
+ *
+ * Sources (web pages on microscaling formats):
+ *  - "Microscaling MXFP4/NVFP4 on Blackwell for reasoning LLMs"
+ *    (produtoramaxvision.com.br), sections "Fundamentos matematicos do formato
+ *    MXFP4 e E8M0" (E2M1 layout and value set, E8M0 = 2^(E-127),
+ *    x_real = S * x_elem, 4.25 effective bits), the format table (FP8 E4M3
+ *    range +-448, NVFP4 row) and the FAQ answer on the shared exponent
+ *    (E = ceil(log2(max|x| / max_E2M1)) + 127).
+ *  - zubnet.ai news summary: NVFP4 = E2M1 in 16-element blocks; MXFP8 =
+ *    E4M3/E5M2 in 32-element blocks.
+ *  - gist.science summary of "Unveiling the Potential of Quantization with
+ *    MXFP4", section 2.A: the standard MX rule maps the block amax into (3, 6];
+ *    NVFP4 scales carry a mantissa.
+ */
+#ifndef MX_ORACLE_H
+#define MX_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Format identifiers (numbered like the GPU library's, but defined here
+ * independently). */
+enum {
+  MXO_FMT_BF16 = 0,  /* plain bf16, no scales (activation side of W4A16) */
+  MXO_FMT_MXFP4 = 1, /* E2M1 codes, one E8M0 scale per 32 elements */
+  MXO_FMT_MXFP8 = 2, /* E4M3 codes, one E8M0 scale per 32 elements */
+  MXO_FMT_NVFP4 = 3  /* E2M1 codes, one E4M3 scale per 16, fp32 tensor scale */
+};
+enum { MXO_OUT_F32 = 0, MXO_OUT_BF16 = 1 };
+enum { MXO_OK = 0, MXO_ERR_ARG = 1 };
+
+/* ---- element and scale formats (decoded from their bit-field definitions) */
+double mxo_bf16_value(uint16_t bits);
+double mxo_e2m1_value(uint8_t code);  /* low 4 bits used */
+double mxo_e4m3_value(uint8_t code);  /* 0x7F / 0xFF -> NaN */
+double mxo_e8m0_value(uint8_t e);     /* 255 -> NaN */
+
+/* Nearest representable value, ties to the even code, saturating at the
+ * largest magnitude; the sign bit of v is copied (so -0 encodes as -0). */
+uint8_t mxo_encode_e2m1(double v);
+uint8_t mxo_encode_e4m3(double v);
+
+/* Round a float to bf16, nearest-even (NaN stays NaN, overflow goes to Inf). */
+uint16_t mxo_f32_to_bf16(float f);
+
+/* MX shared exponent for a block amax: the smallest integer n with
+ * amax <= emax * 2^n, biased by 127 and clamped to [0, 254]; 255 (NaN) for a
+ * non-finite amax. emax = 6 (E2M1) or 448 (E4M3). */
+int mxo_mx_scale_exponent(double amax, double emax);
+
+/* Bytes of codes + scales (+4 for the NVFP4 tensor scale). */
+int64_t mxo_storage_bytes(int fmt, int64_t rows, int64_t cols);
+
+/* ---- tensor operations, row-major, blocks along cols ------------------- */
+/* x: bf16 bits [rows][cols]; codes: [rows][cols/2] (FP4, even element in the
+ * low nibble) or [rows][cols] (FP8); scales: [rows][cols/block] bytes;
+ * tensor_scale: NVFP4 only (written), may be NULL otherwise. */
+int mxo_quantize(int fmt, int block, int64_t rows, int64_t cols,
+                 const uint16_t* x, uint8_t* codes, uint8_t* scales,
+                 float* tensor_scale);
+
+/* NVFP4 only, information: codes from the exact quotient x / (s_b * s_t)
+ * instead of the fp32 reciprocal sequence; scales are as mxo_quantize's. */
+int mxo_quantize_nvfp4_exact_quotient(int64_t rows, int64_t cols,
+                                      const uint16_t* x, uint8_t* codes,
+                                      uint8_t* scales, float* tensor_scale);
+
+/* y: float [rows][cols] (MXO_OUT_F32) or bf16 bits (MXO_OUT_BF16). */
+int mxo_dequantize(int fmt, int block, int64_t rows, int64_t cols,
+                   const uint8_t* codes, const uint8_t* scales,
+                   float tensor_scale, int out_dtype, void* y);
+
+/* C[i][j] = sum_k a[i][k] * b[j][k] and S[i][j] = sum_k |a[i][k] * b[j][k]|,
+ * both in double, over exactly dequantized operands. A is M x K (fmt_a;
+ * MXO_FMT_BF16 means bf16 bits, no scales), B is stored N x K (fmt_b). */
+int mxo_gemm(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
+             const void* a, const uint8_t* a_scales, float a_ts,
+             const void* b, const uint8_t* b_scales, float b_ts,
+             double* C, double* S);
+
+/* Same definition, only for the listed (ii[t], jj[t]) output entries. */
+int mxo_gemm_entries(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
+                     const void* a, const uint8_t* a_scales, float a_ts,
+                     const void* b, const uint8_t* b_scales, float b_ts,
+                     int64_t n_entries, const int64_t* ii, const int64_t* jj,
+                     double* C, double* S);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MX_ORACLE_H */
