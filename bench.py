@@ -1,0 +1,200 @@
+"""Benchmark of the microscaling hot path on one MI355X.
+
+Default workload: the MXFP4 W4A4 DiT MLP-down layer, M=4608 tokens, K=12288,
+N=3072, activations Laplace(0,1) with 0.5% outlier channels x100, weights
+N(0,0.02) quantized beforehand. One step = quantize the bf16 activations to
+MXFP4 (codes + E8M0 scales) and run the block-scaled GEMM against the
+pre-quantized weights, bf16 output. Everything in the timed region runs in
+libmx's HIP kernels; inputs are resident in HBM before timing starts.
+
+Prints one JSON line. `value` is whole-step throughput, 2MNK / step time, in
+TFLOP/s. The `roofline` object is for the dominant kernel (the GEMM), timed
+with HIP events on its own stream; `quantize` reports the activation
+quantizer's algorithmic GB/s; `cpu_baseline` times the oracle on a bounded
+sample of the same step on the host.
+
+Other workloads (--workload c1..c5) are for profiling; the default is the one
+the headline metric is quoted on.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks.
+PEAK_HBM_GBPS = 8000.0
+PEAK_TFLOPS = {"mxfp4": 10100.0, "mxfp8": 5000.0, "nvfp4": 2500.0, "w4a16": 2500.0}
+ROTATE_BYTES = 1 << 30  # activation copies cycled per step: > 256 MB MALL
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="c4")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=32,
+                   help="activation rows in the oracle's CPU sample")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the kernels "
+              "and their measurement are single-GPU in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import microscaling_precision_quantization_amd as mx
+    import synth
+
+    name = synth.ALIASES.get(args.workload, args.workload)
+    w = synth.WORKLOADS[name]
+    fmt, M, N, K = w["fmt"], w["M"], w["N"], w["K"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    A_bits, B_bits = synth.workload(name)
+    gen_s = time.time() - t0
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    A = to_dev(A_bits)
+    Bx = to_dev(B_bits)
+    wfmt = "mxfp4" if fmt == "w4a16" else fmt
+    qb = mx.quantize(Bx, wfmt)  # weights: pre-quantized, outside the timed step
+    del Bx
+    ncopies = max(1, min(8, ROTATE_BYTES // A.numel() // 2))
+    acts = [A] + [A.clone() for _ in range(ncopies - 1)]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    wsb = mx.mx_gemm_workspace_bytes(mx.FORMATS.get(fmt, mx.MX_FMT_BF16) if fmt != "w4a16" else mx.MX_FMT_BF16,
+                                     mx.FORMATS[wfmt], M, N, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    quantize_a = fmt != "w4a16"
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        a = acts[i % len(acts)]
+        if ev is not None:
+            ev[0].record(stream)
+        if quantize_a:
+            qa = mx.quantize(a, fmt)
+        else:
+            qa = a
+        if ev is not None:
+            ev[1].record(stream)
+        mx.gemm(qa, qb, torch.bfloat16, out=out, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    q_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    g_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    q_avg = sum(q_ms) / len(q_ms)
+    g_avg = sum(g_ms) / len(g_ms)
+
+    flops = 2.0 * M * N * K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    gemm_tflops = flops / (g_avg * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[fmt]
+    # Algorithmic bytes of the quantizer: read bf16 once, write codes + scales.
+    elem_bytes = {"mxfp4": 0.5 + 1 / 32, "mxfp8": 1 + 1 / 32, "nvfp4": 0.5 + 1 / 16}
+    q_bytes = M * K * (2 + elem_bytes.get(fmt, 0)) + (4 if fmt == "nvfp4" else 0)
+
+    if fmt == "w4a16":
+        # Decode GEMM is HBM-bound: algorithmic bytes = weights + scales +
+        # activations + output.
+        g_bytes = N * K / 2 + N * K / 32 + M * K * 2 + M * N * 2
+        roof = {"bound": "hbm", "achieved": g_bytes / (g_avg * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel_ms"] = g_avg
+
+    line = {
+        "metric": "block-scaled GEMM TFLOP/s + quantize GB/s, % of MXFP4/FP8 MFMA & HBM peak",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"mxfp4": "e2m1+e8m0 (fp32 accumulate)", "mxfp8": "e4m3+e8m0 (fp32 accumulate)",
+                  "nvfp4": "e2m1+e4m3 via bf16 (fp32 accumulate)",
+                  "w4a16": "bf16 x e2m1+e8m0 (fp32 accumulate)"}[fmt],
+        "data": "synthetic",
+        "config": {"workload": name, "format": fmt, "M": M, "N": N, "K": K,
+                   "step": ("quantize(A) + gemm" if quantize_a else "gemm") + ", bf16 out",
+                   "weights": "pre-quantized", "activation_copies_rotated": len(acts)},
+        "roofline": roof,
+        "gemm": {"TFLOP/s": gemm_tflops, "ms": g_avg, "frac_of_peak": gemm_tflops / peak},
+    }
+    if quantize_a:
+        q_gbps = q_bytes / (q_avg * 1e-3) / 1e9
+        line["quantize"] = {"GB/s": q_gbps, "ms": q_avg, "frac_of_hbm": q_gbps / PEAK_HBM_GBPS,
+                            "algorithmic_bytes": q_bytes}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(name, fmt, A_bits, qb, M, N, K, args.cpu_rows)
+    line["input_gen_s"] = round(gen_s, 2)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(name, fmt, A_bits, qb, M, N, K, rows):
+    """The oracle (single-threaded C) on the first `rows` activation rows of the
+    same step: quantize those rows, then their GEMM against all N weight rows
+    (exact operands, double accumulation). Scaled to TFLOP/s of 2*rows*N*K."""
+    import numpy as np
+
+    import oracle as orc
+    ofmt = {"mxfp4": orc.FMT_MXFP4, "mxfp8": orc.FMT_MXFP8, "nvfp4": orc.FMT_NVFP4,
+            "w4a16": orc.FMT_BF16}[fmt]
+    bcodes = qb.codes.cpu().numpy()
+    bscales = qb.scales.cpu().numpy()
+    bts = float(qb.tensor_scale.cpu().numpy()[0]) if qb.tensor_scale is not None else 1.0
+    a = np.ascontiguousarray(A_bits[:rows])
+    t0 = time.perf_counter()
+    if ofmt == orc.FMT_BF16:
+        ac, asc, ats = a, None, 1.0
+        fb = orc.FMT_MXFP4
+    else:
+        ac, asc, ats = orc.quantize(ofmt, a)
+        fb = ofmt
+    orc.gemm(ofmt, fb, rows, N, K, ac, asc, ats, bcodes, bscales, bts)
+    dt = time.perf_counter() - t0
+    return {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"first {rows} of {M} activation rows: oracle quantize + exact GEMM against "
+                      f"all {N} weight rows, K={K}, one thread"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,150 @@
+/*
+ * mx.h -- C ABI of libmx: microscaling (MX / NVFP4) block quantization and the
+ * block-scaled GEMM on AMD Instinct MI355X (gfx950).
+ *
+ * Formats (pages: "Microscaling MXFP4/NVFP4 on Blackwell for reasoning LLMs",
+ * section "Fundamentos matematicos do formato MXFP4 e E8M0" and its format
+ * table; zubnet.ai summary, opening paragraph):
+ *   MXFP4  E2M1 element codes, one E8M0 scale 2^(E-127) per 32 elements.
+ *   MXFP8  E4M3 (OCP, max 448) element codes, one E8M0 scale per 32.
+ *   NVFP4  E2M1 element codes, one E4M3 scale per 16 elements, plus one fp32
+ *          scale for the whole tensor (x ~ e * s_b * s_t).
+ *
+ * Layouts (all row-major, blocks run along the contiguous "cols"/K axis):
+ *   x       bf16 [rows][cols]
+ *   codes   FP4: uint8 [rows][cols/2], element 2j in bits 3:0 of byte j and
+ *                element 2j+1 in bits 7:4;   FP8: uint8 [rows][cols]
+ *   scales  uint8 [rows][cols/block]: E8M0 exponent byte (MX) or E4M3 code
+ *           (NVFP4)
+ *   GEMM    A is M x K, B is stored N x K (the Linear weight layout, K
+ *           contiguous), C is M x N with leading dimension ldc.
+ *
+ * Ownership and threading: every pointer is a device pointer owned by the
+ * caller, unless stated otherwise. The library never allocates or frees
+ * memory and never synchronizes. Work is enqueued on `stream` (a hipStream_t;
+ * NULL is the default stream) and the call returns at once. Calls keep no state
+ * between them and may be made from several threads at once.
+ *
+ * Errors: every argument is checked before anything is launched.
+ *   MX_ERR_INVALID_ARG  null pointer, a size <= 0, cols or K not a multiple of
+ *                       the block, a pointer not 16-byte aligned, ldc < N, or
+ *                       workspace_bytes below the size the call needs.
+ *   MX_ERR_UNSUPPORTED  a format/block pair or format combination outside the
+ *                       list below, a rounding mode other than MX_ROUND_RNE,
+ *                       an unknown output dtype.
+ *   MX_ERR_HIP          a HIP launch failed; mx_last_hip_error() returns the
+ *                       hipError_t (per calling thread).
+ * Nothing is printed and no C++ exception crosses this interface.
+ */
+#ifndef MX_H
+#define MX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MX_FMT_BF16 = 0,  /* plain bf16 (only as the A operand of a W4A16 GEMM) */
+  MX_FMT_MXFP4 = 1, /* E2M1 + E8M0 per 32 */
+  MX_FMT_MXFP8 = 2, /* E4M3 + E8M0 per 32 */
+  MX_FMT_NVFP4 = 3  /* E2M1 + E4M3 per 16 + fp32 tensor scale */
+} mx_format;
+
+typedef enum { MX_ROUND_RNE = 0 } mx_round; /* nearest, ties to even */
+
+typedef enum { MX_OUT_F32 = 0, MX_OUT_BF16 = 1 } mx_dtype;
+
+typedef enum {
+  MX_OK = 0,
+  MX_ERR_INVALID_ARG = 1,
+  MX_ERR_UNSUPPORTED = 2,
+  MX_ERR_HIP = 3
+} mx_status;
+
+/*
+ * Block quantization (the shared-exponent rule of the FAQ on the
+ * produtoramaxvision page; x_real = 2^(E-127) * x_elem).
+ *   MXFP4/MXFP8 (block 32): per block, E = ceil(log2(amax / emax)) + 127
+ *     clamped to [0, 254] with emax = 6 (E2M1) or 448 (E4M3), evaluated
+ *     exactly from the bf16 bits of amax; each element is x / 2^(E-127)
+ *     rounded to nearest-even with saturation, sign copied (-0 stays -0).
+ *     A block holding Inf/NaN gets scale 255 (E8M0 NaN) and zero codes.
+ *   NVFP4 (block 16), fp32 arithmetic, one rounding per step:
+ *     T = max|x| over the tensor; s_t = T / 2688 (1 if T = 0);
+ *     s_b = E4M3(amax_b / (6 s_t)) nearest-even, saturating at 448;
+ *     D = s_b * s_t; code = E2M1(x * (1/D)) nearest-even, saturating; a zero
+ *     x or D = 0 gives a signed zero code. Non-finite T: s_t = NaN, every
+ *     block scale 0x7F (E4M3 NaN), every code 0.
+ * x: bf16 [rows][cols]; codes, scales: outputs as in the layout above.
+ * tensor_scale: NVFP4 only, one device fp32 written with s_t; NULL otherwise.
+ * workspace: NVFP4 only, device scratch of at least
+ *   mx_quantize_workspace_bytes(...) bytes (contents need no initialization);
+ *   may be NULL with workspace_bytes 0 for MX formats.
+ */
+mx_status mx_quantize(mx_format fmt, int block, mx_round rnd, int64_t rows, int64_t cols,
+                      const void* x, void* codes, void* scales, float* tensor_scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+size_t mx_quantize_workspace_bytes(mx_format fmt, int64_t rows, int64_t cols);
+
+/*
+ * Dequantization (x_real = S * x_elem on the produtoramaxvision page): MX
+ * y = val(code) * 2^(E-127); NVFP4 y = fl32(fl32(val(code) * s_b) * s_t).
+ * The fp32 value is the output for MX_OUT_F32; MX_OUT_BF16 rounds it to bf16,
+ * nearest-even (overflow gives Inf; E = 255 or an E4M3 NaN scale gives NaN).
+ * tensor_scale: NVFP4 only, device pointer to one fp32; NULL otherwise.
+ * y: [rows][cols] fp32 or bf16.
+ */
+mx_status mx_dequantize(mx_format fmt, int block, mx_round rnd, int64_t rows, int64_t cols,
+                        const void* codes, const void* scales, const float* tensor_scale,
+                        mx_dtype out_dtype, void* y, void* stream);
+
+/*
+ * Block-scaled GEMM, C = A * B^T over the dequantized operands, fp32
+ * accumulation (the block-scaled dot product of the produtoramaxvision page,
+ * section "Arquitetura Blackwell SM100 e aceleracao nativa de NVFP4": scales
+ * are applied during FP32 accumulation, with no up-conversion of the operands).
+ * Supported (fmt_a, fmt_b, block):
+ *   (MXFP4, MXFP4, 32)  W4A4 on the FP4 scaled MFMA (codes and E8M0 scales go
+ *                       to the matrix core as stored)
+ *   (MXFP8, MXFP8, 32)  W8A8: e * 2^(E-127) is exact in bf16 and runs on the
+ *                       bf16 MFMA (the FP8 scaled MFMA truncates block sums
+ *                       beyond the accuracy bound below)
+ *   (NVFP4, NVFP4, 16)  W4A4 with E4M3 block scales; e * s_b is exact in bf16,
+ *                       so the product runs on bf16 MFMA and s_t^A * s_t^B is
+ *                       applied to the fp32 result
+ *   (BF16,  MXFP4, 32)  W4A16: bf16 activations times MXFP4 weights expanded
+ *                       exactly to bf16 (weight-only quantization)
+ * a: codes (or bf16 for MX_FMT_BF16) [M][...]; a_scales [M][K/block] (NULL for
+ * BF16); a_ts, b_ts: NVFP4 tensor scales (device fp32), NULL otherwise.
+ * b: codes [N][...]; b_scales [N][K/block].
+ * c: [M][ldc] fp32 or bf16 (rnd rounds the bf16 epilogue).
+ * workspace: device scratch of at least mx_gemm_workspace_bytes(...) bytes
+ * (may be NULL when that is 0).
+ * K must be a multiple of 32 for every pair. Accuracy: each fp32 output is
+ * within 2^-18 * sum_k |a_ik b_jk| of the exact sum over the dequantized
+ * operands (a bf16 output adds its own rounding), provided no product or
+ * partial sum leaves fp32's range.
+ */
+mx_status mx_gemm(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd,
+                  int64_t M, int64_t N, int64_t K,
+                  const void* a, const void* a_scales, const float* a_ts,
+                  const void* b, const void* b_scales, const float* b_ts,
+                  mx_dtype out_dtype, void* c, int64_t ldc,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+size_t mx_gemm_workspace_bytes(mx_format fmt_a, mx_format fmt_b, int64_t M, int64_t N, int64_t K);
+
+/* hipError_t saved by the last MX_ERR_HIP returned on the calling thread. */
+int mx_last_hip_error(void);
+
+/* Static, human-readable name of a status. */
+const char* mx_status_string(mx_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MX_H */

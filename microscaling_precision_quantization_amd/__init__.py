@@ -1,0 +1,203 @@
+"""Python binding for libmx: microscaling (MX / NVFP4) quantization and the
+block-scaled GEMM on AMD Instinct MI355X (gfx950).
+
+Two layers:
+  * mx_quantize, mx_dequantize, mx_gemm, ... : the C ABI (include/mx.h) under
+    the same names, taking integers and raw device pointers;
+  * quantize, dequantize, gemm : torch conveniences that allocate outputs on
+    the input's device and pass data_ptr() plus the current HIP stream.
+
+Every step of the computation runs in libmx's HIP kernels. If libmx.so is not
+built, loading fails with an error; there is no fallback path.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmx.so")
+
+MX_FMT_BF16, MX_FMT_MXFP4, MX_FMT_MXFP8, MX_FMT_NVFP4 = 0, 1, 2, 3
+MX_ROUND_RNE = 0
+MX_OUT_F32, MX_OUT_BF16 = 0, 1
+MX_OK, MX_ERR_INVALID_ARG, MX_ERR_UNSUPPORTED, MX_ERR_HIP = 0, 1, 2, 3
+
+FORMATS = {"mxfp4": MX_FMT_MXFP4, "mxfp8": MX_FMT_MXFP8, "nvfp4": MX_FMT_NVFP4, "bf16": MX_FMT_BF16}
+BLOCK = {MX_FMT_MXFP4: 32, MX_FMT_MXFP8: 32, MX_FMT_NVFP4: 16, MX_FMT_BF16: 32}
+
+# Symbols declared in include/mx.h.
+EXPORTS = ("mx_quantize", "mx_quantize_workspace_bytes", "mx_dequantize", "mx_gemm",
+           "mx_gemm_workspace_bytes", "mx_last_hip_error", "mx_status_string")
+
+_lib = None
+
+
+class MXError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        msg = f"{what}: {status_string(status)}"
+        if status == MX_ERR_HIP:
+            msg += f" (hipError_t {mx_last_hip_error()})"
+        super().__init__(msg)
+
+
+def lib():
+    """Load libmx.so (built by build.py). Raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "microscaling_precision_quantization_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        L.mx_quantize.restype = i32
+        L.mx_quantize.argtypes = [i32, i32, i32, i64, i64, P, P, P, P, P, sz, P]
+        L.mx_quantize_workspace_bytes.restype = sz
+        L.mx_quantize_workspace_bytes.argtypes = [i32, i64, i64]
+        L.mx_dequantize.restype = i32
+        L.mx_dequantize.argtypes = [i32, i32, i32, i64, i64, P, P, P, i32, P, P]
+        L.mx_gemm.restype = i32
+        L.mx_gemm.argtypes = [i32, i32, i32, i32, i64, i64, i64, P, P, P, P, P, P, i32, P, i64,
+                              P, sz, P]
+        L.mx_gemm_workspace_bytes.restype = sz
+        L.mx_gemm_workspace_bytes.argtypes = [i32, i32, i64, i64, i64]
+        L.mx_last_hip_error.restype = i32
+        L.mx_last_hip_error.argtypes = []
+        L.mx_status_string.restype = ctypes.c_char_p
+        L.mx_status_string.argtypes = [i32]
+        _lib = L
+    return _lib
+
+
+# ---- the C ABI, same names ---------------------------------------------------
+def mx_quantize(fmt, block, rnd, rows, cols, x, codes, scales, tensor_scale, workspace,
+                workspace_bytes, stream):
+    return lib().mx_quantize(fmt, block, rnd, rows, cols, x, codes, scales, tensor_scale,
+                             workspace, workspace_bytes, stream)
+
+
+def mx_quantize_workspace_bytes(fmt, rows, cols):
+    return lib().mx_quantize_workspace_bytes(fmt, rows, cols)
+
+
+def mx_dequantize(fmt, block, rnd, rows, cols, codes, scales, tensor_scale, out_dtype, y, stream):
+    return lib().mx_dequantize(fmt, block, rnd, rows, cols, codes, scales, tensor_scale,
+                               out_dtype, y, stream)
+
+
+def mx_gemm(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts, out_dtype,
+            c, ldc, workspace, workspace_bytes, stream):
+    return lib().mx_gemm(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts,
+                         out_dtype, c, ldc, workspace, workspace_bytes, stream)
+
+
+def mx_gemm_workspace_bytes(fmt_a, fmt_b, M, N, K):
+    return lib().mx_gemm_workspace_bytes(fmt_a, fmt_b, M, N, K)
+
+
+def mx_last_hip_error():
+    return lib().mx_last_hip_error()
+
+
+def mx_status_string(status):
+    return lib().mx_status_string(status).decode()
+
+
+def status_string(status):
+    return mx_status_string(status)
+
+
+# ---- torch conveniences --------------------------------------------------------
+@dataclass
+class QTensor:
+    """A block-quantized [rows][cols] tensor: codes, scales and (NVFP4) the
+    fp32 tensor scale, all device tensors."""
+    fmt: int
+    rows: int
+    cols: int
+    codes: "object"
+    scales: "object"
+    tensor_scale: "object" = None
+
+    @property
+    def block(self):
+        return BLOCK[self.fmt]
+
+
+def _fmt_id(fmt):
+    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def _stream(torch, device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(status, what):
+    if status != MX_OK:
+        raise MXError(status, what)
+
+
+def quantize(x, fmt):
+    """Quantize a contiguous bf16 [rows][cols] device tensor."""
+    import torch
+    f = _fmt_id(fmt)
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("quantize expects a contiguous 2-D bfloat16 tensor")
+    rows, cols = x.shape
+    dev = x.device
+    codes = torch.empty((rows, cols if f == MX_FMT_MXFP8 else cols // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, cols // BLOCK[f]), dtype=torch.uint8, device=dev)
+    ts = ws = None
+    wsb = 0
+    if f == MX_FMT_NVFP4:
+        ts = torch.empty(1, dtype=torch.float32, device=dev)
+        wsb = mx_quantize_workspace_bytes(f, rows, cols)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    _check(mx_quantize(f, BLOCK[f], MX_ROUND_RNE, rows, cols, _ptr(x), _ptr(codes), _ptr(scales),
+                       _ptr(ts), _ptr(ws), wsb, _stream(torch, dev)), "mx_quantize")
+    return QTensor(f, rows, cols, codes, scales, ts)
+
+
+def dequantize(q, out_dtype=None):
+    """Expand a QTensor to float32 (default) or bfloat16."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    od = MX_OUT_F32 if out_dtype == torch.float32 else MX_OUT_BF16
+    y = torch.empty((q.rows, q.cols), dtype=out_dtype, device=q.codes.device)
+    _check(mx_dequantize(q.fmt, q.block, MX_ROUND_RNE, q.rows, q.cols, _ptr(q.codes),
+                         _ptr(q.scales), _ptr(q.tensor_scale), od, _ptr(y),
+                         _stream(torch, q.codes.device)), "mx_dequantize")
+    return y
+
+
+def gemm(a, b, out_dtype=None, out=None, workspace=None):
+    """C = A * B^T. a: QTensor (MXFP4/MXFP8/NVFP4, M x K) or a bf16 [M][K]
+    tensor (with an MXFP4 b: W4A16); b: QTensor stored N x K."""
+    import torch
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    od = MX_OUT_F32 if out_dtype == torch.float32 else MX_OUT_BF16
+    if isinstance(a, QTensor):
+        fa, M, K = a.fmt, a.rows, a.cols
+        pa, psa, pta = _ptr(a.codes), _ptr(a.scales), _ptr(a.tensor_scale)
+        dev = a.codes.device
+    else:
+        if a.dtype != torch.bfloat16 or a.dim() != 2 or not a.is_contiguous():
+            raise ValueError("bf16 activations must be a contiguous 2-D bfloat16 tensor")
+        fa, (M, K) = MX_FMT_BF16, a.shape
+        pa, psa, pta = _ptr(a), None, None
+        dev = a.device
+    N = b.rows
+    if b.cols != K:
+        raise ValueError(f"K mismatch: A has {K}, B has {b.cols}")
+    c = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=dev)
+    wsb = mx_gemm_workspace_bytes(fa, b.fmt, M, N, K)
+    if wsb and workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    _check(mx_gemm(fa, b.fmt, b.block, MX_ROUND_RNE, M, N, K, pa, psa, pta, _ptr(b.codes),
+                   _ptr(b.scales), _ptr(b.tensor_scale), od, _ptr(c), c.stride(0),
+                   _ptr(workspace), wsb, _stream(torch, dev)), "mx_gemm")
+    return c

@@ -1,0 +1,190 @@
+// Block-scaled GEMM for MXFP4 x MXFP4 and MXFP8 x MXFP8 on gfx950's scaled
+// MFMA (v_mfma_scale_f32_16x16x128_f8f6f4). C = A * B^T, A is M x K codes,
+// B is stored N x K codes, one E8M0 scale per 32 K per row. The matrix core
+// applies both E8M0 scales inside its fp32 accumulation, so codes go to the
+// instruction unexpanded (the block-scaled dot product described in
+// "Arquitetura Blackwell SM100 e aceleracao nativa de NVFP4" on the
+// produtoramaxvision page, there for B200 tensor cores).
+//
+// Operand layout of the 16x16x128 instruction (measured on gfx950): lane
+// l = r + 16 g (r = row in the 16-row tile, g = 0..3) supplies
+//   FP4: K elements [32g, 32g + 32) of row r, 16 bytes, even element in the low
+//        nibble (the same packing as the codes in memory);
+//   FP8: K elements [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16), 32 bytes;
+// and, for both, the E8M0 scale of K block g of row r. Output: lane l holds
+// column l % 16, rows 4 (l / 16) + 0..3.
+#include "mx_internal.h"
+
+namespace mx {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int BM = 128, BN = 128, BK = 128;  // tile sizes in elements
+constexpr uint32_t kUnitScale = 127u;        // 2^0 for padded blocks
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int FMT>
+struct MxTile {
+  static constexpr int kBits = (FMT == kMXFP4) ? 4 : 8;
+  static constexpr int kRowBytes = BK * kBits / 8;          // bytes per tile row per K step
+  static constexpr int kStride = kRowBytes + 16;            // padded LDS row
+  static constexpr int kChunksPerRow = kRowBytes / 16;
+  static constexpr int kLoads = BM * kChunksPerRow / kThreads;  // 16-byte loads per thread
+  static constexpr int kMfmaFmt = (FMT == kMXFP4) ? 4 : 0;  // cbsz / blgp selector
+};
+
+template <int FMT, int OUT>
+__global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __restrict__ A,
+                                                           const uint8_t* __restrict__ SA,
+                                                           const uint8_t* __restrict__ B,
+                                                           const uint8_t* __restrict__ SB,
+                                                           void* __restrict__ C, int64_t ldc,
+                                                           int M, int N, int K) {
+  using T = MxTile<FMT>;
+  __shared__ __attribute__((aligned(16))) uint8_t lA[BM * T::kStride];
+  __shared__ __attribute__((aligned(16))) uint8_t lB[BN * T::kStride];
+  __shared__ uint32_t lSA[BM];
+  __shared__ uint32_t lSB[BN];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int64_t rowbytes = (int64_t)K * T::kBits / 8;
+  const int kblocks = K / 32;
+  const int nk = (K + BK - 1) / BK;
+
+  u32x4 ra[T::kLoads], rb[T::kLoads];
+  uint32_t rs = 0;
+
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < T::kLoads; i++) {
+      const int chunk = tid + i * kThreads;
+      const int row = chunk / T::kChunksPerRow, c16 = chunk % T::kChunksPerRow;
+      const int64_t kb = (int64_t)kt * T::kRowBytes + c16 * 16;
+      const int ga = m0 + row, gb = n0 + row;
+      ra[i] = (ga < M && kb < rowbytes) ? *(const u32x4*)(A + ga * rowbytes + kb) : u32x4{0, 0, 0, 0};
+      rb[i] = (gb < N && kb < rowbytes) ? *(const u32x4*)(B + gb * rowbytes + kb) : u32x4{0, 0, 0, 0};
+    }
+    // Threads 0..127 fetch the 4 A-scale bytes of one tile row, 128..255 B's.
+    const int row = tid & 127;
+    const bool isA = tid < 128;
+    const int grow = (isA ? m0 : n0) + row;
+    const int glim = isA ? M : N;
+    const uint8_t* S = isA ? SA : SB;
+    rs = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int kbk = kt * 4 + j;
+      const uint32_t e = (grow < glim && kbk < kblocks) ? S[(int64_t)grow * kblocks + kbk] : kUnitScale;
+      rs |= e << (8 * j);
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < T::kLoads; i++) {
+      const int chunk = tid + i * kThreads;
+      const int row = chunk / T::kChunksPerRow, c16 = chunk % T::kChunksPerRow;
+      *(u32x4*)(lA + row * T::kStride + c16 * 16) = ra[i];
+      *(u32x4*)(lB + row * T::kStride + c16 * 16) = rb[i];
+    }
+    if (tid < 128)
+      lSA[tid] = rs;
+    else
+      lSB[tid - 128] = rs;
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0, 0, 0, 0};
+
+  const int r = lane & 15, g = lane >> 4;
+  gload(0);
+  for (int kt = 0; kt < nk; kt++) {
+    __syncthreads();
+    lstore();
+    __syncthreads();
+    if (kt + 1 < nk) gload(kt + 1);
+    i32x8 af[4], bf[4];
+    int sa[4], sb[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int ra_ = wm * 64 + i * 16 + r;
+      const int rb_ = wn * 64 + i * 16 + r;
+      if (FMT == kMXFP4) {
+        const u32x4 x = *(const u32x4*)(lA + ra_ * T::kStride + g * 16);
+        const u32x4 y = *(const u32x4*)(lB + rb_ * T::kStride + g * 16);
+        af[i] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+        bf[i] = i32x8{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
+      } else {
+        const u32x4 x0 = *(const u32x4*)(lA + ra_ * T::kStride + g * 16);
+        const u32x4 x1 = *(const u32x4*)(lA + ra_ * T::kStride + 64 + g * 16);
+        const u32x4 y0 = *(const u32x4*)(lB + rb_ * T::kStride + g * 16);
+        const u32x4 y1 = *(const u32x4*)(lB + rb_ * T::kStride + 64 + g * 16);
+        af[i] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        bf[i] = i32x8{(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w, (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
+      }
+      sa[i] = (int)((lSA[ra_] >> (8 * g)) & 0xFFu);
+      sb[i] = (int)((lSB[rb_] >> (8 * g)) & 0xFFu);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            af[i], bf[j], acc[i][j], T::kMfmaFmt, T::kMfmaFmt, 0, sa[i], 0, sb[j]);
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int col = n0 + wn * 64 + j * 16 + r;
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        const int row = m0 + wm * 64 + i * 16 + 4 * g + t;
+        if (row < M && col < N) {
+          if (OUT == kOutF32)
+            ((float*)C)[(int64_t)row * ldc + col] = acc[i][j][t];
+          else
+            ((uint16_t*)C)[(int64_t)row * ldc + col] = (uint16_t)bf16_rne(acc[i][j][t]);
+        }
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t gemm_mx(int fmt, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
+                   const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
+                   hipStream_t s) {
+  const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
+  const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
+                *SB = (const uint8_t*)sb;
+  const int m = (int)M, n = (int)N, k = (int)K;
+  if (fmt == kMXFP4) {
+    if (out_dtype == kOutF32)
+      gemm_mx_kernel<kMXFP4, kOutF32><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k);
+    else
+      gemm_mx_kernel<kMXFP4, kOutBF16><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k);
+  } else {
+    if (out_dtype == kOutF32)
+      gemm_mx_kernel<kMXFP8, kOutF32><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k);
+    else
+      gemm_mx_kernel<kMXFP8, kOutBF16><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mx

@@ -1,0 +1,150 @@
+// C ABI of libmx: argument checks, dispatch to the gfx950 kernels, and error
+// mapping. Every check runs before anything is enqueued; nothing here
+// allocates, synchronizes or prints.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "../../include/mx.h"
+#include "mx_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+bool is_quant_fmt(int f) { return f == MX_FMT_MXFP4 || f == MX_FMT_MXFP8 || f == MX_FMT_NVFP4; }
+int block_of(int f) { return f == MX_FMT_NVFP4 ? 16 : 32; }
+
+// Elements per tensor stay below 2^40 and every GEMM extent below 2^30 so that
+// the kernels' index arithmetic (int64 offsets, int extents) cannot overflow.
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+constexpr int64_t kMaxExtent = (int64_t)1 << 30;
+
+mx_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MX_OK;
+  g_last_hip_error = (int)e;
+  return MX_ERR_HIP;
+}
+
+// Common checks for a [rows][cols] quantized tensor.
+mx_status check_tensor(int fmt, int block, int rnd, int64_t rows, int64_t cols) {
+  if (!is_quant_fmt(fmt) || block != block_of(fmt)) return MX_ERR_UNSUPPORTED;
+  if (rnd != MX_ROUND_RNE) return MX_ERR_UNSUPPORTED;
+  if (rows <= 0 || cols <= 0 || cols % block != 0) return MX_ERR_INVALID_ARG;
+  if (rows > kMaxElems / cols) return MX_ERR_INVALID_ARG;
+  return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mx_quantize_workspace_bytes(mx_format fmt, int64_t rows, int64_t cols) {
+  if (fmt != MX_FMT_NVFP4 || rows <= 0 || cols <= 0) return 0;
+  return mx::quant_nvfp4_workspace(rows, cols);
+}
+
+mx_status mx_quantize(mx_format fmt, int block, mx_round rnd, int64_t rows, int64_t cols,
+                      const void* x, void* codes, void* scales, float* tensor_scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  mx_status st = check_tensor(fmt, block, rnd, rows, cols);
+  if (st != MX_OK) return st;
+  if (!x || !codes || !scales) return MX_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (fmt == MX_FMT_NVFP4) {
+    if (!tensor_scale || !aligned4(tensor_scale)) return MX_ERR_INVALID_ARG;
+    if (!workspace || !aligned16(workspace)) return MX_ERR_INVALID_ARG;
+    if (workspace_bytes < mx::quant_nvfp4_workspace(rows, cols)) return MX_ERR_INVALID_ARG;
+    return hip_status(mx::quant_nvfp4(rows, cols, x, codes, scales, tensor_scale, workspace, s));
+  }
+  if (tensor_scale) return MX_ERR_INVALID_ARG;
+  return hip_status(mx::quant_mx(fmt, rows, cols, x, codes, scales, s));
+}
+
+mx_status mx_dequantize(mx_format fmt, int block, mx_round rnd, int64_t rows, int64_t cols,
+                        const void* codes, const void* scales, const float* tensor_scale,
+                        mx_dtype out_dtype, void* y, void* stream) {
+  mx_status st = check_tensor(fmt, block, rnd, rows, cols);
+  if (st != MX_OK) return st;
+  if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16) return MX_ERR_UNSUPPORTED;
+  if (!codes || !scales || !y) return MX_ERR_INVALID_ARG;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(y)) return MX_ERR_INVALID_ARG;
+  if (fmt == MX_FMT_NVFP4) {
+    if (!tensor_scale || !aligned4(tensor_scale)) return MX_ERR_INVALID_ARG;
+  } else if (tensor_scale) {
+    return MX_ERR_INVALID_ARG;
+  }
+  return hip_status(mx::dequant(fmt, rows, cols, codes, scales, tensor_scale, out_dtype, y,
+                                (hipStream_t)stream));
+}
+
+size_t mx_gemm_workspace_bytes(mx_format fmt_a, mx_format fmt_b, int64_t M, int64_t N, int64_t K) {
+  if (fmt_a == MX_FMT_BF16 && fmt_b == MX_FMT_MXFP4 && M > 0 && N > 0 && K > 0 && K % 32 == 0 &&
+      M <= kMaxExtent && N <= kMaxExtent && K <= kMaxExtent)
+    return mx::gemm_w4a16_workspace(M, N, K);
+  return 0;
+}
+
+mx_status mx_gemm(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int64_t M, int64_t N,
+                  int64_t K, const void* a, const void* a_scales, const float* a_ts,
+                  const void* b, const void* b_scales, const float* b_ts, mx_dtype out_dtype,
+                  void* c, int64_t ldc, void* workspace, size_t workspace_bytes, void* stream) {
+  const bool w4a4 = fmt_a == MX_FMT_MXFP4 && fmt_b == MX_FMT_MXFP4 && block == 32;
+  const bool w8a8 = fmt_a == MX_FMT_MXFP8 && fmt_b == MX_FMT_MXFP8 && block == 32;
+  const bool nv = fmt_a == MX_FMT_NVFP4 && fmt_b == MX_FMT_NVFP4 && block == 16;
+  const bool w4a16 = fmt_a == MX_FMT_BF16 && fmt_b == MX_FMT_MXFP4 && block == 32;
+  if (!(w4a4 || w8a8 || nv || w4a16)) return MX_ERR_UNSUPPORTED;
+  if (rnd != MX_ROUND_RNE) return MX_ERR_UNSUPPORTED;
+  if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16) return MX_ERR_UNSUPPORTED;
+  if (M <= 0 || N <= 0 || K <= 0 || M > kMaxExtent || N > kMaxExtent || K > kMaxExtent)
+    return MX_ERR_INVALID_ARG;
+  // K is a whole number of 32-element groups for every path (NVFP4 included:
+  // its 16-blocks are staged in pairs).
+  if (K % 32 != 0) return MX_ERR_INVALID_ARG;
+  if (ldc < N) return MX_ERR_INVALID_ARG;
+  // Row tiles run along gridDim.y (at most 65535): 128 rows per tile for the
+  // W4A4/W8A8 kernels, 16 for W4A16.
+  if (M > (w4a16 ? 16 : 128) * (int64_t)65535) return MX_ERR_INVALID_ARG;
+  if (!a || !b || !b_scales || !c) return MX_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(b_scales) || !aligned16(c))
+    return MX_ERR_INVALID_ARG;
+  if (w4a16) {
+    if (a_scales || a_ts || b_ts) return MX_ERR_INVALID_ARG;
+  } else {
+    if (!a_scales || !aligned16(a_scales)) return MX_ERR_INVALID_ARG;
+  }
+  if (nv) {
+    if (!a_ts || !b_ts || !aligned4(a_ts) || !aligned4(b_ts)) return MX_ERR_INVALID_ARG;
+  } else if (a_ts || b_ts) {
+    return MX_ERR_INVALID_ARG;
+  }
+  const size_t need = mx_gemm_workspace_bytes(fmt_a, fmt_b, M, N, K);
+  if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
+    return MX_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (w4a4)
+    return hip_status(mx::gemm_mx(fmt_a, M, N, K, a, a_scales, b, b_scales, out_dtype, c, ldc, s));
+  if (w8a8 || nv)
+    return hip_status(mx::gemm_bf16x(fmt_a, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts,
+                                     out_dtype, c, ldc, s));
+  return hip_status(mx::gemm_w4a16(M, N, K, a, b, b_scales, out_dtype, c, ldc, workspace, s));
+}
+
+int mx_last_hip_error(void) { return g_last_hip_error; }
+
+const char* mx_status_string(mx_status s) {
+  switch (s) {
+    case MX_OK: return "MX_OK";
+    case MX_ERR_INVALID_ARG: return "MX_ERR_INVALID_ARG";
+    case MX_ERR_UNSUPPORTED: return "MX_ERR_UNSUPPORTED";
+    case MX_ERR_HIP: return "MX_ERR_HIP";
+  }
+  return "MX_ERR_UNKNOWN";
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// Internal launch interface of libmx (not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace mx {
+
+// Format ids, kept equal to the public mx_format values.
+enum : int { kBF16 = 0, kMXFP4 = 1, kMXFP8 = 2, kNVFP4 = 3 };
+enum : int { kOutF32 = 0, kOutBF16 = 1 };
+
+// ---- quantize.hip
+hipError_t quant_mx(int fmt, int64_t rows, int64_t cols, const void* x, void* codes,
+                    void* scales, hipStream_t s);
+size_t quant_nvfp4_workspace(int64_t rows, int64_t cols);
+hipError_t quant_nvfp4(int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
+                       float* tensor_scale, void* workspace, hipStream_t s);
+
+// ---- dequantize.hip
+hipError_t dequant(int fmt, int64_t rows, int64_t cols, const void* codes, const void* scales,
+                   const float* tensor_scale, int out_dtype, void* y, hipStream_t s);
+
+// ---- gemm_mx.hip (MXFP4 x MXFP4 on the FP4 scaled MFMA)
+hipError_t gemm_mx(int fmt, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
+                   const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
+                   hipStream_t s);
+
+// ---- gemm_bf16x.hip (MXFP8 x MXFP8 and NVFP4 x NVFP4, expanded exactly to bf16)
+hipError_t gemm_bf16x(int fmt, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
+                      const float* ta, const void* b, const void* sb, const float* tb,
+                      int out_dtype, void* c, int64_t ldc, hipStream_t s);
+
+// ---- gemm_w4a16.hip (bf16 activations x MXFP4 weights)
+size_t gemm_w4a16_workspace(int64_t M, int64_t N, int64_t K);
+hipError_t gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* a, const void* b,
+                      const void* sb, int out_dtype, void* c, int64_t ldc, void* workspace,
+                      hipStream_t s);
+
+}  // namespace mx

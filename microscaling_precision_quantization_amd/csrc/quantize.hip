@@ -1,0 +1,261 @@
+// Block quantization kernels for gfx950 (MXFP4, MXFP8, NVFP4).
+//
+// Shared-exponent rule: FAQ of "Microscaling MXFP4/NVFP4 on Blackwell for
+// reasoning LLMs" (E = ceil(log2(amax / max_elem)) + 127); element and scale
+// formats from its section "Fundamentos matematicos do formato MXFP4 e E8M0";
+// NVFP4 block size 16 from the zubnet.ai summary.
+//
+// Layout of the work: the input is treated as a flat array of 16-byte chunks
+// (8 bf16). Blocks never straddle rows because cols is a multiple of the block,
+// so codes and scales are flat too. MX: 4 consecutive lanes own one 32-block;
+// NVFP4: 2 lanes own one 16-block. The block amax is an integer max of
+// (bits & 0x7FFF) over the lanes' chunks, reduced with DPP quad permutes.
+//
+// Encoding uses gfx950's scaled converts. v_cvt_scalef32_pk_fp4_bf16 and
+// v_cvt_scalef32_pk_fp8_bf16 return nearest-even of x / scale (saturating for
+// FP4, -0 kept); with scale = 2^(E-127) that is exactly the MX element
+// encoding (checked exhaustively over all bf16 inputs and all scales).
+#include "mx_internal.h"
+
+namespace mx {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;  // 16-byte chunks per thread
+
+// DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_shr:n.
+constexpr int kDppSwap1 = 0xB1;
+constexpr int kDppSwap2 = 0x4E;
+constexpr int dpp_row_shr(int n) { return 0x110 + n; }
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+
+// Max of |x| over the 8 bf16 of a chunk, as the integer bits & 0x7FFF (a
+// larger magnitude has larger bits; Inf is 0x7F80 and NaN is above it).
+__device__ __forceinline__ uint32_t chunk_absmax(u32x4 v) {
+  const uint32_t m = 0x7FFF7FFFu;
+  u16x2 a = __builtin_bit_cast(u16x2, v.x & m);
+  u16x2 b = __builtin_bit_cast(u16x2, v.y & m);
+  u16x2 c = __builtin_bit_cast(u16x2, v.z & m);
+  u16x2 d = __builtin_bit_cast(u16x2, v.w & m);
+  u16x2 r = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  return r.x > r.y ? r.x : r.y;
+}
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// 2^(E-127) as an fp32 bit pattern; E = 0 is the subnormal 2^-127.
+__device__ __forceinline__ float e8m0_to_float(uint32_t E) {
+  return __builtin_bit_cast(float, E == 0 ? 0x00400000u : E << 23);
+}
+
+// MXFP4 (FMT 1) / MXFP8 (FMT 2).
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restrict__ x,
+                                                            void* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales,
+                                                            int64_t nchunks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+  u32x4 v[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; u++) {
+    const int64_t c = base + u * kThreads;
+    v[u] = (c < nchunks) ? __builtin_nontemporal_load(x + c) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; u++) {
+    const int64_t c = base + u * kThreads;
+    uint32_t m = chunk_absmax(v[u]);
+    m = umax(m, dpp<kDppSwap1>(m));
+    m = umax(m, dpp<kDppSwap2>(m));
+    // E = ceil(log2(amax / emax)) + 127 from the bf16 fields of amax:
+    // emax = 6 = 1.5 * 2^2  -> E = ea - 2 + [mantissa > 0x40]
+    // emax = 448 = 1.75 * 2^8 -> E = ea - 8 + [mantissa > 0x60]
+    const int ea = (int)(m >> 7), ma = (int)(m & 0x7F);
+    int e = (FMT == kMXFP4) ? ea - 2 + (ma > 0x40) : ea - 8 + (ma > 0x60);
+    e = e < 0 ? 0 : e;
+    const bool nonfinite = m >= 0x7F80u;
+    const uint32_t E = nonfinite ? 255u : (uint32_t)e;
+    const float scale = e8m0_to_float((uint32_t)e);
+    if (FMT == kMXFP4) {
+      uint32_t q = 0;
+      q = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(q, as_bf16x2(v[u].x), scale, 0);
+      q = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(q, as_bf16x2(v[u].y), scale, 1);
+      q = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(q, as_bf16x2(v[u].z), scale, 2);
+      q = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(q, as_bf16x2(v[u].w), scale, 3);
+      if (nonfinite) q = 0;
+      if (c < nchunks) __builtin_nontemporal_store(q, (uint32_t*)codes + c);
+    } else {
+      i16x2 lo = {0, 0}, hi = {0, 0};
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, as_bf16x2(v[u].x), scale, false);
+      lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, as_bf16x2(v[u].y), scale, true);
+      hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, as_bf16x2(v[u].z), scale, false);
+      hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, as_bf16x2(v[u].w), scale, true);
+      u32x2 q = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+      if (nonfinite) q = u32x2{0, 0};
+      if (c < nchunks) __builtin_nontemporal_store(q, (u32x2*)codes + c);
+    }
+    // Scale bytes: lanes 3, 7, 11, 15 of each 16-lane DPP row hold 4
+    // consecutive blocks; lane 15 assembles them into one dword store.
+    const uint32_t s4 = dpp<dpp_row_shr(4)>(E);
+    const uint32_t s8 = dpp<dpp_row_shr(8)>(E);
+    const uint32_t s12 = dpp<dpp_row_shr(12)>(E);
+    const int64_t blk = c >> 2;
+    if ((lane & 15) == 15 && c < nchunks) {
+      *(uint32_t*)(scales + (blk - 3)) = s12 | (s8 << 8) | (s4 << 16) | (E << 24);
+    }
+    // Ragged end: the row's lane 15 is past the end, store bytes instead.
+    if ((lane & 3) == 0 && c < nchunks && c - (lane & 15) + 15 >= nchunks) scales[blk] = (uint8_t)E;
+  }
+}
+
+// ---- NVFP4 ---------------------------------------------------------------
+
+constexpr int kMaxPartials = 1024;
+
+// Per-workgroup partial of max |x| (as bf16 magnitude bits).
+__global__ __launch_bounds__(kThreads) void nvfp4_amax_partial(const u32x4* __restrict__ x,
+                                                               int64_t nchunks,
+                                                               uint32_t* __restrict__ partial) {
+  uint32_t m = 0;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nchunks;
+       c += (int64_t)gridDim.x * kThreads)
+    m = umax(m, chunk_absmax(__builtin_nontemporal_load(x + c)));
+  for (int off = 32; off > 0; off >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, off));
+  __shared__ uint32_t wmax[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int w = 0; w < kThreads / 64; w++) r = umax(r, wmax[w]);
+    partial[blockIdx.x] = r;
+  }
+}
+
+// s_t = T / 2688 (T = 0 -> 1, non-finite T -> NaN), written to tensor_scale.
+__global__ __launch_bounds__(kThreads) void nvfp4_finalize(const uint32_t* __restrict__ partial,
+                                                           int npartial,
+                                                           float* __restrict__ tensor_scale) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < npartial; i += kThreads) m = umax(m, partial[i]);
+  for (int off = 32; off > 0; off >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, off));
+  __shared__ uint32_t wmax[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int w = 0; w < kThreads / 64; w++) r = umax(r, wmax[w]);
+    float st;
+    if (r >= 0x7F80u) {
+      st = __builtin_nanf("");
+    } else {
+      const float T = __builtin_bit_cast(float, r << 16);
+      st = (T == 0.0f) ? 1.0f : T / 2688.0f;  // 2688 = 6 * 448
+    }
+    tensor_scale[0] = st;
+  }
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
+
+// x * (1/D), with x = +-0 kept as is (no 0 * Inf) and D = 0 giving +-0.
+__device__ __forceinline__ float nv_scaled(float xv, float rz) { return xv == 0.0f ? xv : xv * rz; }
+
+__global__ __launch_bounds__(kThreads) void quant_nvfp4_kernel(const u32x4* __restrict__ x,
+                                                               uint32_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ scales,
+                                                               const float* __restrict__ tensor_scale,
+                                                               int64_t nchunks) {
+  const int lane = threadIdx.x & 63;
+  const float st = tensor_scale[0];
+  const bool bad = __builtin_isnan(st);
+  const float d6 = 6.0f * st;
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+  u32x4 v[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; u++) {
+    const int64_t c = base + u * kThreads;
+    v[u] = (c < nchunks) ? __builtin_nontemporal_load(x + c) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; u++) {
+    const int64_t c = base + u * kThreads;
+    uint32_t m = chunk_absmax(v[u]);
+    m = umax(m, dpp<kDppSwap1>(m));  // the partner lane holds the other half
+    const float bamax = __builtin_bit_cast(float, m << 16);
+    const float r = bamax / d6;
+    // E4M3 nearest-even, saturating: clamp to 448 first (the convert itself
+    // does not saturate above 448).
+    const float rs = r < 448.0f ? r : 448.0f;
+    uint32_t sbc = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(rs, rs, 0, false) & 0xFFu;
+    const float sb = __builtin_amdgcn_cvt_f32_fp8((int)sbc, 0);
+    const float D = sb * st;
+    const float R = 1.0f / D;
+    const float rz = (D == 0.0f) ? 0.0f : R;
+    uint32_t q = 0;
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, nv_scaled(bf16_lo(v[u].x), rz), nv_scaled(bf16_hi(v[u].x), rz), 1.0f, 0);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, nv_scaled(bf16_lo(v[u].y), rz), nv_scaled(bf16_hi(v[u].y), rz), 1.0f, 1);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, nv_scaled(bf16_lo(v[u].z), rz), nv_scaled(bf16_hi(v[u].z), rz), 1.0f, 2);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, nv_scaled(bf16_lo(v[u].w), rz), nv_scaled(bf16_hi(v[u].w), rz), 1.0f, 3);
+    if (bad) {
+      q = 0;
+      sbc = 0x7F;
+    }
+    if (c < nchunks) __builtin_nontemporal_store(q, codes + c);
+    // Lanes 1, 3, 5, 7 of each group of 8 hold 4 consecutive block scales.
+    const uint32_t s2 = dpp<dpp_row_shr(2)>(sbc);
+    const uint32_t s4 = dpp<dpp_row_shr(4)>(sbc);
+    const uint32_t s6 = dpp<dpp_row_shr(6)>(sbc);
+    const int64_t blk = c >> 1;
+    if ((lane & 7) == 7 && c < nchunks) {
+      *(uint32_t*)(scales + (blk - 3)) = s6 | (s4 << 8) | (s2 << 16) | (sbc << 24);
+    }
+    if ((lane & 1) == 0 && c < nchunks && c - (lane & 7) + 7 >= nchunks) scales[blk] = (uint8_t)sbc;
+  }
+}
+
+int64_t grid_for(int64_t nchunks) { return (nchunks + kThreads * kUnroll - 1) / (kThreads * kUnroll); }
+
+}  // namespace
+
+hipError_t quant_mx(int fmt, int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
+                    hipStream_t s) {
+  const int64_t nchunks = rows * cols / 8;
+  const dim3 grid((unsigned)grid_for(nchunks));
+  if (fmt == kMXFP4)
+    quant_mx_kernel<kMXFP4><<<grid, kThreads, 0, s>>>((const u32x4*)x, codes, (uint8_t*)scales, nchunks);
+  else
+    quant_mx_kernel<kMXFP8><<<grid, kThreads, 0, s>>>((const u32x4*)x, codes, (uint8_t*)scales, nchunks);
+  return hipGetLastError();
+}
+
+size_t quant_nvfp4_workspace(int64_t, int64_t) { return kMaxPartials * sizeof(uint32_t); }
+
+hipError_t quant_nvfp4(int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
+                       float* tensor_scale, void* workspace, hipStream_t s) {
+  const int64_t nchunks = rows * cols / 8;
+  int64_t np = (nchunks + kThreads * 8 - 1) / (kThreads * 8);
+  if (np > kMaxPartials) np = kMaxPartials;
+  if (np < 1) np = 1;
+  uint32_t* partial = (uint32_t*)workspace;
+  nvfp4_amax_partial<<<(unsigned)np, kThreads, 0, s>>>((const u32x4*)x, nchunks, partial);
+  nvfp4_finalize<<<1, kThreads, 0, s>>>(partial, (int)np, tensor_scale);
+  quant_nvfp4_kernel<<<(unsigned)grid_for(nchunks), kThreads, 0, s>>>(
+      (const u32x4*)x, (uint32_t*)codes, (uint8_t*)scales, tensor_scale, nchunks);
+  return hipGetLastError();
+}
+
+}  // namespace mx
