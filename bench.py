@@ -38,7 +38,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="c4")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=32,
+    p.add_argument("--cpu-rows", type=int, default=640,
                    help="activation rows in the oracle's CPU sample")
     return p.parse_args()
 
