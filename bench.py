@@ -40,11 +40,31 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=640,
                    help="activation rows in the oracle's CPU sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain device-to-device copy of 1 GiB, 5 times (reference "
+                        "for scaling the HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size: each dispatch reads and writes exactly 1 GiB.
+    rocprofv3's FETCH_SIZE / WRITE_SIZE for it give the scale factor applied
+    to the same counters of the kernels."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_dispatch": n, "dispatches": 5}))
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the kernels "
               "and their measurement are single-GPU in this build.", file=sys.stderr)
@@ -134,7 +154,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(name)
     roof["kernel_ms"] = g_avg
 
     line = {
@@ -166,6 +186,30 @@ def main():
         line["cpu_baseline"] = cpu_baseline(name, fmt, A_bits, qb, M, N, K, args.cpu_rows)
     line["input_gen_s"] = round(gen_s, 2)
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(workload):
+    """HBM bytes per GEMM dispatch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (scaled by the copy calibration), or None when there is
+    none for this workload or the kernel source changed since it was taken."""
+    import glob
+    import hashlib
+    import re
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*.md")):
+        text = open(path).read()
+        for block in re.findall(r"```json\n(.*?)\n```", text, re.S):
+            try:
+                rec = json.loads(block)
+            except ValueError:
+                continue
+            if rec.get("workload") != workload or "traffic_bytes" not in rec:
+                continue
+            src = os.path.join(ROOT, rec["source"])
+            if not os.path.exists(src):
+                return None
+            sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+            return rec["traffic_bytes"] if sha == rec["source_sha256_16"] else None
+    return None
 
 
 def cpu_baseline(name, fmt, A_bits, qb, M, N, K, rows):

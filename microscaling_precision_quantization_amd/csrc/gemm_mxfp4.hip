@@ -1,0 +1,351 @@
+// MXFP4 x MXFP4 block-scaled GEMM for gfx950, the large-tile kernel.
+//
+// C = A * B^T with A: M x K E2M1 codes, B: N x K codes (the Linear weight
+// layout), one E8M0 scale per 32 K per row. The matrix core applies both E8M0
+// scales during its fp32 accumulation (v_mfma_scale_f32_32x32x64_f8f6f4), so
+// codes travel from HBM to the MFMA unexpanded -- the block-scaled dot product
+// described in "Arquitetura Blackwell SM100 e aceleracao nativa de NVFP4" on
+// the produtoramaxvision page (there for B200 tensor cores).
+//
+// Design for CDNA4:
+//  * 256 x 256 output tile per workgroup, 4 waves (one per SIMD) of 128 x 128,
+//    each wave 4 x 4 MFMAs of 32 x 32 with 256 fp32 accumulators per lane.
+//  * K advances in super-steps of 256 elements (128 code bytes per row). Both
+//    operand tiles and their scales go HBM -> LDS with buffer_load ... lds
+//    (16 bytes per lane, no register staging), double-buffered: 2 x 68 KB.
+//    Buffer range checking returns zeros for rows past M or N.
+//  * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at slot
+//    c ^ ((r / 2) mod 8) so that the lanes reading one column of chunks hit
+//    distinct banks (measured with the LDS bank-conflict counter).
+//  * K order inside a super-step is permuted identically for A and B: the MFMA
+//    of sub-step j gives lane group g (lanes 32g .. 32g+31) code block 4g + j.
+//    A lane therefore owns 4 consecutive blocks of its row: its 4 scales are
+//    one dword, and opsel j picks byte j for sub-step j.
+//  * Workgroup ids are remapped so that each XCD (ids round-robin over 8
+//    XCDs) gets a contiguous, grouped block of output tiles and its L2 serves
+//    the shared A rows and B columns.
+// 32x32x64 FP4 operand layout (measured): lane l = r + 32 g supplies K
+// elements [32g, 32g + 32) of row r (16 bytes, even element in the low
+// nibble) and the E8M0 scale of that K block; the output lane l holds column
+// l % 32 and rows 8 (t / 4) + 4 g + (t % 4) in accumulator t. The kernel passes
+// B as the first operand, so the output tile is C^T and each lane holds runs
+// of 4 consecutive columns of one row of C.
+#include "mx_internal.h"
+
+namespace mx {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int kThreads = 256;
+constexpr int BM = 256, BN = 256;
+constexpr int kSuperK = 256;                       // elements per super-step
+constexpr int kRowBytes = kSuperK / 2;             // 128 code bytes per row
+constexpr int kTileBytes = BM * kRowBytes;         // 32 KB per operand
+constexpr int kScaleBytes = BM * (kSuperK / 32);   // 2 KB per operand (8 per row)
+constexpr int kStage = 2 * kTileBytes + 2 * kScaleBytes;
+constexpr uint32_t kRsrcFlags = 0x00020000u;       // raw buffer, gfx9 data format
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// LDS swizzle: the 16-byte chunk c of tile row r lives in slot c ^ swz(r).
+// gfx950's LDS serves a ds_read_b128 16 lanes at a time across 64 banks
+// (256 bytes); two 128-byte rows share that window, so the 16 rows read by one
+// group must spread over 8 slots per row parity: swz(r) = (r / 2) mod 8.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Issue part P (0..3) of the loads of super-step s into `stage`. A wave moves
+// 8 KB of each code tile (8 x 64 lanes x 16 B) and 512 B of each scale tile
+// (2 x 64 lanes x 4 B) per super-step; part P carries 1/4 of them so that the
+// loads can be spread between the MFMA groups of the previous super-step.
+template <int P>
+__device__ __forceinline__ void issue_part(uint8_t* stage, __amdgpu_buffer_rsrc_t rA,
+                                           __amdgpu_buffer_rsrc_t rB, __amdgpu_buffer_rsrc_t rSA,
+                                           __amdgpu_buffer_rsrc_t rSB, int m0, int n0,
+                                           uint32_t rowbytes, uint32_t scalebytes, int s, int wave,
+                                           int lane) {
+  const uint32_t kb = (uint32_t)s * kRowBytes;
+#pragma unroll
+  for (int i = 2 * P; i < 2 * P + 2; i++) {
+    const int b = wave * 8 + i;          // 1 KB block of the tile = 8 rows
+    const int row = b * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(row);  // physical slot lane&7 holds this chunk
+    const uint32_t off = kb + (uint32_t)chunk * 16u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(stage + b * 1024), 16,
+                                             (uint32_t)(m0 + row) * rowbytes + off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(stage + kTileBytes + b * 1024), 16,
+                                             (uint32_t)(n0 + row) * rowbytes + off, 0, 0, 0);
+  }
+  // Scales: 256 B block = 32 rows x 8 bytes; part P carries block P / 2 of
+  // A (even P) or of B (odd P).
+  const int b = wave * 2 + (P >> 1);
+  const int row = b * 32 + (lane >> 1);
+  const uint32_t off = (uint32_t)s * (kSuperK / 32) + (uint32_t)(lane & 1) * 4u;
+  if ((P & 1) == 0)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_ptr_t)(stage + 2 * kTileBytes + b * 256), 4,
+                                             (uint32_t)(m0 + row) * scalebytes + off, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rSB, (lds_ptr_t)(stage + 2 * kTileBytes + kScaleBytes + b * 256), 4,
+        (uint32_t)(n0 + row) * scalebytes + off, 0, 0, 0);
+}
+
+__device__ __forceinline__ void issue_stage(uint8_t* stage, __amdgpu_buffer_rsrc_t rA,
+                                            __amdgpu_buffer_rsrc_t rB, __amdgpu_buffer_rsrc_t rSA,
+                                            __amdgpu_buffer_rsrc_t rSB, int m0, int n0,
+                                            uint32_t rowbytes, uint32_t scalebytes, int s, int wave,
+                                            int lane) {
+  issue_part<0>(stage, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s, wave, lane);
+  issue_part<1>(stage, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s, wave, lane);
+  issue_part<2>(stage, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s, wave, lane);
+  issue_part<3>(stage, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s, wave, lane);
+}
+
+// Operand fragments of one 64-element sub-step: 4 A and 4 B tiles of 32 rows,
+// 16 code bytes per lane each.
+struct Frags {
+  i32x4 a[4], b[4];
+};
+
+template <int J>
+__device__ __forceinline__ void load_frags(const uint8_t* As, const uint8_t* Bs, int wm, int wn,
+                                           int r, int g, Frags& f) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int ra = wm * 128 + i * 32 + r;
+    const int rb = wn * 128 + i * 32 + r;
+    f.a[i] = *(const i32x4*)(As + ra * kRowBytes + (((4 * g + J) ^ swz(ra)) * 16));
+    f.b[i] = *(const i32x4*)(Bs + rb * kRowBytes + (((4 * g + J) ^ swz(rb)) * 16));
+  }
+}
+
+template <int J>
+__device__ __forceinline__ void mfma_substep(const Frags& f, const int (&sa)[4], const int (&sb)[4],
+                                             f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const i32x8 a = i32x8{f.a[i].x, f.a[i].y, f.a[i].z, f.a[i].w, 0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const i32x8 b = i32x8{f.b[j].x, f.b[j].y, f.b[j].z, f.b[j].w, 0, 0, 0, 0};
+      // Operands swapped (B first): the result tile is C^T, so a lane ends up
+      // with 4 consecutive output columns of one output row.
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc[i][j], 4, 4, J, sb[j],
+                                                                  J, sa[i]);
+    }
+  }
+}
+
+// Keep the compiler from moving LDS reads across this point: the reads of the
+// next sub-step are issued before the current sub-step's 16 MFMAs so that
+// their latency hides behind the matrix work.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Issue pattern for one region (sched_group_barrier masks: 0x008 MFMA,
+// 0x100 LDS read, 0x020 VMEM read), closed by a fence.
+template <bool WITH_READS>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int k = 0; k < 5; k++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    if (WITH_READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < 3; k++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    if (WITH_READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int OUT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ SB, void* __restrict__ C, int64_t ldc, int M, int N, int K,
+    int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 31, g = lane >> 5;
+
+  // Tile order: XCD x (= blockIdx % 8) gets the contiguous id range
+  // [x * n/8, (x+1) * n/8); ids are rastered in groups of 4 tile rows.
+  const int ntiles = tiles_m * tiles_n;
+  const int bid = blockIdx.x;
+  const int t = (ntiles % 8 == 0) ? (bid % 8) * (ntiles / 8) + bid / 8 : bid;
+  constexpr int GM = 4;
+  const int group = t / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int tm = first_m + (t % (GM * tiles_n)) % gsize;
+  const int tn = (t % (GM * tiles_n)) / gsize;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const uint32_t rowbytes = (uint32_t)(K / 2), scalebytes = (uint32_t)(K / 32);
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, (int)((uint32_t)M * rowbytes), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)B, 0, (int)((uint32_t)N * rowbytes), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc((void*)SA, 0, (int)((uint32_t)M * scalebytes), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rSB = __builtin_amdgcn_make_buffer_rsrc((void*)SB, 0, (int)((uint32_t)N * scalebytes), kRsrcFlags);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
+
+  const int nsteps = K / kSuperK;
+  issue_stage(smem, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane);
+  for (int s = 0; s < nsteps; s++) {
+    // Stage s is complete for every wave, and every wave is done with stage
+    // s-1, whose buffer the loads below refill with stage s+1. (At the top of
+    // the body: a barrier at the bottom gets scheduled above the last MFMAs.)
+    wait_vmem();
+    __syncthreads();
+    const uint8_t* cur = smem + (s & 1) * kStage;
+    uint8_t* nxt = smem + ((s + 1) & 1) * kStage;
+    // Branch-free body (a branch here lets the compiler sink every MFMA below
+    // the loads): the last iteration re-fetches its own stage into the idle
+    // buffer, which nobody reads; the wait after the loop drains it.
+    const int snext = min(s + 1, nsteps - 1);
+    const uint8_t* As = cur;
+    const uint8_t* Bs = cur + kTileBytes;
+    const uint8_t* SAs = cur + 2 * kTileBytes;
+    const uint8_t* SBs = SAs + kScaleBytes;
+    int sa[4], sb[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      sa[i] = *(const int*)(SAs + (wm * 128 + i * 32 + r) * 8 + g * 4);
+      sb[i] = *(const int*)(SBs + (wn * 128 + i * 32 + r) * 8 + g * 4);
+    }
+    // Each of the 4 regions below issues the 16 MFMAs of one sub-step, the 8
+    // LDS reads of the next sub-step's fragments and a quarter (5 DMA loads)
+    // of the next super-step, interleaved as {2 MFMA, 1 LDS read, 1 load} x 5
+    // then {2 MFMA, 1 LDS read} x 3, so every load's M0 set-up and issue sits
+    // in the shadow of an MFMA instead of stalling the in-order issue.
+    Frags f0, f1;
+    load_frags<0>(As, Bs, wm, wn, r, g, f0);
+    sched_fence();
+    load_frags<1>(As, Bs, wm, wn, r, g, f1);
+    issue_part<0>(nxt, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, snext, wave, lane);
+    mfma_substep<0>(f0, sa, sb, acc);
+    interleave<true>();
+    load_frags<2>(As, Bs, wm, wn, r, g, f0);
+    issue_part<1>(nxt, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, snext, wave, lane);
+    mfma_substep<1>(f1, sa, sb, acc);
+    interleave<true>();
+    load_frags<3>(As, Bs, wm, wn, r, g, f1);
+    issue_part<2>(nxt, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, snext, wave, lane);
+    mfma_substep<2>(f0, sa, sb, acc);
+    interleave<true>();
+    issue_part<3>(nxt, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, snext, wave, lane);
+    mfma_substep<3>(f1, sa, sb, acc);
+    interleave<false>();
+  }
+  wait_vmem();
+
+  // Epilogue. Accumulator t of tile (i, j) is C[row][col] with row = A-tile
+  // row r and col = 8 (t / 4) + 4 g + (t % 4): runs of 4 consecutive columns.
+  // Each wave stages its 128 x 128 block in LDS (its own region; fp32 in two
+  // halves of 64 rows) and writes it back row-contiguously, 16 bytes per lane,
+  // so whole 128-byte lines reach the L2. All LDS DMA has drained (wait above)
+  // before the barrier, so the stage buffers are free.
+  __syncthreads();
+  constexpr int kEs = (OUT == kOutF32) ? 4 : 2;       // bytes per element
+  constexpr int kRows = (OUT == kOutF32) ? 64 : 128;  // rows staged per pass
+  constexpr int kPitch = 128 * kEs + 16;              // padded LDS row
+  uint8_t* wbuf = smem + wave * (kRows * kPitch);
+  const int wrow0 = m0 + wm * 128, wcol0 = n0 + wn * 128;
+  const bool vec_ok = (ldc % (16 / kEs)) == 0;
+#pragma unroll
+  for (int pass = 0; pass < 128 / kRows; pass++) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      if ((i * 32) / kRows != pass) continue;
+      const int lrow = i * 32 + r - pass * kRows;
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int lcol = j * 32 + 8 * q + 4 * g;
+          uint8_t* dst = wbuf + lrow * kPitch + lcol * kEs;
+          if (OUT == kOutF32) {
+            *(f32x4*)dst = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                 acc[i][j][4 * q + 3]};
+          } else {
+            const uint32_t lo = bf16_rne(acc[i][j][4 * q]) | (bf16_rne(acc[i][j][4 * q + 1]) << 16);
+            const uint32_t hi = bf16_rne(acc[i][j][4 * q + 2]) | (bf16_rne(acc[i][j][4 * q + 3]) << 16);
+            *(u32x2*)dst = u32x2{lo, hi};
+          }
+        }
+    }
+    // Row-contiguous write-back: 128 columns = 16 lanes x 16 bytes (bf16) or
+    // 32 lanes (fp32); the wave covers 64 / (lanes per row) rows per step.
+    constexpr int kLanesPerRow = 128 * kEs / 16;
+    constexpr int kRowsPerStep = 64 / kLanesPerRow;
+#pragma unroll 4
+    for (int rr = 0; rr < kRows; rr += kRowsPerStep) {
+      const int lrow = rr + lane / kLanesPerRow;
+      const int lcol = (lane % kLanesPerRow) * (16 / kEs);
+      const int row = wrow0 + pass * kRows + lrow;
+      const int col = wcol0 + lcol;
+      if (row >= M) continue;
+      const u32x4 v = *(const u32x4*)(wbuf + lrow * kPitch + lcol * kEs);
+      uint8_t* gdst = (uint8_t*)C + ((int64_t)row * ldc + col) * kEs;
+      if (vec_ok && col + 16 / kEs <= N) {
+        *(u32x4*)gdst = v;
+      } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 16 / kEs; e++) {
+          if (col + e >= N) continue;
+          if (OUT == kOutF32)
+            ((uint32_t*)gdst)[e] = w[e];
+          else
+            ((uint16_t*)gdst)[e] = (uint16_t)(w[e / 2] >> (16 * (e % 2)));
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// The large-tile kernel needs whole super-steps along K and 32-bit buffer
+// offsets (including the zero-filled rows past the last tile).
+bool gemm_mxfp4_fits(int64_t M, int64_t N, int64_t K) {
+  if (K % kSuperK != 0) return false;
+  const int64_t lim = (int64_t)1 << 31;
+  return (M + BM) * (K / 2) < lim && (N + BN) * (K / 2) < lim;
+}
+
+hipError_t gemm_mxfp4(int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
+                      const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
+                      hipStream_t s) {
+  const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
+  const dim3 grid((unsigned)(tm * tn));
+  const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
+                *SB = (const uint8_t*)sb;
+  if (out_dtype == kOutF32)
+    gemm_mxfp4_kernel<kOutF32><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, (int)M, (int)N, (int)K, tm, tn);
+  else
+    gemm_mxfp4_kernel<kOutBF16><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, (int)M, (int)N, (int)K, tm, tn);
+  return hipGetLastError();
+}
+
+}  // namespace mx

@@ -27,6 +27,12 @@ hipError_t gemm_mx(int fmt, int64_t M, int64_t N, int64_t K, const void* a, cons
                    const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
                    hipStream_t s);
 
+// ---- gemm_mxfp4.hip (MXFP4 x MXFP4, 256 x 256 tiles, direct-to-LDS pipeline)
+bool gemm_mxfp4_fits(int64_t M, int64_t N, int64_t K);
+hipError_t gemm_mxfp4(int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
+                      const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
+                      hipStream_t s);
+
 // ---- gemm_bf16x.hip (MXFP8 x MXFP8 and NVFP4 x NVFP4, expanded exactly to bf16)
 hipError_t gemm_bf16x(int fmt, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
                       const float* ta, const void* b, const void* sb, const float* tb,
