@@ -5,6 +5,7 @@
 // One thread expands one 16-byte group of 8 outputs' codes. The scaled decodes
 // v_cvt_scalef32_pk_{f32,bf16}_fp4 and v_cvt_scalef32_pk_f32_fp8 multiply by a
 // power-of-two scale exactly and round once to the output type.
+#include "bf16.h"
 #include "mx_internal.h"
 
 namespace mx {
@@ -23,14 +24,6 @@ __device__ __forceinline__ float e8m0_to_float(uint32_t E) {
   return __builtin_bit_cast(float, E == 0 ? 0x00400000u : E << 23);
 }
 
-// fp32 -> bf16 bits, nearest-even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return bf16_rne(lo) | (bf16_rne(hi) << 16); }
 
 template <int OUT>
 __device__ __forceinline__ void store8(void* y, int64_t c, const float (&o)[8]) {
@@ -39,7 +32,7 @@ __device__ __forceinline__ void store8(void* y, int64_t c, const float (&o)[8]) 
     __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, p);
     __builtin_nontemporal_store(f32x4{o[4], o[5], o[6], o[7]}, p + 1);
   } else {
-    u32x4 w = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]), pack_bf16(o[6], o[7])};
+    u32x4 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
     __builtin_nontemporal_store(w, (u32x4*)y + c);
   }
 }

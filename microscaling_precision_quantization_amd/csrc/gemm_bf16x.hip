@@ -20,6 +20,7 @@
 // Expansion happens once per tile while staging global -> LDS. bf16 MFMA
 // layout (measured): lane l = r + 16 g holds K elements [8g, 8g + 8) of row r;
 // the output lane l holds column l % 16, rows 4 (l / 16) + 0..3.
+#include "bf16.h"
 #include "mx_internal.h"
 
 namespace mx {
@@ -33,12 +34,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kThreads = 256;
 constexpr int BM = 128, BN = 128, BK = 64;  // elements
 constexpr int kStride = BK * 2 + 16;         // bytes per LDS row of bf16 (padded)
-
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 
 __device__ __forceinline__ float e8m0_to_float(uint32_t E) {
   return __builtin_bit_cast(float, E == 0 ? 0x00400000u : E << 23);
@@ -183,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16x_kernel(const uint8_t* __r
           if (OUT == kOutF32)
             ((float*)C)[(int64_t)row * ldc + col] = v;
           else
-            ((uint16_t*)C)[(int64_t)row * ldc + col] = (uint16_t)bf16_rne(v);
+            ((uint16_t*)C)[(int64_t)row * ldc + col] = bf16_bits(v);
         }
       }
     }

@@ -13,6 +13,7 @@
 //   FP8: K elements [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16), 32 bytes;
 // and, for both, the E8M0 scale of K block g of row r. Output: lane l holds
 // column l % 16, rows 4 (l / 16) + 0..3.
+#include "bf16.h"
 #include "mx_internal.h"
 
 namespace mx {
@@ -25,12 +26,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int BM = 128, BN = 128, BK = 128;  // tile sizes in elements
 constexpr uint32_t kUnitScale = 127u;        // 2^0 for padded blocks
-
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 
 template <int FMT>
 struct MxTile {
@@ -158,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __rest
           if (OUT == kOutF32)
             ((float*)C)[(int64_t)row * ldc + col] = acc[i][j][t];
           else
-            ((uint16_t*)C)[(int64_t)row * ldc + col] = (uint16_t)bf16_rne(acc[i][j][t]);
+            ((uint16_t*)C)[(int64_t)row * ldc + col] = bf16_bits(acc[i][j][t]);
         }
       }
     }

@@ -30,6 +30,7 @@
 // l % 32 and rows 8 (t / 4) + 4 g + (t % 4) in accumulator t. The kernel passes
 // B as the first operand, so the output tile is C^T and each lane holds runs
 // of 4 consecutive columns of one row of C.
+#include "bf16.h"
 #include "mx_internal.h"
 
 namespace mx {
@@ -41,7 +42,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kThreads = 256;
 constexpr int BM = 256, BN = 256;
@@ -52,65 +52,60 @@ constexpr int kScaleBytes = BM * (kSuperK / 32);   // 2 KB per operand (8 per ro
 constexpr int kStage = 2 * kTileBytes + 2 * kScaleBytes;
 constexpr uint32_t kRsrcFlags = 0x00020000u;       // raw buffer, gfx9 data format
 
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // LDS swizzle: the 16-byte chunk c of tile row r lives in slot c ^ swz(r).
 // gfx950's LDS serves a ds_read_b128 16 lanes at a time across 64 banks
 // (256 bytes); two 128-byte rows share that window, so the 16 rows read by one
 // group must spread over 8 slots per row parity: swz(r) = (r / 2) mod 8.
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// One wave's share of a super-step, staged in registers: 8 KB of each code
+// tile (8 blocks of 8 rows x 128 B; lane l holds 16 bytes of row l / 8) and
+// 512 B of each scale tile (64 rows x 8 B, one row per lane).
+struct Stage {
+  i32x4 a[8], b[8];
+  u32x2 sa, sb;
+};
 
-// Issue part P (0..3) of the loads of super-step s into `stage`. A wave moves
-// 8 KB of each code tile (8 x 64 lanes x 16 B) and 512 B of each scale tile
-// (2 x 64 lanes x 4 B) per super-step; part P carries 1/4 of them so that the
-// loads can be spread between the MFMA groups of the previous super-step.
+// Part P (0..3) of the global loads of super-step s: code blocks 2P and 2P+1
+// of A and B, plus the A scales (P = 0) or the B scales (P = 1). Rows past M
+// or N fall outside the buffer range and load as zeros.
 template <int P>
-__device__ __forceinline__ void issue_part(uint8_t* stage, __amdgpu_buffer_rsrc_t rA,
-                                           __amdgpu_buffer_rsrc_t rB, __amdgpu_buffer_rsrc_t rSA,
-                                           __amdgpu_buffer_rsrc_t rSB, int m0, int n0,
-                                           uint32_t rowbytes, uint32_t scalebytes, int s, int wave,
-                                           int lane) {
+__device__ __forceinline__ void load_part(Stage& st, __amdgpu_buffer_rsrc_t rA,
+                                          __amdgpu_buffer_rsrc_t rB, __amdgpu_buffer_rsrc_t rSA,
+                                          __amdgpu_buffer_rsrc_t rSB, int m0, int n0,
+                                          uint32_t rowbytes, uint32_t scalebytes, int s, int wave,
+                                          int lane) {
   const uint32_t kb = (uint32_t)s * kRowBytes;
 #pragma unroll
   for (int i = 2 * P; i < 2 * P + 2; i++) {
-    const int b = wave * 8 + i;          // 1 KB block of the tile = 8 rows
-    const int row = b * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ swz(row);  // physical slot lane&7 holds this chunk
+    const int row = (wave * 8 + i) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(row);  // slot lane&7 of the LDS row holds this chunk
     const uint32_t off = kb + (uint32_t)chunk * 16u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(stage + b * 1024), 16,
-                                             (uint32_t)(m0 + row) * rowbytes + off, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(stage + kTileBytes + b * 1024), 16,
-                                             (uint32_t)(n0 + row) * rowbytes + off, 0, 0, 0);
+    st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, (uint32_t)(m0 + row) * rowbytes + off, 0, 0);
+    st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, (uint32_t)(n0 + row) * rowbytes + off, 0, 0);
   }
-  // Scales: 256 B block = 32 rows x 8 bytes; part P carries block P / 2 of
-  // A (even P) or of B (odd P).
-  const int b = wave * 2 + (P >> 1);
-  const int row = b * 32 + (lane >> 1);
-  const uint32_t off = (uint32_t)s * (kSuperK / 32) + (uint32_t)(lane & 1) * 4u;
-  if ((P & 1) == 0)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_ptr_t)(stage + 2 * kTileBytes + b * 256), 4,
-                                             (uint32_t)(m0 + row) * scalebytes + off, 0, 0, 0);
-  else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rSB, (lds_ptr_t)(stage + 2 * kTileBytes + kScaleBytes + b * 256), 4,
-        (uint32_t)(n0 + row) * scalebytes + off, 0, 0, 0);
+  const int srow = wave * 64 + lane;
+  const uint32_t soff = (uint32_t)s * (kSuperK / 32);
+  if (P == 0)
+    st.sa = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                          rSA, (uint32_t)(m0 + srow) * scalebytes + soff, 0, 0));
+  if (P == 1)
+    st.sb = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                          rSB, (uint32_t)(n0 + srow) * scalebytes + soff, 0, 0));
 }
 
-__device__ __forceinline__ void issue_stage(uint8_t* stage, __amdgpu_buffer_rsrc_t rA,
-                                            __amdgpu_buffer_rsrc_t rB, __amdgpu_buffer_rsrc_t rSA,
-                                            __amdgpu_buffer_rsrc_t rSB, int m0, int n0,
-                                            uint32_t rowbytes, uint32_t scalebytes, int s, int wave,
-                                            int lane) {
-  issue_part<0>(stage, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s, wave, lane);
-  issue_part<1>(stage, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s, wave, lane);
-  issue_part<2>(stage, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s, wave, lane);
-  issue_part<3>(stage, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s, wave, lane);
+// Part P of the LDS writes of a staged super-step (the same pieces as
+// load_part<P>). Code rows are 128 bytes with the chunk swizzle applied by
+// the loads; scales are 8 bytes per row.
+template <int P>
+__device__ __forceinline__ void store_part(const Stage& st, uint8_t* stage, int wave, int lane) {
+#pragma unroll
+  for (int i = 2 * P; i < 2 * P + 2; i++) {
+    *(i32x4*)(stage + (wave * 8 + i) * 1024 + lane * 16) = st.a[i];
+    *(i32x4*)(stage + kTileBytes + (wave * 8 + i) * 1024 + lane * 16) = st.b[i];
+  }
+  if (P == 0) *(u32x2*)(stage + 2 * kTileBytes + (wave * 64 + lane) * 8) = st.sa;
+  if (P == 1) *(u32x2*)(stage + 2 * kTileBytes + kScaleBytes + (wave * 64 + lane) * 8) = st.sb;
 }
 
 // Operand fragments of one 64-element sub-step: 4 A and 4 B tiles of 32 rows,
@@ -148,26 +143,33 @@ __device__ __forceinline__ void mfma_substep(const Frags& f, const int (&sa)[4],
   }
 }
 
-// Keep the compiler from moving LDS reads across this point: the reads of the
-// next sub-step are issued before the current sub-step's 16 MFMAs so that
-// their latency hides behind the matrix work.
+// Keep the compiler from moving instructions across this point.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// Issue pattern for one region (sched_group_barrier masks: 0x008 MFMA,
-// 0x100 LDS read, 0x020 VMEM read), closed by a fence.
+// Issue order of one region of 16 MFMAs (sched_group_barrier masks: 0x008
+// MFMA, 0x100 LDS read, 0x200 LDS write, 0x020 VMEM read), closed by a fence:
+// the next sub-step's 8 fragment reads go out within the first 4 MFMAs, so
+// they reach the LDS queue ahead of the other waves' staging writes and land
+// before the region ends; then the global loads, then the LDS writes of the
+// staged super-step, which are only needed by the next barrier.
 template <bool WITH_READS>
 __device__ __forceinline__ void interleave() {
 #pragma unroll
+  for (int k = 0; k < 4; k++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (WITH_READS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+#pragma unroll
   for (int k = 0; k < 5; k++) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    if (WITH_READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   }
 #pragma unroll
-  for (int k = 0; k < 3; k++) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    if (WITH_READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  for (int k = 0; k < 5; k++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
   }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -210,19 +212,44 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
   const int nsteps = K / kSuperK;
-  issue_stage(smem, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane);
+  // Three-deep pipeline: LDS buffer s & 1 feeds the MFMAs, LDS buffer
+  // (s + 1) & 1 receives super-step s + 1 from registers, and the registers
+  // receive super-step s + 2 from memory while the MFMAs run.
+  Stage R;
+  load_part<0>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane);
+  load_part<1>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane);
+  load_part<2>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane);
+  load_part<3>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane);
+  store_part<0>(R, smem, wave, lane);
+  store_part<1>(R, smem, wave, lane);
+  store_part<2>(R, smem, wave, lane);
+  store_part<3>(R, smem, wave, lane);
+  {
+    // Issued in the loop's order (the fences keep the scheduler from
+    // reordering them), so that the in-order load counter lets the loop's
+    // first LDS writes wait only for their own part.
+    const int s1 = min(1, nsteps - 1);
+    sched_fence();
+    load_part<0>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane);
+    sched_fence();
+    load_part<1>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane);
+    sched_fence();
+    load_part<2>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane);
+    sched_fence();
+    load_part<3>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane);
+    sched_fence();
+  }
   for (int s = 0; s < nsteps; s++) {
-    // Stage s is complete for every wave, and every wave is done with stage
-    // s-1, whose buffer the loads below refill with stage s+1. (At the top of
-    // the body: a barrier at the bottom gets scheduled above the last MFMAs.)
-    wait_vmem();
-    __syncthreads();
+    // Every wave's LDS writes of super-step s are done and every wave is done
+    // reading super-step s-1, whose buffer receives super-step s+1 below. Only
+    // LDS work is waited for: the global loads stay in flight.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    sched_fence();
     const uint8_t* cur = smem + (s & 1) * kStage;
     uint8_t* nxt = smem + ((s + 1) & 1) * kStage;
-    // Branch-free body (a branch here lets the compiler sink every MFMA below
-    // the loads): the last iteration re-fetches its own stage into the idle
-    // buffer, which nobody reads; the wait after the loop drains it.
-    const int snext = min(s + 1, nsteps - 1);
+    // Branch-free body (a branch here lets the compiler sink the MFMAs): the
+    // last iterations re-stage the final super-step into the idle buffer.
+    const int s2 = min(s + 2, nsteps - 1);
     const uint8_t* As = cur;
     const uint8_t* Bs = cur + kTileBytes;
     const uint8_t* SAs = cur + 2 * kTileBytes;
@@ -234,37 +261,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
       sb[i] = *(const int*)(SBs + (wn * 128 + i * 32 + r) * 8 + g * 4);
     }
     // Each of the 4 regions below issues the 16 MFMAs of one sub-step, the 8
-    // LDS reads of the next sub-step's fragments and a quarter (5 DMA loads)
-    // of the next super-step, interleaved as {2 MFMA, 1 LDS read, 1 load} x 5
-    // then {2 MFMA, 1 LDS read} x 3, so every load's M0 set-up and issue sits
-    // in the shadow of an MFMA instead of stalling the in-order issue.
+    // LDS reads of the next sub-step's fragments, a quarter of the staged
+    // super-step's LDS writes and a quarter of the next global loads,
+    // interleaved so that each memory instruction issues in an MFMA's shadow.
     Frags f0, f1;
     load_frags<0>(As, Bs, wm, wn, r, g, f0);
     sched_fence();
     load_frags<1>(As, Bs, wm, wn, r, g, f1);
-    issue_part<0>(nxt, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, snext, wave, lane);
+    store_part<0>(R, nxt, wave, lane);
+    load_part<0>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane);
     mfma_substep<0>(f0, sa, sb, acc);
     interleave<true>();
     load_frags<2>(As, Bs, wm, wn, r, g, f0);
-    issue_part<1>(nxt, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, snext, wave, lane);
+    store_part<1>(R, nxt, wave, lane);
+    load_part<1>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane);
     mfma_substep<1>(f1, sa, sb, acc);
     interleave<true>();
     load_frags<3>(As, Bs, wm, wn, r, g, f1);
-    issue_part<2>(nxt, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, snext, wave, lane);
+    store_part<2>(R, nxt, wave, lane);
+    load_part<2>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane);
     mfma_substep<2>(f0, sa, sb, acc);
     interleave<true>();
-    issue_part<3>(nxt, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, snext, wave, lane);
+    store_part<3>(R, nxt, wave, lane);
+    load_part<3>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane);
     mfma_substep<3>(f1, sa, sb, acc);
     interleave<false>();
   }
-  wait_vmem();
 
   // Epilogue. Accumulator t of tile (i, j) is C[row][col] with row = A-tile
   // row r and col = 8 (t / 4) + 4 g + (t % 4): runs of 4 consecutive columns.
   // Each wave stages its 128 x 128 block in LDS (its own region; fp32 in two
   // halves of 64 rows) and writes it back row-contiguously, 16 bytes per lane,
-  // so whole 128-byte lines reach the L2. All LDS DMA has drained (wait above)
-  // before the barrier, so the stage buffers are free.
+  // so whole 128-byte lines reach the L2.
   __syncthreads();
   constexpr int kEs = (OUT == kOutF32) ? 4 : 2;       // bytes per element
   constexpr int kRows = (OUT == kOutF32) ? 64 : 128;  // rows staged per pass
@@ -288,8 +316,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
             *(f32x4*)dst = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                  acc[i][j][4 * q + 3]};
           } else {
-            const uint32_t lo = bf16_rne(acc[i][j][4 * q]) | (bf16_rne(acc[i][j][4 * q + 1]) << 16);
-            const uint32_t hi = bf16_rne(acc[i][j][4 * q + 2]) | (bf16_rne(acc[i][j][4 * q + 3]) << 16);
+            const uint32_t lo = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+            const uint32_t hi = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
             *(u32x2*)dst = u32x2{lo, hi};
           }
         }

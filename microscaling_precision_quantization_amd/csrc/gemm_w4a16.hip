@@ -13,6 +13,7 @@
 //  * activations for the workgroup's K range are staged once in LDS;
 //  * K is split across workgroups; partial sums go to a workspace and a second
 //    kernel adds them in a fixed order (deterministic, no float atomics).
+#include "bf16.h"
 #include "mx_internal.h"
 
 namespace mx {
@@ -28,12 +29,6 @@ constexpr int TM = 16;    // activation rows per workgroup
 constexpr int KC = 512;   // K elements of activations staged in LDS at once
 constexpr int kAStride = KC * 2 + 16;  // bytes per LDS activation row (padded)
 constexpr uint32_t kUnitScale = 127u;
-
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 
 __device__ __forceinline__ float e8m0_to_float(uint32_t E) {
   return __builtin_bit_cast(float, E == 0 ? 0x00400000u : E << 23);
@@ -113,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(const uint16_t* __
       if (OUT == kOutF32)
         ((float*)out)[(int64_t)m * ldc + n] = sum[t];
       else
-        ((uint16_t*)out)[(int64_t)m * ldc + n] = (uint16_t)bf16_rne(sum[t]);
+        ((uint16_t*)out)[(int64_t)m * ldc + n] = bf16_bits(sum[t]);
     } else {
       ((float*)out)[((int64_t)blockIdx.z * M + m) * N + n] = sum[t];
     }
@@ -132,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const float* __
   if (OUT == kOutF32)
     ((float*)C)[(int64_t)m * ldc + n] = s;
   else
-    ((uint16_t*)C)[(int64_t)m * ldc + n] = (uint16_t)bf16_rne(s);
+    ((uint16_t*)C)[(int64_t)m * ldc + n] = bf16_bits(s);
 }
 
 struct Plan {
