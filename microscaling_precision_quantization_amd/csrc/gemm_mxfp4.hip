@@ -10,10 +10,14 @@
 // Design for CDNA4:
 //  * 256 x 256 output tile per workgroup, 4 waves (one per SIMD) of 128 x 128,
 //    each wave 4 x 4 MFMAs of 32 x 32 with 256 fp32 accumulators per lane.
-//  * K advances in super-steps of 256 elements (128 code bytes per row). Both
-//    operand tiles and their scales go HBM -> LDS with buffer_load ... lds
-//    (16 bytes per lane, no register staging), double-buffered: 2 x 68 KB.
-//    Buffer range checking returns zeros for rows past M or N.
+//  * K advances in super-steps of 256 elements (128 code bytes per row). A
+//    super-step (both code tiles and their scales, 68 KB) moves through a
+//    three-deep pipeline: global -> VGPRs (16-byte buffer loads, issued two
+//    super-steps ahead), VGPRs -> LDS (ds_write, one super-step ahead, into
+//    the idle half of a 2 x 68 KB double buffer), LDS -> MFMA. The barrier
+//    between super-steps waits for LDS work only, so global loads stay in
+//    flight across it and get a whole super-step to return. Buffer range
+//    checking returns zeros for rows past M or N.
 //  * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at slot
 //    c ^ ((r / 2) mod 8) so that the lanes reading one column of chunks hit
 //    distinct banks (measured with the LDS bank-conflict counter).
