@@ -17,6 +17,7 @@ Other workloads (--workload c1..c5) are for profiling; the default is the one
 the headline metric is quoted on.
 """
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -29,6 +30,9 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 PEAK_TFLOPS = {"mxfp4": 10100.0, "mxfp8": 5000.0, "nvfp4": 2500.0, "w4a16": 2500.0}
 ROTATE_BYTES = 1 << 30  # activation copies cycled per step: > 256 MB MALL
+WEIGHT_ROTATE_BYTES = 512 << 20  # weight copies cycled per step: > 256 MB MALL, so
+                                 # every step streams its weights from HBM, as the
+                                 # layers of a model would
 
 
 def parse():
@@ -94,6 +98,10 @@ def main():
     wfmt = "mxfp4" if fmt == "w4a16" else fmt
     qb = mx.quantize(Bx, wfmt)  # weights: pre-quantized, outside the timed step
     del Bx
+    wbytes = qb.codes.numel() * qb.codes.element_size() + qb.scales.numel() * qb.scales.element_size()
+    nwcopies = max(2, -(-WEIGHT_ROTATE_BYTES // wbytes))
+    weights = [qb] + [dataclasses.replace(qb, codes=qb.codes.clone(), scales=qb.scales.clone())
+                      for _ in range(nwcopies - 1)]
     ncopies = max(1, min(8, ROTATE_BYTES // A.numel() // 2))
     acts = [A] + [A.clone() for _ in range(ncopies - 1)]
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -113,7 +121,7 @@ def main():
             qa = a
         if ev is not None:
             ev[1].record(stream)
-        mx.gemm(qa, qb, torch.bfloat16, out=out, workspace=ws)
+        mx.gemm(qa, weights[i % len(weights)], torch.bfloat16, out=out, workspace=ws)
         if ev is not None:
             ev[2].record(stream)
 
@@ -174,7 +182,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "format": fmt, "M": M, "N": N, "K": K,
                    "step": ("quantize(A) + gemm" if quantize_a else "gemm") + ", bf16 out",
-                   "weights": "pre-quantized", "activation_copies_rotated": len(acts)},
+                   "weights": "pre-quantized", "activation_copies_rotated": len(acts),
+                   "weight_copies_rotated": len(weights)},
         "roofline": roof,
         "gemm": {"TFLOP/s": gemm_tflops, "ms": g_avg, "frac_of_peak": gemm_tflops / peak},
     }

@@ -2,17 +2,32 @@
 // weights (stored N x K) with fp32 accumulation. Weight-only quantization saves
 // memory traffic rather than compute (noticiai.com.br page on Nunchaku W4A4:
 // dequantizing weights at compute time mainly saves memory), so this kernel is
-// built to stream the weight codes once from HBM:
-//  * each lane loads 16 bytes (32 codes, exactly one E8M0 block) per step and
-//    expands them to bf16 with v_cvt_scalef32_pk_bf16_fp4, which multiplies by
-//    the power-of-two scale exactly;
-//  * the 32 codes feed four v_mfma_f32_16x16x32_bf16 in a row. The K order
-//    inside a 128-element step is permuted the same way for both operands:
-//    MFMA j uses elements 32g + 8j .. 32g + 8j + 7 in lane group g, so a lane's
-//    codes, its one scale and its activation slice stay contiguous;
-//  * activations for the workgroup's K range are staged once in LDS;
+// built to stream the weight codes once from HBM at full bandwidth:
+//  * a workgroup covers TN = 256 weight rows x 16 activation rows x KP = 2048
+//    K (16 steps of 128). Wave w owns rows 64 w .. 64 w + 63 as 4 groups of
+//    16; lane l takes row l % 16 of a group, and at step s lane group
+//    g = l / 16 takes E8M0 block 4 s + g, so one 16-byte load instruction
+//    covers 16 rows x 64 contiguous bytes;
+//  * a wave loads half a row group at a time, 8 steps back to back (16 rows x
+//    512 contiguous bytes, so DRAM pages are read in bursts), double-buffered
+//    in VGPRs: the next half is in flight while this one is used. (Steps
+//    spread over the whole kernel re-open every page many times and cap the
+//    stream at about half of the HBM rate.) Each block (32 codes) is
+//    expanded to bf16 with v_cvt_scalef32_pk_bf16_fp4, which multiplies by
+//    the power-of-two scale exactly, and feeds four v_mfma_f32_16x16x32_bf16:
+//    MFMA j takes elements 8 j .. 8 j + 7 of the block from every lane group.
+//    The activations follow the same K permutation, so the sum over K is
+//    unchanged;
+//  * the workgroup's activations (16 x KP bf16, 64 KB, 16-byte chunks XOR-
+//    swizzled by row) are staged once in LDS, loaded before the weights so
+//    that the LDS writes wait for them alone; the 4 waves x 4 row groups share
+//    them, so the activation traffic is a quarter of the weights';
+//  * every global load is a range-checked buffer load without a branch (rows
+//    past N or M, and blocks past K, read as zeros), which keeps the in-order
+//    load counter exact so that waits name only the data they need;
 //  * K is split across workgroups; partial sums go to a workspace and a second
 //    kernel adds them in a fixed order (deterministic, no float atomics).
+// Two accumulator chains per row, each 32 MFMAs per split.
 #include "bf16.h"
 #include "mx_internal.h"
 
@@ -24,11 +39,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
-constexpr int TN = 64;    // output columns per workgroup (16 per wave)
-constexpr int TM = 16;    // activation rows per workgroup
-constexpr int KC = 512;   // K elements of activations staged in LDS at once
-constexpr int kAStride = KC * 2 + 16;  // bytes per LDS activation row (padded)
-constexpr uint32_t kUnitScale = 127u;
+constexpr int TN = 256;                 // weight rows per workgroup (64 per wave)
+constexpr int TM = 16;                  // activation rows per workgroup
+constexpr int KP = 2048;                // K elements per split
+constexpr int kSteps = KP / 128;        // 16 steps: 4 blocks (one per lane group) each
+constexpr int kHalf = kSteps / 2;       // steps loaded together
+constexpr int kARow = KP * 2;           // bytes per LDS activation row
+constexpr int kALoads = TM * KP / 8 / kThreads;  // 16-byte activation loads per thread
+constexpr uint32_t kRsrcFlags = 0x00020000u;     // raw buffer, gfx9 data format
+constexpr uint32_t kOOB = 0x80000000u;           // an offset past every buffer's range
 
 __device__ __forceinline__ float e8m0_to_float(uint32_t E) {
   return __builtin_bit_cast(float, E == 0 ? 0x00400000u : E << 23);
@@ -44,73 +63,143 @@ __device__ __forceinline__ bf16x8 expand8(uint32_t q, float s) {
   return __builtin_bit_cast(bf16x8, o);
 }
 
-// grid: x = N tiles, y = M tiles, z = K splits. Each split covers kper
-// elements (a multiple of 128) starting at z * kper.
+// The lane's codes of steps 8 u .. 8 u + 7 for one row (block bbase + 4 s + g
+// at step s), and their scales: word q of sc[v] holds the scales of blocks
+// bbase + 16 (2 u + v) + 4 q .. + 3, byte g being this lane's block of step
+// 8 u + 4 v + q. Blocks past K read as zero codes (and scale 0, harmless
+// against them); with valid false nothing is read (all offsets out of range).
+__device__ __forceinline__ void load_half(u32x4 (&q)[kHalf], u32x4 (&sc)[kHalf / 4],
+                                          __amdgpu_buffer_rsrc_t rB, __amdgpu_buffer_rsrc_t rS,
+                                          uint32_t wrow, uint32_t srow, int bbase, int g,
+                                          int kblocks, int u, bool valid) {
+#pragma unroll
+  for (int i = 0; i < kHalf; i++) {
+    const int b = bbase + 4 * (kHalf * u + i) + g;
+    q[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, valid && b < kblocks ? wrow + (uint32_t)b * 16u : kOOB, 0, 0);
+  }
+  if (kblocks % 16 == 0) {
+#pragma unroll
+    for (int v = 0; v < kHalf / 4; v++) {
+      const int b = bbase + 16 * (2 * u + v);
+      sc[v] = __builtin_amdgcn_raw_buffer_load_b128(rS, valid && b < kblocks ? srow + (uint32_t)b : kOOB, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < kHalf / 4; v++) {
+      uint32_t w[4];
+#pragma unroll
+      for (int qq = 0; qq < 4; qq++) {
+        const int b = bbase + 16 * (2 * u + v) + 4 * qq + g;  // only byte g is used
+        w[qq] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rS, valid && b < kblocks ? srow + (uint32_t)b : kOOB, 0, 0) << (8 * g);
+      }
+      sc[v] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
+// The MFMAs of one loaded half: steps 8 u .. 8 u + 7, two accumulator chains.
+__device__ __forceinline__ void compute_half(const u32x4 (&q)[kHalf], const u32x4 (&sc)[kHalf / 4],
+                                             const uint8_t* arow, int r, int g, int u,
+                                             f32x4 (&acc)[2]) {
+#pragma unroll
+  for (int i = 0; i < kHalf; i++) {
+    const int bl = 4 * (kHalf * u + i) + g;  // block within the split
+    const uint32_t E = (sc[i / 4][i % 4] >> (8 * g)) & 0xFFu;
+    const float scale = e8m0_to_float(E);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const bf16x8 a = *(const bf16x8*)(arow + (((4 * bl + j) ^ r) * 16));
+      const bf16x8 w = (E == 255) ? __builtin_bit_cast(bf16x8, u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u})
+                                  : expand8(q[i][j], scale);
+      acc[j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w, acc[j & 1], 0, 0, 0);
+    }
+    // One step per scheduling window: hoisting later steps' LDS reads and
+    // expansions would need more registers than two waves per SIMD allow.
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// grid: x = N tiles, y = M tiles, z = K splits of KP elements.
 template <bool DIRECT, int OUT>
-__global__ __launch_bounds__(kThreads) void gemm_w4a16_kernel(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(kThreads, 2) void gemm_w4a16_kernel(const uint16_t* __restrict__ A,
                                                               const uint8_t* __restrict__ B,
                                                               const uint8_t* __restrict__ SB,
                                                               void* __restrict__ out, int64_t ldc,
-                                                              int M, int N, int K, int kper) {
-  __shared__ __attribute__((aligned(16))) uint8_t lA[TM * kAStride];
+                                                              int M, int N, int K) {
+  __shared__ __attribute__((aligned(16))) uint8_t lA[TM * kARow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int m0 = blockIdx.y * TM;
-  const int n = blockIdx.x * TN + wave * 16 + r;  // this lane's weight row
-  const int kbeg = blockIdx.z * kper;
-  const int kend = min(K, kbeg + kper);
-  const int64_t rowbytes = K / 2;
+  const int kbeg = blockIdx.z * KP;
+  const int kend = min(K, kbeg + KP);
   const int kblocks = K / 32;
+  const int bbase = kbeg / 32;      // first block of the split
 
-  // Four accumulators, one per MFMA of a 128-element step: independent chains
-  // keep the matrix pipeline busy and each chain at most K/128 steps long.
-  f32x4 acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-  for (int kc = kbeg; kc < kend; kc += KC) {
-    __syncthreads();
-    // Stage activations [m0, m0+16) x [kc, kc+KC) as bf16, zero-padded.
-    for (int i = tid; i < TM * KC / 8; i += kThreads) {
-      const int row = i / (KC / 8), c8 = i % (KC / 8);
-      const int k = kc + c8 * 8;
-      u32x4 v = {0, 0, 0, 0};
-      if (m0 + row < M && k < kend) v = *(const u32x4*)(A + (int64_t)(m0 + row) * K + k);
-      *(u32x4*)(lA + row * kAStride + c8 * 16) = v;
-    }
-    __syncthreads();
-    const int ksteps = min(KC, kend - kc);  // multiple of 32
-    for (int ks = 0; ks < ksteps; ks += 128) {
-      const int k = kc + ks + 32 * g;  // first element of this lane's block
-      u32x4 q = {0, 0, 0, 0};
-      uint32_t E = kUnitScale;
-      if (n < N && k < kend) {
-        q = __builtin_nontemporal_load((const u32x4*)(B + (int64_t)n * rowbytes + k / 2));
-        E = SB[(int64_t)n * kblocks + k / 32];
-      }
-      const float s = e8m0_to_float(E);
-      const uint8_t* arow = lA + r * kAStride + (ks + 32 * g) * 2;
-      const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+  // Buffer views based at this workgroup's first weight row and first
+  // activation row: 32-bit offsets, and rows past N or M read as zeros.
+  const int n0 = blockIdx.x * TN;
+  const int nrows = min(TN, N - n0), mrows = min(TM, M - m0);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(B + (int64_t)n0 * (K / 2)), 0, nrows * (K / 2), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rS = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(SB + (int64_t)n0 * kblocks), 0, nrows * kblocks, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + (int64_t)m0 * K), 0, mrows * K * 2, kRsrcFlags);
+  const int lr0 = wave * 64 + r;  // row within the tile, row group 0
+  const uint32_t wstride = (uint32_t)16 * (uint32_t)(K / 2), sstride = (uint32_t)16 * (uint32_t)kblocks;
+  const uint32_t wrow0 = (uint32_t)lr0 * (uint32_t)(K / 2), srow0 = (uint32_t)lr0 * (uint32_t)kblocks;
+
+  // 1. Activation loads first: [m0, m0 + 16) x [kbeg, kbeg + KP), zero-padded.
+  u32x4 av[kALoads];
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const bf16x8 a = *(const bf16x8*)(arow + j * 16);
-        const bf16x8 w = (E == 255) ? __builtin_bit_cast(bf16x8, u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u})
-                                    : expand8(qw[j], s);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w, acc[j], 0, 0, 0);
-      }
-    }
+  for (int i = 0; i < kALoads; i++) {
+    const int idx = tid + i * kThreads;
+    const int row = idx / (KP / 8), c8 = idx % (KP / 8);
+    const int k = kbeg + c8 * 8;
+    const uint32_t off = k < kend ? ((uint32_t)row * (uint32_t)K + (uint32_t)k) * 2u : kOOB;
+    av[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
   }
-  const f32x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  // Lane l holds column n (= l % 16 within the wave's 16) for rows 4g + t.
-  if (n >= N) return;
+  // 2. The first half row group's codes and scales.
+  u32x4 q0[kHalf], q1[kHalf], s0[kHalf / 4], s1[kHalf / 4];
+  load_half(q0, s0, rB, rS, wrow0, srow0, bbase, g, kblocks, 0, true);
+  // 3. Activations to LDS (waits only for the activation loads, which were
+  //    issued first): 16-byte chunk c of row m at slot c ^ (m mod 16).
 #pragma unroll
-  for (int t = 0; t < 4; t++) {
-    const int m = m0 + 4 * g + t;
-    if (m >= M) continue;
-    if (DIRECT) {
-      if (OUT == kOutF32)
-        ((float*)out)[(int64_t)m * ldc + n] = sum[t];
-      else
-        ((uint16_t*)out)[(int64_t)m * ldc + n] = bf16_bits(sum[t]);
-    } else {
-      ((float*)out)[((int64_t)blockIdx.z * M + m) * N + n] = sum[t];
+  for (int i = 0; i < kALoads; i++) {
+    const int idx = tid + i * kThreads;
+    const int row = idx / (KP / 8), c8 = idx % (KP / 8);
+    *(u32x4*)(lA + row * kARow + ((c8 ^ (row & 15)) * 16)) = av[i];
+  }
+  __syncthreads();
+
+  // 4. Row groups one after another; loads run one half ahead of the MFMAs
+  //    (branch-free: the load past the last group is all out of range).
+  const uint8_t* arow = lA + r * kARow;
+#pragma unroll 1
+  for (int h = 0; h < 4; h++) {
+    const uint32_t wrow = wrow0 + (uint32_t)h * wstride, srow = srow0 + (uint32_t)h * sstride;
+    f32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    load_half(q1, s1, rB, rS, wrow, srow, bbase, g, kblocks, 1, true);
+    compute_half(q0, s0, arow, r, g, 0, acc);
+    load_half(q0, s0, rB, rS, wrow + wstride, srow + sstride, bbase, g, kblocks, 0, h + 1 < 4);
+    compute_half(q1, s1, arow, r, g, 1, acc);
+    // Lane l holds column n of activation rows 4 g + t.
+    const int n = n0 + lr0 + 16 * h;
+    const f32x4 sum = acc[0] + acc[1];
+    if (n < N) {
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        const int m = m0 + 4 * g + t;
+        if (m >= M) continue;
+        if (DIRECT) {
+          if (OUT == kOutF32)
+            ((float*)out)[(int64_t)m * ldc + n] = sum[t];
+          else
+            ((uint16_t*)out)[(int64_t)m * ldc + n] = bf16_bits(sum[t]);
+        } else {
+          ((float*)out)[((int64_t)blockIdx.z * M + m) * N + n] = sum[t];
+        }
+      }
     }
   }
 }
@@ -130,55 +219,36 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const float* __
     ((uint16_t*)C)[(int64_t)m * ldc + n] = bf16_bits(s);
 }
 
-struct Plan {
-  int splits;
-  int kper;
-};
-
-// Enough workgroups to cover the chip several times (7 per CU on 256 CUs),
-// with each split at most 16 steps of 128 elements (16 MFMAs per chain).
-Plan plan(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((N + TN - 1) / TN) * ((M + TM - 1) / TM);
-  const int64_t ksteps = (K + 127) / 128;
-  int splits = 1;
-  while (splits < 64 && (tiles * splits < 1792 || (ksteps + splits - 1) / splits > 16) &&
-         splits * 2 <= ksteps)
-    splits *= 2;
-  const int64_t kper_steps = (ksteps + splits - 1) / splits;
-  Plan p;
-  p.kper = (int)(kper_steps * 128);
-  p.splits = (int)((K + p.kper - 1) / p.kper);
-  return p;
-}
+int splits_for(int64_t K) { return (int)((K + KP - 1) / KP); }
 
 }  // namespace
 
 size_t gemm_w4a16_workspace(int64_t M, int64_t N, int64_t K) {
-  const Plan p = plan(M, N, K);
-  return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
+  const int splits = splits_for(K);
+  return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
 }
 
 hipError_t gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* a, const void* b,
                       const void* sb, int out_dtype, void* c, int64_t ldc, void* workspace,
                       hipStream_t s) {
-  const Plan p = plan(M, N, K);
-  const dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM), (unsigned)p.splits);
+  const int splits = splits_for(K);
+  const dim3 grid((unsigned)((N + TN - 1) / TN), (unsigned)((M + TM - 1) / TM), (unsigned)splits);
   const uint16_t* A = (const uint16_t*)a;
   const uint8_t *B = (const uint8_t*)b, *SB = (const uint8_t*)sb;
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (p.splits == 1) {
+  if (splits == 1) {
     if (out_dtype == kOutF32)
-      gemm_w4a16_kernel<true, kOutF32><<<grid, kThreads, 0, s>>>(A, B, SB, c, ldc, m, n, k, p.kper);
+      gemm_w4a16_kernel<true, kOutF32><<<grid, kThreads, 0, s>>>(A, B, SB, c, ldc, m, n, k);
     else
-      gemm_w4a16_kernel<true, kOutBF16><<<grid, kThreads, 0, s>>>(A, B, SB, c, ldc, m, n, k, p.kper);
+      gemm_w4a16_kernel<true, kOutBF16><<<grid, kThreads, 0, s>>>(A, B, SB, c, ldc, m, n, k);
     return hipGetLastError();
   }
-  gemm_w4a16_kernel<false, kOutF32><<<grid, kThreads, 0, s>>>(A, B, SB, workspace, 0, m, n, k, p.kper);
+  gemm_w4a16_kernel<false, kOutF32><<<grid, kThreads, 0, s>>>(A, B, SB, workspace, 0, m, n, k);
   const unsigned rblocks = (unsigned)((M * N + kThreads - 1) / kThreads);
   if (out_dtype == kOutF32)
-    splitk_reduce_kernel<kOutF32><<<rblocks, kThreads, 0, s>>>((const float*)workspace, c, ldc, m, n, p.splits);
+    splitk_reduce_kernel<kOutF32><<<rblocks, kThreads, 0, s>>>((const float*)workspace, c, ldc, m, n, splits);
   else
-    splitk_reduce_kernel<kOutBF16><<<rblocks, kThreads, 0, s>>>((const float*)workspace, c, ldc, m, n, p.splits);
+    splitk_reduce_kernel<kOutBF16><<<rblocks, kThreads, 0, s>>>((const float*)workspace, c, ldc, m, n, splits);
   return hipGetLastError();
 }
 
