@@ -15,7 +15,7 @@ OUT = os.path.join(HERE, "libmx.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["mx_api.cpp", "quantize.hip", "dequantize.hip", "gemm_mx.hip", "gemm_mxfp4.hip", "gemm_bf16x.hip",
+SOURCES = ["mx_api.cpp", "quantize.hip", "dequantize.hip", "gemm_mx.hip", "gemm_mxfp4.hip", "gemm_bf16x.hip", "gemm_bf16x_large.hip",
            "gemm_w4a16.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.

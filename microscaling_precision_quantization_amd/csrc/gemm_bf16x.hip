@@ -199,6 +199,8 @@ void launch(const dim3& grid, hipStream_t s, const uint8_t* A, const uint8_t* SA
 hipError_t gemm_bf16x(int fmt, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
                       const float* ta, const void* b, const void* sb, const float* tb,
                       int out_dtype, void* c, int64_t ldc, hipStream_t s) {
+  if (gemm_bf16x_large_fits(fmt, M, N, K))
+    return gemm_bf16x_large(fmt, M, N, K, a, sa, ta, b, sb, tb, out_dtype, c, ldc, s);
   const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;

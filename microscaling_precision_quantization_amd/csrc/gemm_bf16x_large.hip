@@ -1,0 +1,388 @@
+// Large-tile MXFP8 x MXFP8 and NVFP4 x NVFP4 GEMM for gfx950 on the 16-bit
+// MFMAs, every operand expanded exactly to bf16 (MXFP8) or fp16 (NVFP4) (why
+// not the FP8/FP4 matrix paths is explained in gemm_bf16x.hip).
+//
+// Design for CDNA4:
+//  * 256 x 256 output tile per workgroup, 4 waves (one per SIMD) of 128 x 128,
+//    each wave 4 x 4 MFMAs of 32 x 32 with 256 fp32 accumulators per lane.
+//  * K advances in stages of 64 elements. A stage moves through a three-deep
+//    pipeline: global -> VGPRs (16-byte code chunks, range-checked buffer
+//    loads issued two stages ahead), VGPRs -> bf16 -> LDS (each code expanded
+//    once, one stage ahead, into the idle half of a 2 x 64 KB double buffer),
+//    LDS -> MFMA. The barrier between stages waits for LDS work only, so the
+//    global loads stay in flight across it.
+//  * Expansion: MXFP8 to bf16 with v_cvt_scalef32_pk_bf16_fp8 and the E8M0
+//    scale as an fp32 power of two (the instruction reads only the scale's
+//    exponent; 255 makes every output NaN, as in the oracle). NVFP4 to fp16:
+//    v_cvt_scalef32_pk_f16_fp4 at unit scale and one packed fp16 multiply by
+//    the E4M3 block scale, exact because every E2M1 x E4M3 product has at
+//    most 6 significant bits and lies in [2^-10, 2688]; the NVFP4 kernel then
+//    runs on v_mfma_f32_32x32x16_f16.
+//  * LDS rows hold 64 16-bit values (128 bytes, 8 chunks of 16); chunk k of row m
+//    lives in slot k ^ ((m / 2) mod 8), conflict-free for the staging writes
+//    and for the MFMA reads (16 rows at one chunk index per 16-lane group).
+//  * MFMA sub-step s (K = 16) gives lane group g chunk 2 s + g of its row
+//    (32 x 32 x 16 layout: lane r + 32 g supplies K elements
+//    [8 g, 8 g + 8) of row r), the same permutation for A and B.
+//  * Tile order and epilogue as in the MXFP4 kernel (tile256.h); the NVFP4
+//    tensor scales multiply the fp32 result there.
+#include <type_traits>
+
+#include "mx_internal.h"
+#include "tile256.h"
+
+namespace mx {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int BM = 256, BN = 256;
+constexpr int BK = 64;                            // K elements per stage
+constexpr int kRowBytes = BK * 2;                 // one LDS row: 64 bf16
+constexpr int kTileBytes = BM * kRowBytes;        // 32 KB per operand
+constexpr int kStage = 2 * kTileBytes;            // 64 KB
+constexpr int kSmem = 139264;                     // 2 stages (128 KB) or the epilogue (136 KB)
+constexpr uint32_t kRsrcFlags = 0x00020000u;      // raw buffer, gfx9 data format
+constexpr uint32_t kOOB = 0x80000000u;            // an offset past every buffer's range
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// Per-format staging geometry. A thread owns kChunks code chunks of 16 bytes
+// per operand per stage: MXFP8 chunk = 16 codes (4 per row, rows t/4 + 64u),
+// NVFP4 chunk = 32 codes (2 per row, rows t/2 + 128u).
+template <int FMT>
+struct Geo {
+  static constexpr int kCodesPerChunk = (FMT == kMXFP8) ? 16 : 32;
+  static constexpr int kChunksPerRow = BK / kCodesPerChunk;      // 4 or 2
+  static constexpr int kChunks = BM * kChunksPerRow / kThreads;  // per thread per operand: 4 or 2
+  static constexpr int kRowStep = kThreads / kChunksPerRow;      // 64 or 128
+  static constexpr int kBlock = (FMT == kMXFP8) ? 32 : 16;       // elements per scale
+};
+
+// One thread's share of a stage for both operands: codes and raw scale bits
+// (MXFP8: the E8M0 byte of the chunk's block; NVFP4: the chunk's two E4M3
+// bytes).
+template <int FMT>
+struct Stage {
+  u32x4 qa[Geo<FMT>::kChunks], qb[Geo<FMT>::kChunks];
+  uint32_t sa[Geo<FMT>::kChunks], sb[Geo<FMT>::kChunks];
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_op(u32x4 (&q)[Geo<FMT>::kChunks], uint32_t (&sc)[Geo<FMT>::kChunks],
+                                        __amdgpu_buffer_rsrc_t rX, __amdgpu_buffer_rsrc_t rS,
+                                        uint32_t rowbytes, uint32_t scalebytes, int K, int s,
+                                        int tid, int u) {
+  using G = Geo<FMT>;
+  const int row = tid / G::kChunksPerRow + G::kRowStep * u;
+  const int c = tid % G::kChunksPerRow;
+  const int k = s * BK + c * G::kCodesPerChunk;  // first element of the chunk
+  const bool ok = k < K;
+  const uint32_t cb = (FMT == kMXFP8) ? (uint32_t)k : (uint32_t)k / 2;
+  q[u] = __builtin_amdgcn_raw_buffer_load_b128(rX, ok ? (uint32_t)row * rowbytes + cb : kOOB, 0, 0);
+  const uint32_t so = (uint32_t)row * scalebytes + (uint32_t)(k / G::kBlock);
+  if (FMT == kMXFP8)
+    sc[u] = __builtin_amdgcn_raw_buffer_load_b8(rS, ok ? so : kOOB, 0, 0);
+  else
+    sc[u] = __builtin_amdgcn_raw_buffer_load_b16(rS, ok ? so : kOOB, 0, 0);
+}
+
+// The stage's staging work is split into 4 parts, one per MFMA sub-step: an
+// item is one (operand, chunk u) pair, 2 kChunks items per stage, so a part
+// holds 2 items (MXFP8: chunk P of A and of B) or 1 (NVFP4: chunk P % 2 of A
+// for P < 2, of B otherwise).
+template <int FMT, int P>
+__device__ __forceinline__ void load_part(Stage<FMT>& st, __amdgpu_buffer_rsrc_t rA,
+                                          __amdgpu_buffer_rsrc_t rSA, __amdgpu_buffer_rsrc_t rB,
+                                          __amdgpu_buffer_rsrc_t rSB, uint32_t rowbytes,
+                                          uint32_t scalebytes, int K, int s, int tid) {
+  if (FMT == kMXFP8) {
+    load_op<FMT>(st.qa, st.sa, rA, rSA, rowbytes, scalebytes, K, s, tid, P);
+    load_op<FMT>(st.qb, st.sb, rB, rSB, rowbytes, scalebytes, K, s, tid, P);
+  } else if (P < 2) {
+    load_op<FMT>(st.qa, st.sa, rA, rSA, rowbytes, scalebytes, K, s, tid, P % 2);
+  } else {
+    load_op<FMT>(st.qb, st.sb, rB, rSB, rowbytes, scalebytes, K, s, tid, P % 2);
+  }
+}
+
+// Expands one chunk to bf16 and writes it to LDS row `row` of `tile`.
+template <int FMT>
+__device__ __forceinline__ void expand_chunk(const u32x4& q, uint32_t sbits, uint8_t* tile, int row,
+                                             int c) {
+  uint8_t* base = tile + row * kRowBytes;
+  const int sw = swz(row);
+  if (FMT == kMXFP8) {
+    // 16 codes -> LDS chunks 2c, 2c + 1.
+    const float s = __builtin_bit_cast(float, sbits << 23);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], s, false));
+      o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], s, true));
+    }
+    *(u32x4*)(base + (((2 * c) ^ sw) * 16)) = u32x4{o[0], o[1], o[2], o[3]};
+    *(u32x4*)(base + (((2 * c + 1) ^ sw) * 16)) = u32x4{o[4], o[5], o[6], o[7]};
+  } else {
+    // 32 codes (two 16-blocks) -> LDS chunks 4c .. 4c + 3, as fp16: every
+    // e * s_b (E2M1 times E4M3: at most 6 significant bits, magnitude in
+    // [2^-10, 2688]) is exact in fp16, so one packed fp16 multiply per pair
+    // is exact; v_cvt_scalef32_pk_f16_fp4 at unit scale gives the codes.
+    const f16x2 s0 = (f16x2)(_Float16)__builtin_amdgcn_cvt_f32_fp8((int)(sbits & 0xFFu), 0);
+    const f16x2 s1 = (f16x2)(_Float16)__builtin_amdgcn_cvt_f32_fp8((int)(sbits >> 8), 0);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const f16x2 sc = (i < 2) ? s0 : s1;
+      uint32_t o[4];
+#pragma unroll
+      for (int p = 0; p < 4; p++) {
+        f16x2 e;
+        switch (p) {
+          case 0: e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 0); break;
+          case 1: e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 1); break;
+          case 2: e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 2); break;
+          default: e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 3); break;
+        }
+        o[p] = __builtin_bit_cast(uint32_t, e * sc);
+      }
+      *(u32x4*)(base + (((4 * c + i) ^ sw) * 16)) = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  }
+}
+
+// Part P of a staged stage's expansion (the items of load_part<P>).
+template <int FMT, int P>
+__device__ __forceinline__ void store_part(const Stage<FMT>& st, uint8_t* stage, int tid) {
+  using G = Geo<FMT>;
+  const int c = tid % G::kChunksPerRow;
+  if (FMT == kMXFP8) {
+    const int row = tid / G::kChunksPerRow + G::kRowStep * P;
+    expand_chunk<FMT>(st.qa[P], st.sa[P], stage, row, c);
+    expand_chunk<FMT>(st.qb[P], st.sb[P], stage + kTileBytes, row, c);
+  } else {
+    const int u = P % 2;
+    const int row = tid / G::kChunksPerRow + G::kRowStep * u;
+    if (P < 2)
+      expand_chunk<FMT>(st.qa[u], st.sa[u], stage, row, c);
+    else
+      expand_chunk<FMT>(st.qb[u], st.sb[u], stage + kTileBytes, row, c);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_stage(Stage<FMT>& st, __amdgpu_buffer_rsrc_t rA,
+                                           __amdgpu_buffer_rsrc_t rSA, __amdgpu_buffer_rsrc_t rB,
+                                           __amdgpu_buffer_rsrc_t rSB, uint32_t rowbytes,
+                                           uint32_t scalebytes, int K, int s, int tid) {
+  __builtin_amdgcn_sched_barrier(0);
+  load_part<FMT, 0>(st, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s, tid);
+  __builtin_amdgcn_sched_barrier(0);
+  load_part<FMT, 1>(st, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s, tid);
+  __builtin_amdgcn_sched_barrier(0);
+  load_part<FMT, 2>(st, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s, tid);
+  __builtin_amdgcn_sched_barrier(0);
+  load_part<FMT, 3>(st, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s, tid);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Fragments of sub-step S: 4 A and 4 B tiles of 32 rows, chunk 2S + g.
+template <int S, typename V>
+__device__ __forceinline__ void load_frags(const uint8_t* As, const uint8_t* Bs, int wm, int wn,
+                                           int r, int g, V (&fa)[4], V (&fb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int ra = wm * 128 + i * 32 + r;
+    const int rb = wn * 128 + i * 32 + r;
+    fa[i] = *(const V*)(As + ra * kRowBytes + (((2 * S + g) ^ swz(ra)) * 16));
+    fb[i] = *(const V*)(Bs + rb * kRowBytes + (((2 * S + g) ^ swz(rb)) * 16));
+  }
+}
+
+__device__ __forceinline__ void mfma16(const bf16x8 (&fa)[4], const bf16x8 (&fb)[4], f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+      // Operands swapped (B first): the result tile is C^T (see tile256.h).
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+}
+
+__device__ __forceinline__ void mfma16(const f16x8 (&fa)[4], const f16x8 (&fb)[4], f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+}
+
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Issue order of one sub-step region (sched_group_barrier masks: 0x008 MFMA,
+// 0x100 LDS read, 0x200 LDS write, 0x020 VMEM read, 0x002 VALU), closed by a
+// fence: the next sub-step's 8 fragment reads go out within the first 4
+// MFMAs, ahead of the staging traffic, then the global loads, then the
+// expansion and its LDS writes spread over the MFMAs that remain.
+template <int FMT, bool WITH_READS>
+__device__ __forceinline__ void region_order() {
+  if (WITH_READS) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  }
+  if (FMT == kMXFP8) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, WITH_READS ? 4 : 8, 0);
+  } else {
+#pragma unroll
+    for (int k = 0; k < (WITH_READS ? 12 : 16); k++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+#pragma unroll
+    for (int k = 0; k < 2; k++) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int FMT, int OUT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16x_large_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const float* __restrict__ TA,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB, const float* __restrict__ TB,
+    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 31, g = lane >> 5;
+  int tm, tn;
+  tile256::tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // Buffer views based at the tile's first rows: rows past M or N read as 0.
+  const uint32_t rowbytes = (FMT == kMXFP8) ? (uint32_t)K : (uint32_t)(K / 2);
+  const uint32_t scalebytes = (uint32_t)(K / Geo<FMT>::kBlock);
+  const int mrows = min(BM, M - m0), nrows = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * rowbytes), 0, (int)(mrows * rowbytes), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)(B + (int64_t)n0 * rowbytes), 0, (int)(nrows * rowbytes), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc((void*)(SA + (int64_t)m0 * scalebytes), 0, (int)(mrows * scalebytes), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rSB = __builtin_amdgcn_make_buffer_rsrc((void*)(SB + (int64_t)n0 * scalebytes), 0, (int)(nrows * scalebytes), kRsrcFlags);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
+
+  const int nsteps = (K + BK - 1) / BK;
+  // Prologue: stage 0 to LDS, stage 1 in registers (issued in the loop's
+  // order so that the in-order load counter lets the loop's first expansions
+  // wait only for their own part).
+  Stage<FMT> R;
+  load_stage<FMT>(R, rA, rSA, rB, rSB, rowbytes, scalebytes, K, 0, tid);
+  store_part<FMT, 0>(R, smem, tid);
+  store_part<FMT, 1>(R, smem, tid);
+  store_part<FMT, 2>(R, smem, tid);
+  store_part<FMT, 3>(R, smem, tid);
+  load_stage<FMT>(R, rA, rSA, rB, rSB, rowbytes, scalebytes, K, min(1, nsteps - 1), tid);
+  for (int s = 0; s < nsteps; s++) {
+    // Every thread's LDS writes of stage s are done and every wave is done
+    // reading stage s-1, whose buffer receives stage s+1 below. Only LDS work
+    // is waited for: the global loads stay in flight.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    fence();
+    const uint8_t* cur = smem + (s & 1) * kStage;
+    uint8_t* nxt = smem + ((s + 1) & 1) * kStage;
+    // Branch-free body (a branch lets the compiler sink the MFMAs): the last
+    // iterations re-stage the final stage into the idle buffer.
+    const int s2 = min(s + 2, nsteps - 1);
+    const uint8_t* As = cur;
+    const uint8_t* Bs = cur + kTileBytes;
+    // Operand elements: bf16 for MXFP8, fp16 for NVFP4.
+    using V = typename std::conditional<FMT == kMXFP8, bf16x8, f16x8>::type;
+    V fa0[4], fb0[4], fa1[4], fb1[4];
+    load_frags<0>(As, Bs, wm, wn, r, g, fa0, fb0);
+    fence();
+    // Sub-step 0: next fragments, expansion of chunk 0 of stage s+1, loads of
+    // chunk 0 of stage s+2, MFMAs. Likewise for the other sub-steps.
+    load_frags<1>(As, Bs, wm, wn, r, g, fa1, fb1);
+    store_part<FMT, 0>(R, nxt, tid);
+    load_part<FMT, 0>(R, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
+    mfma16(fa0, fb0, acc);
+    region_order<FMT, true>();
+    load_frags<2>(As, Bs, wm, wn, r, g, fa0, fb0);
+    store_part<FMT, 1>(R, nxt, tid);
+    load_part<FMT, 1>(R, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
+    mfma16(fa1, fb1, acc);
+    region_order<FMT, true>();
+    load_frags<3>(As, Bs, wm, wn, r, g, fa1, fb1);
+    store_part<FMT, 2>(R, nxt, tid);
+    load_part<FMT, 2>(R, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
+    mfma16(fa0, fb0, acc);
+    region_order<FMT, true>();
+    store_part<FMT, 3>(R, nxt, tid);
+    load_part<FMT, 3>(R, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
+    mfma16(fa1, fb1, acc);
+    region_order<FMT, false>();
+  }
+  __syncthreads();
+  const float ts = (FMT == kNVFP4) ? TA[0] * TB[0] : 1.0f;
+  tile256::store_tile<OUT>(acc, smem, ts, C, ldc, M, N, m0, n0, wave, lane);
+}
+
+template <int FMT>
+void launch(hipStream_t s, int tm, int tn, const uint8_t* A, const uint8_t* SA, const float* TA,
+            const uint8_t* B, const uint8_t* SB, const float* TB, int out_dtype, void* c,
+            int64_t ldc, int M, int N, int K) {
+  const dim3 grid((unsigned)(tm * tn));
+  if (out_dtype == kOutF32)
+    gemm_bf16x_large_kernel<FMT, kOutF32><<<grid, kThreads, 0, s>>>(A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn);
+  else
+    gemm_bf16x_large_kernel<FMT, kOutBF16><<<grid, kThreads, 0, s>>>(A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn);
+}
+
+}  // namespace
+
+// 32-bit buffer offsets cover the tile's rows (codes and scales).
+bool gemm_bf16x_large_fits(int fmt, int64_t M, int64_t N, int64_t K) {
+  const int64_t rowbytes = (fmt == kMXFP8) ? K : K / 2;
+  const int64_t lim = (int64_t)1 << 31;
+  return (int64_t)BM * rowbytes < lim && (M + N) > 0;
+}
+
+hipError_t gemm_bf16x_large(int fmt, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
+                            const float* ta, const void* b, const void* sb, const float* tb,
+                            int out_dtype, void* c, int64_t ldc, hipStream_t s) {
+  const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
+  const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
+                *SB = (const uint8_t*)sb;
+  if (fmt == kMXFP8)
+    launch<kMXFP8>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
+  else
+    launch<kNVFP4>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
+  return hipGetLastError();
+}
+
+}  // namespace mx

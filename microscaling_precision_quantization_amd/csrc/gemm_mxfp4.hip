@@ -34,8 +34,8 @@
 // l % 32 and rows 8 (t / 4) + 4 g + (t % 4) in accumulator t. The kernel passes
 // B as the first operand, so the output tile is C^T and each lane holds runs
 // of 4 consecutive columns of one row of C.
-#include "bf16.h"
 #include "mx_internal.h"
+#include "tile256.h"
 
 namespace mx {
 namespace {
@@ -188,17 +188,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, g = lane >> 5;
 
-  // Tile order: XCD x (= blockIdx % 8) gets the contiguous id range
-  // [x * n/8, (x+1) * n/8); ids are rastered in groups of 4 tile rows.
-  const int ntiles = tiles_m * tiles_n;
-  const int bid = blockIdx.x;
-  const int t = (ntiles % 8 == 0) ? (bid % 8) * (ntiles / 8) + bid / 8 : bid;
-  constexpr int GM = 4;
-  const int group = t / (GM * tiles_n);
-  const int first_m = group * GM;
-  const int gsize = min(tiles_m - first_m, GM);
-  const int tm = first_m + (t % (GM * tiles_n)) % gsize;
-  const int tn = (t % (GM * tiles_n)) / gsize;
+  int tm, tn;
+  tile256::tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const uint32_t rowbytes = (uint32_t)(K / 2), scalebytes = (uint32_t)(K / 32);
@@ -292,68 +283,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
     interleave<false>();
   }
 
-  // Epilogue. Accumulator t of tile (i, j) is C[row][col] with row = A-tile
-  // row r and col = 8 (t / 4) + 4 g + (t % 4): runs of 4 consecutive columns.
-  // Each wave stages its 128 x 128 block in LDS (its own region; fp32 in two
-  // halves of 64 rows) and writes it back row-contiguously, 16 bytes per lane,
-  // so whole 128-byte lines reach the L2.
+  // Epilogue: the stage buffers are free once every wave is past its loop.
   __syncthreads();
-  constexpr int kEs = (OUT == kOutF32) ? 4 : 2;       // bytes per element
-  constexpr int kRows = (OUT == kOutF32) ? 64 : 128;  // rows staged per pass
-  constexpr int kPitch = 128 * kEs + 16;              // padded LDS row
-  uint8_t* wbuf = smem + wave * (kRows * kPitch);
-  const int wrow0 = m0 + wm * 128, wcol0 = n0 + wn * 128;
-  const bool vec_ok = (ldc % (16 / kEs)) == 0;
-#pragma unroll
-  for (int pass = 0; pass < 128 / kRows; pass++) {
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      if ((i * 32) / kRows != pass) continue;
-      const int lrow = i * 32 + r - pass * kRows;
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-          const int lcol = j * 32 + 8 * q + 4 * g;
-          uint8_t* dst = wbuf + lrow * kPitch + lcol * kEs;
-          if (OUT == kOutF32) {
-            *(f32x4*)dst = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                 acc[i][j][4 * q + 3]};
-          } else {
-            const uint32_t lo = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-            const uint32_t hi = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            *(u32x2*)dst = u32x2{lo, hi};
-          }
-        }
-    }
-    // Row-contiguous write-back: 128 columns = 16 lanes x 16 bytes (bf16) or
-    // 32 lanes (fp32); the wave covers 64 / (lanes per row) rows per step.
-    constexpr int kLanesPerRow = 128 * kEs / 16;
-    constexpr int kRowsPerStep = 64 / kLanesPerRow;
-#pragma unroll 4
-    for (int rr = 0; rr < kRows; rr += kRowsPerStep) {
-      const int lrow = rr + lane / kLanesPerRow;
-      const int lcol = (lane % kLanesPerRow) * (16 / kEs);
-      const int row = wrow0 + pass * kRows + lrow;
-      const int col = wcol0 + lcol;
-      if (row >= M) continue;
-      const u32x4 v = *(const u32x4*)(wbuf + lrow * kPitch + lcol * kEs);
-      uint8_t* gdst = (uint8_t*)C + ((int64_t)row * ldc + col) * kEs;
-      if (vec_ok && col + 16 / kEs <= N) {
-        *(u32x4*)gdst = v;
-      } else {
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 16 / kEs; e++) {
-          if (col + e >= N) continue;
-          if (OUT == kOutF32)
-            ((uint32_t*)gdst)[e] = w[e];
-          else
-            ((uint16_t*)gdst)[e] = (uint16_t)(w[e / 2] >> (16 * (e % 2)));
-        }
-      }
-    }
-  }
+  tile256::store_tile<OUT>(acc, smem, 1.0f, C, ldc, M, N, m0, n0, wave, lane);
 }
 
 }  // namespace

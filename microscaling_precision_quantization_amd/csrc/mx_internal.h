@@ -38,6 +38,12 @@ hipError_t gemm_bf16x(int fmt, int64_t M, int64_t N, int64_t K, const void* a, c
                       const float* ta, const void* b, const void* sb, const float* tb,
                       int out_dtype, void* c, int64_t ldc, hipStream_t s);
 
+// ---- gemm_bf16x_large.hip (256 x 256 tiles; MXFP8 / NVFP4 on the bf16 MFMA)
+bool gemm_bf16x_large_fits(int fmt, int64_t M, int64_t N, int64_t K);
+hipError_t gemm_bf16x_large(int fmt, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
+                            const float* ta, const void* b, const void* sb, const float* tb,
+                            int out_dtype, void* c, int64_t ldc, hipStream_t s);
+
 // ---- gemm_w4a16.hip (bf16 activations x MXFP4 weights)
 size_t gemm_w4a16_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* a, const void* b,

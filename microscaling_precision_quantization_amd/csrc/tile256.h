@@ -1,0 +1,109 @@
+// Pieces shared by the 256 x 256-tile GEMM kernels (4 waves of 128 x 128, each
+// 4 x 4 MFMAs of 32 x 32 with operands passed B first): the XCD-aware tile
+// order and the epilogue.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "bf16.h"
+#include "mx_internal.h"
+
+namespace mx {
+namespace tile256 {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 256;
+
+// Output tile of workgroup `bid`. Workgroup ids go round-robin over the 8
+// XCDs; when the tile count allows, XCD x gets the contiguous id range
+// [x n/8, (x+1) n/8), rastered in groups of 4 tile rows, so that its L2 holds
+// the A rows and B columns its tiles share.
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int ntiles = tiles_m * tiles_n;
+  const int t = (ntiles % 8 == 0) ? (bid % 8) * (ntiles / 8) + bid / 8 : bid;
+  constexpr int GM = 4;
+  const int group = t / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  tm = first_m + (t % (GM * tiles_n)) % gsize;
+  tn = (t % (GM * tiles_n)) / gsize;
+}
+
+// Epilogue. With B passed as the first MFMA operand, accumulator t of tile
+// (i, j) of wave (wm, wn) holds C[row][col] with row = m0 + 128 wm + 32 i + r
+// (r = lane % 32) and col = n0 + 128 wn + 32 j + 8 (t / 4) + 4 g + (t % 4)
+// (g = lane / 32): runs of 4 consecutive columns. Each wave stages its
+// 128 x 128 block in LDS (its own region of `smem`, at least 4 x 34,816
+// bytes; fp32 in two halves of 64 rows) and writes it back row-contiguously,
+// 16 bytes per lane, so whole lines reach the L2. Values are multiplied by
+// `scale` (exactly 1 unless a tensor scale applies). The caller has finished
+// every use of `smem` and synchronised the workgroup.
+template <int OUT>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], uint8_t* smem, float scale,
+                                           void* __restrict__ C, int64_t ldc, int M, int N,
+                                           int m0, int n0, int wave, int lane) {
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 31, g = lane >> 5;
+  constexpr int kEs = (OUT == kOutF32) ? 4 : 2;       // bytes per element
+  constexpr int kRows = (OUT == kOutF32) ? 64 : 128;  // rows staged per pass
+  constexpr int kPitch = 128 * kEs + 16;              // padded LDS row
+  uint8_t* wbuf = smem + wave * (kRows * kPitch);
+  const int wrow0 = m0 + wm * 128, wcol0 = n0 + wn * 128;
+  const bool vec_ok = (ldc % (16 / kEs)) == 0;
+#pragma unroll
+  for (int pass = 0; pass < 128 / kRows; pass++) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      if ((i * 32) / kRows != pass) continue;
+      const int lrow = i * 32 + r - pass * kRows;
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int lcol = j * 32 + 8 * q + 4 * g;
+          uint8_t* dst = wbuf + lrow * kPitch + lcol * kEs;
+          const float v0 = acc[i][j][4 * q] * scale, v1 = acc[i][j][4 * q + 1] * scale;
+          const float v2 = acc[i][j][4 * q + 2] * scale, v3 = acc[i][j][4 * q + 3] * scale;
+          if (OUT == kOutF32)
+            *(f32x4*)dst = f32x4{v0, v1, v2, v3};
+          else
+            *(u32x2*)dst = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        }
+    }
+    // Row-contiguous write-back: 128 columns = 16 lanes x 16 bytes (bf16) or
+    // 32 lanes (fp32); the wave covers 64 / (lanes per row) rows per step.
+    constexpr int kLanesPerRow = 128 * kEs / 16;
+    constexpr int kRowsPerStep = 64 / kLanesPerRow;
+#pragma unroll 4
+    for (int rr = 0; rr < kRows; rr += kRowsPerStep) {
+      const int lrow = rr + lane / kLanesPerRow;
+      const int lcol = (lane % kLanesPerRow) * (16 / kEs);
+      const int row = wrow0 + pass * kRows + lrow;
+      const int col = wcol0 + lcol;
+      if (row >= M) continue;
+      const u32x4 v = *(const u32x4*)(wbuf + lrow * kPitch + lcol * kEs);
+      uint8_t* gdst = (uint8_t*)C + ((int64_t)row * ldc + col) * kEs;
+      if (vec_ok && col + 16 / kEs <= N) {
+        *(u32x4*)gdst = v;
+      } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 16 / kEs; e++) {
+          if (col + e >= N) continue;
+          if (OUT == kOutF32)
+            ((uint32_t*)gdst)[e] = w[e];
+          else
+            ((uint16_t*)gdst)[e] = (uint16_t)(w[e / 2] >> (16 * (e % 2)));
+        }
+      }
+    }
+  }
+}
+
+}  // namespace tile256
+}  // namespace mx
