@@ -17,6 +17,8 @@ import numpy as np
 from . import build as _build
 
 FMT_BF16, FMT_MXFP4, FMT_MXFP8, FMT_NVFP4 = 0, 1, 2, 3
+RULE_CEIL, RULE_OAS = 0, 1
+ROT_NONE, ROT_WHT32 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 BLOCK = {FMT_MXFP4: 32, FMT_MXFP8: 32, FMT_NVFP4: 16}
 
@@ -49,6 +51,8 @@ def lib():
         L.mxo_quantize.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, P, P, P, P]
         L.mxo_quantize_nvfp4_exact_quotient.restype = ctypes.c_int
         L.mxo_quantize_nvfp4_exact_quotient.argtypes = [i64, i64, P, P, P, P]
+        L.mxo_quantize_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, P, P, P]
+        L.mxo_wht32.argtypes = [i64, i64, P, P]
         L.mxo_dequantize.restype = ctypes.c_int
         L.mxo_dequantize.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, P, P,
                                      ctypes.c_float, ctypes.c_int, P]
@@ -126,6 +130,27 @@ def quantize(fmt, x_bits):
     _check(lib().mxo_quantize(fmt, blk, rows, cols, _ptr(x), _ptr(codes),
                               _ptr(scales), _ptr(ts)), "quantize")
     return codes, scales, float(ts[0])
+
+
+def quantize_ex(fmt, x_bits, rule=RULE_CEIL, rot=ROT_NONE):
+    """MX quantization variants (mx_oracle.h: mxo_quantize_ex): overflow-aware
+    scaling (MXFP4) and/or the 32-point Walsh-Hadamard rotation first.
+    Returns (codes, scales)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    rows, cols = x.shape
+    codes = np.zeros(code_shape(fmt, rows, cols), np.uint8)
+    scales = np.zeros((rows, cols // 32), np.uint8)
+    _check(lib().mxo_quantize_ex(fmt, 32, rule, rot, rows, cols, _ptr(x), _ptr(codes), _ptr(scales)),
+           "quantize_ex")
+    return codes, scales
+
+
+def wht32(x_bits):
+    """bf16 bits [rows][cols] -> the rotated bf16 bits (mx_oracle.h: mxo_wht32)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    y = np.zeros_like(x)
+    _check(lib().mxo_wht32(x.shape[0], x.shape[1], _ptr(x), _ptr(y)), "wht32")
+    return y
 
 
 def quantize_nvfp4_exact_quotient(x_bits):

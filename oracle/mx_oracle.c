@@ -179,11 +179,12 @@ static int bf16_is_finite(uint16_t bits) {
 
 /* MXFP4 / MXFP8: per 32-element block, E from the block amax, then each
  * element divided by 2^(E-127) (exact in double) and rounded to the nearest
- * element value. A block holding Inf or NaN gets the NaN scale and zero codes. */
+ * element value. A block holding Inf or NaN gets the NaN scale and zero codes.
+ * emax is the value the scale rule maps the amax onto: the element format's
+ * largest value (6 or 448), or 7 for MXFP4 under OAS. */
 static void quantize_mx(int fmt, int64_t rows, int64_t cols, const uint16_t* x,
-                        uint8_t* codes, uint8_t* scales) {
+                        uint8_t* codes, uint8_t* scales, double emax) {
   const int B = 32;
-  const double emax = (fmt == MXO_FMT_MXFP4) ? 6.0 : 448.0;
   for (int64_t r = 0; r < rows; r++) {
     for (int64_t b = 0; b < cols / B; b++) {
       const uint16_t* xb = x + r * cols + b * B;
@@ -292,7 +293,7 @@ int mxo_quantize(int fmt, int block, int64_t rows, int64_t cols,
   if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_NVFP4) return MXO_ERR_ARG;
   if (block != fmt_block(fmt) || cols % block != 0) return MXO_ERR_ARG;
   if (fmt == MXO_FMT_MXFP4 || fmt == MXO_FMT_MXFP8) {
-    quantize_mx(fmt, rows, cols, x, codes, scales);
+    quantize_mx(fmt, rows, cols, x, codes, scales, fmt == MXO_FMT_MXFP4 ? 6.0 : 448.0);
     if (tensor_scale) *tensor_scale = 1.0f;
   } else {
     quantize_nvfp4(rows, cols, x, codes, scales, tensor_scale, 0);
@@ -439,5 +440,53 @@ int mxo_gemm_entries(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
   }
   free(ar);
   free(br);
+  return MXO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Variants: overflow-aware scaling and the 32-point Walsh-Hadamard rotation */
+/* ------------------------------------------------------------------------ */
+
+int mxo_wht32(int64_t rows, int64_t cols, const uint16_t* x, uint16_t* y) {
+  if (rows <= 0 || cols <= 0 || cols % 32 != 0 || !x || !y) return MXO_ERR_ARG;
+  const float c = (float)(1.0 / sqrt(32.0));
+  for (int64_t r = 0; r < rows; r++) {
+    for (int64_t b = 0; b < cols / 32; b++) {
+      float v[32];
+      for (int i = 0; i < 32; i++) v[i] = (float)mxo_bf16_value(x[r * cols + b * 32 + i]);
+      for (int h = 1; h < 32; h *= 2) {
+        for (int i = 0; i < 32; i++) {
+          if (i & h) continue;
+          const float a = v[i], d = v[i + h];
+          v[i] = a + d;
+          v[i + h] = a - d;
+        }
+      }
+      for (int i = 0; i < 32; i++) {
+        const float t = v[i] * c;
+        y[r * cols + b * 32 + i] = mxo_f32_to_bf16(t);
+      }
+    }
+  }
+  return MXO_OK;
+}
+
+int mxo_quantize_ex(int fmt, int block, int rule, int rot, int64_t rows, int64_t cols,
+                    const uint16_t* x, uint8_t* codes, uint8_t* scales) {
+  if (rows <= 0 || cols <= 0 || !x || !codes || !scales) return MXO_ERR_ARG;
+  if (fmt != MXO_FMT_MXFP4 && fmt != MXO_FMT_MXFP8) return MXO_ERR_ARG;
+  if (block != 32 || cols % 32 != 0) return MXO_ERR_ARG;
+  if (rule != MXO_RULE_CEIL && !(rule == MXO_RULE_OAS && fmt == MXO_FMT_MXFP4)) return MXO_ERR_ARG;
+  if (rot != MXO_ROT_NONE && rot != MXO_ROT_WHT32) return MXO_ERR_ARG;
+  const double emax = (fmt == MXO_FMT_MXFP8) ? 448.0 : (rule == MXO_RULE_OAS ? 7.0 : 6.0);
+  if (rot == MXO_ROT_NONE) {
+    quantize_mx(fmt, rows, cols, x, codes, scales, emax);
+    return MXO_OK;
+  }
+  uint16_t* t = (uint16_t*)malloc((size_t)(rows * cols) * sizeof(uint16_t));
+  if (!t) return MXO_ERR_ARG;
+  mxo_wht32(rows, cols, x, t);
+  quantize_mx(fmt, rows, cols, t, codes, scales, emax);
+  free(t);
   return MXO_OK;
 }

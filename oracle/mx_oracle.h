@@ -20,7 +20,11 @@
  *    E4M3/E5M2 in 32-element blocks.
  *  - gist.science summary of "Unveiling the Potential of Quantization with
  *    MXFP4", section 2.A: the standard MX rule maps the block amax into (3, 6];
- *    NVFP4 scales carry a mantissa.
+ *    NVFP4 scales carry a mantissa; overflow-aware scaling (OAS) widens the
+ *    scaled-amax range to (3.5, 7].
+ *  - produtoramaxvision page, section "Tecnicas de preservacao de acuracia:
+ *    QuaRot, SpinQuant e ReSET": Hadamard / Walsh-Hadamard rotations spread
+ *    a block's energy evenly over its 32 elements.
  */
 #ifndef MX_ORACLE_H
 #define MX_ORACLE_H
@@ -72,6 +76,25 @@ int64_t mxo_storage_bytes(int fmt, int64_t rows, int64_t cols);
 int mxo_quantize(int fmt, int block, int64_t rows, int64_t cols,
                  const uint16_t* x, uint8_t* codes, uint8_t* scales,
                  float* tensor_scale);
+
+/* Variants of MX quantization (MXFP4 / MXFP8, block 32):
+ *  rule: MXO_RULE_CEIL -- the standard rule above;
+ *        MXO_RULE_OAS  -- MXFP4 only: E = smallest n with amax <= 7 * 2^n
+ *                         (+127, clamped), so the scaled amax lies in
+ *                         (3.5, 7] and values in (6, 7] saturate to 6.
+ *  rot:  MXO_ROT_NONE, or MXO_ROT_WHT32 -- every 32-block is first replaced by
+ *        bf16(fl32(fl32(H x) * fl32(1/sqrt(32)))), see mxo_wht32. */
+enum { MXO_RULE_CEIL = 0, MXO_RULE_OAS = 1 };
+enum { MXO_ROT_NONE = 0, MXO_ROT_WHT32 = 1 };
+int mxo_quantize_ex(int fmt, int block, int rule, int rot, int64_t rows, int64_t cols,
+                    const uint16_t* x, uint8_t* codes, uint8_t* scales);
+
+/* 32-point Walsh-Hadamard rotation of every 32-element block of bf16 rows:
+ * y = bf16(fl32(fl32(H32 x) * c)), c = fl32(1/sqrt(32)), H32 the Sylvester
+ * matrix (H[i][j] = (-1)^popcount(i & j)), computed in fp32 by the radix-2
+ * butterfly with spans 1, 2, 4, 8, 16, each pair (i, i + h) becoming
+ * (x_i + x_{i+h}, x_i - x_{i+h}). */
+int mxo_wht32(int64_t rows, int64_t cols, const uint16_t* x, uint16_t* y);
 
 /* NVFP4 only, information: codes from the exact quotient x / (s_b * s_t)
  * instead of the fp32 reciprocal sequence; scales are as mxo_quantize's. */
