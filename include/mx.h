@@ -90,6 +90,41 @@ mx_status mx_quantize(mx_format fmt, int block, mx_round rnd, int64_t rows, int6
 
 size_t mx_quantize_workspace_bytes(mx_format fmt, int64_t rows, int64_t cols);
 
+/* Scale rule and rotation variants of MX quantization (MXFP4 / MXFP8). */
+typedef enum {
+  MX_SCALE_CEIL = 0, /* the rule above: scaled block amax in (3, 6] for E2M1 */
+  MX_SCALE_OAS = 1   /* overflow-aware scaling, MXFP4 only (gist.science
+                        summary of "Unveiling the Potential of Quantization
+                        with MXFP4", section 2.A): E = ceil(log2(amax / 7))
+                        + 127, so the scaled amax lies in (3.5, 7] and
+                        elements in (6, 7] saturate to 6 */
+} mx_scale_rule;
+
+typedef enum {
+  MX_ROTATE_NONE = 0,
+  MX_ROTATE_WHT32 = 1 /* each 32-block x is first replaced by
+                         bf16(fl32(fl32(H32 x) * fl32(1/sqrt(32)))), H32 the
+                         Sylvester Walsh-Hadamard matrix, H x by the fp32
+                         radix-2 butterfly with spans 1, 2, 4, 8, 16 (pair
+                         (i, i+h) -> (x_i + x_{i+h}, x_i - x_{i+h})); the
+                         Hadamard rotation of the produtoramaxvision page,
+                         section "Tecnicas de preservacao de acuracia: QuaRot,
+                         SpinQuant e ReSET". Rotating both GEMM operands along
+                         K leaves A * B^T unchanged up to rounding, since
+                         (H/sqrt 32)(H/sqrt 32)^T = I. */
+} mx_rotation;
+
+/*
+ * mx_quantize with a scale rule and a rotation: MX formats (block 32) only;
+ * MX_SCALE_OAS with MXFP8, or NVFP4 with anything but (MX_SCALE_CEIL,
+ * MX_ROTATE_NONE), returns MX_ERR_UNSUPPORTED. Outputs have the layout of
+ * mx_quantize (the GEMM reads them unchanged); tensor_scale must be NULL and
+ * no workspace is used. (MX_SCALE_CEIL, MX_ROTATE_NONE) is mx_quantize.
+ */
+mx_status mx_quantize_ex(mx_format fmt, int block, mx_round rnd, mx_scale_rule rule,
+                         mx_rotation rot, int64_t rows, int64_t cols, const void* x,
+                         void* codes, void* scales, void* stream);
+
 /*
  * Dequantization (x_real = S * x_elem on the produtoramaxvision page): MX
  * y = val(code) * 2^(E-127); NVFP4 y = fl32(fl32(val(code) * s_b) * s_t).

@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(HERE, "libmx.so")
 
 MX_FMT_BF16, MX_FMT_MXFP4, MX_FMT_MXFP8, MX_FMT_NVFP4 = 0, 1, 2, 3
 MX_ROUND_RNE = 0
+MX_SCALE_CEIL, MX_SCALE_OAS = 0, 1
+MX_ROTATE_NONE, MX_ROTATE_WHT32 = 0, 1
 MX_OUT_F32, MX_OUT_BF16 = 0, 1
 MX_OK, MX_ERR_INVALID_ARG, MX_ERR_UNSUPPORTED, MX_ERR_HIP = 0, 1, 2, 3
 
@@ -26,8 +28,8 @@ FORMATS = {"mxfp4": MX_FMT_MXFP4, "mxfp8": MX_FMT_MXFP8, "nvfp4": MX_FMT_NVFP4, 
 BLOCK = {MX_FMT_MXFP4: 32, MX_FMT_MXFP8: 32, MX_FMT_NVFP4: 16, MX_FMT_BF16: 32}
 
 # Symbols declared in include/mx.h.
-EXPORTS = ("mx_quantize", "mx_quantize_workspace_bytes", "mx_dequantize", "mx_gemm",
-           "mx_gemm_workspace_bytes", "mx_last_hip_error", "mx_status_string")
+EXPORTS = ("mx_quantize", "mx_quantize_workspace_bytes", "mx_quantize_ex", "mx_dequantize",
+           "mx_gemm", "mx_gemm_workspace_bytes", "mx_last_hip_error", "mx_status_string")
 
 _lib = None
 
@@ -52,6 +54,8 @@ def lib():
         P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
         L.mx_quantize.restype = i32
         L.mx_quantize.argtypes = [i32, i32, i32, i64, i64, P, P, P, P, P, sz, P]
+        L.mx_quantize_ex.restype = i32
+        L.mx_quantize_ex.argtypes = [i32, i32, i32, i32, i32, i64, i64, P, P, P, P]
         L.mx_quantize_workspace_bytes.restype = sz
         L.mx_quantize_workspace_bytes.argtypes = [i32, i64, i64]
         L.mx_dequantize.restype = i32
@@ -74,6 +78,10 @@ def mx_quantize(fmt, block, rnd, rows, cols, x, codes, scales, tensor_scale, wor
                 workspace_bytes, stream):
     return lib().mx_quantize(fmt, block, rnd, rows, cols, x, codes, scales, tensor_scale,
                              workspace, workspace_bytes, stream)
+
+
+def mx_quantize_ex(fmt, block, rnd, rule, rot, rows, cols, x, codes, scales, stream):
+    return lib().mx_quantize_ex(fmt, block, rnd, rule, rot, rows, cols, x, codes, scales, stream)
 
 
 def mx_quantize_workspace_bytes(fmt, rows, cols):
@@ -141,10 +149,25 @@ def _check(status, what):
         raise MXError(status, what)
 
 
-def quantize(x, fmt):
-    """Quantize a contiguous bf16 [rows][cols] device tensor."""
+SCALE_RULES = {"ceil": MX_SCALE_CEIL, "oas": MX_SCALE_OAS}
+ROTATIONS = {None: MX_ROTATE_NONE, "none": MX_ROTATE_NONE, "wht32": MX_ROTATE_WHT32}
+
+
+def quantize(x, fmt, scale_rule="ceil", rotation=None):
+    """Quantize a contiguous bf16 [rows][cols] device tensor. scale_rule "oas"
+    (MXFP4) and rotation "wht32" (MX formats) select mx_quantize_ex."""
     import torch
     f = _fmt_id(fmt)
+    if scale_rule != "ceil" or rotation not in (None, "none"):
+        if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+            raise ValueError("quantize expects a contiguous 2-D bfloat16 tensor")
+        rows, cols = x.shape
+        codes = torch.empty((rows, cols if f == MX_FMT_MXFP8 else cols // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((rows, cols // BLOCK[f]), dtype=torch.uint8, device=x.device)
+        _check(mx_quantize_ex(f, BLOCK[f], MX_ROUND_RNE, SCALE_RULES[scale_rule], ROTATIONS[rotation], rows,
+                              cols, _ptr(x), _ptr(codes), _ptr(scales), _stream(torch, x.device)),
+               "mx_quantize_ex")
+        return QTensor(f, rows, cols, codes, scales, None)
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
         raise ValueError("quantize expects a contiguous 2-D bfloat16 tensor")
     rows, cols = x.shape

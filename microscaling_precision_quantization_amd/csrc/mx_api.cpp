@@ -66,6 +66,21 @@ mx_status mx_quantize(mx_format fmt, int block, mx_round rnd, int64_t rows, int6
   return hip_status(mx::quant_mx(fmt, rows, cols, x, codes, scales, s));
 }
 
+mx_status mx_quantize_ex(mx_format fmt, int block, mx_round rnd, mx_scale_rule rule,
+                         mx_rotation rot, int64_t rows, int64_t cols, const void* x,
+                         void* codes, void* scales, void* stream) {
+  mx_status st = check_tensor(fmt, block, rnd, rows, cols);
+  if (st != MX_OK) return st;
+  if (fmt != MX_FMT_MXFP4 && fmt != MX_FMT_MXFP8) return MX_ERR_UNSUPPORTED;
+  if (rule != MX_SCALE_CEIL && !(rule == MX_SCALE_OAS && fmt == MX_FMT_MXFP4))
+    return MX_ERR_UNSUPPORTED;
+  if (rot != MX_ROTATE_NONE && rot != MX_ROTATE_WHT32) return MX_ERR_UNSUPPORTED;
+  if (!x || !codes || !scales) return MX_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_INVALID_ARG;
+  return hip_status(mx::quant_mx(fmt, rows, cols, x, codes, scales, (hipStream_t)stream,
+                                 rule == MX_SCALE_OAS, rot == MX_ROTATE_WHT32));
+}
+
 mx_status mx_dequantize(mx_format fmt, int block, mx_round rnd, int64_t rows, int64_t cols,
                         const void* codes, const void* scales, const float* tensor_scale,
                         mx_dtype out_dtype, void* y, void* stream) {

@@ -12,8 +12,10 @@ enum : int { kBF16 = 0, kMXFP4 = 1, kMXFP8 = 2, kNVFP4 = 3 };
 enum : int { kOutF32 = 0, kOutBF16 = 1 };
 
 // ---- quantize.hip
+// oas: MXFP4's overflow-aware scale rule; rot: 32-point Walsh-Hadamard rotation first.
 hipError_t quant_mx(int fmt, int64_t rows, int64_t cols, const void* x, void* codes,
-                    void* scales, hipStream_t s);
+                    void* scales, hipStream_t s, bool oas = false,
+                    bool rot = false);
 size_t quant_nvfp4_workspace(int64_t rows, int64_t cols);
 hipError_t quant_nvfp4(int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
                        float* tensor_scale, void* workspace, hipStream_t s);

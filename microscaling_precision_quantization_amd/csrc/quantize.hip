@@ -11,6 +11,16 @@
 // NVFP4: 2 lanes own one 16-block. The block amax is an integer max of
 // (bits & 0x7FFF) over the lanes' chunks, reduced with DPP quad permutes.
 //
+// Variants (MX formats): overflow-aware scaling for MXFP4 (gist.science
+// summary of "Unveiling the Potential of Quantization with MXFP4", section
+// 2.A: the scaled amax range (3, 6] becomes (3.5, 7], values in (6, 7]
+// saturate), i.e. the rule with 7 in place of 6; and a 32-point
+// Walsh-Hadamard rotation of every block before quantization
+// (produtoramaxvision page, QuaRot / SpinQuant section), computed in fp32 by
+// the radix-2 butterfly with spans 1, 2, 4 inside a lane and 8, 16 across the
+// block's 4 lanes (DPP quad permutes), then scaled by fl32(1/sqrt(32)) and
+// rounded to bf16 (v_cvt_pk_bf16_f32, nearest-even) before the usual steps.
+//
 // Encoding uses gfx950's scaled converts. v_cvt_scalef32_pk_fp4_bf16 and
 // v_cvt_scalef32_pk_fp8_bf16 return nearest-even of x / scale (saturating for
 // FP4, -0 kept); with scale = 2^(E-127) that is exactly the MX element
@@ -60,8 +70,57 @@ __device__ __forceinline__ float e8m0_to_float(uint32_t E) {
   return __builtin_bit_cast(float, E == 0 ? 0x00400000u : E << 23);
 }
 
-// MXFP4 (FMT 1) / MXFP8 (FMT 2).
-template <int FMT>
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fl32(1/sqrt(32)).
+constexpr float kInvSqrt32 = 0x1.6a09e6p-3f;
+
+// The 32-point Walsh-Hadamard rotation of the block whose 8 elements
+// 8 j .. 8 j + 7 this lane holds (j = lane % 4): y = bf16(fl32(H x) * c), the
+// butterfly pairing (i, i + h) into (x_i + x_{i+h}, x_i - x_{i+h}) for
+// h = 1, 2, 4 (inside the lane) and 8, 16 (lane j with j ^ 1, j ^ 2).
+__device__ __forceinline__ u32x4 wht32_chunk(u32x4 v, int lane) {
+  float f[8];
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+  }
+#pragma unroll
+  for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      if (i & h) continue;
+      const float a = f[i], d = f[i + h];
+      f[i] = a + d;
+      f[i + h] = a - d;
+    }
+  const bool up8 = (lane & 1) != 0, up16 = (lane & 2) != 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float p = __builtin_bit_cast(float, dpp<kDppSwap1>(__builtin_bit_cast(uint32_t, f[i])));
+    f[i] = up8 ? p - f[i] : f[i] + p;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float p = __builtin_bit_cast(float, dpp<kDppSwap2>(__builtin_bit_cast(uint32_t, f[i])));
+    f[i] = up16 ? p - f[i] : f[i] + p;
+  }
+  u32x4 o;
+  uint32_t r[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const float lo = f[2 * i] * kInvSqrt32, hi = f[2 * i + 1] * kInvSqrt32;
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+  }
+  o.x = r[0]; o.y = r[1]; o.z = r[2]; o.w = r[3];
+  return o;
+}
+
+// MXFP4 (FMT 1) / MXFP8 (FMT 2); OAS: MXFP4's overflow-aware scale rule;
+// ROT: rotate every block first.
+template <int FMT, bool OAS, bool ROT>
 __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restrict__ x,
                                                             void* __restrict__ codes,
                                                             uint8_t* __restrict__ scales,
@@ -77,14 +136,16 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restr
 #pragma unroll
   for (int u = 0; u < kUnroll; u++) {
     const int64_t c = base + u * kThreads;
+    if (ROT) v[u] = wht32_chunk(v[u], lane);
     uint32_t m = chunk_absmax(v[u]);
     m = umax(m, dpp<kDppSwap1>(m));
     m = umax(m, dpp<kDppSwap2>(m));
     // E = ceil(log2(amax / emax)) + 127 from the bf16 fields of amax:
     // emax = 6 = 1.5 * 2^2  -> E = ea - 2 + [mantissa > 0x40]
+    // emax = 7 = 1.75 * 2^2 (OAS) -> E = ea - 2 + [mantissa > 0x60]
     // emax = 448 = 1.75 * 2^8 -> E = ea - 8 + [mantissa > 0x60]
     const int ea = (int)(m >> 7), ma = (int)(m & 0x7F);
-    int e = (FMT == kMXFP4) ? ea - 2 + (ma > 0x40) : ea - 8 + (ma > 0x60);
+    int e = (FMT == kMXFP4) ? ea - 2 + (ma > (OAS ? 0x60 : 0x40)) : ea - 8 + (ma > 0x60);
     e = e < 0 ? 0 : e;
     const bool nonfinite = m >= 0x7F80u;
     const uint32_t E = nonfinite ? 255u : (uint32_t)e;
@@ -232,13 +293,26 @@ int64_t grid_for(int64_t nchunks) { return (nchunks + kThreads * kUnroll - 1) / 
 }  // namespace
 
 hipError_t quant_mx(int fmt, int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
-                    hipStream_t s) {
+                    hipStream_t s, bool oas, bool rot) {
   const int64_t nchunks = rows * cols / 8;
   const dim3 grid((unsigned)grid_for(nchunks));
-  if (fmt == kMXFP4)
-    quant_mx_kernel<kMXFP4><<<grid, kThreads, 0, s>>>((const u32x4*)x, codes, (uint8_t*)scales, nchunks);
-  else
-    quant_mx_kernel<kMXFP8><<<grid, kThreads, 0, s>>>((const u32x4*)x, codes, (uint8_t*)scales, nchunks);
+  const u32x4* X = (const u32x4*)x;
+  uint8_t* S = (uint8_t*)scales;
+  if (fmt == kMXFP4) {
+    if (oas && rot)
+      quant_mx_kernel<kMXFP4, true, true><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
+    else if (oas)
+      quant_mx_kernel<kMXFP4, true, false><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
+    else if (rot)
+      quant_mx_kernel<kMXFP4, false, true><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
+    else
+      quant_mx_kernel<kMXFP4, false, false><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
+  } else {
+    if (rot)
+      quant_mx_kernel<kMXFP8, false, true><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
+    else
+      quant_mx_kernel<kMXFP8, false, false><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
+  }
   return hipGetLastError();
 }
 

@@ -67,6 +67,25 @@ def test_quantize_rejects(kw, status):
     assert q(**kw) == status
 
 
+def qx(fmt=mx.MX_FMT_MXFP4, block=32, rnd=0, rule=0, rot=0, rows=4, cols=64, x=P, codes=P, scales=P):
+    return mx.mx_quantize_ex(fmt, block, rnd, rule, rot, rows, cols, x, codes, scales, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), mx.MX_ERR_INVALID_ARG),
+    (dict(scales=MIS), mx.MX_ERR_INVALID_ARG),
+    (dict(cols=48), mx.MX_ERR_INVALID_ARG),
+    (dict(fmt=mx.MX_FMT_MXFP8, rule=mx.MX_SCALE_OAS), mx.MX_ERR_UNSUPPORTED),  # OAS is MXFP4's
+    (dict(fmt=mx.MX_FMT_NVFP4, block=16), mx.MX_ERR_UNSUPPORTED),
+    (dict(fmt=mx.MX_FMT_NVFP4, block=16, rot=mx.MX_ROTATE_WHT32), mx.MX_ERR_UNSUPPORTED),
+    (dict(rule=2), mx.MX_ERR_UNSUPPORTED),
+    (dict(rot=2), mx.MX_ERR_UNSUPPORTED),
+    (dict(rnd=1), mx.MX_ERR_UNSUPPORTED),
+])
+def test_quantize_ex_rejects(kw, status):
+    assert qx(**kw) == status
+
+
 def test_dequantize_rejects():
     d = mx.mx_dequantize
     assert d(1, 32, 0, 4, 64, P, P, None, 0, None, None) == mx.MX_ERR_INVALID_ARG  # y null
