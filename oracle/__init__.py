@@ -17,10 +17,11 @@ import numpy as np
 from . import build as _build
 
 FMT_BF16, FMT_MXFP4, FMT_MXFP8, FMT_NVFP4 = 0, 1, 2, 3
+FMT_MXFP8_E5M2, FMT_MXFP6_E3M2 = 4, 5
 RULE_CEIL, RULE_OAS = 0, 1
 ROT_NONE, ROT_WHT32 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
-BLOCK = {FMT_MXFP4: 32, FMT_MXFP8: 32, FMT_NVFP4: 16}
+BLOCK = {FMT_MXFP4: 32, FMT_MXFP8: 32, FMT_NVFP4: 16, FMT_MXFP8_E5M2: 32, FMT_MXFP6_E3M2: 32}
 
 _lib = None
 
@@ -35,10 +36,11 @@ def lib():
         i64 = ctypes.c_int64
         L.mxo_bf16_value.restype = ctypes.c_double
         L.mxo_bf16_value.argtypes = [ctypes.c_uint16]
-        for n in ("mxo_e2m1_value", "mxo_e4m3_value", "mxo_e8m0_value"):
+        for n in ("mxo_e2m1_value", "mxo_e4m3_value", "mxo_e8m0_value", "mxo_e5m2_value",
+                  "mxo_e3m2_value"):
             getattr(L, n).restype = ctypes.c_double
             getattr(L, n).argtypes = [ctypes.c_uint8]
-        for n in ("mxo_encode_e2m1", "mxo_encode_e4m3"):
+        for n in ("mxo_encode_e2m1", "mxo_encode_e4m3", "mxo_encode_e5m2", "mxo_encode_e3m2"):
             getattr(L, n).restype = ctypes.c_uint8
             getattr(L, n).argtypes = [ctypes.c_double]
         L.mxo_f32_to_bf16.restype = ctypes.c_uint16
@@ -101,6 +103,22 @@ def encode_e4m3(v):
     return lib().mxo_encode_e4m3(float(v))
 
 
+def e5m2_value(code):
+    return lib().mxo_e5m2_value(int(code))
+
+
+def e3m2_value(code):
+    return lib().mxo_e3m2_value(int(code))
+
+
+def encode_e5m2(v):
+    return lib().mxo_encode_e5m2(float(v))
+
+
+def encode_e3m2(v):
+    return lib().mxo_encode_e3m2(float(v))
+
+
 def f32_to_bf16(f):
     return lib().mxo_f32_to_bf16(float(f))
 
@@ -115,7 +133,11 @@ def storage_bytes(fmt, rows, cols):
 
 # ---- tensor operations -----------------------------------------------------
 def code_shape(fmt, rows, cols):
-    return (rows, cols) if fmt == FMT_MXFP8 else (rows, cols // 2)
+    if fmt in (FMT_MXFP8, FMT_MXFP8_E5M2):
+        return (rows, cols)
+    if fmt == FMT_MXFP6_E3M2:
+        return (rows, cols * 3 // 4)
+    return (rows, cols // 2)
 
 
 def quantize(fmt, x_bits):

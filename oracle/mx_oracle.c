@@ -69,6 +69,35 @@ double mxo_e4m3_value(uint8_t code) {
   return s ? -v : v;
 }
 
+/* FP8 E5M2 (OCP): exponent bias 15, 2 mantissa bits, field 0 subnormal,
+ * field 31 is Inf (mantissa 0) or NaN; largest finite 1.75 * 2^15 = 57344. */
+double mxo_e5m2_value(uint8_t code) {
+  int s = (code >> 7) & 1;
+  int e = (code >> 2) & 31;
+  int m = code & 3;
+  double v;
+  if (e == 31) v = (m == 0) ? INFINITY : NAN;
+  else if (e == 0)
+    v = ldexp((double)m / 4.0, 1 - 15);
+  else
+    v = ldexp(1.0 + m / 4.0, e - 15);
+  return s ? -v : v;
+}
+
+/* FP6 E3M2 (OCP MX): exponent bias 3, 2 mantissa bits, field 0 subnormal, no
+ * Inf or NaN; largest 1.75 * 2^4 = 28. */
+double mxo_e3m2_value(uint8_t code) {
+  int s = (code >> 5) & 1;
+  int e = (code >> 2) & 7;
+  int m = code & 3;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m / 4.0, 1 - 3);
+  else
+    v = ldexp(1.0 + m / 4.0, e - 3);
+  return s ? -v : v;
+}
+
 /* E8M0: an unsigned power of two, 2^(E-127). E = 255 is the format's NaN
  * (2^128 is not finite in fp32 either). */
 double mxo_e8m0_value(uint8_t e) {
@@ -106,6 +135,18 @@ uint8_t mxo_encode_e4m3(double v) {
   return (uint8_t)((neg << 7) | c);
 }
 
+uint8_t mxo_encode_e5m2(double v) {
+  int neg = signbit(v) ? 1 : 0;
+  int c = nearest_code(fabs(v), mxo_e5m2_value, 124); /* 0x00..0x7B finite */
+  return (uint8_t)((neg << 7) | c);
+}
+
+uint8_t mxo_encode_e3m2(double v) {
+  int neg = signbit(v) ? 1 : 0;
+  int c = nearest_code(fabs(v), mxo_e3m2_value, 32);
+  return (uint8_t)((neg << 5) | c);
+}
+
 /* bf16 nearest-even: keep the high half, adding half an ulp plus the LSB of
  * the kept part so that exact halves go to the even neighbour. */
 uint16_t mxo_f32_to_bf16(float f) {
@@ -134,7 +175,41 @@ int mxo_mx_scale_exponent(double amax, double emax) {
 }
 
 static int elem_bits(int fmt) {
-  return (fmt == MXO_FMT_MXFP8) ? 8 : 4;
+  if (fmt == MXO_FMT_MXFP8 || fmt == MXO_FMT_MXFP8_E5M2) return 8;
+  return (fmt == MXO_FMT_MXFP6_E3M2) ? 6 : 4;
+}
+
+static int is_mx(int fmt) {
+  return fmt == MXO_FMT_MXFP4 || fmt == MXO_FMT_MXFP8 || fmt == MXO_FMT_MXFP8_E5M2 ||
+         fmt == MXO_FMT_MXFP6_E3M2;
+}
+
+/* Largest element value: what the MX scale rule maps the block amax onto. */
+static double elem_max(int fmt) {
+  switch (fmt) {
+    case MXO_FMT_MXFP8: return 448.0;
+    case MXO_FMT_MXFP8_E5M2: return 57344.0;
+    case MXO_FMT_MXFP6_E3M2: return 28.0;
+    default: return 6.0;
+  }
+}
+
+static double elem_value(int fmt, uint8_t code) {
+  switch (fmt) {
+    case MXO_FMT_MXFP8: return mxo_e4m3_value(code);
+    case MXO_FMT_MXFP8_E5M2: return mxo_e5m2_value(code);
+    case MXO_FMT_MXFP6_E3M2: return mxo_e3m2_value(code);
+    default: return mxo_e2m1_value(code);
+  }
+}
+
+static uint8_t elem_encode(int fmt, double v) {
+  switch (fmt) {
+    case MXO_FMT_MXFP8: return mxo_encode_e4m3(v);
+    case MXO_FMT_MXFP8_E5M2: return mxo_encode_e5m2(v);
+    case MXO_FMT_MXFP6_E3M2: return mxo_encode_e3m2(v);
+    default: return mxo_encode_e2m1(v);
+  }
 }
 
 static int fmt_block(int fmt) {
@@ -144,7 +219,7 @@ static int fmt_block(int fmt) {
 /* 4 bits per element plus 8 bits per 32-element block is the page's
  * "4 + 8/32 = 4.25 bits per element". */
 int64_t mxo_storage_bytes(int fmt, int64_t rows, int64_t cols) {
-  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_NVFP4) return -1;
+  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_MXFP6_E3M2) return -1;
   int64_t n = rows * cols;
   int64_t code_bytes = n * elem_bits(fmt) / 8;
   int64_t scale_bytes = n / fmt_block(fmt);
@@ -156,21 +231,31 @@ int64_t mxo_storage_bytes(int fmt, int64_t rows, int64_t cols) {
 /* ------------------------------------------------------------------------ */
 
 static void put_code(uint8_t* codes, int fmt, int64_t idx, uint8_t code) {
-  if (fmt == MXO_FMT_MXFP8) {
+  const int w = elem_bits(fmt);
+  if (w == 8) {
     codes[idx] = code;
-  } else {
-    uint8_t* byte = &codes[idx / 2];
-    if (idx % 2 == 0)
-      *byte = (uint8_t)((*byte & 0xF0) | (code & 0x0F));
+    return;
+  }
+  /* bit b of the code goes to bit (w idx + b) of the byte string */
+  for (int b = 0; b < w; b++) {
+    int64_t bit = (int64_t)w * idx + b;
+    uint8_t* byte = &codes[bit / 8];
+    if ((code >> b) & 1)
+      *byte = (uint8_t)(*byte | (1u << (bit % 8)));
     else
-      *byte = (uint8_t)((*byte & 0x0F) | ((code & 0x0F) << 4));
+      *byte = (uint8_t)(*byte & ~(1u << (bit % 8)));
   }
 }
 
 static uint8_t get_code(const uint8_t* codes, int fmt, int64_t idx) {
-  if (fmt == MXO_FMT_MXFP8) return codes[idx];
-  uint8_t byte = codes[idx / 2];
-  return (idx % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+  const int w = elem_bits(fmt);
+  if (w == 8) return codes[idx];
+  uint8_t code = 0;
+  for (int b = 0; b < w; b++) {
+    int64_t bit = (int64_t)w * idx + b;
+    code = (uint8_t)(code | (((codes[bit / 8] >> (bit % 8)) & 1u) << b));
+  }
+  return code;
 }
 
 static int bf16_is_finite(uint16_t bits) {
@@ -205,8 +290,7 @@ static void quantize_mx(int fmt, int64_t rows, int64_t cols, const uint16_t* x,
       scales[r * (cols / B) + b] = (uint8_t)E;
       for (int i = 0; i < B; i++) {
         double v = ldexp(mxo_bf16_value(xb[i]), 127 - E); /* x / 2^(E-127) */
-        uint8_t c = (fmt == MXO_FMT_MXFP4) ? mxo_encode_e2m1(v)
-                                           : mxo_encode_e4m3(v);
+        uint8_t c = elem_encode(fmt, v);
         put_code(codes, fmt, first + i, c);
       }
     }
@@ -290,10 +374,10 @@ int mxo_quantize(int fmt, int block, int64_t rows, int64_t cols,
                  const uint16_t* x, uint8_t* codes, uint8_t* scales,
                  float* tensor_scale) {
   if (rows <= 0 || cols <= 0 || !x || !codes || !scales) return MXO_ERR_ARG;
-  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_NVFP4) return MXO_ERR_ARG;
+  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_MXFP6_E3M2) return MXO_ERR_ARG;
   if (block != fmt_block(fmt) || cols % block != 0) return MXO_ERR_ARG;
-  if (fmt == MXO_FMT_MXFP4 || fmt == MXO_FMT_MXFP8) {
-    quantize_mx(fmt, rows, cols, x, codes, scales, fmt == MXO_FMT_MXFP4 ? 6.0 : 448.0);
+  if (is_mx(fmt)) {
+    quantize_mx(fmt, rows, cols, x, codes, scales, elem_max(fmt));
     if (tensor_scale) *tensor_scale = 1.0f;
   } else {
     quantize_nvfp4(rows, cols, x, codes, scales, tensor_scale, 0);
@@ -323,7 +407,7 @@ static double exact_value(int fmt, const uint8_t* codes, const uint8_t* scales,
   int64_t r = idx / cols, c = idx % cols;
   uint8_t sc = scales[r * (cols / block) + c / block];
   uint8_t code = get_code(codes, fmt, idx);
-  double e = (fmt == MXO_FMT_MXFP8) ? mxo_e4m3_value(code) : mxo_e2m1_value(code);
+  double e = elem_value(fmt, code);
   if (fmt == MXO_FMT_NVFP4) return e * mxo_e4m3_value(sc) * (double)ts;
   return e * mxo_e8m0_value(sc);
 }
@@ -332,7 +416,7 @@ int mxo_dequantize(int fmt, int block, int64_t rows, int64_t cols,
                    const uint8_t* codes, const uint8_t* scales,
                    float tensor_scale, int out_dtype, void* y) {
   if (rows <= 0 || cols <= 0 || !codes || !scales || !y) return MXO_ERR_ARG;
-  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_NVFP4) return MXO_ERR_ARG;
+  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_MXFP6_E3M2) return MXO_ERR_ARG;
   if (block != fmt_block(fmt) || cols % block != 0) return MXO_ERR_ARG;
   if (out_dtype != MXO_OUT_F32 && out_dtype != MXO_OUT_BF16) return MXO_ERR_ARG;
   for (int64_t i = 0; i < rows * cols; i++) {
@@ -374,8 +458,8 @@ static int gemm_args_ok(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
                         const void* a, const uint8_t* a_scales, const void* b,
                         const uint8_t* b_scales) {
   if (M <= 0 || N <= 0 || K <= 0 || !a || !b) return 0;
-  if (fmt_a < MXO_FMT_BF16 || fmt_a > MXO_FMT_NVFP4) return 0;
-  if (fmt_b < MXO_FMT_MXFP4 || fmt_b > MXO_FMT_NVFP4) return 0;
+  if (fmt_a < MXO_FMT_BF16 || fmt_a > MXO_FMT_MXFP6_E3M2) return 0;
+  if (fmt_b < MXO_FMT_MXFP4 || fmt_b > MXO_FMT_MXFP6_E3M2) return 0;
   if (fmt_a != MXO_FMT_BF16 && (!a_scales || K % fmt_block(fmt_a) != 0)) return 0;
   if (!b_scales || K % fmt_block(fmt_b) != 0) return 0;
   return 1;

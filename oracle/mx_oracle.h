@@ -17,7 +17,9 @@
  *    range +-448, NVFP4 row) and the FAQ answer on the shared exponent
  *    (E = ceil(log2(max|x| / max_E2M1)) + 127).
  *  - zubnet.ai news summary: NVFP4 = E2M1 in 16-element blocks; MXFP8 =
- *    E4M3/E5M2 in 32-element blocks.
+ *    E4M3/E5M2 in 32-element blocks (the OCP FP8 formats).
+ *  - produtoramaxvision format table: MXFP6 = E3M2 elements with an E8M0
+ *    scale per 32, 6.25 bits per element.
  *  - gist.science summary of "Unveiling the Potential of Quantization with
  *    MXFP4", section 2.A: the standard MX rule maps the block amax into (3, 6];
  *    NVFP4 scales carry a mantissa; overflow-aware scaling (OAS) widens the
@@ -42,7 +44,9 @@ enum {
   MXO_FMT_BF16 = 0,  /* plain bf16, no scales (activation side of W4A16) */
   MXO_FMT_MXFP4 = 1, /* E2M1 codes, one E8M0 scale per 32 elements */
   MXO_FMT_MXFP8 = 2, /* E4M3 codes, one E8M0 scale per 32 elements */
-  MXO_FMT_NVFP4 = 3  /* E2M1 codes, one E4M3 scale per 16, fp32 tensor scale */
+  MXO_FMT_NVFP4 = 3, /* E2M1 codes, one E4M3 scale per 16, fp32 tensor scale */
+  MXO_FMT_MXFP8_E5M2 = 4, /* E5M2 codes, one E8M0 scale per 32 */
+  MXO_FMT_MXFP6_E3M2 = 5  /* E3M2 codes (6 bits, packed), one E8M0 scale per 32 */
 };
 enum { MXO_OUT_F32 = 0, MXO_OUT_BF16 = 1 };
 enum { MXO_OK = 0, MXO_ERR_ARG = 1 };
@@ -52,11 +56,15 @@ double mxo_bf16_value(uint16_t bits);
 double mxo_e2m1_value(uint8_t code);  /* low 4 bits used */
 double mxo_e4m3_value(uint8_t code);  /* 0x7F / 0xFF -> NaN */
 double mxo_e8m0_value(uint8_t e);     /* 255 -> NaN */
+double mxo_e5m2_value(uint8_t code);  /* exponent 31: Inf (mantissa 0) or NaN */
+double mxo_e3m2_value(uint8_t code);  /* low 6 bits used; no Inf or NaN */
 
 /* Nearest representable value, ties to the even code, saturating at the
  * largest magnitude; the sign bit of v is copied (so -0 encodes as -0). */
 uint8_t mxo_encode_e2m1(double v);
 uint8_t mxo_encode_e4m3(double v);
+uint8_t mxo_encode_e5m2(double v);
+uint8_t mxo_encode_e3m2(double v);
 
 /* Round a float to bf16, nearest-even (NaN stays NaN, overflow goes to Inf). */
 uint16_t mxo_f32_to_bf16(float f);
@@ -71,7 +79,8 @@ int64_t mxo_storage_bytes(int fmt, int64_t rows, int64_t cols);
 
 /* ---- tensor operations, row-major, blocks along cols ------------------- */
 /* x: bf16 bits [rows][cols]; codes: [rows][cols/2] (FP4, even element in the
- * low nibble) or [rows][cols] (FP8); scales: [rows][cols/block] bytes;
+ * low nibble), [rows][cols] (FP8) or [rows][3 cols/4] (FP6: element i of a row
+ * in bits 6i .. 6i+5 of the row's bytes, little-endian); scales: [rows][cols/block] bytes;
  * tensor_scale: NVFP4 only (written), may be NULL otherwise. */
 int mxo_quantize(int fmt, int block, int64_t rows, int64_t cols,
                  const uint16_t* x, uint8_t* codes, uint8_t* scales,
