@@ -50,7 +50,11 @@ typedef enum {
   MX_FMT_BF16 = 0,  /* plain bf16 (only as the A operand of a W4A16 GEMM) */
   MX_FMT_MXFP4 = 1, /* E2M1 + E8M0 per 32 */
   MX_FMT_MXFP8 = 2, /* E4M3 + E8M0 per 32 */
-  MX_FMT_NVFP4 = 3  /* E2M1 + E4M3 per 16 + fp32 tensor scale */
+  MX_FMT_NVFP4 = 3, /* E2M1 + E4M3 per 16 + fp32 tensor scale */
+  MX_FMT_MXFP8_E5M2 = 4, /* E5M2 + E8M0 per 32 (the OCP MXFP8 alternative) */
+  MX_FMT_MXFP6_E3M2 = 5  /* E3M2 + E8M0 per 32; 6-bit codes, element i of a row
+                            in bits 6i .. 6i+5 of the row's bytes (little-endian),
+                            3 cols / 4 bytes per row */
 } mx_format;
 
 typedef enum { MX_ROUND_RNE = 0 } mx_round; /* nearest, ties to even */
@@ -67,8 +71,10 @@ typedef enum {
 /*
  * Block quantization (the shared-exponent rule of the FAQ on the
  * produtoramaxvision page; x_real = 2^(E-127) * x_elem).
- *   MXFP4/MXFP8 (block 32): per block, E = ceil(log2(amax / emax)) + 127
- *     clamped to [0, 254] with emax = 6 (E2M1) or 448 (E4M3), evaluated
+ *   MXFP4/MXFP8/MXFP6 (block 32): per block, E = ceil(log2(amax / emax))
+ *     + 127 clamped to [0, 254] with emax = 6 (E2M1), 448 (E4M3), 57344
+ *     (E5M2) or 28 (E3M2; E5M2 and E3M2 as named by the zubnet.ai summary and
+ *     the produtoramaxvision format table, fields as in the OCP formats), evaluated
  *     exactly from the bf16 bits of amax; each element is x / 2^(E-127)
  *     rounded to nearest-even with saturation, sign copied (-0 stays -0).
  *     A block holding Inf/NaN gets scale 255 (E8M0 NaN) and zero codes.
@@ -151,6 +157,10 @@ mx_status mx_dequantize(mx_format fmt, int block, mx_round rnd, int64_t rows, in
  *   (NVFP4, NVFP4, 16)  W4A4 with E4M3 block scales; e * s_b is exact in bf16,
  *                       so the product runs on bf16 MFMA and s_t^A * s_t^B is
  *                       applied to the fp32 result
+ *   (MXFP8_E5M2, MXFP8_E5M2, 32) and (MXFP6_E3M2, MXFP6_E3M2, 32): exact
+ *                       bf16 expansion on the bf16 MFMA, as for MXFP8 (these
+ *                       need 256 * (bytes per code row) < 2^31, else
+ *                       MX_ERR_INVALID_ARG)
  *   (BF16,  MXFP4, 32)  W4A16: bf16 activations times MXFP4 weights expanded
  *                       exactly to bf16 (weight-only quantization)
  * a: codes (or bf16 for MX_FMT_BF16) [M][...]; a_scales [M][K/block] (NULL for

@@ -18,14 +18,26 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmx.so")
 
 MX_FMT_BF16, MX_FMT_MXFP4, MX_FMT_MXFP8, MX_FMT_NVFP4 = 0, 1, 2, 3
+MX_FMT_MXFP8_E5M2, MX_FMT_MXFP6_E3M2 = 4, 5
 MX_ROUND_RNE = 0
 MX_SCALE_CEIL, MX_SCALE_OAS = 0, 1
 MX_ROTATE_NONE, MX_ROTATE_WHT32 = 0, 1
 MX_OUT_F32, MX_OUT_BF16 = 0, 1
 MX_OK, MX_ERR_INVALID_ARG, MX_ERR_UNSUPPORTED, MX_ERR_HIP = 0, 1, 2, 3
 
-FORMATS = {"mxfp4": MX_FMT_MXFP4, "mxfp8": MX_FMT_MXFP8, "nvfp4": MX_FMT_NVFP4, "bf16": MX_FMT_BF16}
-BLOCK = {MX_FMT_MXFP4: 32, MX_FMT_MXFP8: 32, MX_FMT_NVFP4: 16, MX_FMT_BF16: 32}
+FORMATS = {"mxfp4": MX_FMT_MXFP4, "mxfp8": MX_FMT_MXFP8, "nvfp4": MX_FMT_NVFP4, "bf16": MX_FMT_BF16,
+           "mxfp8_e5m2": MX_FMT_MXFP8_E5M2, "mxfp6_e3m2": MX_FMT_MXFP6_E3M2}
+BLOCK = {MX_FMT_MXFP4: 32, MX_FMT_MXFP8: 32, MX_FMT_NVFP4: 16, MX_FMT_BF16: 32,
+         MX_FMT_MXFP8_E5M2: 32, MX_FMT_MXFP6_E3M2: 32}
+
+
+def code_cols(fmt, cols):
+    """Bytes of codes per row of `cols` elements."""
+    if fmt in (MX_FMT_MXFP8, MX_FMT_MXFP8_E5M2):
+        return cols
+    if fmt == MX_FMT_MXFP6_E3M2:
+        return cols * 3 // 4
+    return cols // 2
 
 # Symbols declared in include/mx.h.
 EXPORTS = ("mx_quantize", "mx_quantize_workspace_bytes", "mx_quantize_ex", "mx_dequantize",
@@ -162,7 +174,7 @@ def quantize(x, fmt, scale_rule="ceil", rotation=None):
         if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
             raise ValueError("quantize expects a contiguous 2-D bfloat16 tensor")
         rows, cols = x.shape
-        codes = torch.empty((rows, cols if f == MX_FMT_MXFP8 else cols // 2), dtype=torch.uint8, device=x.device)
+        codes = torch.empty((rows, code_cols(f, cols)), dtype=torch.uint8, device=x.device)
         scales = torch.empty((rows, cols // BLOCK[f]), dtype=torch.uint8, device=x.device)
         _check(mx_quantize_ex(f, BLOCK[f], MX_ROUND_RNE, SCALE_RULES[scale_rule], ROTATIONS[rotation], rows,
                               cols, _ptr(x), _ptr(codes), _ptr(scales), _stream(torch, x.device)),
@@ -172,7 +184,7 @@ def quantize(x, fmt, scale_rule="ceil", rotation=None):
         raise ValueError("quantize expects a contiguous 2-D bfloat16 tensor")
     rows, cols = x.shape
     dev = x.device
-    codes = torch.empty((rows, cols if f == MX_FMT_MXFP8 else cols // 2), dtype=torch.uint8, device=dev)
+    codes = torch.empty((rows, code_cols(f, cols)), dtype=torch.uint8, device=dev)
     scales = torch.empty((rows, cols // BLOCK[f]), dtype=torch.uint8, device=dev)
     ts = ws = None
     wsb = 0
@@ -198,7 +210,7 @@ def dequantize(q, out_dtype=None):
 
 
 def gemm(a, b, out_dtype=None, out=None, workspace=None):
-    """C = A * B^T. a: QTensor (MXFP4/MXFP8/NVFP4, M x K) or a bf16 [M][K]
+    """C = A * B^T. a: QTensor (any quantized format, M x K; b of the same format) or a bf16 [M][K]
     tensor (with an MXFP4 b: W4A16); b: QTensor stored N x K."""
     import torch
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype

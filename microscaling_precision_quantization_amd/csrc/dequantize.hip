@@ -1,5 +1,6 @@
 // Dequantization kernels for gfx950: x_real = S * x_elem ("Fundamentos
-// matematicos do formato MXFP4 e E8M0" on the produtoramaxvision page). MX:
+// matematicos do formato MXFP4 e E8M0" on the produtoramaxvision page). MX
+// (MXFP4, MXFP8 E4M3 / E5M2, MXFP6 E3M2):
 // y = val(code) * 2^(E-127); NVFP4: y = fl32(fl32(val * s_b) * s_t).
 //
 // One thread expands one 16-byte group of 8 outputs' codes. The scaled decodes
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void dequant_mxfp4_kernel(const uint32_t*
   store8<OUT>(y, c, o);
 }
 
-template <int OUT>
+template <int OUT, bool E5M2>
 __global__ __launch_bounds__(kThreads) void dequant_mxfp8_kernel(const u32x2* __restrict__ codes,
                                                                  const uint8_t* __restrict__ scales,
                                                                  void* __restrict__ y, int64_t nchunks) {
@@ -83,14 +84,49 @@ __global__ __launch_bounds__(kThreads) void dequant_mxfp8_kernel(const u32x2* __
     for (int i = 0; i < 8; i++) o[i] = __builtin_bit_cast(float, kNaNf);
   } else {
     const float s = e8m0_to_float(E);
-    f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q.x, s, false);
-    f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q.x, s, true);
-    f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q.y, s, false);
-    f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q.y, s, true);
+    f32x2 p0, p1, p2, p3;
+    if (E5M2) {
+      p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(q.x, s, false);
+      p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(q.x, s, true);
+      p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(q.y, s, false);
+      p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(q.y, s, true);
+    } else {
+      p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q.x, s, false);
+      p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q.x, s, true);
+      p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q.y, s, false);
+      p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(q.y, s, true);
+    }
     o[0] = p0.x; o[1] = p0.y; o[2] = p1.x; o[3] = p1.y;
     o[4] = p2.x; o[5] = p2.y; o[6] = p3.x; o[7] = p3.y;
   }
   store8<OUT>(y, c, o);
+}
+
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+
+// MXFP6 (E3M2): one thread per 32-block (24 code bytes).
+template <int OUT>
+__global__ __launch_bounds__(kThreads) void dequant_mxfp6_kernel(const u32x2* __restrict__ codes,
+                                                                 const uint8_t* __restrict__ scales,
+                                                                 void* __restrict__ y, int64_t nblocks) {
+  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (b >= nblocks) return;
+  const u32x2 q0 = codes[3 * b], q1 = codes[3 * b + 1], q2 = codes[3 * b + 2];
+  const uint32_t E = scales[b];
+  f32x32 v;
+  if (E == 255) {
+#pragma unroll
+    for (int i = 0; i < 32; i++) v[i] = __builtin_bit_cast(float, kNaNf);
+  } else {
+    v = __builtin_amdgcn_cvt_scalef32_pk32_f32_bf6(u32x6{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y}, e8m0_to_float(E));
+  }
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const float o[8] = {v[8 * j], v[8 * j + 1], v[8 * j + 2], v[8 * j + 3],
+                        v[8 * j + 4], v[8 * j + 5], v[8 * j + 6], v[8 * j + 7]};
+    store8<OUT>(y, 4 * b + j, o);
+  }
 }
 
 template <int OUT>
@@ -130,9 +166,21 @@ hipError_t dequant(int fmt, int64_t rows, int64_t cols, const void* codes, const
       dequant_mxfp4_kernel<kOutBF16><<<grid, kThreads, 0, s>>>((const uint32_t*)codes, sc, y, nchunks);
   } else if (fmt == kMXFP8) {
     if (out_dtype == kOutF32)
-      dequant_mxfp8_kernel<kOutF32><<<grid, kThreads, 0, s>>>((const u32x2*)codes, sc, y, nchunks);
+      dequant_mxfp8_kernel<kOutF32, false><<<grid, kThreads, 0, s>>>((const u32x2*)codes, sc, y, nchunks);
     else
-      dequant_mxfp8_kernel<kOutBF16><<<grid, kThreads, 0, s>>>((const u32x2*)codes, sc, y, nchunks);
+      dequant_mxfp8_kernel<kOutBF16, false><<<grid, kThreads, 0, s>>>((const u32x2*)codes, sc, y, nchunks);
+  } else if (fmt == kMXFP8E5M2) {
+    if (out_dtype == kOutF32)
+      dequant_mxfp8_kernel<kOutF32, true><<<grid, kThreads, 0, s>>>((const u32x2*)codes, sc, y, nchunks);
+    else
+      dequant_mxfp8_kernel<kOutBF16, true><<<grid, kThreads, 0, s>>>((const u32x2*)codes, sc, y, nchunks);
+  } else if (fmt == kMXFP6) {
+    const int64_t nblocks = rows * cols / 32;
+    const dim3 g6((unsigned)((nblocks + kThreads - 1) / kThreads));
+    if (out_dtype == kOutF32)
+      dequant_mxfp6_kernel<kOutF32><<<g6, kThreads, 0, s>>>((const u32x2*)codes, sc, y, nblocks);
+    else
+      dequant_mxfp6_kernel<kOutBF16><<<g6, kThreads, 0, s>>>((const u32x2*)codes, sc, y, nblocks);
   } else {
     if (out_dtype == kOutF32)
       dequant_nvfp4_kernel<kOutF32><<<grid, kThreads, 0, s>>>((const uint32_t*)codes, sc, tensor_scale, y, nchunks);

@@ -1,6 +1,8 @@
-// Large-tile MXFP8 x MXFP8 and NVFP4 x NVFP4 GEMM for gfx950 on the 16-bit
-// MFMAs, every operand expanded exactly to bf16 (MXFP8) or fp16 (NVFP4) (why
-// not the FP8/FP4 matrix paths is explained in gemm_bf16x.hip).
+// Large-tile GEMM for gfx950 on the 16-bit MFMAs for MXFP8 (E4M3 or E5M2
+// elements), MXFP6 (E3M2) and NVFP4, each operand pair of one format, every
+// operand expanded exactly to bf16 (MX formats) or fp16 (NVFP4) (why not the
+// FP8/FP4 matrix paths is explained in gemm_bf16x.hip; E5M2 and E3M2 have 3
+// significant bits, exact in bf16 like E4M3).
 //
 // Design for CDNA4:
 //  * 256 x 256 output tile per workgroup, 4 waves (one per SIMD) of 128 x 128,
@@ -11,8 +13,9 @@
 //    once, one stage ahead, into the idle half of a 2 x 64 KB double buffer),
 //    LDS -> MFMA. The barrier between stages waits for LDS work only, so the
 //    global loads stay in flight across it.
-//  * Expansion: MXFP8 to bf16 with v_cvt_scalef32_pk_bf16_fp8 and the E8M0
-//    scale as an fp32 power of two (the instruction reads only the scale's
+//  * Expansion: MXFP8 to bf16 with v_cvt_scalef32_pk_bf16_fp8 (E4M3) or
+//    _bf8 (E5M2), MXFP6 with v_cvt_scalef32_pk32_bf16_bf6, the E8M0 scale
+//    passed as an fp32 power of two (the instructions read only the scale's
 //    exponent; 255 makes every output NaN, as in the oracle). NVFP4 to fp16:
 //    v_cvt_scalef32_pk_f16_fp4 at unit scale and one packed fp16 multiply by
 //    the E4M3 block scale, exact because every E2M1 x E4M3 product has at
@@ -37,6 +40,10 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+typedef __bf16 bf16x32 __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -58,12 +65,20 @@ __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 // NVFP4 chunk = 32 codes (2 per row, rows t/2 + 128u).
 template <int FMT>
 struct Geo {
-  static constexpr int kCodesPerChunk = (FMT == kMXFP8) ? 16 : 32;
+  static constexpr bool kByte = (FMT == kMXFP8 || FMT == kMXFP8E5M2);   // 8-bit codes
+  static constexpr int kCodesPerChunk = kByte ? 16 : 32;
   static constexpr int kChunksPerRow = BK / kCodesPerChunk;      // 4 or 2
   static constexpr int kChunks = BM * kChunksPerRow / kThreads;  // per thread per operand: 4 or 2
   static constexpr int kRowStep = kThreads / kChunksPerRow;      // 64 or 128
-  static constexpr int kBlock = (FMT == kMXFP8) ? 32 : 16;       // elements per scale
+  static constexpr int kBlock = (FMT == kNVFP4) ? 16 : 32;       // elements per scale
+  static constexpr bool kFp16 = (FMT == kNVFP4);                  // fp16 operands
 };
+
+// Code bytes per row of K elements.
+template <int FMT>
+__host__ __device__ constexpr int64_t row_bytes(int64_t K) {
+  return (FMT == kMXFP8 || FMT == kMXFP8E5M2) ? K : (FMT == kMXFP6) ? K * 3 / 4 : K / 2;
+}
 
 // One thread's share of a stage for both operands: codes and raw scale bits
 // (MXFP8: the E8M0 byte of the chunk's block; NVFP4: the chunk's two E4M3
@@ -71,11 +86,13 @@ struct Geo {
 template <int FMT>
 struct Stage {
   u32x4 qa[Geo<FMT>::kChunks], qb[Geo<FMT>::kChunks];
+  u32x4 ta[Geo<FMT>::kChunks], tb[Geo<FMT>::kChunks];  // MXFP6: bytes 16 .. 23 of a chunk (.xy)
   uint32_t sa[Geo<FMT>::kChunks], sb[Geo<FMT>::kChunks];
 };
 
 template <int FMT>
-__device__ __forceinline__ void load_op(u32x4 (&q)[Geo<FMT>::kChunks], uint32_t (&sc)[Geo<FMT>::kChunks],
+__device__ __forceinline__ void load_op(u32x4 (&q)[Geo<FMT>::kChunks], u32x4 (&t)[Geo<FMT>::kChunks],
+                                        uint32_t (&sc)[Geo<FMT>::kChunks],
                                         __amdgpu_buffer_rsrc_t rX, __amdgpu_buffer_rsrc_t rS,
                                         uint32_t rowbytes, uint32_t scalebytes, int K, int s,
                                         int tid, int u) {
@@ -84,52 +101,70 @@ __device__ __forceinline__ void load_op(u32x4 (&q)[Geo<FMT>::kChunks], uint32_t 
   const int c = tid % G::kChunksPerRow;
   const int k = s * BK + c * G::kCodesPerChunk;  // first element of the chunk
   const bool ok = k < K;
-  const uint32_t cb = (FMT == kMXFP8) ? (uint32_t)k : (uint32_t)k / 2;
-  q[u] = __builtin_amdgcn_raw_buffer_load_b128(rX, ok ? (uint32_t)row * rowbytes + cb : kOOB, 0, 0);
+  const uint32_t cb = (uint32_t)row_bytes<FMT>(k);
+  const uint32_t off = (uint32_t)row * rowbytes + cb;
+  q[u] = __builtin_amdgcn_raw_buffer_load_b128(rX, ok ? off : kOOB, 0, 0);
+  if (FMT == kMXFP6) {
+    const u32x2 t2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rX, ok ? off + 16 : kOOB, 0, 0));
+    t[u] = u32x4{t2.x, t2.y, 0, 0};
+  }
   const uint32_t so = (uint32_t)row * scalebytes + (uint32_t)(k / G::kBlock);
-  if (FMT == kMXFP8)
-    sc[u] = __builtin_amdgcn_raw_buffer_load_b8(rS, ok ? so : kOOB, 0, 0);
-  else
+  if (FMT == kNVFP4)
     sc[u] = __builtin_amdgcn_raw_buffer_load_b16(rS, ok ? so : kOOB, 0, 0);
+  else
+    sc[u] = __builtin_amdgcn_raw_buffer_load_b8(rS, ok ? so : kOOB, 0, 0);
 }
 
 // The stage's staging work is split into 4 parts, one per MFMA sub-step: an
 // item is one (operand, chunk u) pair, 2 kChunks items per stage, so a part
-// holds 2 items (MXFP8: chunk P of A and of B) or 1 (NVFP4: chunk P % 2 of A
-// for P < 2, of B otherwise).
+// holds 2 items (8-bit codes: chunk P of A and of B) or 1 (4- and 6-bit codes:
+// chunk P % 2 of A for P < 2, of B otherwise).
 template <int FMT, int P>
 __device__ __forceinline__ void load_part(Stage<FMT>& st, __amdgpu_buffer_rsrc_t rA,
                                           __amdgpu_buffer_rsrc_t rSA, __amdgpu_buffer_rsrc_t rB,
                                           __amdgpu_buffer_rsrc_t rSB, uint32_t rowbytes,
                                           uint32_t scalebytes, int K, int s, int tid) {
-  if (FMT == kMXFP8) {
-    load_op<FMT>(st.qa, st.sa, rA, rSA, rowbytes, scalebytes, K, s, tid, P);
-    load_op<FMT>(st.qb, st.sb, rB, rSB, rowbytes, scalebytes, K, s, tid, P);
+  if (Geo<FMT>::kChunks == 4) {
+    load_op<FMT>(st.qa, st.ta, st.sa, rA, rSA, rowbytes, scalebytes, K, s, tid, P);
+    load_op<FMT>(st.qb, st.tb, st.sb, rB, rSB, rowbytes, scalebytes, K, s, tid, P);
   } else if (P < 2) {
-    load_op<FMT>(st.qa, st.sa, rA, rSA, rowbytes, scalebytes, K, s, tid, P % 2);
+    load_op<FMT>(st.qa, st.ta, st.sa, rA, rSA, rowbytes, scalebytes, K, s, tid, P % 2);
   } else {
-    load_op<FMT>(st.qb, st.sb, rB, rSB, rowbytes, scalebytes, K, s, tid, P % 2);
+    load_op<FMT>(st.qb, st.tb, st.sb, rB, rSB, rowbytes, scalebytes, K, s, tid, P % 2);
   }
 }
 
 // Expands one chunk to bf16 and writes it to LDS row `row` of `tile`.
 template <int FMT>
-__device__ __forceinline__ void expand_chunk(const u32x4& q, uint32_t sbits, uint8_t* tile, int row,
-                                             int c) {
+__device__ __forceinline__ void expand_chunk(const u32x4& q, const u32x4& qt, uint32_t sbits,
+                                             uint8_t* tile, int row, int c) {
   uint8_t* base = tile + row * kRowBytes;
   const int sw = swz(row);
-  if (FMT == kMXFP8) {
+  if (FMT == kMXFP8 || FMT == kMXFP8E5M2) {
     // 16 codes -> LDS chunks 2c, 2c + 1.
     const float s = __builtin_bit_cast(float, sbits << 23);
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
     uint32_t o[8];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], s, false));
-      o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], s, true));
+      if (FMT == kMXFP8) {
+        o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], s, false));
+        o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], s, true));
+      } else {
+        o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w[i], s, false));
+        o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w[i], s, true));
+      }
     }
     *(u32x4*)(base + (((2 * c) ^ sw) * 16)) = u32x4{o[0], o[1], o[2], o[3]};
     *(u32x4*)(base + (((2 * c + 1) ^ sw) * 16)) = u32x4{o[4], o[5], o[6], o[7]};
+  } else if (FMT == kMXFP6) {
+    // 32 codes (24 bytes) -> LDS chunks 4c .. 4c + 3.
+    const float s = __builtin_bit_cast(float, sbits << 23);
+    const u32x6 w = __builtin_shufflevector(q, qt, 0, 1, 2, 3, 4, 5);
+    const u32x16 o = __builtin_bit_cast(u32x16, __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(w, s));
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      *(u32x4*)(base + (((4 * c + i) ^ sw) * 16)) = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
   } else {
     // 32 codes (two 16-blocks) -> LDS chunks 4c .. 4c + 3, as fp16: every
     // e * s_b (E2M1 times E4M3: at most 6 significant bits, magnitude in
@@ -163,17 +198,17 @@ template <int FMT, int P>
 __device__ __forceinline__ void store_part(const Stage<FMT>& st, uint8_t* stage, int tid) {
   using G = Geo<FMT>;
   const int c = tid % G::kChunksPerRow;
-  if (FMT == kMXFP8) {
+  if (G::kChunks == 4) {
     const int row = tid / G::kChunksPerRow + G::kRowStep * P;
-    expand_chunk<FMT>(st.qa[P], st.sa[P], stage, row, c);
-    expand_chunk<FMT>(st.qb[P], st.sb[P], stage + kTileBytes, row, c);
+    expand_chunk<FMT>(st.qa[P], st.ta[P], st.sa[P], stage, row, c);
+    expand_chunk<FMT>(st.qb[P], st.tb[P], st.sb[P], stage + kTileBytes, row, c);
   } else {
     const int u = P % 2;
     const int row = tid / G::kChunksPerRow + G::kRowStep * u;
     if (P < 2)
-      expand_chunk<FMT>(st.qa[u], st.sa[u], stage, row, c);
+      expand_chunk<FMT>(st.qa[u], st.ta[u], st.sa[u], stage, row, c);
     else
-      expand_chunk<FMT>(st.qb[u], st.sb[u], stage + kTileBytes, row, c);
+      expand_chunk<FMT>(st.qb[u], st.tb[u], st.sb[u], stage + kTileBytes, row, c);
   }
 }
 
@@ -239,7 +274,7 @@ __device__ __forceinline__ void region_order() {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   }
-  if (FMT == kMXFP8) {
+  if (Geo<FMT>::kChunks == 4) {
 #pragma unroll
     for (int k = 0; k < 4; k++) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -280,7 +315,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16x_large_kernel(
   const int m0 = tm * BM, n0 = tn * BN;
 
   // Buffer views based at the tile's first rows: rows past M or N read as 0.
-  const uint32_t rowbytes = (FMT == kMXFP8) ? (uint32_t)K : (uint32_t)(K / 2);
+  const uint32_t rowbytes = (uint32_t)row_bytes<FMT>(K);
   const uint32_t scalebytes = (uint32_t)(K / Geo<FMT>::kBlock);
   const int mrows = min(BM, M - m0), nrows = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * rowbytes), 0, (int)(mrows * rowbytes), kRsrcFlags);
@@ -320,8 +355,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16x_large_kernel(
     const int s2 = min(s + 2, nsteps - 1);
     const uint8_t* As = cur;
     const uint8_t* Bs = cur + kTileBytes;
-    // Operand elements: bf16 for MXFP8, fp16 for NVFP4.
-    using V = typename std::conditional<FMT == kMXFP8, bf16x8, f16x8>::type;
+    // Operand elements: bf16 for the MX formats, fp16 for NVFP4.
+    using V = typename std::conditional<Geo<FMT>::kFp16, f16x8, bf16x8>::type;
     V fa0[4], fb0[4], fa1[4], fb1[4];
     load_frags<0>(As, Bs, wm, wn, r, g, fa0, fb0);
     fence();
@@ -367,7 +402,7 @@ void launch(hipStream_t s, int tm, int tn, const uint8_t* A, const uint8_t* SA, 
 
 // 32-bit buffer offsets cover the tile's rows (codes and scales).
 bool gemm_bf16x_large_fits(int fmt, int64_t M, int64_t N, int64_t K) {
-  const int64_t rowbytes = (fmt == kMXFP8) ? K : K / 2;
+  const int64_t rowbytes = (fmt == kMXFP8 || fmt == kMXFP8E5M2) ? K : (fmt == kMXFP6) ? K * 3 / 4 : K / 2;
   const int64_t lim = (int64_t)1 << 31;
   return (int64_t)BM * rowbytes < lim && (M + N) > 0;
 }
@@ -380,6 +415,10 @@ hipError_t gemm_bf16x_large(int fmt, int64_t M, int64_t N, int64_t K, const void
                 *SB = (const uint8_t*)sb;
   if (fmt == kMXFP8)
     launch<kMXFP8>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
+  else if (fmt == kMXFP8E5M2)
+    launch<kMXFP8E5M2>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
+  else if (fmt == kMXFP6)
+    launch<kMXFP6>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
   else
     launch<kNVFP4>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
   return hipGetLastError();

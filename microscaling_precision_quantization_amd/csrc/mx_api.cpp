@@ -16,7 +16,10 @@ thread_local int g_last_hip_error = 0;
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
-bool is_quant_fmt(int f) { return f == MX_FMT_MXFP4 || f == MX_FMT_MXFP8 || f == MX_FMT_NVFP4; }
+bool is_quant_fmt(int f) {
+  return f == MX_FMT_MXFP4 || f == MX_FMT_MXFP8 || f == MX_FMT_NVFP4 || f == MX_FMT_MXFP8_E5M2 ||
+         f == MX_FMT_MXFP6_E3M2;
+}
 int block_of(int f) { return f == MX_FMT_NVFP4 ? 16 : 32; }
 
 // Elements per tensor stay below 2^40 and every GEMM extent below 2^30 so that
@@ -113,7 +116,9 @@ mx_status mx_gemm(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int
   const bool w8a8 = fmt_a == MX_FMT_MXFP8 && fmt_b == MX_FMT_MXFP8 && block == 32;
   const bool nv = fmt_a == MX_FMT_NVFP4 && fmt_b == MX_FMT_NVFP4 && block == 16;
   const bool w4a16 = fmt_a == MX_FMT_BF16 && fmt_b == MX_FMT_MXFP4 && block == 32;
-  if (!(w4a4 || w8a8 || nv || w4a16)) return MX_ERR_UNSUPPORTED;
+  const bool alt = fmt_a == fmt_b && block == 32 &&
+                   (fmt_a == MX_FMT_MXFP8_E5M2 || fmt_a == MX_FMT_MXFP6_E3M2);
+  if (!(w4a4 || w8a8 || nv || w4a16 || alt)) return MX_ERR_UNSUPPORTED;
   if (rnd != MX_ROUND_RNE) return MX_ERR_UNSUPPORTED;
   if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16) return MX_ERR_UNSUPPORTED;
   if (M <= 0 || N <= 0 || K <= 0 || M > kMaxExtent || N > kMaxExtent || K > kMaxExtent)
@@ -150,6 +155,11 @@ mx_status mx_gemm(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int
   if (w8a8 || nv)
     return hip_status(mx::gemm_bf16x(fmt_a, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts,
                                      out_dtype, c, ldc, s));
+  if (alt) {
+    if (!mx::gemm_bf16x_large_fits(fmt_a, M, N, K)) return MX_ERR_INVALID_ARG;
+    return hip_status(mx::gemm_bf16x_large(fmt_a, M, N, K, a, a_scales, nullptr, b, b_scales,
+                                           nullptr, out_dtype, c, ldc, s));
+  }
   return hip_status(mx::gemm_w4a16(M, N, K, a, b, b_scales, out_dtype, c, ldc, workspace, s));
 }
 

@@ -8,7 +8,7 @@
 namespace mx {
 
 // Format ids, kept equal to the public mx_format values.
-enum : int { kBF16 = 0, kMXFP4 = 1, kMXFP8 = 2, kNVFP4 = 3 };
+enum : int { kBF16 = 0, kMXFP4 = 1, kMXFP8 = 2, kNVFP4 = 3, kMXFP8E5M2 = 4, kMXFP6 = 5 };
 enum : int { kOutF32 = 0, kOutBF16 = 1 };
 
 // ---- quantize.hip

@@ -1,4 +1,5 @@
-// Block quantization kernels for gfx950 (MXFP4, MXFP8, NVFP4).
+// Block quantization kernels for gfx950 (MXFP4, MXFP8 with E4M3 or E5M2
+// elements, MXFP6 with E3M2 elements, NVFP4).
 //
 // Shared-exponent rule: FAQ of "Microscaling MXFP4/NVFP4 on Blackwell for
 // reasoning LLMs" (E = ceil(log2(amax / max_elem)) + 127); element and scale
@@ -118,8 +119,8 @@ __device__ __forceinline__ u32x4 wht32_chunk(u32x4 v, int lane) {
   return o;
 }
 
-// MXFP4 (FMT 1) / MXFP8 (FMT 2); OAS: MXFP4's overflow-aware scale rule;
-// ROT: rotate every block first.
+// MXFP4 / MXFP8 (E4M3) / MXFP8 (E5M2); OAS: MXFP4's overflow-aware scale
+// rule; ROT: rotate every block first.
 template <int FMT, bool OAS, bool ROT>
 __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restrict__ x,
                                                             void* __restrict__ codes,
@@ -144,8 +145,11 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restr
     // emax = 6 = 1.5 * 2^2  -> E = ea - 2 + [mantissa > 0x40]
     // emax = 7 = 1.75 * 2^2 (OAS) -> E = ea - 2 + [mantissa > 0x60]
     // emax = 448 = 1.75 * 2^8 -> E = ea - 8 + [mantissa > 0x60]
+    // emax = 57344 = 1.75 * 2^15 (E5M2) -> E = ea - 15 + [mantissa > 0x60]
     const int ea = (int)(m >> 7), ma = (int)(m & 0x7F);
-    int e = (FMT == kMXFP4) ? ea - 2 + (ma > (OAS ? 0x60 : 0x40)) : ea - 8 + (ma > 0x60);
+    int e = (FMT == kMXFP4) ? ea - 2 + (ma > (OAS ? 0x60 : 0x40))
+            : (FMT == kMXFP8) ? ea - 8 + (ma > 0x60)
+                              : ea - 15 + (ma > 0x60);
     e = e < 0 ? 0 : e;
     const bool nonfinite = m >= 0x7F80u;
     const uint32_t E = nonfinite ? 255u : (uint32_t)e;
@@ -160,10 +164,17 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restr
       if (c < nchunks) __builtin_nontemporal_store(q, (uint32_t*)codes + c);
     } else {
       i16x2 lo = {0, 0}, hi = {0, 0};
-      lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, as_bf16x2(v[u].x), scale, false);
-      lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, as_bf16x2(v[u].y), scale, true);
-      hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, as_bf16x2(v[u].z), scale, false);
-      hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, as_bf16x2(v[u].w), scale, true);
+      if (FMT == kMXFP8) {
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, as_bf16x2(v[u].x), scale, false);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, as_bf16x2(v[u].y), scale, true);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, as_bf16x2(v[u].z), scale, false);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, as_bf16x2(v[u].w), scale, true);
+      } else {
+        lo = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(lo, as_bf16x2(v[u].x), scale, false);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(lo, as_bf16x2(v[u].y), scale, true);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(hi, as_bf16x2(v[u].z), scale, false);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(hi, as_bf16x2(v[u].w), scale, true);
+      }
       u32x2 q = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
       if (nonfinite) q = u32x2{0, 0};
       if (c < nchunks) __builtin_nontemporal_store(q, (u32x2*)codes + c);
@@ -180,6 +191,41 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restr
     // Ragged end: the row's lane 15 is past the end, store bytes instead.
     if ((lane & 3) == 0 && c < nchunks && c - (lane & 15) + 15 >= nchunks) scales[blk] = (uint8_t)E;
   }
+}
+
+// ---- MXFP6 (E3M2) ---------------------------------------------------------
+
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+typedef __bf16 bf16x32 __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+
+// One lane per 32-block: 64 bytes of bf16 in, 24 bytes of 6-bit codes out
+// (v_cvt_scalef32_pk32_bf6_bf16: nearest-even of x / scale, element i in bits
+// 6i .. 6i+5), one scale byte. emax = 28 = 1.75 * 2^4 -> E = ea - 4 + [m > 0x60].
+__global__ __launch_bounds__(kThreads) void quant_mxfp6_kernel(const u32x4* __restrict__ x,
+                                                               u32x2* __restrict__ codes,
+                                                               uint8_t* __restrict__ scales,
+                                                               int64_t nblocks) {
+  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (b >= nblocks) return;
+  u32x4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) v[i] = __builtin_nontemporal_load(x + 4 * b + i);
+  const uint32_t m = umax(umax(chunk_absmax(v[0]), chunk_absmax(v[1])),
+                          umax(chunk_absmax(v[2]), chunk_absmax(v[3])));
+  const int ea = (int)(m >> 7), ma = (int)(m & 0x7F);
+  int e = ea - 4 + (ma > 0x60);
+  e = e < 0 ? 0 : e;
+  const bool nonfinite = m >= 0x7F80u;
+  const u32x16 w = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w,
+                    v[2].x, v[2].y, v[2].z, v[2].w, v[3].x, v[3].y, v[3].z, v[3].w};
+  u32x6 q = __builtin_bit_cast(u32x6, __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(
+                                          __builtin_bit_cast(bf16x32, w), e8m0_to_float((uint32_t)e)));
+  if (nonfinite) q = u32x6{0, 0, 0, 0, 0, 0};
+  __builtin_nontemporal_store(u32x2{q[0], q[1]}, codes + 3 * b);
+  __builtin_nontemporal_store(u32x2{q[2], q[3]}, codes + 3 * b + 1);
+  __builtin_nontemporal_store(u32x2{q[4], q[5]}, codes + 3 * b + 2);
+  scales[b] = nonfinite ? (uint8_t)255 : (uint8_t)e;
 }
 
 // ---- NVFP4 ---------------------------------------------------------------
@@ -307,11 +353,17 @@ hipError_t quant_mx(int fmt, int64_t rows, int64_t cols, const void* x, void* co
       quant_mx_kernel<kMXFP4, false, true><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
     else
       quant_mx_kernel<kMXFP4, false, false><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
-  } else {
+  } else if (fmt == kMXFP8) {
     if (rot)
       quant_mx_kernel<kMXFP8, false, true><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
     else
       quant_mx_kernel<kMXFP8, false, false><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
+  } else if (fmt == kMXFP8E5M2) {
+    quant_mx_kernel<kMXFP8E5M2, false, false><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
+  } else {
+    const int64_t nblocks = rows * cols / 32;
+    quant_mxfp6_kernel<<<(unsigned)((nblocks + kThreads - 1) / kThreads), kThreads, 0, s>>>(
+        X, (u32x2*)codes, S, nblocks);
   }
   return hipGetLastError();
 }

@@ -10,8 +10,10 @@ import microscaling_precision_quantization_amd as mx
 import oracle as orc
 import synth
 
-ORC_FMT = {"mxfp4": orc.FMT_MXFP4, "mxfp8": orc.FMT_MXFP8, "nvfp4": orc.FMT_NVFP4}
-MX_FMT = {"mxfp4": mx.MX_FMT_MXFP4, "mxfp8": mx.MX_FMT_MXFP8, "nvfp4": mx.MX_FMT_NVFP4}
+ORC_FMT = {"mxfp4": orc.FMT_MXFP4, "mxfp8": orc.FMT_MXFP8, "nvfp4": orc.FMT_NVFP4,
+           "mxfp8_e5m2": orc.FMT_MXFP8_E5M2, "mxfp6_e3m2": orc.FMT_MXFP6_E3M2}
+MX_FMT = {"mxfp4": mx.MX_FMT_MXFP4, "mxfp8": mx.MX_FMT_MXFP8, "nvfp4": mx.MX_FMT_NVFP4,
+          "mxfp8_e5m2": mx.MX_FMT_MXFP8_E5M2, "mxfp6_e3m2": mx.MX_FMT_MXFP6_E3M2}
 
 
 def require_gpu():
