@@ -28,7 +28,13 @@ sys.path.insert(0, ROOT)
 
 # MI355X published peaks.
 PEAK_HBM_GBPS = 8000.0
-PEAK_TFLOPS = {"mxfp4": 10100.0, "mxfp8": 5000.0, "nvfp4": 2500.0, "w4a16": 2500.0}
+# Dense MFMA peaks the GEMM is measured against: the element format's own
+# matrix rate where a native path exists or would exist (MXFP4 on the FP4
+# scaled MFMA; MXFP8 against FP8 even though the exact path runs on bf16),
+# otherwise the 16-bit MFMA the exact path runs on (NVFP4: fp16 operands,
+# W4A16: bf16; MXFP6 against the FP6/FP4 rate, as MXFP8 against FP8).
+PEAK_TFLOPS = {"mxfp4": 10100.0, "mxfp8": 5000.0, "nvfp4": 2500.0, "w4a16": 2500.0,
+               "mxfp8_e5m2": 5000.0, "mxfp6_e3m2": 10100.0}
 ROTATE_BYTES = 1 << 30  # activation copies cycled per step: > 256 MB MALL
 WEIGHT_ROTATE_BYTES = 512 << 20  # weight copies cycled per step: > 256 MB MALL, so
                                  # every step streams its weights from HBM, as the
@@ -96,7 +102,11 @@ def main():
     A = to_dev(A_bits)
     Bx = to_dev(B_bits)
     wfmt = "mxfp4" if fmt == "w4a16" else fmt
-    qb = mx.quantize(Bx, wfmt)  # weights: pre-quantized, outside the timed step
+    variant = dict(scale_rule=w.get("scale_rule", "ceil"), rotation=w.get("rotation"))
+    # weights: pre-quantized, outside the timed step (rotated like A when the
+    # step rotates, so that the product is unchanged; OAS is an activation-side
+    # choice and W keeps the standard rule)
+    qb = mx.quantize(Bx, wfmt, rotation=variant["rotation"])
     del Bx
     wbytes = qb.codes.numel() * qb.codes.element_size() + qb.scales.numel() * qb.scales.element_size()
     nwcopies = max(2, -(-WEIGHT_ROTATE_BYTES // wbytes))
@@ -116,7 +126,7 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         if quantize_a:
-            qa = mx.quantize(a, fmt)
+            qa = mx.quantize(a, fmt, **variant)
         else:
             qa = a
         if ev is not None:
@@ -168,7 +178,8 @@ def main():
     gemm_tflops = flops / (g_avg * 1e-3) / 1e12
     peak = PEAK_TFLOPS[fmt]
     # Algorithmic bytes of the quantizer: read bf16 once, write codes + scales.
-    elem_bytes = {"mxfp4": 0.5 + 1 / 32, "mxfp8": 1 + 1 / 32, "nvfp4": 0.5 + 1 / 16}
+    elem_bytes = {"mxfp4": 0.5 + 1 / 32, "mxfp8": 1 + 1 / 32, "nvfp4": 0.5 + 1 / 16,
+                  "mxfp8_e5m2": 1 + 1 / 32, "mxfp6_e3m2": 0.75 + 1 / 32}
     q_bytes = M * K * (2 + elem_bytes.get(fmt, 0)) + (4 if fmt == "nvfp4" else 0)
 
     if fmt == "w4a16":
@@ -194,11 +205,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"mxfp4": "e2m1+e8m0 (fp32 accumulate)", "mxfp8": "e4m3+e8m0 (fp32 accumulate)",
-                  "nvfp4": "e2m1+e4m3 via bf16 (fp32 accumulate)",
-                  "w4a16": "bf16 x e2m1+e8m0 (fp32 accumulate)"}[fmt],
+        "dtype": {"mxfp4": "e2m1+e8m0 (fp32 accumulate)", "mxfp8": "e4m3+e8m0 via bf16 (fp32 accumulate)",
+                  "nvfp4": "e2m1+e4m3 via fp16 (fp32 accumulate)",
+                  "w4a16": "bf16 x e2m1+e8m0 (fp32 accumulate)",
+                  "mxfp8_e5m2": "e5m2+e8m0 via bf16 (fp32 accumulate)",
+                  "mxfp6_e3m2": "e3m2+e8m0 via bf16 (fp32 accumulate)"}[fmt],
         "data": "synthetic",
         "config": {"workload": name, "format": fmt, "M": M, "N": N, "K": K,
+                   "scale_rule": variant["scale_rule"], "rotation": variant["rotation"],
                    "step": ("quantize(A) + gemm" if quantize_a else "gemm") + ", bf16 out",
                    "weights": "pre-quantized", "activation_copies_rotated": len(acts),
                    "weight_copies_rotated": len(weights)},
@@ -214,7 +228,7 @@ def main():
         line["quantize"] = {"GB/s": q_gbps, "ms": q_avg, "frac_of_hbm": q_gbps / PEAK_HBM_GBPS,
                             "algorithmic_bytes": q_bytes}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(name, fmt, A_bits, qb, M, N, K, args.cpu_rows)
+        line["cpu_baseline"] = cpu_baseline(name, fmt, A_bits, qb, M, N, K, args.cpu_rows, variant)
     line["input_gen_s"] = round(gen_s, 2)
     print(json.dumps(line), flush=True)
 
@@ -243,7 +257,7 @@ def measured_traffic(workload):
     return None
 
 
-def cpu_baseline(name, fmt, A_bits, qb, M, N, K, rows):
+def cpu_baseline(name, fmt, A_bits, qb, M, N, K, rows, variant):
     """The oracle (single-threaded C) on the first `rows` activation rows of the
     same step: quantize those rows, then their GEMM against all N weight rows
     (exact operands, double accumulation). Scaled to TFLOP/s of 2*rows*N*K."""
@@ -251,7 +265,8 @@ def cpu_baseline(name, fmt, A_bits, qb, M, N, K, rows):
 
     import oracle as orc
     ofmt = {"mxfp4": orc.FMT_MXFP4, "mxfp8": orc.FMT_MXFP8, "nvfp4": orc.FMT_NVFP4,
-            "w4a16": orc.FMT_BF16}[fmt]
+            "w4a16": orc.FMT_BF16, "mxfp8_e5m2": orc.FMT_MXFP8_E5M2,
+            "mxfp6_e3m2": orc.FMT_MXFP6_E3M2}[fmt]
     bcodes = qb.codes.cpu().numpy()
     bscales = qb.scales.cpu().numpy()
     bts = float(qb.tensor_scale.cpu().numpy()[0]) if qb.tensor_scale is not None else 1.0
@@ -260,6 +275,10 @@ def cpu_baseline(name, fmt, A_bits, qb, M, N, K, rows):
     if ofmt == orc.FMT_BF16:
         ac, asc, ats = a, None, 1.0
         fb = orc.FMT_MXFP4
+    elif variant["scale_rule"] != "ceil" or variant["rotation"]:
+        ac, asc = orc.quantize_ex(ofmt, a, orc.RULE_OAS if variant["scale_rule"] == "oas" else orc.RULE_CEIL,
+                                  orc.ROT_WHT32 if variant["rotation"] == "wht32" else orc.ROT_NONE)
+        ats, fb = 1.0, ofmt
     else:
         ac, asc, ats = orc.quantize(ofmt, a)
         fb = ofmt

@@ -94,6 +94,21 @@ WORKLOADS = {
     "w4a16_decode_16x8192x28672": dict(
         fmt="w4a16", M=16, N=28672, K=8192,
         a=("normal", 1.0, 501), b=("normal", 0.02, 502)),
+    # Format and quantizer variants on the shapes and data of the rows above.
+    "mxfp8e5m2_dit_qkv_4608x3072x9216": dict(
+        fmt="mxfp8_e5m2", M=4608, N=9216, K=3072,
+        a=("normal", 1.0, 201), b=("normal", 0.02, 202)),
+    "mxfp6e3m2_dit_qkv_4608x3072x9216": dict(
+        fmt="mxfp6_e3m2", M=4608, N=9216, K=3072,
+        a=("normal", 1.0, 201), b=("normal", 0.02, 202)),
+    "mxfp4oas_dit_mlp_down_4608x12288x3072": dict(
+        fmt="mxfp4", M=4608, N=3072, K=12288, scale_rule="oas",
+        a=("laplace_outlier_channels", 401, 403, 0.005, 100.0),
+        b=("normal", 0.02, 402)),
+    "mxfp4wht32_dit_mlp_down_4608x12288x3072": dict(
+        fmt="mxfp4", M=4608, N=3072, K=12288, rotation="wht32",
+        a=("laplace_outlier_channels", 401, 403, 0.005, 100.0),
+        b=("normal", 0.02, 402)),
 }
 
 # Short names used on the command line and in tests.
@@ -103,6 +118,10 @@ ALIASES = {
     "c3": "nvfp4_dit_mlp_up_4608x3072x12288",
     "c4": "mxfp4_dit_mlp_down_4608x12288x3072",
     "c5": "w4a16_decode_16x8192x28672",
+    "f1": "mxfp4oas_dit_mlp_down_4608x12288x3072",
+    "f2a": "mxfp8e5m2_dit_qkv_4608x3072x9216",
+    "f2b": "mxfp6e3m2_dit_qkv_4608x3072x9216",
+    "f4": "mxfp4wht32_dit_mlp_down_4608x12288x3072",
 }
 
 
