@@ -17,11 +17,12 @@ import numpy as np
 from . import build as _build
 
 FMT_BF16, FMT_MXFP4, FMT_MXFP8, FMT_NVFP4 = 0, 1, 2, 3
-FMT_MXFP8_E5M2, FMT_MXFP6_E3M2 = 4, 5
+FMT_MXFP8_E5M2, FMT_MXFP6_E3M2, FMT_MXFP4_MBS = 4, 5, 6
 RULE_CEIL, RULE_OAS = 0, 1
 ROT_NONE, ROT_WHT32 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
-BLOCK = {FMT_MXFP4: 32, FMT_MXFP8: 32, FMT_NVFP4: 16, FMT_MXFP8_E5M2: 32, FMT_MXFP6_E3M2: 32}
+BLOCK = {FMT_MXFP4: 32, FMT_MXFP8: 32, FMT_NVFP4: 16, FMT_MXFP8_E5M2: 32, FMT_MXFP6_E3M2: 32,
+         FMT_MXFP4_MBS: 32}
 
 _lib = None
 
@@ -47,6 +48,8 @@ def lib():
         L.mxo_f32_to_bf16.argtypes = [ctypes.c_float]
         L.mxo_mx_scale_exponent.restype = ctypes.c_int
         L.mxo_mx_scale_exponent.argtypes = [ctypes.c_double, ctypes.c_double]
+        L.mxo_mbs_macro_mantissa.restype = ctypes.c_int
+        L.mxo_mbs_macro_mantissa.argtypes = [ctypes.c_double]
         L.mxo_storage_bytes.restype = i64
         L.mxo_storage_bytes.argtypes = [ctypes.c_int, i64, i64]
         L.mxo_quantize.restype = ctypes.c_int
@@ -127,6 +130,10 @@ def mx_scale_exponent(amax, emax):
     return lib().mxo_mx_scale_exponent(float(amax), float(emax))
 
 
+def mbs_macro_mantissa(alpha):
+    return lib().mxo_mbs_macro_mantissa(float(alpha))
+
+
 def storage_bytes(fmt, rows, cols):
     return lib().mxo_storage_bytes(fmt, rows, cols)
 
@@ -140,14 +147,30 @@ def code_shape(fmt, rows, cols):
     return (rows, cols // 2)
 
 
+def scale_shape(fmt, rows, cols):
+    """[rows][cols/block]; MXFP4-MBS: one flat buffer holding the E8M0 plane
+    [rows][cols/32] and then the macro plane [rows][cols/128]."""
+    if fmt == FMT_MXFP4_MBS:
+        return (rows * (cols // 32) + rows * (cols // 128),)
+    return (rows, cols // BLOCK[fmt])
+
+
+def mbs_planes(scales, rows, cols):
+    """Split an MXFP4-MBS scale buffer into (E8M0 [rows][cols/32],
+    macro mantissas [rows][cols/128])."""
+    s = np.asarray(scales).reshape(-1)
+    n = rows * (cols // 32)
+    return s[:n].reshape(rows, cols // 32), s[n:].reshape(rows, cols // 128)
+
+
 def quantize(fmt, x_bits):
     """x_bits: uint16 [rows][cols] bf16 bit patterns.
-    Returns (codes uint8, scales uint8 [rows][cols/block], tensor_scale float)."""
+    Returns (codes uint8, scales uint8 (scale_shape), tensor_scale float)."""
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
     rows, cols = x.shape
     blk = BLOCK[fmt]
     codes = np.zeros(code_shape(fmt, rows, cols), np.uint8)
-    scales = np.zeros((rows, cols // blk), np.uint8)
+    scales = np.zeros(scale_shape(fmt, rows, cols), np.uint8)
     ts = np.zeros(1, np.float32)
     _check(lib().mxo_quantize(fmt, blk, rows, cols, _ptr(x), _ptr(codes),
                               _ptr(scales), _ptr(ts)), "quantize")

@@ -216,14 +216,21 @@ static int fmt_block(int fmt) {
   return (fmt == MXO_FMT_NVFP4) ? 16 : 32;
 }
 
+/* Elements per row must be a multiple of this: the block, or the 128-element
+ * macro block of MXFP4-MBS. */
+static int fmt_granule(int fmt) {
+  return (fmt == MXO_FMT_MXFP4_MBS) ? 128 : fmt_block(fmt);
+}
+
 /* 4 bits per element plus 8 bits per 32-element block is the page's
  * "4 + 8/32 = 4.25 bits per element". */
 int64_t mxo_storage_bytes(int fmt, int64_t rows, int64_t cols) {
-  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_MXFP6_E3M2) return -1;
+  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_MXFP4_MBS) return -1;
   int64_t n = rows * cols;
   int64_t code_bytes = n * elem_bits(fmt) / 8;
   int64_t scale_bytes = n / fmt_block(fmt);
-  return code_bytes + scale_bytes + (fmt == MXO_FMT_NVFP4 ? 4 : 0);
+  int64_t extra = (fmt == MXO_FMT_NVFP4) ? 4 : (fmt == MXO_FMT_MXFP4_MBS) ? n / 128 : 0;
+  return code_bytes + scale_bytes + extra;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -312,6 +319,68 @@ static uint8_t e2m1_nearest_scaled(double x, double D) {
   return (uint8_t)((signbit(x) ? 8 : 0) | c);
 }
 
+/* MBS-static macro mantissa (gist.science summary, section 2.B: a factor
+ * 1 + m with 8 mantissa bits per macro block, computed directly from the
+ * block maximum so that the outlier is normalised before the standard
+ * quantization). n is found by search with exact products, as in the MX
+ * rule; rho = alpha / 2^n is exact; m by search over the 8-bit grid. */
+int mxo_mbs_macro_mantissa(double alpha) {
+  if (!isfinite(alpha) || alpha == 0.0) return 0;
+  int n = -300;
+  while (!(alpha <= ldexp(6.0, n))) n++;
+  const double rho = ldexp(alpha, -n);
+  for (int m = 0; m < 256; m++)
+    if (3.0 * (1.0 + m / 256.0) >= rho) return m;
+  return 0; /* rho in (3 (1 + 255/256), 6]: already at the top of the grid */
+}
+
+/* MXFP4-MBS: per macro block of 128, the factor f from the macro amax; then
+ * each 32-block quantizes x / f by the MX rule. The scale search compares
+ * amax_b with (6 f) 2^n and the codes compare |x| with midpoint * f * 2^(E-127):
+ * every product is exact in double, so x / f is never rounded. */
+static void quantize_mbs(int64_t rows, int64_t cols, const uint16_t* x, uint8_t* codes,
+                         uint8_t* scales) {
+  const int64_t nb = cols / 32, nm = cols / 128;
+  uint8_t* macro = scales + rows * nb;
+  for (int64_t r = 0; r < rows; r++) {
+    for (int64_t q = 0; q < nm; q++) {
+      const uint16_t* xm = x + r * cols + q * 128;
+      int finite = 1;
+      double alpha = 0.0;
+      for (int i = 0; i < 128; i++) {
+        if (!bf16_is_finite(xm[i])) finite = 0;
+        double a = fabs(mxo_bf16_value(xm[i]));
+        if (a > alpha) alpha = a;
+      }
+      const int m = finite ? mxo_mbs_macro_mantissa(alpha) : 0;
+      macro[r * nm + q] = (uint8_t)m;
+      const double f = 1.0 + m / 256.0;
+      for (int b = 0; b < 4; b++) {
+        const uint16_t* xb = xm + 32 * b;
+        const int64_t first = r * cols + q * 128 + 32 * b;
+        const int64_t sidx = r * nb + q * 4 + b;
+        int bfinite = 1;
+        double amax = 0.0;
+        for (int i = 0; i < 32; i++) {
+          if (!bf16_is_finite(xb[i])) bfinite = 0;
+          double a = fabs(mxo_bf16_value(xb[i]));
+          if (a > amax) amax = a;
+        }
+        if (!bfinite) {
+          scales[sidx] = 255;
+          for (int i = 0; i < 32; i++) put_code(codes, MXO_FMT_MXFP4, first + i, 0);
+          continue;
+        }
+        const int E = mxo_mx_scale_exponent(amax, 6.0 * f);
+        scales[sidx] = (uint8_t)E;
+        const double D = ldexp(f, E - 127);
+        for (int i = 0; i < 32; i++)
+          put_code(codes, MXO_FMT_MXFP4, first + i, e2m1_nearest_scaled(mxo_bf16_value(xb[i]), D));
+      }
+    }
+  }
+}
+
 /* NVFP4, fp32 throughout (one rounding per operation):
  *  1. T = max |x| over the tensor.
  *  2. s_t = T / 2688 (2688 = 6 * 448 maps T onto the largest E2M1 value times
@@ -374,9 +443,12 @@ int mxo_quantize(int fmt, int block, int64_t rows, int64_t cols,
                  const uint16_t* x, uint8_t* codes, uint8_t* scales,
                  float* tensor_scale) {
   if (rows <= 0 || cols <= 0 || !x || !codes || !scales) return MXO_ERR_ARG;
-  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_MXFP6_E3M2) return MXO_ERR_ARG;
-  if (block != fmt_block(fmt) || cols % block != 0) return MXO_ERR_ARG;
-  if (is_mx(fmt)) {
+  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_MXFP4_MBS) return MXO_ERR_ARG;
+  if (block != fmt_block(fmt) || cols % fmt_granule(fmt) != 0) return MXO_ERR_ARG;
+  if (fmt == MXO_FMT_MXFP4_MBS) {
+    quantize_mbs(rows, cols, x, codes, scales);
+    if (tensor_scale) *tensor_scale = 1.0f;
+  } else if (is_mx(fmt)) {
     quantize_mx(fmt, rows, cols, x, codes, scales, elem_max(fmt));
     if (tensor_scale) *tensor_scale = 1.0f;
   } else {
@@ -400,15 +472,19 @@ int mxo_quantize_nvfp4_exact_quotient(int64_t rows, int64_t cols,
 
 /* Exact dequantized value of element idx (row-major), in double.
  * MX: element value * 2^(E-127) (x_real = S * x_elem). NVFP4: e * s_b * s_t,
- * which needs at most 2 + 4 + 24 significant bits, so it is exact. */
+ * which needs at most 2 + 4 + 24 significant bits, so it is exact. MXFP4-MBS:
+ * e * 2^(E-127) * (1 + m / 256), m from the macro plane `macro`
+ * ([rows][cols/128]; NULL for the other formats). */
 static double exact_value(int fmt, const uint8_t* codes, const uint8_t* scales,
-                          float ts, int64_t cols, int64_t idx) {
+                          const uint8_t* macro, float ts, int64_t cols, int64_t idx) {
   int block = fmt_block(fmt);
   int64_t r = idx / cols, c = idx % cols;
   uint8_t sc = scales[r * (cols / block) + c / block];
   uint8_t code = get_code(codes, fmt, idx);
   double e = elem_value(fmt, code);
   if (fmt == MXO_FMT_NVFP4) return e * mxo_e4m3_value(sc) * (double)ts;
+  if (fmt == MXO_FMT_MXFP4_MBS)
+    return e * mxo_e8m0_value(sc) * (1.0 + macro[r * (cols / 128) + c / 128] / 256.0);
   return e * mxo_e8m0_value(sc);
 }
 
@@ -416,9 +492,10 @@ int mxo_dequantize(int fmt, int block, int64_t rows, int64_t cols,
                    const uint8_t* codes, const uint8_t* scales,
                    float tensor_scale, int out_dtype, void* y) {
   if (rows <= 0 || cols <= 0 || !codes || !scales || !y) return MXO_ERR_ARG;
-  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_MXFP6_E3M2) return MXO_ERR_ARG;
-  if (block != fmt_block(fmt) || cols % block != 0) return MXO_ERR_ARG;
+  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_MXFP4_MBS) return MXO_ERR_ARG;
+  if (block != fmt_block(fmt) || cols % fmt_granule(fmt) != 0) return MXO_ERR_ARG;
   if (out_dtype != MXO_OUT_F32 && out_dtype != MXO_OUT_BF16) return MXO_ERR_ARG;
+  const uint8_t* macro = (fmt == MXO_FMT_MXFP4_MBS) ? scales + rows * (cols / 32) : NULL;
   for (int64_t i = 0; i < rows * cols; i++) {
     float f;
     if (fmt == MXO_FMT_NVFP4) {
@@ -428,7 +505,7 @@ int mxo_dequantize(int fmt, int block, int64_t rows, int64_t cols,
       float es = (float)(mxo_e2m1_value(get_code(codes, fmt, i)) * mxo_e4m3_value(sc));
       f = es * tensor_scale;
     } else {
-      f = (float)exact_value(fmt, codes, scales, 1.0f, cols, i);
+      f = (float)exact_value(fmt, codes, scales, macro, 1.0f, cols, i);
     }
     if (out_dtype == MXO_OUT_F32)
       ((float*)y)[i] = f;
@@ -443,7 +520,7 @@ int mxo_dequantize(int fmt, int block, int64_t rows, int64_t cols,
 /* ------------------------------------------------------------------------ */
 
 static void dequant_row(int fmt, const void* data, const uint8_t* scales,
-                        float ts, int64_t K, int64_t row, double* out) {
+                        const uint8_t* macro, float ts, int64_t K, int64_t row, double* out) {
   if (fmt == MXO_FMT_BF16) {
     const uint16_t* x = (const uint16_t*)data + row * K;
     for (int64_t k = 0; k < K; k++) out[k] = mxo_bf16_value(x[k]);
@@ -451,18 +528,23 @@ static void dequant_row(int fmt, const void* data, const uint8_t* scales,
   }
   /* exact_value indexes the whole matrix; pass the row's element index. */
   for (int64_t k = 0; k < K; k++)
-    out[k] = exact_value(fmt, (const uint8_t*)data, scales, ts, K, row * K + k);
+    out[k] = exact_value(fmt, (const uint8_t*)data, scales, macro, ts, K, row * K + k);
 }
 
 static int gemm_args_ok(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
                         const void* a, const uint8_t* a_scales, const void* b,
                         const uint8_t* b_scales) {
   if (M <= 0 || N <= 0 || K <= 0 || !a || !b) return 0;
-  if (fmt_a < MXO_FMT_BF16 || fmt_a > MXO_FMT_MXFP6_E3M2) return 0;
-  if (fmt_b < MXO_FMT_MXFP4 || fmt_b > MXO_FMT_MXFP6_E3M2) return 0;
-  if (fmt_a != MXO_FMT_BF16 && (!a_scales || K % fmt_block(fmt_a) != 0)) return 0;
-  if (!b_scales || K % fmt_block(fmt_b) != 0) return 0;
+  if (fmt_a < MXO_FMT_BF16 || fmt_a > MXO_FMT_MXFP4_MBS) return 0;
+  if (fmt_b < MXO_FMT_MXFP4 || fmt_b > MXO_FMT_MXFP4_MBS) return 0;
+  if (fmt_a != MXO_FMT_BF16 && (!a_scales || K % fmt_granule(fmt_a) != 0)) return 0;
+  if (!b_scales || K % fmt_granule(fmt_b) != 0) return 0;
   return 1;
+}
+
+/* The macro plane of an MXFP4-MBS operand with `rows` rows, else NULL. */
+static const uint8_t* macro_plane(int fmt, const uint8_t* scales, int64_t rows, int64_t K) {
+  return (fmt == MXO_FMT_MXFP4_MBS) ? scales + rows * (K / 32) : NULL;
 }
 
 static void dot_abs(const double* x, const double* y, int64_t K, double* c,
@@ -490,9 +572,11 @@ int mxo_gemm(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
     free(ar);
     return MXO_ERR_ARG;
   }
-  for (int64_t j = 0; j < N; j++) dequant_row(fmt_b, b, b_scales, b_ts, K, j, bt + j * K);
+  const uint8_t* ma = macro_plane(fmt_a, a_scales, M, K);
+  const uint8_t* mb = macro_plane(fmt_b, b_scales, N, K);
+  for (int64_t j = 0; j < N; j++) dequant_row(fmt_b, b, b_scales, mb, b_ts, K, j, bt + j * K);
   for (int64_t i = 0; i < M; i++) {
-    dequant_row(fmt_a, a, a_scales, a_ts, K, i, ar);
+    dequant_row(fmt_a, a, a_scales, ma, a_ts, K, i, ar);
     for (int64_t j = 0; j < N; j++) dot_abs(ar, bt + j * K, K, &C[i * N + j], &S[i * N + j]);
   }
   free(bt);
@@ -517,9 +601,11 @@ int mxo_gemm_entries(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
     free(br);
     return MXO_ERR_ARG;
   }
+  const uint8_t* ma = macro_plane(fmt_a, a_scales, M, K);
+  const uint8_t* mb = macro_plane(fmt_b, b_scales, N, K);
   for (int64_t t = 0; t < n_entries; t++) {
-    dequant_row(fmt_a, a, a_scales, a_ts, K, ii[t], ar);
-    dequant_row(fmt_b, b, b_scales, b_ts, K, jj[t], br);
+    dequant_row(fmt_a, a, a_scales, ma, a_ts, K, ii[t], ar);
+    dequant_row(fmt_b, b, b_scales, mb, b_ts, K, jj[t], br);
     dot_abs(ar, br, K, &C[t], &S[t]);
   }
   free(ar);

@@ -24,6 +24,10 @@
  *    MXFP4", section 2.A: the standard MX rule maps the block amax into (3, 6];
  *    NVFP4 scales carry a mantissa; overflow-aware scaling (OAS) widens the
  *    scaled-amax range to (3.5, 7].
+ *  - the same gist.science summary, section 2.B: macro-block scaling (MBS)
+ *    adds a scale factor 1 + m with an 8-bit mantissa per 1 x 128 macro
+ *    block, computed in the static variant directly from the block maximum
+ *    to normalise outliers before the standard quantization.
  *  - produtoramaxvision page, section "Tecnicas de preservacao de acuracia:
  *    QuaRot, SpinQuant e ReSET": Hadamard / Walsh-Hadamard rotations spread
  *    a block's energy evenly over its 32 elements.
@@ -46,7 +50,8 @@ enum {
   MXO_FMT_MXFP8 = 2, /* E4M3 codes, one E8M0 scale per 32 elements */
   MXO_FMT_NVFP4 = 3, /* E2M1 codes, one E4M3 scale per 16, fp32 tensor scale */
   MXO_FMT_MXFP8_E5M2 = 4, /* E5M2 codes, one E8M0 scale per 32 */
-  MXO_FMT_MXFP6_E3M2 = 5  /* E3M2 codes (6 bits, packed), one E8M0 scale per 32 */
+  MXO_FMT_MXFP6_E3M2 = 5, /* E3M2 codes (6 bits, packed), one E8M0 scale per 32 */
+  MXO_FMT_MXFP4_MBS = 6   /* MXFP4 plus one 8-bit macro mantissa per 128 (MBS-static) */
 };
 enum { MXO_OUT_F32 = 0, MXO_OUT_BF16 = 1 };
 enum { MXO_OK = 0, MXO_ERR_ARG = 1 };
@@ -74,14 +79,32 @@ uint16_t mxo_f32_to_bf16(float f);
  * non-finite amax. emax = 6 (E2M1) or 448 (E4M3). */
 int mxo_mx_scale_exponent(double amax, double emax);
 
-/* Bytes of codes + scales (+4 for the NVFP4 tensor scale). */
+/* MBS-static macro mantissa m (0..255, factor f = 1 + m / 256) of a macro
+ * block with amax alpha: with n the smallest integer such that
+ * alpha <= 6 * 2^n and rho = alpha / 2^n (in (3, 6]), m is the smallest
+ * integer >= 0 with 3 f >= rho, so that alpha / f lies in
+ * (6 (1 - 2^-8), 6] * 2^(n-1), the top of the E2M1 grid one binade down;
+ * m = 256 (rho within 2^-8 of 6 already) becomes 0. alpha = 0 or non-finite
+ * gives 0. */
+int mxo_mbs_macro_mantissa(double alpha);
+
+/* Bytes of codes + scales (+4 for the NVFP4 tensor scale, + one macro byte
+ * per 128 elements for MXFP4-MBS). */
 int64_t mxo_storage_bytes(int fmt, int64_t rows, int64_t cols);
 
 /* ---- tensor operations, row-major, blocks along cols ------------------- */
 /* x: bf16 bits [rows][cols]; codes: [rows][cols/2] (FP4, even element in the
  * low nibble), [rows][cols] (FP8) or [rows][3 cols/4] (FP6: element i of a row
  * in bits 6i .. 6i+5 of the row's bytes, little-endian); scales: [rows][cols/block] bytes;
- * tensor_scale: NVFP4 only (written), may be NULL otherwise. */
+ * tensor_scale: NVFP4 only (written), may be NULL otherwise.
+ * MXFP4-MBS (block 32, cols a multiple of 128): codes as MXFP4; scales holds
+ * two planes, the E8M0 bytes [rows][cols/32] followed by the macro mantissas
+ * [rows][cols/128]. Per macro block of 128: m = mxo_mbs_macro_mantissa(amax)
+ * (0 if the macro block holds Inf or NaN), f = 1 + m / 256; per 32-block:
+ * E = smallest n with amax_b <= 6 f 2^n, plus 127, clamped to [0, 254], and
+ * each code the nearest-even E2M1 value of x / (f 2^(E-127)), saturating, sign
+ * copied; a 32-block holding Inf or NaN gets E = 255 and zero codes. The
+ * dequantized value is e * 2^(E-127) * f. */
 int mxo_quantize(int fmt, int block, int64_t rows, int64_t cols,
                  const uint16_t* x, uint8_t* codes, uint8_t* scales,
                  float* tensor_scale);
