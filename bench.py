@@ -34,7 +34,12 @@ PEAK_HBM_GBPS = 8000.0
 # otherwise the 16-bit MFMA the exact path runs on (NVFP4: fp16 operands,
 # W4A16: bf16; MXFP6 against the FP6/FP4 rate, as MXFP8 against FP8).
 PEAK_TFLOPS = {"mxfp4": 10100.0, "mxfp8": 5000.0, "nvfp4": 2500.0, "w4a16": 2500.0,
-               "mxfp8_e5m2": 5000.0, "mxfp6_e3m2": 10100.0}
+               "mxfp8_e5m2": 5000.0, "mxfp6_e3m2": 10100.0, "mxfp4_mbs": 10100.0}
+# fp32 vector lane-operations per second (one mul or one fma per lane per
+# cycle, no packed math): 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz. The MBS GEMM
+# is bound by its per-macro-block rescale on the vector ALU (2 operations per
+# output element per 128 K), so it is measured against this.
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 ROTATE_BYTES = 1 << 30  # activation copies cycled per step: > 256 MB MALL
 WEIGHT_ROTATE_BYTES = 512 << 20  # weight copies cycled per step: > 256 MB MALL, so
                                  # every step streams its weights from HBM, as the
@@ -179,7 +184,8 @@ def main():
     peak = PEAK_TFLOPS[fmt]
     # Algorithmic bytes of the quantizer: read bf16 once, write codes + scales.
     elem_bytes = {"mxfp4": 0.5 + 1 / 32, "mxfp8": 1 + 1 / 32, "nvfp4": 0.5 + 1 / 16,
-                  "mxfp8_e5m2": 1 + 1 / 32, "mxfp6_e3m2": 0.75 + 1 / 32}
+                  "mxfp8_e5m2": 1 + 1 / 32, "mxfp6_e3m2": 0.75 + 1 / 32,
+                  "mxfp4_mbs": 0.5 + 1 / 32 + 1 / 128}
     q_bytes = M * K * (2 + elem_bytes.get(fmt, 0)) + (4 if fmt == "nvfp4" else 0)
 
     if fmt == "w4a16":
@@ -188,6 +194,12 @@ def main():
         g_bytes = N * K / 2 + N * K / 32 + M * K * 2 + M * N * 2
         roof = {"bound": "hbm", "achieved": g_bytes / (g_avg * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s"}
+    elif fmt == "mxfp4_mbs":
+        # 2 vector operations (factor product, fma into the accumulator) per
+        # output element per 128-element macro block.
+        valu_ops = 2.0 * M * N * (K // 128)
+        roof = {"bound": "alu", "achieved": valu_ops / (g_avg * 1e-3) / 1e12, "peak": PEAK_VALU_TOPS,
+                "unit": "Top/s (fp32 vector lane operations)"}
     else:
         roof = {"bound": "mfma", "achieved": gemm_tflops, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
@@ -209,7 +221,8 @@ def main():
                   "nvfp4": "e2m1+e4m3 via fp16 (fp32 accumulate)",
                   "w4a16": "bf16 x e2m1+e8m0 (fp32 accumulate)",
                   "mxfp8_e5m2": "e5m2+e8m0 via bf16 (fp32 accumulate)",
-                  "mxfp6_e3m2": "e3m2+e8m0 via bf16 (fp32 accumulate)"}[fmt],
+                  "mxfp6_e3m2": "e3m2+e8m0 via bf16 (fp32 accumulate)",
+                  "mxfp4_mbs": "e2m1+e8m0, macro factor 1+m/256 (fp32 accumulate)"}[fmt],
         "data": "synthetic",
         "config": {"workload": name, "format": fmt, "M": M, "N": N, "K": K,
                    "scale_rule": variant["scale_rule"], "rotation": variant["rotation"],
@@ -266,7 +279,7 @@ def cpu_baseline(name, fmt, A_bits, qb, M, N, K, rows, variant):
     import oracle as orc
     ofmt = {"mxfp4": orc.FMT_MXFP4, "mxfp8": orc.FMT_MXFP8, "nvfp4": orc.FMT_NVFP4,
             "w4a16": orc.FMT_BF16, "mxfp8_e5m2": orc.FMT_MXFP8_E5M2,
-            "mxfp6_e3m2": orc.FMT_MXFP6_E3M2}[fmt]
+            "mxfp6_e3m2": orc.FMT_MXFP6_E3M2, "mxfp4_mbs": orc.FMT_MXFP4_MBS}[fmt]
     bcodes = qb.codes.cpu().numpy()
     bscales = qb.scales.cpu().numpy()
     bts = float(qb.tensor_scale.cpu().numpy()[0]) if qb.tensor_scale is not None else 1.0

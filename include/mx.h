@@ -27,7 +27,8 @@
  *
  * Errors: every argument is checked before anything is launched.
  *   MX_ERR_INVALID_ARG  null pointer, a size <= 0, cols or K not a multiple of
- *                       the block, a pointer not 16-byte aligned, ldc < N, or
+ *                       the block (of 128 for MXFP4_MBS), a pointer not
+ *                       16-byte aligned, ldc < N, or
  *                       workspace_bytes below the size the call needs.
  *   MX_ERR_UNSUPPORTED  a format/block pair or format combination outside the
  *                       list below, a rounding mode other than MX_ROUND_RNE,
@@ -52,9 +53,15 @@ typedef enum {
   MX_FMT_MXFP8 = 2, /* E4M3 + E8M0 per 32 */
   MX_FMT_NVFP4 = 3, /* E2M1 + E4M3 per 16 + fp32 tensor scale */
   MX_FMT_MXFP8_E5M2 = 4, /* E5M2 + E8M0 per 32 (the OCP MXFP8 alternative) */
-  MX_FMT_MXFP6_E3M2 = 5  /* E3M2 + E8M0 per 32; 6-bit codes, element i of a row
+  MX_FMT_MXFP6_E3M2 = 5, /* E3M2 + E8M0 per 32; 6-bit codes, element i of a row
                             in bits 6i .. 6i+5 of the row's bytes (little-endian),
                             3 cols / 4 bytes per row */
+  MX_FMT_MXFP4_MBS = 6   /* MXFP4 with static macro-block scaling: E2M1 + E8M0
+                            per 32, plus one 8-bit macro mantissa m per 128
+                            (factor 1 + m/256); cols must be a multiple of 128.
+                            scales = two planes in one buffer: the E8M0 bytes
+                            [rows][cols/32], then the macro bytes
+                            [rows][cols/128] */
 } mx_format;
 
 typedef enum { MX_ROUND_RNE = 0 } mx_round; /* nearest, ties to even */
@@ -78,6 +85,16 @@ typedef enum {
  *     exactly from the bf16 bits of amax; each element is x / 2^(E-127)
  *     rounded to nearest-even with saturation, sign copied (-0 stays -0).
  *     A block holding Inf/NaN gets scale 255 (E8M0 NaN) and zero codes.
+ *   MXFP4_MBS (block 32; the static macro-block scaling of the gist.science
+ *     summary of "Unveiling the Potential of Quantization with MXFP4",
+ *     section 2.B): per macro block of 128 with amax alpha, n = the smallest
+ *     integer with alpha <= 6 * 2^n, rho = alpha / 2^n, and m = the smallest
+ *     integer >= 0 with 3 (1 + m/256) >= rho (m = 256 becomes 0; a zero or
+ *     non-finite alpha gives 0); f = 1 + m/256. Each 32-block then gets
+ *     E = the smallest n with amax_b <= 6 f 2^n, plus 127, clamped to [0, 254],
+ *     and codes = nearest-even E2M1 of x / (f 2^(E-127)) with saturation, the
+ *     sign copied; a 32-block holding Inf/NaN gets 255 and zero codes. The
+ *     element's value is e * 2^(E-127) * f.
  *   NVFP4 (block 16), fp32 arithmetic, one rounding per step:
  *     T = max|x| over the tensor; s_t = T / 2688 (1 if T = 0);
  *     s_b = E4M3(amax_b / (6 s_t)) nearest-even, saturating at 448;
@@ -133,7 +150,8 @@ mx_status mx_quantize_ex(mx_format fmt, int block, mx_round rnd, mx_scale_rule r
 
 /*
  * Dequantization (x_real = S * x_elem on the produtoramaxvision page): MX
- * y = val(code) * 2^(E-127); NVFP4 y = fl32(fl32(val(code) * s_b) * s_t).
+ * y = val(code) * 2^(E-127); MXFP4_MBS y = val(code) * 2^(E-127) * (1 + m/256);
+ * NVFP4 y = fl32(fl32(val(code) * s_b) * s_t).
  * The fp32 value is the output for MX_OUT_F32; MX_OUT_BF16 rounds it to bf16,
  * nearest-even (overflow gives Inf; E = 255 or an E4M3 NaN scale gives NaN).
  * tensor_scale: NVFP4 only, device pointer to one fp32; NULL otherwise.
@@ -161,11 +179,16 @@ mx_status mx_dequantize(mx_format fmt, int block, mx_round rnd, int64_t rows, in
  *                       bf16 expansion on the bf16 MFMA, as for MXFP8 (these
  *                       need 256 * (bytes per code row) < 2^31, else
  *                       MX_ERR_INVALID_ARG)
+ *   (MXFP4_MBS, MXFP4_MBS, 32)  K a multiple of 128: per macro block the FP4
+ *                       scaled MFMA gives the E8M0-scaled partial sum P and
+ *                       the vector ALU adds P * f_A * f_B (f_A f_B exact in
+ *                       fp32) to the accumulator
  *   (BF16,  MXFP4, 32)  W4A16: bf16 activations times MXFP4 weights expanded
  *                       exactly to bf16 (weight-only quantization)
  * a: codes (or bf16 for MX_FMT_BF16) [M][...]; a_scales [M][K/block] (NULL for
- * BF16); a_ts, b_ts: NVFP4 tensor scales (device fp32), NULL otherwise.
- * b: codes [N][...]; b_scales [N][K/block].
+ * BF16; for MXFP4_MBS the two-plane buffer of mx_quantize); a_ts, b_ts: NVFP4
+ * tensor scales (device fp32), NULL otherwise.
+ * b: codes [N][...]; b_scales [N][K/block] (two planes for MXFP4_MBS).
  * c: [M][ldc] fp32 or bf16 (rnd rounds the bf16 epilogue).
  * workspace: device scratch of at least mx_gemm_workspace_bytes(...) bytes
  * (may be NULL when that is 0).

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmx.so")
 
 MX_FMT_BF16, MX_FMT_MXFP4, MX_FMT_MXFP8, MX_FMT_NVFP4 = 0, 1, 2, 3
-MX_FMT_MXFP8_E5M2, MX_FMT_MXFP6_E3M2 = 4, 5
+MX_FMT_MXFP8_E5M2, MX_FMT_MXFP6_E3M2, MX_FMT_MXFP4_MBS = 4, 5, 6
 MX_ROUND_RNE = 0
 MX_SCALE_CEIL, MX_SCALE_OAS = 0, 1
 MX_ROTATE_NONE, MX_ROTATE_WHT32 = 0, 1
@@ -26,9 +26,10 @@ MX_OUT_F32, MX_OUT_BF16 = 0, 1
 MX_OK, MX_ERR_INVALID_ARG, MX_ERR_UNSUPPORTED, MX_ERR_HIP = 0, 1, 2, 3
 
 FORMATS = {"mxfp4": MX_FMT_MXFP4, "mxfp8": MX_FMT_MXFP8, "nvfp4": MX_FMT_NVFP4, "bf16": MX_FMT_BF16,
-           "mxfp8_e5m2": MX_FMT_MXFP8_E5M2, "mxfp6_e3m2": MX_FMT_MXFP6_E3M2}
+           "mxfp8_e5m2": MX_FMT_MXFP8_E5M2, "mxfp6_e3m2": MX_FMT_MXFP6_E3M2,
+           "mxfp4_mbs": MX_FMT_MXFP4_MBS}
 BLOCK = {MX_FMT_MXFP4: 32, MX_FMT_MXFP8: 32, MX_FMT_NVFP4: 16, MX_FMT_BF16: 32,
-         MX_FMT_MXFP8_E5M2: 32, MX_FMT_MXFP6_E3M2: 32}
+         MX_FMT_MXFP8_E5M2: 32, MX_FMT_MXFP6_E3M2: 32, MX_FMT_MXFP4_MBS: 32}
 
 
 def code_cols(fmt, cols):
@@ -38,6 +39,22 @@ def code_cols(fmt, cols):
     if fmt == MX_FMT_MXFP6_E3M2:
         return cols * 3 // 4
     return cols // 2
+
+def scale_shape(fmt, rows, cols):
+    """Shape of the scales tensor: [rows][cols/block]; for MXFP4-MBS one flat
+    buffer, the E8M0 plane [rows][cols/32] followed by the macro mantissa
+    plane [rows][cols/128]."""
+    if fmt == MX_FMT_MXFP4_MBS:
+        return (rows * (cols // 32) + rows * (cols // 128),)
+    return (rows, cols // BLOCK[fmt])
+
+
+def mbs_planes(scales, rows, cols):
+    """Views of an MXFP4-MBS scales buffer: (E8M0 [rows][cols/32],
+    macro mantissas [rows][cols/128])."""
+    n = rows * (cols // 32)
+    return scales[:n].view(rows, cols // 32), scales[n:].view(rows, cols // 128)
+
 
 # Symbols declared in include/mx.h.
 EXPORTS = ("mx_quantize", "mx_quantize_workspace_bytes", "mx_quantize_ex", "mx_dequantize",
@@ -175,7 +192,7 @@ def quantize(x, fmt, scale_rule="ceil", rotation=None):
             raise ValueError("quantize expects a contiguous 2-D bfloat16 tensor")
         rows, cols = x.shape
         codes = torch.empty((rows, code_cols(f, cols)), dtype=torch.uint8, device=x.device)
-        scales = torch.empty((rows, cols // BLOCK[f]), dtype=torch.uint8, device=x.device)
+        scales = torch.empty(scale_shape(f, rows, cols), dtype=torch.uint8, device=x.device)
         _check(mx_quantize_ex(f, BLOCK[f], MX_ROUND_RNE, SCALE_RULES[scale_rule], ROTATIONS[rotation], rows,
                               cols, _ptr(x), _ptr(codes), _ptr(scales), _stream(torch, x.device)),
                "mx_quantize_ex")
@@ -185,7 +202,7 @@ def quantize(x, fmt, scale_rule="ceil", rotation=None):
     rows, cols = x.shape
     dev = x.device
     codes = torch.empty((rows, code_cols(f, cols)), dtype=torch.uint8, device=dev)
-    scales = torch.empty((rows, cols // BLOCK[f]), dtype=torch.uint8, device=dev)
+    scales = torch.empty(scale_shape(f, rows, cols), dtype=torch.uint8, device=dev)
     ts = ws = None
     wsb = 0
     if f == MX_FMT_NVFP4:

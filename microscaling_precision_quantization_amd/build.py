@@ -16,7 +16,7 @@ BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["mx_api.cpp", "quantize.hip", "dequantize.hip", "gemm_mx.hip", "gemm_mxfp4.hip", "gemm_bf16x.hip", "gemm_bf16x_large.hip",
-           "gemm_w4a16.hip"]
+           "gemm_w4a16.hip", "gemm_mbs.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
 # -ffp-contract=off: every fp32 step of the NVFP4 quantizer rounds once.
@@ -25,10 +25,16 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-ffp-contract=
           "-Wall", "-Wno-unused-function", "-I" + os.path.join(ROOT, "include")]
 
 
+# Per-source flags. gemm_mbs.hip: the MFMA partial sums feed vector-ALU
+# arithmetic, so select the MFMA forms that write VGPRs (the default puts them
+# in AGPRs and adds one v_accvgpr_read per element).
+EXTRA = {"gemm_mbs.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, src + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)

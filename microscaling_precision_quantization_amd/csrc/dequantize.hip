@@ -1,7 +1,9 @@
 // Dequantization kernels for gfx950: x_real = S * x_elem ("Fundamentos
 // matematicos do formato MXFP4 e E8M0" on the produtoramaxvision page). MX
 // (MXFP4, MXFP8 E4M3 / E5M2, MXFP6 E3M2):
-// y = val(code) * 2^(E-127); NVFP4: y = fl32(fl32(val * s_b) * s_t).
+// y = val(code) * 2^(E-127); NVFP4: y = fl32(fl32(val * s_b) * s_t); MXFP4
+// with macro-block scaling: y = val(code) * 2^(E-127) * (1 + m / 256), exact in
+// fp32 (the product has at most 11 significant bits) unless it overflows.
 //
 // One thread expands one 16-byte group of 8 outputs' codes. The scaled decodes
 // v_cvt_scalef32_pk_{f32,bf16}_fp4 and v_cvt_scalef32_pk_f32_fp8 multiply by a
@@ -102,6 +104,35 @@ __global__ __launch_bounds__(kThreads) void dequant_mxfp8_kernel(const u32x2* __
   store8<OUT>(y, c, o);
 }
 
+// MXFP4-MBS: the MXFP4 value times the macro factor of its 128-element block.
+template <int OUT>
+__global__ __launch_bounds__(kThreads) void dequant_mbs_kernel(const uint32_t* __restrict__ codes,
+                                                               const uint8_t* __restrict__ scales,
+                                                               const uint8_t* __restrict__ macro,
+                                                               void* __restrict__ y, int64_t nchunks) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= nchunks) return;
+  const uint32_t q = codes[c];
+  const uint32_t E = scales[c >> 2];
+  const float f = (float)(256u + macro[c >> 4]) * 0x1p-8f;
+  float o[8];
+  if (E == 255) {
+    for (int i = 0; i < 8; i++) o[i] = __builtin_bit_cast(float, kNaNf);
+  } else {
+    const float s = e8m0_to_float(E);
+    const f32x2 p[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, s, 0),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, s, 1),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, s, 2),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, s, 3)};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      o[2 * k] = p[k].x * f;
+      o[2 * k + 1] = p[k].y * f;
+    }
+  }
+  store8<OUT>(y, c, o);
+}
+
 typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
 typedef float f32x32 __attribute__((ext_vector_type(32)));
 
@@ -174,6 +205,12 @@ hipError_t dequant(int fmt, int64_t rows, int64_t cols, const void* codes, const
       dequant_mxfp8_kernel<kOutF32, true><<<grid, kThreads, 0, s>>>((const u32x2*)codes, sc, y, nchunks);
     else
       dequant_mxfp8_kernel<kOutBF16, true><<<grid, kThreads, 0, s>>>((const u32x2*)codes, sc, y, nchunks);
+  } else if (fmt == kMXFP4MBS) {
+    const uint8_t* mac = sc + rows * (cols / 32);
+    if (out_dtype == kOutF32)
+      dequant_mbs_kernel<kOutF32><<<grid, kThreads, 0, s>>>((const uint32_t*)codes, sc, mac, y, nchunks);
+    else
+      dequant_mbs_kernel<kOutBF16><<<grid, kThreads, 0, s>>>((const uint32_t*)codes, sc, mac, y, nchunks);
   } else if (fmt == kMXFP6) {
     const int64_t nblocks = rows * cols / 32;
     const dim3 g6((unsigned)((nblocks + kThreads - 1) / kThreads));

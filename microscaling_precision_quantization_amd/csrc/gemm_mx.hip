@@ -13,6 +13,14 @@
 //   FP8: K elements [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16), 32 bytes;
 // and, for both, the E8M0 scale of K block g of row r. Output: lane l holds
 // column l % 16, rows 4 (l / 16) + 0..3.
+//
+// MXFP4-MBS (static macro-block scaling; gist.science summary of "Unveiling
+// the Potential of Quantization with MXFP4", section 2.B): a K step of 128 is
+// exactly one macro block, so each step's MFMA starts from zero and yields the
+// block-scaled partial sum P of that macro block; the vector ALU then adds
+// P * f_A(row) * f_B(col) to the accumulator (f_A f_B has 18 significant bits
+// and is exact in fp32), the factor being applied alongside the matrix core
+// as the summary describes.
 #include "bf16.h"
 #include "mx_internal.h"
 
@@ -37,11 +45,14 @@ struct MxTile {
   static constexpr int kMfmaFmt = (FMT == kMXFP4) ? 4 : 0;  // cbsz / blgp selector
 };
 
-template <int FMT, int OUT>
+// MBS: MA / MB are the macro mantissa planes [rows][K/128] (unused otherwise).
+template <int FMT, int OUT, bool MBS>
 __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __restrict__ A,
                                                            const uint8_t* __restrict__ SA,
                                                            const uint8_t* __restrict__ B,
                                                            const uint8_t* __restrict__ SB,
+                                                           const uint8_t* __restrict__ MA,
+                                                           const uint8_t* __restrict__ MB,
                                                            void* __restrict__ C, int64_t ldc,
                                                            int M, int N, int K) {
   using T = MxTile<FMT>;
@@ -49,6 +60,8 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __rest
   __shared__ __attribute__((aligned(16))) uint8_t lB[BN * T::kStride];
   __shared__ uint32_t lSA[BM];
   __shared__ uint32_t lSB[BN];
+  __shared__ float lFA[MBS ? BM : 1];
+  __shared__ float lFB[MBS ? BN : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -59,6 +72,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __rest
 
   u32x4 ra[T::kLoads], rb[T::kLoads];
   uint32_t rs = 0;
+  float rf = 1.0f;
 
   auto gload = [&](int kt) {
 #pragma unroll
@@ -83,6 +97,12 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __rest
       const uint32_t e = (grow < glim && kbk < kblocks) ? S[(int64_t)grow * kblocks + kbk] : kUnitScale;
       rs |= e << (8 * j);
     }
+    if (MBS) {
+      // Macro factor 1 + m / 256 of this step's macro block (K step = 128).
+      const uint8_t* Mp = isA ? MA : MB;
+      const uint32_t m = (grow < glim) ? Mp[(int64_t)grow * (K / 128) + kt] : 0u;
+      rf = (float)(256u + m) * 0x1p-8f;
+    }
   };
   auto lstore = [&]() {
 #pragma unroll
@@ -96,6 +116,12 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __rest
       lSA[tid] = rs;
     else
       lSB[tid - 128] = rs;
+    if (MBS) {
+      if (tid < 128)
+        lFA[tid] = rf;
+      else
+        lFB[tid - 128] = rf;
+    }
   };
 
   f32x4 acc[4][4];
@@ -133,12 +159,32 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __rest
       sa[i] = (int)((lSA[ra_] >> (8 * g)) & 0xFFu);
       sb[i] = (int)((lSB[rb_] >> (8 * g)) & 0xFFu);
     }
+    if (MBS) {
+      float fa[4][4], fb[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+      for (int i = 0; i < 4; i++) {
+        fb[i] = lFB[wn * 64 + i * 16 + r];
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            af[i], bf[j], acc[i][j], T::kMfmaFmt, T::kMfmaFmt, 0, sa[i], 0, sb[j]);
+        for (int t = 0; t < 4; t++) fa[i][t] = lFA[wm * 64 + i * 16 + 4 * g + t];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[i], bf[j], f32x4{0, 0, 0, 0}, T::kMfmaFmt, T::kMfmaFmt, 0, sa[i], 0, sb[j]);
+#pragma unroll
+          for (int t = 0; t < 4; t++)
+            acc[i][j][t] = __builtin_fmaf(p[t], fa[i][t] * fb[j], acc[i][j][t]);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[i], bf[j], acc[i][j], T::kMfmaFmt, T::kMfmaFmt, 0, sa[i], 0, sb[j]);
+    }
   }
 
 #pragma unroll
@@ -172,15 +218,31 @@ hipError_t gemm_mx(int fmt, int64_t M, int64_t N, int64_t K, const void* a, cons
   const int m = (int)M, n = (int)N, k = (int)K;
   if (fmt == kMXFP4) {
     if (out_dtype == kOutF32)
-      gemm_mx_kernel<kMXFP4, kOutF32><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k);
+      gemm_mx_kernel<kMXFP4, kOutF32, false><<<grid, kThreads, 0, s>>>(A, SA, B, SB, nullptr, nullptr, c, ldc, m, n, k);
     else
-      gemm_mx_kernel<kMXFP4, kOutBF16><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k);
+      gemm_mx_kernel<kMXFP4, kOutBF16, false><<<grid, kThreads, 0, s>>>(A, SA, B, SB, nullptr, nullptr, c, ldc, m, n, k);
   } else {
     if (out_dtype == kOutF32)
-      gemm_mx_kernel<kMXFP8, kOutF32><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k);
+      gemm_mx_kernel<kMXFP8, kOutF32, false><<<grid, kThreads, 0, s>>>(A, SA, B, SB, nullptr, nullptr, c, ldc, m, n, k);
     else
-      gemm_mx_kernel<kMXFP8, kOutBF16><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k);
+      gemm_mx_kernel<kMXFP8, kOutBF16, false><<<grid, kThreads, 0, s>>>(A, SA, B, SB, nullptr, nullptr, c, ldc, m, n, k);
   }
+  return hipGetLastError();
+}
+
+hipError_t gemm_mbs_small(int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
+                          const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
+                          hipStream_t s) {
+  const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
+  const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
+                *SB = (const uint8_t*)sb;
+  const uint8_t* MA = SA + M * (K / 32);  // macro planes follow the E8M0 planes
+  const uint8_t* MB = SB + N * (K / 32);
+  const int m = (int)M, n = (int)N, k = (int)K;
+  if (out_dtype == kOutF32)
+    gemm_mx_kernel<kMXFP4, kOutF32, true><<<grid, kThreads, 0, s>>>(A, SA, B, SB, MA, MB, c, ldc, m, n, k);
+  else
+    gemm_mx_kernel<kMXFP4, kOutBF16, true><<<grid, kThreads, 0, s>>>(A, SA, B, SB, MA, MB, c, ldc, m, n, k);
   return hipGetLastError();
 }
 

@@ -18,9 +18,12 @@ bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 bool is_quant_fmt(int f) {
   return f == MX_FMT_MXFP4 || f == MX_FMT_MXFP8 || f == MX_FMT_NVFP4 || f == MX_FMT_MXFP8_E5M2 ||
-         f == MX_FMT_MXFP6_E3M2;
+         f == MX_FMT_MXFP6_E3M2 || f == MX_FMT_MXFP4_MBS;
 }
 int block_of(int f) { return f == MX_FMT_NVFP4 ? 16 : 32; }
+// cols (and K) must be a multiple of this: the block, or the 128-element macro
+// block of MXFP4-MBS.
+int granule_of(int f) { return f == MX_FMT_MXFP4_MBS ? 128 : block_of(f); }
 
 // Elements per tensor stay below 2^40 and every GEMM extent below 2^30 so that
 // the kernels' index arithmetic (int64 offsets, int extents) cannot overflow.
@@ -37,7 +40,7 @@ mx_status hip_status(hipError_t e) {
 mx_status check_tensor(int fmt, int block, int rnd, int64_t rows, int64_t cols) {
   if (!is_quant_fmt(fmt) || block != block_of(fmt)) return MX_ERR_UNSUPPORTED;
   if (rnd != MX_ROUND_RNE) return MX_ERR_UNSUPPORTED;
-  if (rows <= 0 || cols <= 0 || cols % block != 0) return MX_ERR_INVALID_ARG;
+  if (rows <= 0 || cols <= 0 || cols % granule_of(fmt) != 0) return MX_ERR_INVALID_ARG;
   if (rows > kMaxElems / cols) return MX_ERR_INVALID_ARG;
   return MX_OK;
 }
@@ -66,6 +69,7 @@ mx_status mx_quantize(mx_format fmt, int block, mx_round rnd, int64_t rows, int6
     return hip_status(mx::quant_nvfp4(rows, cols, x, codes, scales, tensor_scale, workspace, s));
   }
   if (tensor_scale) return MX_ERR_INVALID_ARG;
+  if (fmt == MX_FMT_MXFP4_MBS) return hip_status(mx::quant_mbs(rows, cols, x, codes, scales, s));
   return hip_status(mx::quant_mx(fmt, rows, cols, x, codes, scales, s));
 }
 
@@ -118,14 +122,15 @@ mx_status mx_gemm(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int
   const bool w4a16 = fmt_a == MX_FMT_BF16 && fmt_b == MX_FMT_MXFP4 && block == 32;
   const bool alt = fmt_a == fmt_b && block == 32 &&
                    (fmt_a == MX_FMT_MXFP8_E5M2 || fmt_a == MX_FMT_MXFP6_E3M2);
-  if (!(w4a4 || w8a8 || nv || w4a16 || alt)) return MX_ERR_UNSUPPORTED;
+  const bool mbs = fmt_a == MX_FMT_MXFP4_MBS && fmt_b == MX_FMT_MXFP4_MBS && block == 32;
+  if (!(w4a4 || w8a8 || nv || w4a16 || alt || mbs)) return MX_ERR_UNSUPPORTED;
   if (rnd != MX_ROUND_RNE) return MX_ERR_UNSUPPORTED;
   if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16) return MX_ERR_UNSUPPORTED;
   if (M <= 0 || N <= 0 || K <= 0 || M > kMaxExtent || N > kMaxExtent || K > kMaxExtent)
     return MX_ERR_INVALID_ARG;
   // K is a whole number of 32-element groups for every path (NVFP4 included:
   // its 16-blocks are staged in pairs).
-  if (K % 32 != 0) return MX_ERR_INVALID_ARG;
+  if (K % 32 != 0 || (mbs && K % 128 != 0)) return MX_ERR_INVALID_ARG;
   if (ldc < N) return MX_ERR_INVALID_ARG;
   // Row tiles run along gridDim.y (at most 65535): 128 rows per tile for the
   // W4A4/W8A8 kernels, 16 for W4A16.
@@ -152,6 +157,8 @@ mx_status mx_gemm(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int
   hipStream_t s = (hipStream_t)stream;
   if (w4a4)
     return hip_status(mx::gemm_mx(fmt_a, M, N, K, a, a_scales, b, b_scales, out_dtype, c, ldc, s));
+  if (mbs)
+    return hip_status(mx::gemm_mbs(M, N, K, a, a_scales, b, b_scales, out_dtype, c, ldc, s));
   if (w8a8 || nv)
     return hip_status(mx::gemm_bf16x(fmt_a, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts,
                                      out_dtype, c, ldc, s));

@@ -8,7 +8,7 @@
 namespace mx {
 
 // Format ids, kept equal to the public mx_format values.
-enum : int { kBF16 = 0, kMXFP4 = 1, kMXFP8 = 2, kNVFP4 = 3, kMXFP8E5M2 = 4, kMXFP6 = 5 };
+enum : int { kBF16 = 0, kMXFP4 = 1, kMXFP8 = 2, kNVFP4 = 3, kMXFP8E5M2 = 4, kMXFP6 = 5, kMXFP4MBS = 6 };
 enum : int { kOutF32 = 0, kOutBF16 = 1 };
 
 // ---- quantize.hip
@@ -16,6 +16,10 @@ enum : int { kOutF32 = 0, kOutBF16 = 1 };
 hipError_t quant_mx(int fmt, int64_t rows, int64_t cols, const void* x, void* codes,
                     void* scales, hipStream_t s, bool oas = false,
                     bool rot = false);
+// MXFP4 with static macro-block scaling: scales holds the E8M0 plane
+// [rows][cols/32] followed by the macro mantissa plane [rows][cols/128].
+hipError_t quant_mbs(int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
+                     hipStream_t s);
 size_t quant_nvfp4_workspace(int64_t rows, int64_t cols);
 hipError_t quant_nvfp4(int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
                        float* tensor_scale, void* workspace, hipStream_t s);
@@ -28,6 +32,19 @@ hipError_t dequant(int fmt, int64_t rows, int64_t cols, const void* codes, const
 hipError_t gemm_mx(int fmt, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
                    const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
                    hipStream_t s);
+
+// ---- gemm_mx.hip, MXFP4-MBS x MXFP4-MBS (128 x 128 tiles, any K % 128 = 0);
+// sa / sb are the two-plane scale buffers.
+hipError_t gemm_mbs_small(int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
+                          const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
+                          hipStream_t s);
+
+// ---- gemm_mbs.hip (MXFP4-MBS x MXFP4-MBS; 256 x 128 tiles when they fit,
+// else gemm_mbs_small)
+bool gemm_mbs_fits(int64_t M, int64_t N, int64_t K);
+hipError_t gemm_mbs(int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
+                    const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
+                    hipStream_t s);
 
 // ---- gemm_mxfp4.hip (MXFP4 x MXFP4, 256 x 256 tiles, direct-to-LDS pipeline)
 bool gemm_mxfp4_fits(int64_t M, int64_t N, int64_t K);

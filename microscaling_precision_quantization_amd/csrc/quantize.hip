@@ -22,6 +22,11 @@
 // block's 4 lanes (DPP quad permutes), then scaled by fl32(1/sqrt(32)) and
 // rounded to bf16 (v_cvt_pk_bf16_f32, nearest-even) before the usual steps.
 //
+// MXFP4 with static macro-block scaling (MBS; the same gist.science summary,
+// section 2.B): a macro block of 128 elements (16 lanes, one DPP row) gets one
+// factor f = 1 + m / 256 from its amax, and each 32-block inside quantizes
+// x / f by the MX rule (details at quant_mbs_kernel).
+//
 // Encoding uses gfx950's scaled converts. v_cvt_scalef32_pk_fp4_bf16 and
 // v_cvt_scalef32_pk_fp8_bf16 return nearest-even of x / scale (saturating for
 // FP4, -0 kept); with scale = 2^(E-127) that is exactly the MX element
@@ -190,6 +195,99 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restr
     }
     // Ragged end: the row's lane 15 is past the end, store bytes instead.
     if ((lane & 3) == 0 && c < nchunks && c - (lane & 15) + 15 >= nchunks) scales[blk] = (uint8_t)E;
+  }
+}
+
+// ---- MXFP4 with static macro-block scaling ----------------------------------
+
+// DPP row_ror:n (rotate right by n lanes inside a row of 16).
+constexpr int dpp_row_ror(int n) { return 0x120 + n; }
+
+// Macro mantissa m from the macro amax (bf16 magnitude bits a): with S the
+// 8-bit significand of a normalised to [128, 255] and n the smallest integer
+// with amax <= 6 * 2^n, rho = amax / 2^n is S / 32 (S <= 192) or S / 64
+// (S > 192); m is the smallest integer with 3 (1 + m / 256) >= rho, i.e.
+// ceil((256 rho - 768) / 3), and 256 (rho within 2^-8 of 6) becomes 0. Zero
+// and non-finite amax give 0.
+__device__ __forceinline__ uint32_t mbs_mantissa(uint32_t a) {
+  if (a == 0 || a >= 0x7F80u) return 0;
+  const uint32_t S = (a >> 7) ? (0x80u | (a & 0x7Fu)) : (a << (__builtin_clz(a) - 24));
+  const uint32_t num = (S <= 192 ? 8 * S : 4 * S) - 768;
+  const uint32_t m = (num + 2) / 3;
+  return m >= 256 ? 0 : m;
+}
+
+// x / (f 2^(E-127)) for the E2M1 decision: u = x 2^(127-E) is exact (or far
+// below the smallest midpoint), then one Newton step on u * rcp(f). The
+// residual u - q0 f is exact (fma), so q1 is the exact quotient when that is
+// representable -- every tie lands on its midpoint -- and within a few ulps
+// otherwise, while a non-tie quotient differs from every midpoint by more than
+// 2^-13 relative (x has 8 significant bits, midpoint * f at most 12). The sign
+// is copied so that -0 keeps its code.
+__device__ __forceinline__ float mbs_quotient(float x, int sh, float f, float r) {
+  const float u = __builtin_ldexpf(x, sh);
+  const float q0 = u * r;
+  const float e = __builtin_fmaf(-q0, f, u);
+  const float q1 = __builtin_fmaf(e, r, q0);
+  return __builtin_copysignf(q1, u);
+}
+
+// One lane per 16-byte chunk as in quant_mx_kernel; a DPP row of 16 lanes is
+// one macro block. Per 32-block, E is the smallest n with amax <= 6 f 2^n
+// (+127, clamped at 0): the plain MX exponent e0 of amax or e0 - 1, since
+// f is in [1, 2); the comparison with 6 f 2^(e0-128) is exact in fp32.
+__global__ __launch_bounds__(kThreads) void quant_mbs_kernel(const u32x4* __restrict__ x,
+                                                             uint32_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales,
+                                                             uint8_t* __restrict__ macro,
+                                                             int64_t nchunks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+  u32x4 v[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; u++) {
+    const int64_t c = base + u * kThreads;
+    v[u] = (c < nchunks) ? __builtin_nontemporal_load(x + c) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; u++) {
+    const int64_t c = base + u * kThreads;
+    uint32_t mb = chunk_absmax(v[u]);
+    mb = umax(mb, dpp<kDppSwap1>(mb));
+    mb = umax(mb, dpp<kDppSwap2>(mb));
+    uint32_t mm = umax(mb, dpp<dpp_row_ror(4)>(mb));
+    mm = umax(mm, dpp<dpp_row_ror(8)>(mm));
+    const uint32_t mq = mbs_mantissa(mm);
+    const float f = (float)(256u + mq) * 0x1p-8f;
+    const float r = __builtin_amdgcn_rcpf(f);
+    const int ea = (int)(mb >> 7), ma = (int)(mb & 0x7F);
+    int e0 = ea - 2 + (ma > 0x40);
+    e0 = e0 < 0 ? 0 : e0;
+    const float bamax = __builtin_bit_cast(float, mb << 16);
+    const int e = (e0 >= 1 && bamax <= __builtin_ldexpf(6.0f * f, e0 - 128)) ? e0 - 1 : e0;
+    const bool nonfinite = mb >= 0x7F80u;
+    const uint32_t E = nonfinite ? 255u : (uint32_t)e;
+    const int sh = 127 - e;
+    const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    float o[8];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      o[2 * k] = mbs_quotient(__builtin_bit_cast(float, w[k] << 16), sh, f, r);
+      o[2 * k + 1] = mbs_quotient(__builtin_bit_cast(float, w[k] & 0xFFFF0000u), sh, f, r);
+    }
+    uint32_t q = 0;
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, o[0], o[1], 1.0f, 0);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, o[2], o[3], 1.0f, 1);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, o[4], o[5], 1.0f, 2);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, o[6], o[7], 1.0f, 3);
+    if (nonfinite) q = 0;
+    if (c < nchunks) __builtin_nontemporal_store(q, codes + c);
+    const uint32_t s4 = dpp<dpp_row_shr(4)>(E);
+    const uint32_t s8 = dpp<dpp_row_shr(8)>(E);
+    const uint32_t s12 = dpp<dpp_row_shr(12)>(E);
+    if ((lane & 15) == 15 && c < nchunks)
+      *(uint32_t*)(scales + ((c >> 2) - 3)) = s12 | (s8 << 8) | (s4 << 16) | (E << 24);
+    if ((lane & 15) == 0 && c < nchunks) macro[c >> 4] = (uint8_t)mq;
   }
 }
 
@@ -365,6 +463,17 @@ hipError_t quant_mx(int fmt, int64_t rows, int64_t cols, const void* x, void* co
     quant_mxfp6_kernel<<<(unsigned)((nblocks + kThreads - 1) / kThreads), kThreads, 0, s>>>(
         X, (u32x2*)codes, S, nblocks);
   }
+  return hipGetLastError();
+}
+
+// nchunks is a multiple of 16 (cols % 128 = 0), so every DPP row is either
+// wholly inside the tensor or wholly past its end.
+hipError_t quant_mbs(int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
+                     hipStream_t s) {
+  const int64_t nchunks = rows * cols / 8;
+  uint8_t* S = (uint8_t*)scales;
+  quant_mbs_kernel<<<(unsigned)grid_for(nchunks), kThreads, 0, s>>>(
+      (const u32x4*)x, (uint32_t*)codes, S, S + rows * (cols / 32), nchunks);
   return hipGetLastError();
 }
 

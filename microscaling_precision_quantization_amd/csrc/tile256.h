@@ -1,6 +1,7 @@
-// Pieces shared by the 256 x 256-tile GEMM kernels (4 waves of 128 x 128, each
-// 4 x 4 MFMAs of 32 x 32 with operands passed B first): the XCD-aware tile
-// order and the epilogue.
+// Pieces shared by the large-tile GEMM kernels (4 waves of 128 x 32 NT, each
+// 4 x NT MFMAs of 32 x 32 with operands passed B first; NT = 4 for the
+// 256 x 256 tiles, 2 for 256 x 128): the XCD-aware tile order and the
+// epilogue.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -36,24 +37,25 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
 
 // Epilogue. With B passed as the first MFMA operand, accumulator t of tile
 // (i, j) of wave (wm, wn) holds C[row][col] with row = m0 + 128 wm + 32 i + r
-// (r = lane % 32) and col = n0 + 128 wn + 32 j + 8 (t / 4) + 4 g + (t % 4)
+// (r = lane % 32) and col = n0 + 32 NT wn + 32 j + 8 (t / 4) + 4 g + (t % 4)
 // (g = lane / 32): runs of 4 consecutive columns. Each wave stages its
-// 128 x 128 block in LDS (its own region of `smem`, at least 4 x 34,816
-// bytes; fp32 in two halves of 64 rows) and writes it back row-contiguously,
-// 16 bytes per lane, so whole lines reach the L2. Values are multiplied by
-// `scale` (exactly 1 unless a tensor scale applies). The caller has finished
-// every use of `smem` and synchronised the workgroup.
-template <int OUT>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], uint8_t* smem, float scale,
+// 128 x 32 NT block in LDS (its own region of `smem`, at least
+// 4 x 128 x (64 NT + 16) bytes; fp32 in two halves of 64 rows) and writes it
+// back row-contiguously, 16 bytes per lane, so whole lines reach the L2.
+// Values are multiplied by `scale` (exactly 1 unless a tensor scale applies).
+// The caller has finished every use of `smem` and synchronised the workgroup.
+template <int OUT, int NT = 4>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][NT], uint8_t* smem, float scale,
                                            void* __restrict__ C, int64_t ldc, int M, int N,
                                            int m0, int n0, int wave, int lane) {
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, g = lane >> 5;
+  constexpr int kCols = 32 * NT;                      // columns per wave
   constexpr int kEs = (OUT == kOutF32) ? 4 : 2;       // bytes per element
   constexpr int kRows = (OUT == kOutF32) ? 64 : 128;  // rows staged per pass
-  constexpr int kPitch = 128 * kEs + 16;              // padded LDS row
+  constexpr int kPitch = kCols * kEs + 16;            // padded LDS row
   uint8_t* wbuf = smem + wave * (kRows * kPitch);
-  const int wrow0 = m0 + wm * 128, wcol0 = n0 + wn * 128;
+  const int wrow0 = m0 + wm * 128, wcol0 = n0 + wn * kCols;
   const bool vec_ok = (ldc % (16 / kEs)) == 0;
 #pragma unroll
   for (int pass = 0; pass < 128 / kRows; pass++) {
@@ -62,7 +64,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], uint8_t* s
       if ((i * 32) / kRows != pass) continue;
       const int lrow = i * 32 + r - pass * kRows;
 #pragma unroll
-      for (int j = 0; j < 4; j++)
+      for (int j = 0; j < NT; j++)
 #pragma unroll
         for (int q = 0; q < 4; q++) {
           const int lcol = j * 32 + 8 * q + 4 * g;
@@ -75,9 +77,9 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], uint8_t* s
             *(u32x2*)dst = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
         }
     }
-    // Row-contiguous write-back: 128 columns = 16 lanes x 16 bytes (bf16) or
-    // 32 lanes (fp32); the wave covers 64 / (lanes per row) rows per step.
-    constexpr int kLanesPerRow = 128 * kEs / 16;
+    // Row-contiguous write-back: kCols columns, 16 bytes per lane; the wave
+    // covers 64 / (lanes per row) rows per step.
+    constexpr int kLanesPerRow = kCols * kEs / 16;
     constexpr int kRowsPerStep = 64 / kLanesPerRow;
 #pragma unroll 4
     for (int rr = 0; rr < kRows; rr += kRowsPerStep) {

@@ -109,6 +109,10 @@ WORKLOADS = {
         fmt="mxfp4", M=4608, N=3072, K=12288, rotation="wht32",
         a=("laplace_outlier_channels", 401, 403, 0.005, 100.0),
         b=("normal", 0.02, 402)),
+    "mxfp4mbs_dit_mlp_down_4608x12288x3072": dict(
+        fmt="mxfp4_mbs", M=4608, N=3072, K=12288,
+        a=("laplace_outlier_channels", 401, 403, 0.005, 100.0),
+        b=("normal", 0.02, 402)),
 }
 
 # Short names used on the command line and in tests.
@@ -121,6 +125,7 @@ ALIASES = {
     "f1": "mxfp4oas_dit_mlp_down_4608x12288x3072",
     "f2a": "mxfp8e5m2_dit_qkv_4608x3072x9216",
     "f2b": "mxfp6e3m2_dit_qkv_4608x3072x9216",
+    "f3": "mxfp4mbs_dit_mlp_down_4608x12288x3072",
     "f4": "mxfp4wht32_dit_mlp_down_4608x12288x3072",
 }
 

@@ -62,6 +62,9 @@ def q(fmt=mx.MX_FMT_MXFP4, block=32, rnd=0, rows=4, cols=64, x=P, codes=P, scale
     (dict(fmt=mx.MX_FMT_NVFP4, block=16, ts=P), mx.MX_ERR_INVALID_ARG),  # no workspace
     (dict(fmt=mx.MX_FMT_NVFP4, block=16, ts=P, ws=P2, wsb=16), mx.MX_ERR_INVALID_ARG),  # too small
     (dict(fmt=mx.MX_FMT_NVFP4, block=16, cols=40, ts=P, ws=P2, wsb=1 << 20), mx.MX_ERR_INVALID_ARG),
+    (dict(fmt=mx.MX_FMT_MXFP4_MBS, cols=64), mx.MX_ERR_INVALID_ARG),    # macro blocks of 128
+    (dict(fmt=mx.MX_FMT_MXFP4_MBS, cols=128, ts=P), mx.MX_ERR_INVALID_ARG),
+    (dict(fmt=mx.MX_FMT_MXFP4_MBS, cols=128, block=16), mx.MX_ERR_UNSUPPORTED),
 ])
 def test_quantize_rejects(kw, status):
     assert q(**kw) == status
@@ -81,6 +84,7 @@ def qx(fmt=mx.MX_FMT_MXFP4, block=32, rnd=0, rule=0, rot=0, rows=4, cols=64, x=P
     (dict(rule=2), mx.MX_ERR_UNSUPPORTED),
     (dict(rot=2), mx.MX_ERR_UNSUPPORTED),
     (dict(rnd=1), mx.MX_ERR_UNSUPPORTED),
+    (dict(fmt=mx.MX_FMT_MXFP4_MBS, cols=128), mx.MX_ERR_UNSUPPORTED),  # MBS is its own format
 ])
 def test_quantize_ex_rejects(kw, status):
     assert qx(**kw) == status
@@ -94,6 +98,8 @@ def test_dequantize_rejects():
     assert d(2, 32, 0, 4, 64, P, P, P, 0, P2, None) == mx.MX_ERR_INVALID_ARG  # MX takes no ts
     assert d(2, 32, 0, 4, 64, P, MIS, None, 0, P2, None) == mx.MX_ERR_INVALID_ARG
     assert d(2, 16, 0, 4, 64, P, P, None, 0, P2, None) == mx.MX_ERR_UNSUPPORTED
+    assert d(6, 32, 0, 4, 96, P, P, None, 0, P2, None) == mx.MX_ERR_INVALID_ARG  # MBS: cols % 128
+    assert d(6, 32, 0, 4, 128, P, P, P, 0, P2, None) == mx.MX_ERR_INVALID_ARG  # MBS takes no ts
 
 
 def g(fa=1, fb=1, block=32, rnd=0, M=64, N=64, K=128, a=P, sa=P, ta=None, b=P, sb=P, tb=None,
@@ -120,6 +126,10 @@ def g(fa=1, fb=1, block=32, rnd=0, M=64, N=64, K=128, a=P, sa=P, ta=None, b=P, s
     (dict(fa=0, fb=1, sa=P), mx.MX_ERR_INVALID_ARG),            # bf16 A has no scales
     (dict(fa=0, fb=1, sa=None, M=16, N=28672, K=8192), mx.MX_ERR_INVALID_ARG),  # no workspace
     (dict(fa=0, fb=1, sa=None, M=16, N=64, K=1 << 24, ws=P2, wsb=1 << 40), mx.MX_ERR_INVALID_ARG),  # W4A16 K limit
+    (dict(fa=6, fb=6, K=160), mx.MX_ERR_INVALID_ARG),           # MBS: K % 128
+    (dict(fa=6, fb=1), mx.MX_ERR_UNSUPPORTED),                  # MBS pairs with MBS only
+    (dict(fa=6, fb=6, block=16), mx.MX_ERR_UNSUPPORTED),
+    (dict(fa=6, fb=6, ta=P), mx.MX_ERR_INVALID_ARG),
 ])
 def test_gemm_rejects(kw, status):
     assert g(**kw) == status
