@@ -7,21 +7,25 @@
 //   C[i][j] = sum over macro blocks q of f_A[i][q] f_B[j][q] P_q[i][j],
 // P_q the block-scaled MXFP4 dot product over the 128 K of macro block q. The
 // matrix core computes P_q (v_mfma_scale_f32_32x32x64_f8f6f4, two per macro
-// block, the first from zero) and the vector ALU adds P_q * (f_A f_B) to the
-// accumulator (f_A f_B has 18 significant bits: exact in fp32) -- the factor
-// applied on the vector units alongside the matrix core, as the summary
-// describes for its kernel.
+// block, the first from zero) and the tile of factor products f_A f_B (an
+// fp16 MFMA of one nonzero K slot; f_A f_B has 18 significant bits, so it is
+// exact), and the vector ALU adds P_q * (f_A f_B) to the accumulator with one
+// fma per element -- the factor applied on the vector units alongside the
+// matrix core, as the summary describes for its kernel.
 //
 // Design for CDNA4:
 //  * The accumulators must sit in VGPRs next to the partial sums, so a wave
 //    owns 128 x 64 outputs (4 x 2 MFMA tiles of 32 x 32, 128 accumulators per
-//    lane) and a workgroup of 4 waves (one per SIMD) a 256 x 128 tile.
+//    lane). A workgroup of 8 waves (two per SIMD, each within 256 registers)
+//    covers a 256 x 256 tile, which keeps the operand traffic through L2 at
+//    that of the plain MXFP4 kernel; the SIMD's second wave hides each
+//    wave's wait between its MFMAs and the vector ALU work that reads them.
 //  * K advances in super-steps of 256 (two macro blocks, 128 code bytes per
 //    row). Codes and E8M0 scales go HBM -> LDS with buffer_load ... lds into a
-//    2 x 54 KB double buffer; the next super-step's loads are issued between
+//    2 x 72 KB double buffer; the next super-step's loads are issued between
 //    the current one's MFMAs. The two macro-mantissa bytes per row come
-//    through VGPRs and are stored in LDS as fp32 factors at the top of the
-//    super-step they belong to.
+//    through VGPRs and are stored in LDS as fp16 factor operands at the top
+//    of the super-step they belong to.
 //  * LDS rows are 128 bytes with the chunk swizzle c ^ ((r / 2) mod 8).
 //  * K order inside a super-step, identical for A and B: sub-step J (0..3)
 //    gives lane group g (lanes 32g .. 32g+31) code block 2J + g, so sub-steps
@@ -45,22 +49,24 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kThreads = 256;
-constexpr int BM = 256, BN = 128;
+constexpr int kThreads = 512;
+constexpr int kWavesN = 4;                          // waves along N (2 along M)
+constexpr int BM = 256, BN = 256;
 constexpr int kSuperK = 256;                        // elements per super-step
 constexpr int kRowBytes = kSuperK / 2;              // 128 code bytes per row
 constexpr int kOffB = BM * kRowBytes;               // 32 KB of A codes
 constexpr int kOffSA = kOffB + BN * kRowBytes;      // + 16 KB of B codes
 constexpr int kOffSB = kOffSA + BM * 8;             // + 2 KB of A scales (8 per row)
 constexpr int kOffFA = kOffSB + BN * 8;             // + 1 KB of B scales
-constexpr int kOffFB = kOffFA + 2 * BM * 4;         // + A factors [2][BM] fp32
-constexpr int kStage = kOffFB + 2 * BN * 4;         // + B factors [2][BN] fp32
+constexpr int kOffFB = kOffFA + 2 * BM * 4;         // + A factors / 2 [2][BM] (fp16 in a dword)
+constexpr int kStage = kOffFB + 2 * BN * 4;         // + B factors [2][BN] (fp16 in a dword)
 constexpr int kSmem = 2 * kStage;
 constexpr uint32_t kRsrcFlags = 0x00020000u;        // raw buffer, gfx9 data format
 
-static_assert(kSmem >= 4 * 128 * (64 * 2 + 16), "epilogue staging must fit");
+static_assert(kSmem >= 8 * 128 * (64 * 2 + 16), "epilogue staging must fit");
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
@@ -68,57 +74,66 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// Part P (0..3) of the direct-to-LDS loads of super-step s: A code blocks 2P,
-// 2P+1 and B code block P of this wave (1 KB = 8 rows each, lane l filling
-// bytes 16l .. 16l+15 of the block), plus one 256-byte scale block (4 bytes per
-// lane): A scales for P = 0, 1, B scales for P = 2.
+// Per-lane parts of the direct-to-LDS load addresses, the same for every
+// super-step. The K offset of the super-step goes in the scalar offset; the
+// row offsets stay in the lane offset, which the buffer range check sees, so
+// rows past M or N still read as zeros.
+// Code blocks are 8 rows of 128 bytes: lane l fills bytes 16 l .. 16 l + 15 of
+// the LDS block, i.e. row l / 8, slot l % 8, which holds chunk
+// slot ^ swz(row); for a block starting at row 8 b, swz(row) =
+// (l / 16 + 4 (b % 2)) % 8, so two lane offsets (even / odd b) serve every
+// code block of A and B. Scale blocks are 32 rows of 8 bytes, 4 per lane.
+struct LaneOffsets {
+  uint32_t code[2], scale;
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane, uint32_t rowbytes, uint32_t scalebytes) {
+  LaneOffsets o;
+#pragma unroll
+  for (int par = 0; par < 2; par++)
+    o.code[par] = (uint32_t)(lane >> 3) * rowbytes +
+                  (uint32_t)(((lane & 7) ^ (((lane >> 4) + 4 * par) & 7)) * 16);
+  o.scale = (uint32_t)(lane >> 1) * scalebytes + (uint32_t)(lane & 1) * 4u;
+  return o;
+}
+
+// Part P (0..3) of the direct-to-LDS loads of super-step s: code block
+// 4 wave + P of A and of B (1 KB = 8 rows each), plus one 256-byte scale block
+// (32 rows x 8 bytes): A's for P = 0, B's for P = 1. `wave` is wave-uniform.
 template <int P>
 __device__ __forceinline__ void issue_part(uint8_t* stage, __amdgpu_buffer_rsrc_t rA,
                                            __amdgpu_buffer_rsrc_t rB, __amdgpu_buffer_rsrc_t rSA,
-                                           __amdgpu_buffer_rsrc_t rSB, uint32_t rowbytes,
-                                           uint32_t scalebytes, int s, int wave, int lane) {
+                                           __amdgpu_buffer_rsrc_t rSB, const LaneOffsets& lo,
+                                           uint32_t rowbytes, uint32_t scalebytes, int s, int wave) {
   const uint32_t kb = (uint32_t)s * kRowBytes;
-#pragma unroll
-  for (int i = 2 * P; i < 2 * P + 2; i++) {
-    const int b = wave * 8 + i;
-    const int row = b * 8 + (lane >> 3);
-    const uint32_t off = kb + (uint32_t)(((lane & 7) ^ swz(row)) * 16);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(stage + b * 1024), 16,
-                                             (uint32_t)row * rowbytes + off, 0, 0, 0);
-  }
-  {
-    const int b = wave * 4 + P;
-    const int row = b * 8 + (lane >> 3);
-    const uint32_t off = kb + (uint32_t)(((lane & 7) ^ swz(row)) * 16);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(stage + kOffB + b * 1024), 16,
-                                             (uint32_t)row * rowbytes + off, 0, 0, 0);
-  }
-  const uint32_t soff = (uint32_t)s * (kSuperK / 32) + (uint32_t)(lane & 1) * 4u;
-  if (P < 2) {
-    const int b = wave * 2 + P;  // 8 blocks of 32 rows x 8 bytes
-    const int row = b * 32 + (lane >> 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_ptr_t)(stage + kOffSA + b * 256), 4,
-                                             (uint32_t)row * scalebytes + soff, 0, 0, 0);
-  } else if (P == 2) {
-    const int b = wave;  // 4 blocks
-    const int row = b * 32 + (lane >> 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (lds_ptr_t)(stage + kOffSB + b * 256), 4,
-                                             (uint32_t)row * scalebytes + soff, 0, 0, 0);
-  }
+  const int b = wave * 4 + P;
+  const uint32_t voff = lo.code[P & 1] + (uint32_t)(8 * b) * rowbytes;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(stage + b * 1024), 16, voff, (int)kb, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(stage + kOffB + b * 1024), 16, voff,
+                                           (int)kb, 0, 0);
+  const uint32_t ks = (uint32_t)s * (kSuperK / 32);
+  const uint32_t soff = lo.scale + (uint32_t)(32 * wave) * scalebytes;
+  if (P == 0)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_ptr_t)(stage + kOffSA + wave * 256), 4, soff,
+                                             (int)ks, 0, 0);
+  if (P == 1)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (lds_ptr_t)(stage + kOffSB + wave * 256), 4, soff,
+                                             (int)ks, 0, 0);
 }
 
-// Macro mantissas of super-step s (two bytes per row) for A row `tid` and B
-// row `tid` (tid < BN); rows past M or N read as 0 (factor 1).
-__device__ __forceinline__ void load_macro(uint32_t& ma, uint32_t& mb, __amdgpu_buffer_rsrc_t rMA,
-                                           __amdgpu_buffer_rsrc_t rMB, uint32_t macrobytes, int s,
-                                           int tid) {
-  ma = __builtin_amdgcn_raw_buffer_load_b16(rMA, (uint32_t)tid * macrobytes + 2u * s, 0, 0);
-  mb = __builtin_amdgcn_raw_buffer_load_b16(rMB, (uint32_t)(tid & (BN - 1)) * macrobytes + 2u * s,
-                                            0, 0);
+// Macro mantissas of super-step s (two bytes per row): waves 0..3 load A row
+// `tid`, waves 4..7 B row tid - 256; rows past M or N read as 0 (factor 1).
+__device__ __forceinline__ uint32_t load_macro(__amdgpu_buffer_rsrc_t rM, uint32_t macrobytes, int s,
+                                               int row) {
+  return __builtin_amdgcn_raw_buffer_load_b16(rM, (uint32_t)row * macrobytes, 2 * s, 0);
 }
 
-__device__ __forceinline__ float macro_factor(uint32_t m) {
-  return (float)(256u + m) * 0x1p-8f;
+// The macro factor times `w` (1 or 1/2), (1 + m/256) w, as fp16 bits in the
+// low half of a dword (exact: 9 significant bits): one K slot of the factor
+// MFMA's operand.
+__device__ __forceinline__ uint32_t factor_bits(uint32_t m, float w) {
+  const _Float16 h = (_Float16)((float)(256u + m) * 0x1p-8f * w);
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 
 // Fragments of macro block q: A tiles i (rows wm*128 + 32 i + r) and B tiles j
@@ -147,39 +162,51 @@ __device__ __forceinline__ void load_frags(const uint8_t* cur, int q, int wm, in
 
 __device__ __forceinline__ i32x8 widen(i32x4 v) { return i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0}; }
 
-// Macro block q of the current super-step: for each of the wave's 8 tiles,
-// P = the two MFMAs of the block (the first from zero), then
-// acc += P * (f_A f_B).
+// The two MFMAs of tile (i, j) in macro block Q: the block-scaled partial sum
+// over its 128 K, the first from zero.
+template <int Q>
+__device__ __forceinline__ f32x16 partial(const Frags& f, const int (&sa)[4], const int (&sb)[2],
+                                          int i, int j) {
+  f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+      widen(f.b[j][0]), widen(f.a[i][0]), f32x16{}, 4, 4, 2 * Q, sb[j], 2 * Q, sa[i]);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+      widen(f.b[j][1]), widen(f.a[i][1]), p, 4, 4, 2 * Q + 1, sb[j], 2 * Q + 1, sa[i]);
+}
+
+// Macro block Q of the current super-step, tile by tile over the wave's 8
+// tiles k = (i = k % 4, j = k / 4): the matrix core computes the partial sum
+// P_k (two FP4 MFMAs) and the factor tile G_k = f_B (x) f_A (one fp16 MFMA:
+// each lane supplies its row's f_B, or f_A / 2, in the first K slot of its
+// half of K and zeros elsewhere, so G_k = 2 f_B (f_A / 2) = f_A f_B exactly,
+// laid out like P_k); the vector ALU then does acc += P_k * G_k. One tile is
+// in flight per wave (fences keep the compiler from hoisting the next tile's
+// MFMAs, which would not fit in 256 registers); the SIMD's other wave fills
+// the wait between a tile's MFMAs and its ALU work.
 template <int Q>
 __device__ __forceinline__ void macro_step(const uint8_t* cur, const Frags& f, const int (&sa)[4],
-                                           const int (&sb)[2], int wm, int wn, int r, int g,
+                                           const int (&sb)[2], int wm, int wn, int r,
                                            f32x16 (&acc)[4][2]) {
-  const float* FA = (const float*)(cur + kOffFA) + Q * BM;
-  const float* FB = (const float*)(cur + kOffFB) + Q * BN;
-  float fa[4];
+  const uint32_t* FA = (const uint32_t*)(cur + kOffFA) + Q * BM;
+  const uint32_t* FB = (const uint32_t*)(cur + kOffFB) + Q * BN;
+  // The block's factor operands, read once (one dword per tile row).
+  uint32_t fa[4], fb[2];
 #pragma unroll
   for (int i = 0; i < 4; i++) fa[i] = FA[wm * 128 + i * 32 + r];
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
-    float fb[16];
+  for (int j = 0; j < 2; j++) fb[j] = FB[wn * 64 + j * 32 + r];
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const f32x4 v = *(const f32x4*)(FB + wn * 64 + j * 32 + 8 * u + 4 * g);
-      fb[4 * u] = v.x;
-      fb[4 * u + 1] = v.y;
-      fb[4 * u + 2] = v.z;
-      fb[4 * u + 3] = v.w;
-    }
+  for (int k = 0; k < 8; k++) {
+    const int i = k & 3, j = k >> 2;
+    sched_fence();
+    // The factor MFMA first: it runs while the dependent pair of P waits.
+    const f32x16 gk = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(f16x4, u32x2{fb[j], 0u}),
+                                                            __builtin_bit_cast(f16x4, u32x2{fa[i], 0u}),
+                                                            f32x16{}, 0, 0, 0);
+    const f32x16 p = partial<Q>(f, sa, sb, i, j);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          widen(f.b[j][0]), widen(f.a[i][0]), f32x16{}, 4, 4, 2 * Q, sb[j], 2 * Q, sa[i]);
-      p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          widen(f.b[j][1]), widen(f.a[i][1]), p, 4, 4, 2 * Q + 1, sb[j], 2 * Q + 1, sa[i]);
-#pragma unroll
-      for (int t = 0; t < 16; t++) acc[i][j][t] = __builtin_fmaf(p[t], fa[i] * fb[t], acc[i][j][t]);
-    }
+    for (int t = 0; t < 16; t++) acc[i][j][t] = __builtin_fmaf(p[t], gk[t], acc[i][j][t]);
   }
+  sched_fence();
 }
 
 // The lane's four scale bytes of a row (blocks g, g+2, g+4, g+6 of the
@@ -195,9 +222,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mbs_kernel(
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB, const uint8_t* __restrict__ MB,
     void* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int r = lane & 31, g = lane >> 5;
+  const bool a_side = wave < 4;               // which operand's macro row this thread loads
+  const int mrow = a_side ? tid : tid - BM;
   int tm, tn;
   tile256::tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
@@ -205,6 +235,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mbs_kernel(
   // Buffer views based at the tile's first rows: rows past M or N read as 0.
   const uint32_t rowbytes = (uint32_t)(K / 2), scalebytes = (uint32_t)(K / 32);
   const uint32_t macrobytes = (uint32_t)(K / 128);
+  const LaneOffsets lo = lane_offsets(lane, rowbytes, scalebytes);
   const int mrows = min(BM, M - m0), nrows = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * rowbytes), 0, (int)(mrows * rowbytes), kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)(B + (int64_t)n0 * rowbytes), 0, (int)(nrows * rowbytes), kRsrcFlags);
@@ -222,12 +253,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mbs_kernel(
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
   const int nsteps = K / kSuperK;
-  uint32_t ma, mb;
-  load_macro(ma, mb, rMA, rMB, macrobytes, 0, tid);
-  issue_part<0>(smem, rA, rB, rSA, rSB, rowbytes, scalebytes, 0, wave, lane);
-  issue_part<1>(smem, rA, rB, rSA, rSB, rowbytes, scalebytes, 0, wave, lane);
-  issue_part<2>(smem, rA, rB, rSA, rSB, rowbytes, scalebytes, 0, wave, lane);
-  issue_part<3>(smem, rA, rB, rSA, rSB, rowbytes, scalebytes, 0, wave, lane);
+  const __amdgpu_buffer_rsrc_t rM = a_side ? rMA : rMB;
+  uint32_t mv = load_macro(rM, macrobytes, 0, mrow);
+  issue_part<0>(smem, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, 0, wave);
+  issue_part<1>(smem, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, 0, wave);
+  issue_part<2>(smem, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, 0, wave);
+  issue_part<3>(smem, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, 0, wave);
   for (int s = 0; s < nsteps; s++) {
     uint8_t* cur = smem + (s & 1) * kStage;
     uint8_t* nxt = smem + ((s + 1) & 1) * kStage;
@@ -236,20 +267,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mbs_kernel(
     // done with super-step s - 1, whose buffer receives s + 1 below.
     wait_vmem();
     {
-      float* FA = (float*)(cur + kOffFA);
-      float* FB = (float*)(cur + kOffFB);
-      FA[tid] = macro_factor(ma & 0xFFu);
-      FA[BM + tid] = macro_factor(ma >> 8);
-      if (tid < BN) {
-        FB[tid] = macro_factor(mb & 0xFFu);
-        FB[BN + tid] = macro_factor(mb >> 8);
-      }
+      // A factors are stored halved: the factor MFMA sums two K slots.
+      uint32_t* F = (uint32_t*)(cur + (a_side ? kOffFA : kOffFB));
+      const float w = a_side ? 0.5f : 1.0f;
+      F[mrow] = factor_bits(mv & 0xFFu, w);
+      F[BM + mrow] = factor_bits(mv >> 8, w);
     }
     __syncthreads();
     // Branch-free body: the last iteration re-fetches its own super-step into
     // the idle buffer, which nobody reads; the wait after the loop drains it.
     const int snext = min(s + 1, nsteps - 1);
-    load_macro(ma, mb, rMA, rMB, macrobytes, snext, tid);
+    mv = load_macro(rM, macrobytes, snext, mrow);
     int sa[4], sb[2];
 #pragma unroll
     for (int i = 0; i < 4; i++) sa[i] = gather_scales(cur + kOffSA + (wm * 128 + i * 32 + r) * 8, g);
@@ -257,20 +285,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mbs_kernel(
     for (int j = 0; j < 2; j++) sb[j] = gather_scales(cur + kOffSB + (wn * 64 + j * 32 + r) * 8, g);
     Frags f;
     load_frags(cur, 0, wm, wn, r, g, f);
-    issue_part<0>(nxt, rA, rB, rSA, rSB, rowbytes, scalebytes, snext, wave, lane);
-    issue_part<1>(nxt, rA, rB, rSA, rSB, rowbytes, scalebytes, snext, wave, lane);
-    macro_step<0>(cur, f, sa, sb, wm, wn, r, g, acc);
+    issue_part<0>(nxt, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, snext, wave);
+    issue_part<1>(nxt, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, snext, wave);
+    macro_step<0>(cur, f, sa, sb, wm, wn, r, acc);
     load_frags(cur, 1, wm, wn, r, g, f);
-    issue_part<2>(nxt, rA, rB, rSA, rSB, rowbytes, scalebytes, snext, wave, lane);
-    issue_part<3>(nxt, rA, rB, rSA, rSB, rowbytes, scalebytes, snext, wave, lane);
-    macro_step<1>(cur, f, sa, sb, wm, wn, r, g, acc);
+    issue_part<2>(nxt, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, snext, wave);
+    issue_part<3>(nxt, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, snext, wave);
+    macro_step<1>(cur, f, sa, sb, wm, wn, r, acc);
   }
   wait_vmem();
 
   // Epilogue: every load has drained; the stage buffers are free once every
   // wave is past its loop.
   __syncthreads();
-  tile256::store_tile<OUT, 2>(acc, smem, 1.0f, C, ldc, M, N, m0, n0, wave, lane);
+  tile256::store_tile<OUT, 2, kWavesN>(acc, smem, 1.0f, C, ldc, M, N, m0, n0, wave, lane);
 }
 
 }  // namespace

@@ -1,7 +1,7 @@
-// Pieces shared by the large-tile GEMM kernels (4 waves of 128 x 32 NT, each
-// 4 x NT MFMAs of 32 x 32 with operands passed B first; NT = 4 for the
-// 256 x 256 tiles, 2 for 256 x 128): the XCD-aware tile order and the
-// epilogue.
+// Pieces shared by the large-tile GEMM kernels (2 x WNW waves of 128 x 32 NT,
+// each 4 x NT MFMAs of 32 x 32 with operands passed B first: 4 waves of
+// 128 x 128, or 8 waves of 128 x 64, for the 256 x 256 tiles): the XCD-aware
+// tile order and the epilogue.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -35,20 +35,21 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tn = (t % (GM * tiles_n)) / gsize;
 }
 
-// Epilogue. With B passed as the first MFMA operand, accumulator t of tile
-// (i, j) of wave (wm, wn) holds C[row][col] with row = m0 + 128 wm + 32 i + r
-// (r = lane % 32) and col = n0 + 32 NT wn + 32 j + 8 (t / 4) + 4 g + (t % 4)
-// (g = lane / 32): runs of 4 consecutive columns. Each wave stages its
-// 128 x 32 NT block in LDS (its own region of `smem`, at least
-// 4 x 128 x (64 NT + 16) bytes; fp32 in two halves of 64 rows) and writes it
-// back row-contiguously, 16 bytes per lane, so whole lines reach the L2.
-// Values are multiplied by `scale` (exactly 1 unless a tensor scale applies).
-// The caller has finished every use of `smem` and synchronised the workgroup.
-template <int OUT, int NT = 4>
+// Epilogue. Wave w is (wm, wn) = (w / WNW, w % WNW). With B passed as the
+// first MFMA operand, accumulator t of tile (i, j) of the wave holds
+// C[row][col] with row = m0 + 128 wm + 32 i + r (r = lane % 32) and
+// col = n0 + 32 NT wn + 32 j + 8 (t / 4) + 4 g + (t % 4) (g = lane / 32): runs
+// of 4 consecutive columns. Each wave stages its 128 x 32 NT block in LDS (its
+// own region of `smem`, at least 2 WNW x 128 x (64 NT + 16) bytes; fp32 in
+// two halves of 64 rows) and writes it back row-contiguously, 16 bytes per
+// lane, so whole lines reach the L2. Values are multiplied by `scale`
+// (exactly 1 unless a tensor scale applies). The caller has finished every use
+// of `smem` and synchronised the workgroup.
+template <int OUT, int NT = 4, int WNW = 2>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][NT], uint8_t* smem, float scale,
                                            void* __restrict__ C, int64_t ldc, int M, int N,
                                            int m0, int n0, int wave, int lane) {
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNW, wn = wave % WNW;
   const int r = lane & 31, g = lane >> 5;
   constexpr int kCols = 32 * NT;                      // columns per wave
   constexpr int kEs = (OUT == kOutF32) ? 4 : 2;       // bytes per element
