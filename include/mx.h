@@ -192,8 +192,8 @@ mx_status mx_dequantize(mx_format fmt, int block, mx_round rnd, int64_t rows, in
  * c: [M][ldc] fp32 or bf16 (rnd rounds the bf16 epilogue).
  * workspace: device scratch of at least mx_gemm_workspace_bytes(...) bytes
  * (may be NULL when that is 0).
- * K must be a multiple of 32 for every pair, and below 2^24 for W4A16 (its
- * kernel addresses a 256-row slab of weights with 32-bit offsets); larger
+ * K must be a multiple of 32 for every pair, and below 2^23 for W4A16 (its
+ * kernel addresses a 448-row slab of weights with 32-bit offsets); larger
  * shapes return MX_ERR_INVALID_ARG. Accuracy: each fp32 output is
  * within 2^-18 * sum_k |a_ik b_jk| of the exact sum over the dequantized
  * operands (a bf16 output adds its own rounding), provided no product or

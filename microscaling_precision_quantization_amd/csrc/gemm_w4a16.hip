@@ -3,16 +3,19 @@
 // memory traffic rather than compute (noticiai.com.br page on Nunchaku W4A4:
 // dequantizing weights at compute time mainly saves memory), so this kernel is
 // built to stream the weight codes once from HBM at full bandwidth:
-//  * a workgroup covers TN = 256 weight rows x 16 activation rows x KP = 2048
-//    K (16 steps of 128). Wave w owns rows 64 w .. 64 w + 63 as 4 groups of
-//    16; lane l takes row l % 16 of a group, and at step s lane group
+//  * a workgroup covers TN = 448 weight rows x 16 activation rows x KP = 2048
+//    K (16 steps of 128). Wave w owns rows 112 w .. 112 w + 111 as 7 groups
+//    of 16; lane l takes row l % 16 of a group, and at step s lane group
 //    g = l / 16 takes E8M0 block 4 s + g, so one 16-byte load instruction
-//    covers 16 rows x 64 contiguous bytes;
+//    covers 16 rows x 64 contiguous bytes. With 448 rows, the 28672-row decode
+//    weight splits into 64 x 4 K-splits = 256 workgroups: one per CU, every
+//    CU with the same work;
 //  * a wave loads half a row group at a time, 8 steps back to back (16 rows x
-//    512 contiguous bytes, so DRAM pages are read in bursts), double-buffered
-//    in VGPRs: the next half is in flight while this one is used. (Steps
-//    spread over the whole kernel re-open every page many times and cap the
-//    stream at about half of the HBM rate.) Each block (32 codes) is
+//    512 contiguous bytes, so DRAM pages are read in bursts), through a ring
+//    of kRing half buffers in VGPRs: kRing - 1 halves are in flight while one
+//    is used (8 KB each, enough to cover the HBM latency at one wave per
+//    SIMD). (Steps spread over the whole kernel re-open every page many times
+//    and cap the stream at about half of the HBM rate.) Each block (32 codes) is
 //    expanded to bf16 with v_cvt_scalef32_pk_bf16_fp4, which multiplies by
 //    the power-of-two scale exactly, and feeds four v_mfma_f32_16x16x32_bf16:
 //    MFMA j takes elements 8 j .. 8 j + 7 of the block from every lane group.
@@ -39,7 +42,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
-constexpr int TN = 256;                 // weight rows per workgroup (64 per wave)
+constexpr int kGroups = 7;              // row groups of 16 per wave
+constexpr int kRing = 3;                // half buffers in the load ring (kRing - 1 in flight)
+constexpr int TN = 4 * 16 * kGroups;    // weight rows per workgroup (112 per wave)
 constexpr int TM = 16;                  // activation rows per workgroup
 constexpr int KP = 2048;                // K elements per split
 constexpr int kSteps = KP / 128;        // 16 steps: 4 blocks (one per lane group) each
@@ -114,14 +119,14 @@ __device__ __forceinline__ void compute_half(const u32x4 (&q)[kHalf], const u32x
       acc[j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w, acc[j & 1], 0, 0, 0);
     }
     // One step per scheduling window: hoisting later steps' LDS reads and
-    // expansions would need more registers than two waves per SIMD allow.
+    // expansions would need more registers than the load ring leaves.
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // grid: x = N tiles, y = M tiles, z = K splits of KP elements.
 template <bool DIRECT, int OUT>
-__global__ __launch_bounds__(kThreads, 2) void gemm_w4a16_kernel(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(kThreads, 1) void gemm_w4a16_kernel(const uint16_t* __restrict__ A,
                                                               const uint8_t* __restrict__ B,
                                                               const uint8_t* __restrict__ SB,
                                                               void* __restrict__ out, int64_t ldc,
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4a16_kernel(const uint16_t*
       (void*)(SB + (int64_t)n0 * kblocks), 0, nrows * kblocks, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(A + (int64_t)m0 * K), 0, mrows * K * 2, kRsrcFlags);
-  const int lr0 = wave * 64 + r;  // row within the tile, row group 0
+  const int lr0 = wave * (16 * kGroups) + r;  // row within the tile, row group 0
   const uint32_t wstride = (uint32_t)16 * (uint32_t)(K / 2), sstride = (uint32_t)16 * (uint32_t)kblocks;
   const uint32_t wrow0 = (uint32_t)lr0 * (uint32_t)(K / 2), srow0 = (uint32_t)lr0 * (uint32_t)kblocks;
 
@@ -159,9 +164,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4a16_kernel(const uint16_t*
     const uint32_t off = k < kend ? ((uint32_t)row * (uint32_t)K + (uint32_t)k) * 2u : kOOB;
     av[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
   }
-  // 2. The first half row group's codes and scales.
-  u32x4 q0[kHalf], q1[kHalf], s0[kHalf / 4], s1[kHalf / 4];
-  load_half(q0, s0, rB, rS, wrow0, srow0, bbase, g, kblocks, 0, true);
+  // 2. The first kRing - 1 halves' codes and scales (half i = 2 grp + u).
+  u32x4 qb[kRing][kHalf], sb[kRing][kHalf / 4];
+#pragma unroll
+  for (int i = 0; i < kRing - 1; i++)
+    load_half(qb[i], sb[i], rB, rS, wrow0 + (uint32_t)(i / 2) * wstride,
+              srow0 + (uint32_t)(i / 2) * sstride, bbase, g, kblocks, i % 2, true);
   // 3. Activations to LDS (waits only for the activation loads, which were
   //    issued first): 16-byte chunk c of row m at slot c ^ (m mod 16).
 #pragma unroll
@@ -172,32 +180,36 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_w4a16_kernel(const uint16_t*
   }
   __syncthreads();
 
-  // 4. Row groups one after another; loads run one half ahead of the MFMAs
-  //    (branch-free: the load past the last group is all out of range).
+  // 4. Halves i = 2 grp + u of the row groups one after another; the loads
+  //    run kRing - 1 halves ahead of the MFMAs through the ring of buffers.
   const uint8_t* arow = lA + r * kARow;
-#pragma unroll 1
-  for (int h = 0; h < 4; h++) {
-    const uint32_t wrow = wrow0 + (uint32_t)h * wstride, srow = srow0 + (uint32_t)h * sstride;
-    f32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-    load_half(q1, s1, rB, rS, wrow, srow, bbase, g, kblocks, 1, true);
-    compute_half(q0, s0, arow, r, g, 0, acc);
-    load_half(q0, s0, rB, rS, wrow + wstride, srow + sstride, bbase, g, kblocks, 0, h + 1 < 4);
-    compute_half(q1, s1, arow, r, g, 1, acc);
-    // Lane l holds column n of activation rows 4 g + t.
-    const int n = n0 + lr0 + 16 * h;
-    const f32x4 sum = acc[0] + acc[1];
-    if (n < N) {
+  f32x4 acc[2];
 #pragma unroll
-      for (int t = 0; t < 4; t++) {
-        const int m = m0 + 4 * g + t;
-        if (m >= M) continue;
-        if (DIRECT) {
-          if (OUT == kOutF32)
-            ((float*)out)[(int64_t)m * ldc + n] = sum[t];
-          else
-            ((uint16_t*)out)[(int64_t)m * ldc + n] = bf16_bits(sum[t]);
-        } else {
-          ((float*)out)[((int64_t)blockIdx.z * M + m) * N + n] = sum[t];
+  for (int i = 0; i < 2 * kGroups; i++) {
+    const int grp = i / 2, u = i % 2;
+    const int il = i + kRing - 1;  // the half loaded now
+    if (il < 2 * kGroups)
+      load_half(qb[il % kRing], sb[il % kRing], rB, rS, wrow0 + (uint32_t)(il / 2) * wstride,
+                srow0 + (uint32_t)(il / 2) * sstride, bbase, g, kblocks, il % 2, true);
+    if (u == 0) acc[0] = acc[1] = f32x4{0, 0, 0, 0};
+    compute_half(qb[i % kRing], sb[i % kRing], arow, r, g, u, acc);
+    if (u == 1) {
+      // Lane l holds column n of activation rows 4 g + t.
+      const int n = n0 + lr0 + 16 * grp;
+      const f32x4 sum = acc[0] + acc[1];
+      if (n < N) {
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          const int m = m0 + 4 * g + t;
+          if (m >= M) continue;
+          if (DIRECT) {
+            if (OUT == kOutF32)
+              ((float*)out)[(int64_t)m * ldc + n] = sum[t];
+            else
+              ((uint16_t*)out)[(int64_t)m * ldc + n] = bf16_bits(sum[t]);
+          } else {
+            ((float*)out)[((int64_t)blockIdx.z * M + m) * N + n] = sum[t];
+          }
         }
       }
     }

@@ -135,9 +135,9 @@ mx_status mx_gemm(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int
   // Row tiles run along gridDim.y (at most 65535): 128 rows per tile for the
   // W4A4/W8A8 kernels, 16 for W4A16.
   if (M > (w4a16 ? 16 : 128) * (int64_t)65535) return MX_ERR_INVALID_ARG;
-  // The W4A16 kernel addresses a 256-row slab of weights (K / 2 bytes per row)
+  // The W4A16 kernel addresses a 448-row slab of weights (K / 2 bytes per row)
   // with 32-bit buffer offsets.
-  if (w4a16 && K >= ((int64_t)1 << 24)) return MX_ERR_INVALID_ARG;
+  if (w4a16 && K >= ((int64_t)1 << 23)) return MX_ERR_INVALID_ARG;
   if (!a || !b || !b_scales || !c) return MX_ERR_INVALID_ARG;
   if (!aligned16(a) || !aligned16(b) || !aligned16(b_scales) || !aligned16(c))
     return MX_ERR_INVALID_ARG;

@@ -125,7 +125,7 @@ def g(fa=1, fb=1, block=32, rnd=0, M=64, N=64, K=128, a=P, sa=P, ta=None, b=P, s
     (dict(fa=3, fb=3, block=16), mx.MX_ERR_INVALID_ARG),        # NVFP4 needs tensor scales
     (dict(fa=0, fb=1, sa=P), mx.MX_ERR_INVALID_ARG),            # bf16 A has no scales
     (dict(fa=0, fb=1, sa=None, M=16, N=28672, K=8192), mx.MX_ERR_INVALID_ARG),  # no workspace
-    (dict(fa=0, fb=1, sa=None, M=16, N=64, K=1 << 24, ws=P2, wsb=1 << 40), mx.MX_ERR_INVALID_ARG),  # W4A16 K limit
+    (dict(fa=0, fb=1, sa=None, M=16, N=64, K=1 << 23, ws=P2, wsb=1 << 40), mx.MX_ERR_INVALID_ARG),  # W4A16 K limit
     (dict(fa=6, fb=6, K=160), mx.MX_ERR_INVALID_ARG),           # MBS: K % 128
     (dict(fa=6, fb=1), mx.MX_ERR_UNSUPPORTED),                  # MBS pairs with MBS only
     (dict(fa=6, fb=6, block=16), mx.MX_ERR_UNSUPPORTED),

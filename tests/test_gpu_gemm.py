@@ -61,7 +61,8 @@ def test_mxfp4_roundtrip_workload_full(out):
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8", "nvfp4", "w4a16"])
 @pytest.mark.parametrize("shape", [(200, 72, 416), (1, 1, 32), (129, 257, 96), (16, 130, 8192 + 96),
-                                   (300, 520, 768), (257, 255, 512), (513, 40, 2560)])
+                                   (300, 520, 768), (257, 255, 512), (513, 40, 2560),
+                                   (33, 1000, 4128)])
 def test_ragged_shapes(fmt, shape):
     M, N, K = shape
     A = synth.normal_outliers((M, K), 1.0, 11 + M, 0.01, 50.0)
