@@ -43,7 +43,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
 constexpr int kGroups = 7;              // row groups of 16 per wave
-constexpr int kRing = 3;                // half buffers in the load ring (kRing - 1 in flight)
+constexpr int kRing = 2;                // half buffers in the load ring (kRing - 1 in flight)
 constexpr int TN = 4 * 16 * kGroups;    // weight rows per workgroup (112 per wave)
 constexpr int TM = 16;                  // activation rows per workgroup
 constexpr int KP = 2048;                // K elements per split
@@ -102,20 +102,28 @@ __device__ __forceinline__ void load_half(u32x4 (&q)[kHalf], u32x4 (&sc)[kHalf /
   }
 }
 
-// The MFMAs of one loaded half: steps 8 u .. 8 u + 7, two accumulator chains.
+// The MFMAs of one loaded half: steps kHalf u .. kHalf u + kHalf - 1, two
+// accumulator chains. The activation piece of step i and MFMA j is
+// x = 16 i' + 4 g + j (i' = kHalf u + i), stored at slot x ^ r: the XOR only
+// touches the low 4 bits, so the slot is 16 i' + ((4 g + j) ^ r) and
+// ab[j] = arow + 16 ((4 g + j) ^ r) plus the constant 256 i' addresses it.
 __device__ __forceinline__ void compute_half(const u32x4 (&q)[kHalf], const u32x4 (&sc)[kHalf / 4],
                                              const uint8_t* arow, int r, int g, int u,
                                              f32x4 (&acc)[2]) {
+  const uint8_t* ab[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) ab[j] = arow + (((4 * g + j) ^ r) * 16);
 #pragma unroll
   for (int i = 0; i < kHalf; i++) {
-    const int bl = 4 * (kHalf * u + i) + g;  // block within the split
     const uint32_t E = (sc[i / 4][i % 4] >> (8 * g)) & 0xFFu;
     const float scale = e8m0_to_float(E);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const bf16x8 a = *(const bf16x8*)(arow + (((4 * bl + j) ^ r) * 16));
-      const bf16x8 w = (E == 255) ? __builtin_bit_cast(bf16x8, u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u})
-                                  : expand8(q[i][j], scale);
+      const bf16x8 a = *(const bf16x8*)(ab[j] + 256 * (kHalf * u + i));
+      // A scale byte of 255 (E8M0 NaN) gives a scale with exponent field
+      // 255, for which the scaled converts return NaN for every code (they
+      // read only the scale's exponent): the block dequantizes to NaN.
+      const bf16x8 w = expand8(q[i][j], scale);
       acc[j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, w, acc[j & 1], 0, 0, 0);
     }
     // One step per scheduling window: hoisting later steps' LDS reads and

@@ -101,6 +101,19 @@ def test_nan_scale_propagates():
     _full_check("mxfp4", A, B, "f32", "nan")
 
 
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_w4a16_nan_weight_blocks(out):
+    """Weight blocks holding NaN or Inf get the E8M0 NaN scale: every output
+    of those weight rows is NaN, the rest stay finite and within the bound."""
+    M, N, K = 16, 600, 8192
+    A = synth.normal((M, K), 1.0, 41)
+    B = synth.normal((N, K), 0.02, 42).copy()
+    B[3, 100] = 0x7FC0
+    B[250, 4000] = 0x7F80
+    B[599, 8191] = 0xFF80
+    _full_check("w4a16", A, B, out, "w4a16 nan")
+
+
 # Full-size workloads: the whole output is computed on the GPU; a seeded sample
 # of entries (with every corner and the ragged last tile row/column) is checked
 # against the oracle one by one.
