@@ -334,10 +334,17 @@ constexpr int kMaxPartials = 1024;
 __global__ __launch_bounds__(kThreads) void nvfp4_amax_partial(const u32x4* __restrict__ x,
                                                                int64_t nchunks,
                                                                uint32_t* __restrict__ partial) {
+  // Four loads in flight per thread: chunks c + i G, G the grid's width.
   uint32_t m = 0;
-  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nchunks;
-       c += (int64_t)gridDim.x * kThreads)
-    m = umax(m, chunk_absmax(__builtin_nontemporal_load(x + c)));
+  const int64_t G = (int64_t)gridDim.x * kThreads;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nchunks; c += 4 * G) {
+    u32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      v[i] = (c + i * G < nchunks) ? __builtin_nontemporal_load(x + c + i * G) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; i++) m = umax(m, chunk_absmax(v[i]));
+  }
   for (int off = 32; off > 0; off >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, off));
   __shared__ uint32_t wmax[kThreads / 64];
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
@@ -349,28 +356,28 @@ __global__ __launch_bounds__(kThreads) void nvfp4_amax_partial(const u32x4* __re
   }
 }
 
-// s_t = T / 2688 (T = 0 -> 1, non-finite T -> NaN), written to tensor_scale.
-__global__ __launch_bounds__(kThreads) void nvfp4_finalize(const uint32_t* __restrict__ partial,
-                                                           int npartial,
-                                                           float* __restrict__ tensor_scale) {
+// The tensor scale from the amax partials, in every workgroup of the encode
+// kernel (the maximum does not depend on the order): s_t = T / 2688
+// (T = 0 -> 1, non-finite T -> NaN). Workgroup 0 writes it out.
+__device__ __forceinline__ float nvfp4_tensor_scale(const uint32_t* __restrict__ partial,
+                                                    int npartial, float* __restrict__ tensor_scale) {
   uint32_t m = 0;
   for (int i = threadIdx.x; i < npartial; i += kThreads) m = umax(m, partial[i]);
   for (int off = 32; off > 0; off >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, off));
   __shared__ uint32_t wmax[kThreads / 64];
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = 0;
-    for (int w = 0; w < kThreads / 64; w++) r = umax(r, wmax[w]);
-    float st;
-    if (r >= 0x7F80u) {
-      st = __builtin_nanf("");
-    } else {
-      const float T = __builtin_bit_cast(float, r << 16);
-      st = (T == 0.0f) ? 1.0f : T / 2688.0f;  // 2688 = 6 * 448
-    }
-    tensor_scale[0] = st;
+  uint32_t r = 0;
+  for (int w = 0; w < kThreads / 64; w++) r = umax(r, wmax[w]);
+  float st;
+  if (r >= 0x7F80u) {
+    st = __builtin_nanf("");
+  } else {
+    const float T = __builtin_bit_cast(float, r << 16);
+    st = (T == 0.0f) ? 1.0f : T / 2688.0f;  // 2688 = 6 * 448
   }
+  if (blockIdx.x == 0 && threadIdx.x == 0) tensor_scale[0] = st;
+  return st;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
@@ -382,19 +389,22 @@ __device__ __forceinline__ float nv_scaled(float xv, float rz) { return xv == 0.
 __global__ __launch_bounds__(kThreads) void quant_nvfp4_kernel(const u32x4* __restrict__ x,
                                                                uint32_t* __restrict__ codes,
                                                                uint8_t* __restrict__ scales,
-                                                               const float* __restrict__ tensor_scale,
+                                                               const uint32_t* __restrict__ partial,
+                                                               int npartial,
+                                                               float* __restrict__ tensor_scale,
                                                                int64_t nchunks) {
   const int lane = threadIdx.x & 63;
-  const float st = tensor_scale[0];
-  const bool bad = __builtin_isnan(st);
-  const float d6 = 6.0f * st;
   const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+  // The element loads go out first; the tensor scale is reduced meanwhile.
   u32x4 v[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; u++) {
     const int64_t c = base + u * kThreads;
     v[u] = (c < nchunks) ? __builtin_nontemporal_load(x + c) : u32x4{0, 0, 0, 0};
   }
+  const float st = nvfp4_tensor_scale(partial, npartial, tensor_scale);
+  const bool bad = __builtin_isnan(st);
+  const float d6 = 6.0f * st;
 #pragma unroll
   for (int u = 0; u < kUnroll; u++) {
     const int64_t c = base + u * kThreads;
@@ -487,9 +497,8 @@ hipError_t quant_nvfp4(int64_t rows, int64_t cols, const void* x, void* codes, v
   if (np < 1) np = 1;
   uint32_t* partial = (uint32_t*)workspace;
   nvfp4_amax_partial<<<(unsigned)np, kThreads, 0, s>>>((const u32x4*)x, nchunks, partial);
-  nvfp4_finalize<<<1, kThreads, 0, s>>>(partial, (int)np, tensor_scale);
   quant_nvfp4_kernel<<<(unsigned)grid_for(nchunks), kThreads, 0, s>>>(
-      (const u32x4*)x, (uint32_t*)codes, (uint8_t*)scales, tensor_scale, nchunks);
+      (const u32x4*)x, (uint32_t*)codes, (uint8_t*)scales, partial, (int)np, tensor_scale, nchunks);
   return hipGetLastError();
 }
 
