@@ -5,8 +5,11 @@
 // significant bits, exact in bf16 like E4M3).
 //
 // Design for CDNA4:
-//  * 256 x 256 output tile per workgroup, 4 waves (one per SIMD) of 128 x 128,
-//    each wave 4 x 4 MFMAs of 32 x 32 with 256 fp32 accumulators per lane.
+//  * 256 x 256 output tile per workgroup of 8 waves, two per SIMD, each wave
+//    128 x 64 (4 x 2 MFMAs of 32 x 32, 128 fp32 accumulators per lane): while
+//    one wave of a SIMD expands codes on the vector ALU, the other's MFMAs
+//    keep the matrix core busy (6% faster than 4 waves of 128 x 128 on NVFP4,
+//    2% on MXFP8).
 //  * K advances in stages of 64 elements. A stage moves through a three-deep
 //    pipeline: global -> VGPRs (16-byte code chunks, range-checked buffer
 //    loads issued two stages ahead), VGPRs -> bf16 -> LDS (each code expanded
@@ -48,28 +51,29 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;                     // 8 waves, two per SIMD
+constexpr int kWavesN = 4;                        // waves along N (2 along M)
 constexpr int BM = 256, BN = 256;
 constexpr int BK = 64;                            // K elements per stage
 constexpr int kRowBytes = BK * 2;                 // one LDS row: 64 bf16
 constexpr int kTileBytes = BM * kRowBytes;        // 32 KB per operand
 constexpr int kStage = 2 * kTileBytes;            // 64 KB
-constexpr int kSmem = 139264;                     // 2 stages (128 KB) or the epilogue (136 KB)
+constexpr int kSmem = 147456;                     // 2 stages (128 KB) or the epilogue (144 KB)
 constexpr uint32_t kRsrcFlags = 0x00020000u;      // raw buffer, gfx9 data format
 constexpr uint32_t kOOB = 0x80000000u;            // an offset past every buffer's range
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// Per-format staging geometry. A thread owns kChunks code chunks of 16 bytes
-// per operand per stage: MXFP8 chunk = 16 codes (4 per row, rows t/4 + 64u),
-// NVFP4 chunk = 32 codes (2 per row, rows t/2 + 128u).
+// Per-format staging geometry. A thread owns kChunks code chunks per operand
+// per stage: MXFP8 chunk = 16 codes (4 per row, rows t/4 + 128u, two
+// chunks), NVFP4 / MXFP6 chunk = 32 codes (2 per row, row t/2, one chunk).
 template <int FMT>
 struct Geo {
   static constexpr bool kByte = (FMT == kMXFP8 || FMT == kMXFP8E5M2);   // 8-bit codes
   static constexpr int kCodesPerChunk = kByte ? 16 : 32;
   static constexpr int kChunksPerRow = BK / kCodesPerChunk;      // 4 or 2
-  static constexpr int kChunks = BM * kChunksPerRow / kThreads;  // per thread per operand: 4 or 2
-  static constexpr int kRowStep = kThreads / kChunksPerRow;      // 64 or 128
+  static constexpr int kChunks = BM * kChunksPerRow / kThreads;  // per thread per operand: 2 or 1
+  static constexpr int kRowStep = kThreads / kChunksPerRow;      // 128 or 256
   static constexpr int kBlock = (FMT == kNVFP4) ? 16 : 32;       // elements per scale
   static constexpr bool kFp16 = (FMT == kNVFP4);                  // fp16 operands
 };
@@ -117,20 +121,23 @@ __device__ __forceinline__ void load_op(u32x4 (&q)[Geo<FMT>::kChunks], u32x4 (&t
 
 // The stage's staging work is split into 4 parts, one per MFMA sub-step: an
 // item is one (operand, chunk u) pair, 2 kChunks items per stage, so a part
-// holds 2 items (8-bit codes: chunk P of A and of B) or 1 (4- and 6-bit codes:
-// chunk P % 2 of A for P < 2, of B otherwise).
+// holds 1 item (8-bit codes: chunk P % 2 of A for P < 2, of B otherwise) or
+// none or one (4- and 6-bit codes: A in part 0, B in part 2).
 template <int FMT, int P>
 __device__ __forceinline__ void load_part(Stage<FMT>& st, __amdgpu_buffer_rsrc_t rA,
                                           __amdgpu_buffer_rsrc_t rSA, __amdgpu_buffer_rsrc_t rB,
                                           __amdgpu_buffer_rsrc_t rSB, uint32_t rowbytes,
                                           uint32_t scalebytes, int K, int s, int tid) {
-  if (Geo<FMT>::kChunks == 4) {
-    load_op<FMT>(st.qa, st.ta, st.sa, rA, rSA, rowbytes, scalebytes, K, s, tid, P);
-    load_op<FMT>(st.qb, st.tb, st.sb, rB, rSB, rowbytes, scalebytes, K, s, tid, P);
-  } else if (P < 2) {
-    load_op<FMT>(st.qa, st.ta, st.sa, rA, rSA, rowbytes, scalebytes, K, s, tid, P % 2);
+  if (Geo<FMT>::kChunks == 2) {
+    // Part P: operand P / 2, chunk P % 2.
+    if (P < 2)
+      load_op<FMT>(st.qa, st.ta, st.sa, rA, rSA, rowbytes, scalebytes, K, s, tid, P % 2);
+    else
+      load_op<FMT>(st.qb, st.tb, st.sb, rB, rSB, rowbytes, scalebytes, K, s, tid, P % 2);
   } else {
-    load_op<FMT>(st.qb, st.tb, st.sb, rB, rSB, rowbytes, scalebytes, K, s, tid, P % 2);
+    // One chunk per operand: A in part 0, B in part 2.
+    if (P == 0) load_op<FMT>(st.qa, st.ta, st.sa, rA, rSA, rowbytes, scalebytes, K, s, tid, 0);
+    if (P == 2) load_op<FMT>(st.qb, st.tb, st.sb, rB, rSB, rowbytes, scalebytes, K, s, tid, 0);
   }
 }
 
@@ -198,17 +205,17 @@ template <int FMT, int P>
 __device__ __forceinline__ void store_part(const Stage<FMT>& st, uint8_t* stage, int tid) {
   using G = Geo<FMT>;
   const int c = tid % G::kChunksPerRow;
-  if (G::kChunks == 4) {
-    const int row = tid / G::kChunksPerRow + G::kRowStep * P;
-    expand_chunk<FMT>(st.qa[P], st.ta[P], st.sa[P], stage, row, c);
-    expand_chunk<FMT>(st.qb[P], st.tb[P], st.sb[P], stage + kTileBytes, row, c);
-  } else {
+  if (G::kChunks == 2) {
     const int u = P % 2;
     const int row = tid / G::kChunksPerRow + G::kRowStep * u;
     if (P < 2)
       expand_chunk<FMT>(st.qa[u], st.ta[u], st.sa[u], stage, row, c);
     else
       expand_chunk<FMT>(st.qb[u], st.tb[u], st.sb[u], stage + kTileBytes, row, c);
+  } else {
+    const int row = tid / G::kChunksPerRow;
+    if (P == 0) expand_chunk<FMT>(st.qa[0], st.ta[0], st.sa[0], stage, row, c);
+    if (P == 2) expand_chunk<FMT>(st.qb[0], st.tb[0], st.sb[0], stage + kTileBytes, row, c);
   }
 }
 
@@ -228,33 +235,36 @@ __device__ __forceinline__ void load_stage(Stage<FMT>& st, __amdgpu_buffer_rsrc_
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Fragments of sub-step S: 4 A and 4 B tiles of 32 rows, chunk 2S + g.
+// Fragments of sub-step S: 4 A tiles and 2 B tiles of 32 rows, chunk 2S + g.
 template <int S, typename V>
 __device__ __forceinline__ void load_frags(const uint8_t* As, const uint8_t* Bs, int wm, int wn,
-                                           int r, int g, V (&fa)[4], V (&fb)[4]) {
+                                           int r, int g, V (&fa)[4], V (&fb)[2]) {
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int ra = wm * 128 + i * 32 + r;
-    const int rb = wn * 128 + i * 32 + r;
     fa[i] = *(const V*)(As + ra * kRowBytes + (((2 * S + g) ^ swz(ra)) * 16));
-    fb[i] = *(const V*)(Bs + rb * kRowBytes + (((2 * S + g) ^ swz(rb)) * 16));
+  }
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int rb = wn * 64 + j * 32 + r;
+    fb[j] = *(const V*)(Bs + rb * kRowBytes + (((2 * S + g) ^ swz(rb)) * 16));
   }
 }
 
-__device__ __forceinline__ void mfma16(const bf16x8 (&fa)[4], const bf16x8 (&fb)[4], f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void mfma16(const bf16x8 (&fa)[4], const bf16x8 (&fb)[2], f32x16 (&acc)[4][2]) {
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int j = 0; j < 2; j++)
       // Operands swapped (B first): the result tile is C^T (see tile256.h).
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
 }
 
-__device__ __forceinline__ void mfma16(const f16x8 (&fa)[4], const f16x8 (&fb)[4], f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void mfma16(const f16x8 (&fa)[4], const f16x8 (&fb)[2], f32x16 (&acc)[4][2]) {
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int j = 0; j < 2; j++)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
 }
 
@@ -262,41 +272,30 @@ __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Issue order of one sub-step region (sched_group_barrier masks: 0x008 MFMA,
 // 0x100 LDS read, 0x200 LDS write, 0x020 VMEM read, 0x002 VALU), closed by a
-// fence: the next sub-step's 8 fragment reads go out within the first 4
-// MFMAs, ahead of the staging traffic, then the global loads, then the
-// expansion and its LDS writes spread over the MFMAs that remain.
+// fence: the next sub-step's 6 fragment reads go out within the first 3
+// MFMAs, then the global loads, then the expansion and its LDS writes spread
+// over the MFMAs that remain.
 template <int FMT, bool WITH_READS>
 __device__ __forceinline__ void region_order() {
   if (WITH_READS) {
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
+    for (int k = 0; k < 3; k++) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-  }
-  if (Geo<FMT>::kChunks == 4) {
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, WITH_READS ? 4 : 8, 0);
   } else {
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+  }
 #pragma unroll
-    for (int k = 0; k < (WITH_READS ? 12 : 16); k++) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-    }
+  for (int k = 0; k < 2; k++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
 #pragma unroll
-    for (int k = 0; k < 4; k++) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-#pragma unroll
-    for (int k = 0; k < 2; k++) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  for (int k = 0; k < 3; k++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, Geo<FMT>::kByte ? 4 : 12, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, Geo<FMT>::kByte ? 1 : 2, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -307,8 +306,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16x_large_kernel(
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB, const float* __restrict__ TB,
     void* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int r = lane & 31, g = lane >> 5;
   int tm, tn;
   tile256::tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -323,11 +323,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16x_large_kernel(
   const __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc((void*)(SA + (int64_t)m0 * scalebytes), 0, (int)(mrows * scalebytes), kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rSB = __builtin_amdgcn_make_buffer_rsrc((void*)(SB + (int64_t)n0 * scalebytes), 0, (int)(nrows * scalebytes), kRsrcFlags);
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int j = 0; j < 2; j++)
 #pragma unroll
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16x_large_kernel(
     const uint8_t* Bs = cur + kTileBytes;
     // Operand elements: bf16 for the MX formats, fp16 for NVFP4.
     using V = typename std::conditional<Geo<FMT>::kFp16, f16x8, bf16x8>::type;
-    V fa0[4], fb0[4], fa1[4], fb1[4];
+    V fa0[4], fb0[2], fa1[4], fb1[2];
     load_frags<0>(As, Bs, wm, wn, r, g, fa0, fb0);
     fence();
     // Sub-step 0: next fragments, expansion of chunk 0 of stage s+1, loads of
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16x_large_kernel(
   }
   __syncthreads();
   const float ts = (FMT == kNVFP4) ? TA[0] * TB[0] : 1.0f;
-  tile256::store_tile<OUT>(acc, smem, ts, C, ldc, M, N, m0, n0, wave, lane);
+  tile256::store_tile<OUT, 2, kWavesN>(acc, smem, ts, C, ldc, M, N, m0, n0, wave, lane);
 }
 
 template <int FMT>
