@@ -70,6 +70,17 @@ def test_ragged_shapes(fmt, shape):
     _full_check(fmt, A, B, "f32", f"{fmt} {shape}")
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8", "nvfp4"])
+@pytest.mark.parametrize("shape", [(129, 257, 96), (300, 520, 768), (33, 1000, 4128)])
+def test_ragged_shapes_bf16_out(fmt, shape):
+    """Partial tiles in both directions with bf16 output: the epilogue's
+    row-contiguous write-back and its scalar tail."""
+    M, N, K = shape
+    A = synth.normal_outliers((M, K), 1.0, 51 + M, 0.01, 50.0)
+    B = synth.normal((N, K), 0.02, 52 + N)
+    _full_check(fmt, A, B, "bf16", f"{fmt} {shape} bf16")
+
+
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8", "nvfp4", "w4a16"])
 def test_all_positive_long_k(fmt):
     """|C| = sum|a*b|: the accumulation error is at its worst."""
