@@ -4,7 +4,8 @@ Default workload: the MXFP4 W4A4 DiT MLP-down layer, M=4608 tokens, K=12288,
 N=3072, activations Laplace(0,1) with 0.5% outlier channels x100, weights
 N(0,0.02) quantized beforehand. One step = quantize the bf16 activations to
 MXFP4 (codes + E8M0 scales) and run the block-scaled GEMM against the
-pre-quantized weights, bf16 output. Everything in the timed region runs in
+pre-quantized weights (MXFP4 weights in the K-panel layout of mx_pack), bf16
+output. Everything in the timed region runs in
 libmx's HIP kernels; inputs are resident in HBM before timing starts.
 
 Prints one JSON line. `value` is whole-step throughput, 2MNK / step time, in
@@ -113,9 +114,14 @@ def main():
     # choice and W keeps the standard rule)
     qb = mx.quantize(Bx, wfmt, rotation=variant["rotation"])
     del Bx
-    wbytes = qb.codes.numel() * qb.codes.element_size() + qb.scales.numel() * qb.scales.element_size()
+    # MXFP4 weights are laid out in K panels (mx_pack) with their quantization,
+    # so each GEMM step reads one contiguous range per weight tile; qb keeps
+    # the row layout for the CPU baseline.
+    panel = fmt == "mxfp4" and K % 256 == 0
+    qw = mx.pack(qb) if panel else qb
+    wbytes = qw.codes.numel() * qw.codes.element_size() + qw.scales.numel() * qw.scales.element_size()
     nwcopies = max(2, -(-WEIGHT_ROTATE_BYTES // wbytes))
-    weights = [qb] + [dataclasses.replace(qb, codes=qb.codes.clone(), scales=qb.scales.clone())
+    weights = [qw] + [dataclasses.replace(qw, codes=qw.codes.clone(), scales=qw.scales.clone())
                       for _ in range(nwcopies - 1)]
     ncopies = max(1, min(8, ROTATE_BYTES // A.numel() // 2))
     acts = [A] + [A.clone() for _ in range(ncopies - 1)]
@@ -227,7 +233,8 @@ def main():
         "config": {"workload": name, "format": fmt, "M": M, "N": N, "K": K,
                    "scale_rule": variant["scale_rule"], "rotation": variant["rotation"],
                    "step": ("quantize(A) + gemm" if quantize_a else "gemm") + ", bf16 out",
-                   "weights": "pre-quantized", "activation_copies_rotated": len(acts),
+                   "weights": "pre-quantized" + (", K-panel layout" if panel else ""),
+                   "activation_copies_rotated": len(acts),
                    "weight_copies_rotated": len(weights)},
         "timing": {"ms_per_step": "HIP-graph replay of the timed steps",
                    "eager_ms_per_step": eager_ms_per_step,

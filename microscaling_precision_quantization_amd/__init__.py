@@ -24,6 +24,7 @@ MX_SCALE_CEIL, MX_SCALE_OAS = 0, 1
 MX_ROTATE_NONE, MX_ROTATE_WHT32 = 0, 1
 MX_OUT_F32, MX_OUT_BF16 = 0, 1
 MX_OK, MX_ERR_INVALID_ARG, MX_ERR_UNSUPPORTED, MX_ERR_HIP = 0, 1, 2, 3
+MX_LAYOUT_ROWS, MX_LAYOUT_KPANEL = 0, 1
 
 FORMATS = {"mxfp4": MX_FMT_MXFP4, "mxfp8": MX_FMT_MXFP8, "nvfp4": MX_FMT_NVFP4, "bf16": MX_FMT_BF16,
            "mxfp8_e5m2": MX_FMT_MXFP8_E5M2, "mxfp6_e3m2": MX_FMT_MXFP6_E3M2,
@@ -58,7 +59,8 @@ def mbs_planes(scales, rows, cols):
 
 # Symbols declared in include/mx.h.
 EXPORTS = ("mx_quantize", "mx_quantize_workspace_bytes", "mx_quantize_ex", "mx_dequantize",
-           "mx_gemm", "mx_gemm_workspace_bytes", "mx_last_hip_error", "mx_status_string")
+           "mx_gemm", "mx_gemm_workspace_bytes", "mx_last_hip_error", "mx_status_string",
+           "mx_pack", "mx_gemm_ex")
 
 _lib = None
 
@@ -92,6 +94,11 @@ def lib():
         L.mx_gemm.restype = i32
         L.mx_gemm.argtypes = [i32, i32, i32, i32, i64, i64, i64, P, P, P, P, P, P, i32, P, i64,
                               P, sz, P]
+        L.mx_gemm_ex.restype = i32
+        L.mx_gemm_ex.argtypes = [i32, i32, i32, i32, i64, i64, i64, P, P, P, P, P, P, i32, P, i64,
+                                 P, sz, P, i32]
+        L.mx_pack.restype = i32
+        L.mx_pack.argtypes = [i32, i32, i64, i64, P, P, P, P, P]
         L.mx_gemm_workspace_bytes.restype = sz
         L.mx_gemm_workspace_bytes.argtypes = [i32, i32, i64, i64, i64]
         L.mx_last_hip_error.restype = i32
@@ -128,6 +135,16 @@ def mx_gemm(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales, b
                          out_dtype, c, ldc, workspace, workspace_bytes, stream)
 
 
+def mx_gemm_ex(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts, out_dtype,
+               c, ldc, workspace, workspace_bytes, stream, b_layout):
+    return lib().mx_gemm_ex(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales,
+                            b_ts, out_dtype, c, ldc, workspace, workspace_bytes, stream, b_layout)
+
+
+def mx_pack(fmt, block, rows, cols, codes, scales, packed_codes, packed_scales, stream):
+    return lib().mx_pack(fmt, block, rows, cols, codes, scales, packed_codes, packed_scales, stream)
+
+
 def mx_gemm_workspace_bytes(fmt_a, fmt_b, M, N, K):
     return lib().mx_gemm_workspace_bytes(fmt_a, fmt_b, M, N, K)
 
@@ -148,13 +165,14 @@ def status_string(status):
 @dataclass
 class QTensor:
     """A block-quantized [rows][cols] tensor: codes, scales and (NVFP4) the
-    fp32 tensor scale, all device tensors."""
+    fp32 tensor scale, all device tensors; layout MX_LAYOUT_KPANEL after pack()."""
     fmt: int
     rows: int
     cols: int
     codes: "object"
     scales: "object"
     tensor_scale: "object" = None
+    layout: int = MX_LAYOUT_ROWS
 
     @property
     def block(self):
@@ -226,9 +244,23 @@ def dequantize(q, out_dtype=None):
     return y
 
 
+def pack(q):
+    """An MXFP4 QTensor re-laid into the K-panel layout (mx_pack), for use as
+    the B operand of gemm()."""
+    import torch
+    if q.layout != MX_LAYOUT_ROWS:
+        raise ValueError("pack() takes a tensor in the row layout")
+    codes = torch.empty_like(q.codes)
+    scales = torch.empty_like(q.scales)
+    _check(mx_pack(q.fmt, q.block, q.rows, q.cols, _ptr(q.codes), _ptr(q.scales), _ptr(codes),
+                   _ptr(scales), _stream(torch, q.codes.device)), "mx_pack")
+    return QTensor(q.fmt, q.rows, q.cols, codes, scales, q.tensor_scale, MX_LAYOUT_KPANEL)
+
+
 def gemm(a, b, out_dtype=None, out=None, workspace=None):
     """C = A * B^T. a: QTensor (any quantized format, M x K; b of the same format) or a bf16 [M][K]
-    tensor (with an MXFP4 b: W4A16); b: QTensor stored N x K."""
+    tensor (with an MXFP4 b: W4A16); b: QTensor stored N x K (MXFP4: row or
+    K-panel layout)."""
     import torch
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     od = MX_OUT_F32 if out_dtype == torch.float32 else MX_OUT_BF16
@@ -249,6 +281,13 @@ def gemm(a, b, out_dtype=None, out=None, workspace=None):
     wsb = mx_gemm_workspace_bytes(fa, b.fmt, M, N, K)
     if wsb and workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    if isinstance(a, QTensor) and a.layout != MX_LAYOUT_ROWS:
+        raise ValueError("the A operand must be in the row layout")
+    if b.layout != MX_LAYOUT_ROWS:
+        _check(mx_gemm_ex(fa, b.fmt, b.block, MX_ROUND_RNE, M, N, K, pa, psa, pta, _ptr(b.codes),
+                          _ptr(b.scales), _ptr(b.tensor_scale), od, _ptr(c), c.stride(0),
+                          _ptr(workspace), wsb, _stream(torch, dev), b.layout), "mx_gemm_ex")
+        return c
     _check(mx_gemm(fa, b.fmt, b.block, MX_ROUND_RNE, M, N, K, pa, psa, pta, _ptr(b.codes),
                    _ptr(b.scales), _ptr(b.tensor_scale), od, _ptr(c), c.stride(0),
                    _ptr(workspace), wsb, _stream(torch, dev)), "mx_gemm")

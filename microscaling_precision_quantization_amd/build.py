@@ -16,7 +16,7 @@ BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["mx_api.cpp", "quantize.hip", "dequantize.hip", "gemm_mx.hip", "gemm_mxfp4.hip", "gemm_bf16x.hip", "gemm_bf16x_large.hip",
-           "gemm_w4a16.hip", "gemm_mbs.hip"]
+           "gemm_w4a16.hip", "gemm_mbs.hip", "pack.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
 # -ffp-contract=off: every fp32 step of the NVFP4 quantizer rounds once.

@@ -28,6 +28,12 @@
 //  * Workgroup ids are remapped so that each XCD (ids round-robin over 8
 //    XCDs) gets a contiguous, grouped block of output tiles and its L2 serves
 //    the shared A rows and B columns.
+//  * B may come in the K-panel layout (mx_pack): the 128 code bytes of all N
+//    rows for one super-step back to back, so a tile's loads of one
+//    super-step cover one contiguous 32 KB range instead of 256 pieces of 128
+//    bytes K / 2 bytes apart, which keeps the weights' HBM reads in open DRAM
+//    pages. The buffer view is then rebuilt per super-step to span that
+//    panel's N rows, so rows past N still fall outside its range.
 // 32x32x64 FP4 operand layout (measured): lane l = r + 32 g supplies K
 // elements [32g, 32g + 32) of row r (16 bytes, even element in the low
 // nibble) and the E8M0 scale of that K block; the output lane l holds column
@@ -73,12 +79,15 @@ struct Stage {
 // Part P (0..3) of the global loads of super-step s: code blocks 2P and 2P+1
 // of A and B, plus the A scales (P = 0) or the B scales (P = 1). Rows past M
 // or N fall outside the buffer range and load as zeros.
-template <int P>
+// B in the K-panel layout (PANEL_B): panel s of the codes starts at byte
+// s * N * 128 of B, of the scales at s * N * 8 of SB; its buffer views span
+// the panel's N rows.
+template <int P, bool PANEL_B>
 __device__ __forceinline__ void load_part(Stage& st, __amdgpu_buffer_rsrc_t rA,
                                           __amdgpu_buffer_rsrc_t rB, __amdgpu_buffer_rsrc_t rSA,
                                           __amdgpu_buffer_rsrc_t rSB, int m0, int n0,
                                           uint32_t rowbytes, uint32_t scalebytes, int s, int wave,
-                                          int lane) {
+                                          int lane, const uint8_t* B, const uint8_t* SB, int N) {
   const uint32_t kb = (uint32_t)s * kRowBytes;
 #pragma unroll
   for (int i = 2 * P; i < 2 * P + 2; i++) {
@@ -86,16 +95,31 @@ __device__ __forceinline__ void load_part(Stage& st, __amdgpu_buffer_rsrc_t rA,
     const int chunk = (lane & 7) ^ swz(row);  // slot lane&7 of the LDS row holds this chunk
     const uint32_t off = kb + (uint32_t)chunk * 16u;
     st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, (uint32_t)(m0 + row) * rowbytes + off, 0, 0);
-    st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, (uint32_t)(n0 + row) * rowbytes + off, 0, 0);
+    if (PANEL_B) {
+      const __amdgpu_buffer_rsrc_t rBp = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(B + (int64_t)s * N * kRowBytes), 0, N * kRowBytes, kRsrcFlags);
+      st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rBp, (uint32_t)(n0 + row) * (uint32_t)kRowBytes + (uint32_t)chunk * 16u, 0, 0);
+    } else {
+      st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, (uint32_t)(n0 + row) * rowbytes + off, 0, 0);
+    }
   }
   const int srow = wave * 64 + lane;
   const uint32_t soff = (uint32_t)s * (kSuperK / 32);
   if (P == 0)
     st.sa = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
                                           rSA, (uint32_t)(m0 + srow) * scalebytes + soff, 0, 0));
-  if (P == 1)
-    st.sb = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                          rSB, (uint32_t)(n0 + srow) * scalebytes + soff, 0, 0));
+  if (P == 1) {
+    if (PANEL_B) {
+      const __amdgpu_buffer_rsrc_t rSBp = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(SB + (int64_t)s * N * (kSuperK / 32)), 0, N * (kSuperK / 32), kRsrcFlags);
+      st.sb = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                            rSBp, (uint32_t)(n0 + srow) * (uint32_t)(kSuperK / 32), 0, 0));
+    } else {
+      st.sb = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                            rSB, (uint32_t)(n0 + srow) * scalebytes + soff, 0, 0));
+    }
+  }
 }
 
 // Part P of the LDS writes of a staged super-step (the same pieces as
@@ -177,7 +201,7 @@ __device__ __forceinline__ void interleave() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int OUT>
+template <int OUT, bool PANEL_B>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, void* __restrict__ C, int64_t ldc, int M, int N, int K,
@@ -194,6 +218,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
 
   const uint32_t rowbytes = (uint32_t)(K / 2), scalebytes = (uint32_t)(K / 32);
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, (int)((uint32_t)M * rowbytes), kRsrcFlags);
+  // (unused for a K-panel B, whose views are made per super-step)
   const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)B, 0, (int)((uint32_t)N * rowbytes), kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc((void*)SA, 0, (int)((uint32_t)M * scalebytes), kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rSB = __builtin_amdgcn_make_buffer_rsrc((void*)SB, 0, (int)((uint32_t)N * scalebytes), kRsrcFlags);
@@ -211,10 +236,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
   // (s + 1) & 1 receives super-step s + 1 from registers, and the registers
   // receive super-step s + 2 from memory while the MFMAs run.
   Stage R;
-  load_part<0>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane);
-  load_part<1>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane);
-  load_part<2>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane);
-  load_part<3>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane);
+  load_part<0, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, B, SB, N);
+  load_part<1, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, B, SB, N);
+  load_part<2, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, B, SB, N);
+  load_part<3, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, B, SB, N);
   store_part<0>(R, smem, wave, lane);
   store_part<1>(R, smem, wave, lane);
   store_part<2>(R, smem, wave, lane);
@@ -225,13 +250,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
     // first LDS writes wait only for their own part.
     const int s1 = min(1, nsteps - 1);
     sched_fence();
-    load_part<0>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane);
+    load_part<0, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, B, SB, N);
     sched_fence();
-    load_part<1>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane);
+    load_part<1, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, B, SB, N);
     sched_fence();
-    load_part<2>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane);
+    load_part<2, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, B, SB, N);
     sched_fence();
-    load_part<3>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane);
+    load_part<3, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, B, SB, N);
     sched_fence();
   }
   for (int s = 0; s < nsteps; s++) {
@@ -264,21 +289,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
     sched_fence();
     load_frags<1>(As, Bs, wm, wn, r, g, f1);
     store_part<0>(R, nxt, wave, lane);
-    load_part<0>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane);
+    load_part<0, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, B, SB, N);
     mfma_substep<0>(f0, sa, sb, acc);
     interleave<true>();
     load_frags<2>(As, Bs, wm, wn, r, g, f0);
     store_part<1>(R, nxt, wave, lane);
-    load_part<1>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane);
+    load_part<1, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, B, SB, N);
     mfma_substep<1>(f1, sa, sb, acc);
     interleave<true>();
     load_frags<3>(As, Bs, wm, wn, r, g, f1);
     store_part<2>(R, nxt, wave, lane);
-    load_part<2>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane);
+    load_part<2, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, B, SB, N);
     mfma_substep<2>(f0, sa, sb, acc);
     interleave<true>();
     store_part<3>(R, nxt, wave, lane);
-    load_part<3>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane);
+    load_part<3, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, B, SB, N);
     mfma_substep<3>(f1, sa, sb, acc);
     interleave<false>();
   }
@@ -291,24 +316,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
 }  // namespace
 
 // The large-tile kernel needs whole super-steps along K and 32-bit buffer
-// offsets (including the zero-filled rows past the last tile).
-bool gemm_mxfp4_fits(int64_t M, int64_t N, int64_t K) {
+// offsets (including the zero-filled rows past the last tile); a K-panel B
+// also needs its whole code array within 32-bit scalar offsets.
+bool gemm_mxfp4_fits(int64_t M, int64_t N, int64_t K, bool panel_b) {
   if (K % kSuperK != 0) return false;
   const int64_t lim = (int64_t)1 << 31;
+  if (panel_b && N * (K / 2) >= lim) return false;
   return (M + BM) * (K / 2) < lim && (N + BN) * (K / 2) < lim;
 }
 
 hipError_t gemm_mxfp4(int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
                       const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
-                      hipStream_t s) {
+                      hipStream_t s, bool panel_b) {
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
   const dim3 grid((unsigned)(tm * tn));
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;
-  if (out_dtype == kOutF32)
-    gemm_mxfp4_kernel<kOutF32><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, (int)M, (int)N, (int)K, tm, tn);
-  else
-    gemm_mxfp4_kernel<kOutBF16><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, (int)M, (int)N, (int)K, tm, tn);
+  const int m = (int)M, n = (int)N, k = (int)K;
+  if (out_dtype == kOutF32) {
+    if (panel_b)
+      gemm_mxfp4_kernel<kOutF32, true><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k, tm, tn);
+    else
+      gemm_mxfp4_kernel<kOutF32, false><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k, tm, tn);
+  } else {
+    if (panel_b)
+      gemm_mxfp4_kernel<kOutBF16, true><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k, tm, tn);
+    else
+      gemm_mxfp4_kernel<kOutBF16, false><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k, tm, tn);
+  }
   return hipGetLastError();
 }
 

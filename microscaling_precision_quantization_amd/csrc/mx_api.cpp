@@ -112,10 +112,16 @@ size_t mx_gemm_workspace_bytes(mx_format fmt_a, mx_format fmt_b, int64_t M, int6
   return 0;
 }
 
-mx_status mx_gemm(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int64_t M, int64_t N,
-                  int64_t K, const void* a, const void* a_scales, const float* a_ts,
-                  const void* b, const void* b_scales, const float* b_ts, mx_dtype out_dtype,
-                  void* c, int64_t ldc, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// mx_gemm and mx_gemm_ex; panel_b: B in the K-panel layout of mx_pack.
+mx_status gemm_impl(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int64_t M, int64_t N,
+                    int64_t K, const void* a, const void* a_scales, const float* a_ts,
+                    const void* b, const void* b_scales, const float* b_ts, mx_dtype out_dtype,
+                    void* c, int64_t ldc, void* workspace, size_t workspace_bytes, void* stream,
+                    bool panel_b) {
   const bool w4a4 = fmt_a == MX_FMT_MXFP4 && fmt_b == MX_FMT_MXFP4 && block == 32;
   const bool w8a8 = fmt_a == MX_FMT_MXFP8 && fmt_b == MX_FMT_MXFP8 && block == 32;
   const bool nv = fmt_a == MX_FMT_NVFP4 && fmt_b == MX_FMT_NVFP4 && block == 16;
@@ -124,6 +130,7 @@ mx_status mx_gemm(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int
                    (fmt_a == MX_FMT_MXFP8_E5M2 || fmt_a == MX_FMT_MXFP6_E3M2);
   const bool mbs = fmt_a == MX_FMT_MXFP4_MBS && fmt_b == MX_FMT_MXFP4_MBS && block == 32;
   if (!(w4a4 || w8a8 || nv || w4a16 || alt || mbs)) return MX_ERR_UNSUPPORTED;
+  if (panel_b && !w4a4) return MX_ERR_UNSUPPORTED;
   if (rnd != MX_ROUND_RNE) return MX_ERR_UNSUPPORTED;
   if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16) return MX_ERR_UNSUPPORTED;
   if (M <= 0 || N <= 0 || K <= 0 || M > kMaxExtent || N > kMaxExtent || K > kMaxExtent)
@@ -155,6 +162,11 @@ mx_status mx_gemm(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int
   if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
     return MX_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
+  if (panel_b) {
+    // Only the 256 x 256-tile kernel reads a K-panel B.
+    if (!mx::gemm_mxfp4_fits(M, N, K, true)) return MX_ERR_INVALID_ARG;
+    return hip_status(mx::gemm_mxfp4(M, N, K, a, a_scales, b, b_scales, out_dtype, c, ldc, s, true));
+  }
   if (w4a4)
     return hip_status(mx::gemm_mx(fmt_a, M, N, K, a, a_scales, b, b_scales, out_dtype, c, ldc, s));
   if (mbs)
@@ -168,6 +180,51 @@ mx_status mx_gemm(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int
                                            nullptr, out_dtype, c, ldc, s));
   }
   return hip_status(mx::gemm_w4a16(M, N, K, a, b, b_scales, out_dtype, c, ldc, workspace, s));
+}
+
+// [p, p + n) and [q, q + m) share a byte.
+bool overlap(const void* p, size_t n, const void* q, size_t m) {
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + m && b < a + n;
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status mx_gemm(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int64_t M, int64_t N,
+                  int64_t K, const void* a, const void* a_scales, const float* a_ts,
+                  const void* b, const void* b_scales, const float* b_ts, mx_dtype out_dtype,
+                  void* c, int64_t ldc, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_impl(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts,
+                   out_dtype, c, ldc, workspace, workspace_bytes, stream, false);
+}
+
+mx_status mx_gemm_ex(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int64_t M,
+                     int64_t N, int64_t K, const void* a, const void* a_scales, const float* a_ts,
+                     const void* b, const void* b_scales, const float* b_ts, mx_dtype out_dtype,
+                     void* c, int64_t ldc, void* workspace, size_t workspace_bytes, void* stream,
+                     mx_layout b_layout) {
+  if (b_layout != MX_LAYOUT_ROWS && b_layout != MX_LAYOUT_KPANEL) return MX_ERR_UNSUPPORTED;
+  return gemm_impl(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts,
+                   out_dtype, c, ldc, workspace, workspace_bytes, stream,
+                   b_layout == MX_LAYOUT_KPANEL);
+}
+
+mx_status mx_pack(mx_format fmt, int block, int64_t rows, int64_t cols, const void* codes,
+                  const void* scales, void* packed_codes, void* packed_scales, void* stream) {
+  if (fmt != MX_FMT_MXFP4 || block != 32) return MX_ERR_UNSUPPORTED;
+  if (rows <= 0 || cols <= 0 || cols % 256 != 0) return MX_ERR_INVALID_ARG;
+  if (rows >= ((int64_t)1 << 31) / (cols / 2)) return MX_ERR_INVALID_ARG;
+  if (!codes || !scales || !packed_codes || !packed_scales) return MX_ERR_INVALID_ARG;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(packed_codes) || !aligned16(packed_scales))
+    return MX_ERR_INVALID_ARG;
+  const size_t cb = (size_t)rows * (size_t)(cols / 2), sb = (size_t)rows * (size_t)(cols / 32);
+  if (overlap(codes, cb, packed_codes, cb) || overlap(codes, cb, packed_scales, sb) ||
+      overlap(scales, sb, packed_codes, cb) || overlap(scales, sb, packed_scales, sb))
+    return MX_ERR_INVALID_ARG;
+  return hip_status(mx::pack_mxfp4(rows, cols, codes, scales, packed_codes, packed_scales,
+                                   (hipStream_t)stream));
 }
 
 int mx_last_hip_error(void) { return g_last_hip_error; }

@@ -46,11 +46,16 @@ hipError_t gemm_mbs(int64_t M, int64_t N, int64_t K, const void* a, const void* 
                     const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
                     hipStream_t s);
 
-// ---- gemm_mxfp4.hip (MXFP4 x MXFP4, 256 x 256 tiles, direct-to-LDS pipeline)
-bool gemm_mxfp4_fits(int64_t M, int64_t N, int64_t K);
+// ---- gemm_mxfp4.hip (MXFP4 x MXFP4, 256 x 256 tiles, register-staged
+// pipeline); panel_b: B in the K-panel layout of mx_pack
+bool gemm_mxfp4_fits(int64_t M, int64_t N, int64_t K, bool panel_b);
 hipError_t gemm_mxfp4(int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
                       const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
-                      hipStream_t s);
+                      hipStream_t s, bool panel_b);
+
+// ---- pack.hip (MXFP4 codes and scales into the K-panel layout)
+hipError_t pack_mxfp4(int64_t rows, int64_t cols, const void* codes, const void* scales,
+                      void* packed_codes, void* packed_scales, hipStream_t s);
 
 // ---- gemm_bf16x.hip (MXFP8 x MXFP8 and NVFP4 x NVFP4, expanded exactly to bf16)
 hipError_t gemm_bf16x(int fmt, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,

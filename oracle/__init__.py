@@ -163,6 +163,17 @@ def mbs_planes(scales, rows, cols):
     return s[:n].reshape(rows, cols // 32), s[n:].reshape(rows, cols // 128)
 
 
+def pack_kpanel(codes, scales, rows, cols):
+    """The K-panel layout of an MXFP4 tensor (a byte permutation, no
+    arithmetic): codes [cols/256][rows][128], scales [cols/256][rows][8], from
+    the row layout [rows][cols/2] and [rows][cols/32]."""
+    assert cols % 256 == 0
+    p = cols // 256
+    c = np.asarray(codes, np.uint8).reshape(rows, p, 128).transpose(1, 0, 2).reshape(-1)
+    s = np.asarray(scales, np.uint8).reshape(rows, p, 8).transpose(1, 0, 2).reshape(-1)
+    return c.copy(), s.copy()
+
+
 def quantize(fmt, x_bits):
     """x_bits: uint16 [rows][cols] bf16 bit patterns.
     Returns (codes uint8, scales uint8 (scale_shape), tensor_scale float)."""

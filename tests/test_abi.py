@@ -141,3 +141,46 @@ def test_workspace_sizes():
     assert mx.mx_gemm_workspace_bytes(1, 1, 4608, 3072, 12288) == 0
     w = mx.mx_gemm_workspace_bytes(0, 1, 16, 28672, 8192)
     assert w > 0 and w % (16 * 28672 * 4) == 0
+
+
+def gx(layout=mx.MX_LAYOUT_KPANEL, fa=1, fb=1, block=32, rnd=0, M=64, N=64, K=256, a=P, sa=P,
+       ta=None, b=P, sb=P, tb=None, od=0, c=P2, ldc=64, ws=None, wsb=0):
+    return mx.mx_gemm_ex(fa, fb, block, rnd, M, N, K, a, sa, ta, b, sb, tb, od, c, ldc, ws, wsb,
+                         None, layout)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=7), mx.MX_ERR_UNSUPPORTED),                    # unknown layout
+    (dict(fa=2, fb=2), mx.MX_ERR_UNSUPPORTED),                  # K-panel B is MXFP4 only
+    (dict(fa=0, fb=1, sa=None, M=16), mx.MX_ERR_UNSUPPORTED),   # not for W4A16
+    (dict(fa=6, fb=6), mx.MX_ERR_UNSUPPORTED),                  # not for MBS
+    (dict(K=128 + 32), mx.MX_ERR_INVALID_ARG),                  # K % 256
+    (dict(K=128), mx.MX_ERR_INVALID_ARG),
+    (dict(N=1 << 20, ldc=1 << 20, K=1 << 12), mx.MX_ERR_INVALID_ARG),  # N * K / 2 >= 2^31
+    (dict(b=None), mx.MX_ERR_INVALID_ARG),
+    (dict(sb=MIS), mx.MX_ERR_INVALID_ARG),
+    (dict(layout=mx.MX_LAYOUT_ROWS, fa=1, fb=2), mx.MX_ERR_UNSUPPORTED),  # ROWS is mx_gemm
+])
+def test_gemm_ex_rejects(kw, status):
+    assert gx(**kw) == status
+
+
+def pk(fmt=mx.MX_FMT_MXFP4, block=32, rows=4, cols=256, codes=P, scales=ctypes.c_void_p(0x110000),
+       pc=P2, ps=ctypes.c_void_p(0x210000)):
+    return mx.mx_pack(fmt, block, rows, cols, codes, scales, pc, ps, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fmt=mx.MX_FMT_MXFP8), mx.MX_ERR_UNSUPPORTED),
+    (dict(fmt=mx.MX_FMT_NVFP4, block=16), mx.MX_ERR_UNSUPPORTED),
+    (dict(block=16), mx.MX_ERR_UNSUPPORTED),
+    (dict(rows=0), mx.MX_ERR_INVALID_ARG),
+    (dict(cols=128), mx.MX_ERR_INVALID_ARG),                    # cols % 256
+    (dict(rows=1 << 23, cols=1 << 9), mx.MX_ERR_INVALID_ARG),    # rows * cols / 2 >= 2^31
+    (dict(codes=None), mx.MX_ERR_INVALID_ARG),
+    (dict(ps=MIS), mx.MX_ERR_INVALID_ARG),
+    (dict(pc=ctypes.c_void_p(0x100100)), mx.MX_ERR_INVALID_ARG),  # output overlaps the codes
+    (dict(ps=ctypes.c_void_p(0x110000)), mx.MX_ERR_INVALID_ARG),  # output overlaps the scales
+])
+def test_pack_rejects(kw, status):
+    assert pk(**kw) == status

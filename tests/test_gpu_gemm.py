@@ -9,8 +9,8 @@ import torch
 import microscaling_precision_quantization_amd as mx
 import oracle as orc
 import synth
-from gpu_helpers import (ORC_FMT, check_gemm, dev_bf16, host, oracle_quant, qtensor_from_host,
-                         require_gpu, workload)
+from gpu_helpers import (ORC_FMT, check_gemm, dev_bf16, dev_u8, host, oracle_quant,
+                         qtensor_from_host, require_gpu, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -177,3 +177,48 @@ def test_quantize_then_gemm_on_device():
     b = orc.quantize(orc.FMT_MXFP4, B)
     C, S = orc.gemm(orc.FMT_MXFP4, orc.FMT_MXFP4, 300, 200, 1024, *a, *b)
     check_gemm(host(c), C, S, "f32", "quantize+gemm")
+
+
+# ---- K-panel layout of the B operand (mx_pack / mx_gemm_ex) ------------------
+
+@pytest.mark.parametrize("rows,cols", [(1, 256), (37, 768), (256, 4096), (513, 12288)])
+def test_pack_is_the_kpanel_permutation(rows, cols):
+    g = np.random.Generator(np.random.PCG64(81 + rows))
+    codes = g.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    scales = g.integers(0, 256, (rows, cols // 32), dtype=np.uint8)
+    q = mx.QTensor(mx.MX_FMT_MXFP4, rows, cols, dev_u8(codes), dev_u8(scales), None)
+    p = mx.pack(q)
+    torch.cuda.synchronize()
+    pc, ps = orc.pack_kpanel(codes, scales, rows, cols)
+    assert np.array_equal(host(p.codes).reshape(-1), pc)
+    assert np.array_equal(host(p.scales).reshape(-1), ps)
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 256), (200, 72, 512), (300, 520, 768), (257, 255, 4096),
+                                   (33, 1000, 12288)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_kpanel_b(shape, out):
+    """K-panel weights give bit-for-bit the row-layout result (same kernel,
+    same order), within the oracle's bound, including rows past N in the last
+    tile (each panel's view ends at row N)."""
+    M, N, K = shape
+    A = synth.laplace_outlier_channels((M, K), seed=61 + M, channel_seed=62, frac=0.01, factor=50.0)
+    B = synth.normal((N, K), 0.02, 63 + N)
+    hostops, qa, qb = _operands("mxfp4", A, B)
+    rows_out = _run(qa, qb, out)
+    panel_out = _run(qa, mx.pack(qb), out)
+    assert np.array_equal(rows_out.view(np.uint32), panel_out.view(np.uint32))
+    C, S = orc.gemm(*hostops[:2], M, N, K, *hostops[2:])
+    check_gemm(panel_out, C, S, out, f"kpanel {shape} {out}")
+
+
+def test_gemm_kpanel_b_workload_sampled():
+    """The MLP-down shape with K-panel weights: sampled outputs against the oracle."""
+    A, B = workload("c4")
+    M, K = A.shape
+    N = B.shape[0]
+    hostops, qa, qb = _operands("mxfp4", A, B, "c4")
+    got = _run(qa, mx.pack(qb), "bf16")
+    ii, jj = _sample(M, N, 2000, 17)
+    C, S = orc.gemm_entries(*hostops[:2], M, N, K, *hostops[2:], ii, jj)
+    check_gemm(got[ii, jj], C, S, "bf16", "c4 kpanel")

@@ -112,3 +112,21 @@ def test_gemm_rejects_bad_arguments(orc):
     with pytest.raises(ValueError):
         orc.gemm_entries(orc.FMT_MXFP4, orc.FMT_MXFP4, 4, 4, 32, a, s, 1.0, a, s, 1.0,
                          np.array([4]), np.array([0]))
+
+
+def test_pack_kpanel_brute_force(orc):
+    """The K-panel layout by its definition, byte by byte: code byte
+    (p * rows + r) * 128 + j is byte 128 p + j of row r, scale byte
+    (p * rows + r) * 8 + j is the scale of block 8 p + j of row r."""
+    rows, cols = 5, 768
+    g = np.random.Generator(np.random.PCG64(71))
+    codes = g.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    scales = g.integers(0, 256, (rows, cols // 32), dtype=np.uint8)
+    pc, ps = orc.pack_kpanel(codes, scales, rows, cols)
+    assert pc.size == codes.size and ps.size == scales.size
+    for p in range(cols // 256):
+        for r in range(rows):
+            for j in range(128):
+                assert pc[(p * rows + r) * 128 + j] == codes[r, 128 * p + j]
+            for j in range(8):
+                assert ps[(p * rows + r) * 8 + j] == scales[r, 8 * p + j]
