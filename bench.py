@@ -4,8 +4,9 @@ Default workload: the MXFP4 W4A4 DiT MLP-down layer, M=4608 tokens, K=12288,
 N=3072, activations Laplace(0,1) with 0.5% outlier channels x100, weights
 N(0,0.02) quantized beforehand. One step = quantize the bf16 activations to
 MXFP4 (codes + E8M0 scales) and run the block-scaled GEMM against the
-pre-quantized weights (MXFP4 weights in the K-panel layout of mx_pack), bf16
-output. Everything in the timed region runs in
+pre-quantized weights, bf16 output (MXFP4 operands in the K-panel layout:
+weights re-laid once by mx_pack, activations quantized straight into it).
+Everything in the timed region runs in
 libmx's HIP kernels; inputs are resident in HBM before timing starts.
 
 Prints one JSON line. `value` is whole-step throughput, 2MNK / step time, in
@@ -114,9 +115,10 @@ def main():
     # choice and W keeps the standard rule)
     qb = mx.quantize(Bx, wfmt, rotation=variant["rotation"])
     del Bx
-    # MXFP4 weights are laid out in K panels (mx_pack) with their quantization,
-    # so each GEMM step reads one contiguous range per weight tile; qb keeps
-    # the row layout for the CPU baseline.
+    # MXFP4 operands go to the GEMM in the K-panel layout: the weights re-laid
+    # once with their quantization (mx_pack), the activations quantized
+    # straight into it in the step, so each GEMM step reads one contiguous
+    # range per operand tile; qb keeps the row layout for the CPU baseline.
     panel = fmt == "mxfp4" and K % 256 == 0
     qw = mx.pack(qb) if panel else qb
     wbytes = qw.codes.numel() * qw.codes.element_size() + qw.scales.numel() * qw.scales.element_size()
@@ -137,7 +139,7 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         if quantize_a:
-            qa = mx.quantize(a, fmt, **variant)
+            qa = mx.quantize(a, fmt, layout="kpanel" if panel else "rows", **variant)
         else:
             qa = a
         if ev is not None:
@@ -234,6 +236,7 @@ def main():
                    "scale_rule": variant["scale_rule"], "rotation": variant["rotation"],
                    "step": ("quantize(A) + gemm" if quantize_a else "gemm") + ", bf16 out",
                    "weights": "pre-quantized" + (", K-panel layout" if panel else ""),
+                   "activation_layout": "K-panel" if panel else "rows",
                    "activation_copies_rotated": len(acts),
                    "weight_copies_rotated": len(weights)},
         "timing": {"ms_per_step": "HIP-graph replay of the timed steps",

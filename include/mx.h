@@ -138,15 +138,40 @@ typedef enum {
 } mx_rotation;
 
 /*
- * mx_quantize with a scale rule and a rotation: MX formats (block 32) only;
- * MX_SCALE_OAS with MXFP8, or NVFP4 with anything but (MX_SCALE_CEIL,
- * MX_ROTATE_NONE), returns MX_ERR_UNSUPPORTED. Outputs have the layout of
- * mx_quantize (the GEMM reads them unchanged); tensor_scale must be NULL and
- * no workspace is used. (MX_SCALE_CEIL, MX_ROTATE_NONE) is mx_quantize.
+ * Operand layout for the MXFP4 GEMM. The pages fix no memory layout; this one
+ * is for HBM locality on MI355X. MX_LAYOUT_ROWS is mx_quantize's: codes
+ * [rows][cols/2], scales [rows][cols/32]. MX_LAYOUT_KPANEL cuts K into panels
+ * of 256 elements and stores each panel's rows back to back:
+ *   codes   [cols/256][rows][128]: the 128 code bytes of row r in panel p
+ *           (elements 256 p .. 256 p + 255, packed as in MX_LAYOUT_ROWS) at
+ *           byte (p * rows + r) * 128;
+ *   scales  [cols/256][rows][8]: byte (p * rows + r) * 8 + j is the scale of
+ *           block 8 p + j of row r.
+ * A GEMM step over 256 K then reads one contiguous range per operand tile
+ * instead of one 128-byte piece per row spread over the whole matrix (on the
+ * MXFP4 MLP-down shape the GEMM runs ~10% faster with K-panel weights, ~3%
+ * more with K-panel activations). mx_pack re-lays a tensor;
+ * mx_quantize_ex can write one directly.
+ */
+typedef enum {
+  MX_LAYOUT_ROWS = 0,
+  MX_LAYOUT_KPANEL = 1
+} mx_layout;
+
+/*
+ * mx_quantize with a scale rule, a rotation and an output layout: MX formats
+ * (block 32) only; MX_SCALE_OAS with MXFP8, or NVFP4 with anything but
+ * (MX_SCALE_CEIL, MX_ROTATE_NONE), returns MX_ERR_UNSUPPORTED. layout
+ * MX_LAYOUT_ROWS gives mx_quantize's layout; MX_LAYOUT_KPANEL (MXFP4 only,
+ * else MX_ERR_UNSUPPORTED) writes the same codes and scales in K panels and
+ * needs cols a multiple of 256, cols / 256 <= 65535 and
+ * rows * cols / 2 < 2^31 (MX_ERR_INVALID_ARG otherwise). tensor_scale is not
+ * taken and no workspace is used. (MX_SCALE_CEIL, MX_ROTATE_NONE,
+ * MX_LAYOUT_ROWS) is mx_quantize.
  */
 mx_status mx_quantize_ex(mx_format fmt, int block, mx_round rnd, mx_scale_rule rule,
                          mx_rotation rot, int64_t rows, int64_t cols, const void* x,
-                         void* codes, void* scales, void* stream);
+                         void* codes, void* scales, void* stream, mx_layout layout);
 
 /*
  * Dequantization (x_real = S * x_elem on the produtoramaxvision page): MX
@@ -209,29 +234,11 @@ mx_status mx_gemm(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd,
 size_t mx_gemm_workspace_bytes(mx_format fmt_a, mx_format fmt_b, int64_t M, int64_t N, int64_t K);
 
 /*
- * Weight layout for the MXFP4 GEMM. The pages fix no memory layout; this one
- * is for HBM locality on MI355X. MX_LAYOUT_ROWS is mx_quantize's: codes
- * [rows][cols/2], scales [rows][cols/32]. MX_LAYOUT_KPANEL cuts K into panels
- * of 256 elements and stores each panel's rows back to back:
- *   codes   [cols/256][rows][128]: the 128 code bytes of row r in panel p
- *           (elements 256 p .. 256 p + 255, packed as in MX_LAYOUT_ROWS) at
- *           byte (p * rows + r) * 128;
- *   scales  [cols/256][rows][8]: byte (p * rows + r) * 8 + j is the scale of
- *           block 8 p + j of row r.
- * A GEMM step over 256 K then reads one contiguous range per operand tile
- * instead of one 128-byte piece per row spread over the whole matrix (the
- * weights stream from HBM about 10% faster on the MXFP4 MLP-down shape).
- */
-typedef enum {
-  MX_LAYOUT_ROWS = 0,
-  MX_LAYOUT_KPANEL = 1
-} mx_layout;
-
-/*
  * Re-lays an MXFP4 tensor from MX_LAYOUT_ROWS into MX_LAYOUT_KPANEL: a byte
  * permutation, no arithmetic. fmt must be MX_FMT_MXFP4 with block 32
  * (MX_ERR_UNSUPPORTED otherwise); rows > 0 and cols a positive multiple of 256
- * with rows * cols / 2 < 2^31 (MX_ERR_INVALID_ARG otherwise). codes / scales
+ * with cols / 256 <= 65535 and rows * cols / 2 < 2^31 (MX_ERR_INVALID_ARG
+ * otherwise). codes / scales
  * are the input (sizes as in mx_quantize), packed_codes / packed_scales the
  * output of the same sizes; input and output must not overlap. All pointers
  * 16-byte aligned device pointers.
@@ -240,12 +247,14 @@ mx_status mx_pack(mx_format fmt, int block, int64_t rows, int64_t cols, const vo
                   const void* scales, void* packed_codes, void* packed_scales, void* stream);
 
 /*
- * mx_gemm with the layout of the B operand given. b_layout MX_LAYOUT_ROWS is
- * exactly mx_gemm. MX_LAYOUT_KPANEL (b and b_scales as written by mx_pack) is
- * supported for (MXFP4, MXFP4, 32) with K a multiple of 256 and
- * N * K / 2 < 2^31, on the 256 x 256-tile kernel (MX_ERR_UNSUPPORTED for
- * other pairs, MX_ERR_INVALID_ARG for other shapes); its results are
- * bit-identical to mx_gemm on the same operands in MX_LAYOUT_ROWS.
+ * mx_gemm with the layouts of the operands given. (MX_LAYOUT_ROWS,
+ * MX_LAYOUT_ROWS) is exactly mx_gemm. MX_LAYOUT_KPANEL for A and / or B
+ * (codes and scales as written by mx_pack or mx_quantize_ex) is supported
+ * for (MXFP4, MXFP4, 32) on the 256 x 256-tile kernel: K a multiple of 256,
+ * (M + 256) * K / 2 and (N + 256) * K / 2 below 2^31, and K / 256 <= 65535
+ * (MX_ERR_UNSUPPORTED for other pairs, MX_ERR_INVALID_ARG for other shapes).
+ * The results are bit-identical to mx_gemm on the same operands in
+ * MX_LAYOUT_ROWS.
  */
 mx_status mx_gemm_ex(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd,
                      int64_t M, int64_t N, int64_t K,
@@ -253,7 +262,7 @@ mx_status mx_gemm_ex(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd,
                      const void* b, const void* b_scales, const float* b_ts,
                      mx_dtype out_dtype, void* c, int64_t ldc,
                      void* workspace, size_t workspace_bytes, void* stream,
-                     mx_layout b_layout);
+                     mx_layout a_layout, mx_layout b_layout);
 
 /* hipError_t saved by the last MX_ERR_HIP returned on the calling thread. */
 int mx_last_hip_error(void);

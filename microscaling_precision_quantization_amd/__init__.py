@@ -86,7 +86,7 @@ def lib():
         L.mx_quantize.restype = i32
         L.mx_quantize.argtypes = [i32, i32, i32, i64, i64, P, P, P, P, P, sz, P]
         L.mx_quantize_ex.restype = i32
-        L.mx_quantize_ex.argtypes = [i32, i32, i32, i32, i32, i64, i64, P, P, P, P]
+        L.mx_quantize_ex.argtypes = [i32, i32, i32, i32, i32, i64, i64, P, P, P, P, i32]
         L.mx_quantize_workspace_bytes.restype = sz
         L.mx_quantize_workspace_bytes.argtypes = [i32, i64, i64]
         L.mx_dequantize.restype = i32
@@ -96,7 +96,7 @@ def lib():
                               P, sz, P]
         L.mx_gemm_ex.restype = i32
         L.mx_gemm_ex.argtypes = [i32, i32, i32, i32, i64, i64, i64, P, P, P, P, P, P, i32, P, i64,
-                                 P, sz, P, i32]
+                                 P, sz, P, i32, i32]
         L.mx_pack.restype = i32
         L.mx_pack.argtypes = [i32, i32, i64, i64, P, P, P, P, P]
         L.mx_gemm_workspace_bytes.restype = sz
@@ -116,8 +116,9 @@ def mx_quantize(fmt, block, rnd, rows, cols, x, codes, scales, tensor_scale, wor
                              workspace, workspace_bytes, stream)
 
 
-def mx_quantize_ex(fmt, block, rnd, rule, rot, rows, cols, x, codes, scales, stream):
-    return lib().mx_quantize_ex(fmt, block, rnd, rule, rot, rows, cols, x, codes, scales, stream)
+def mx_quantize_ex(fmt, block, rnd, rule, rot, rows, cols, x, codes, scales, stream, layout):
+    return lib().mx_quantize_ex(fmt, block, rnd, rule, rot, rows, cols, x, codes, scales, stream,
+                                layout)
 
 
 def mx_quantize_workspace_bytes(fmt, rows, cols):
@@ -136,9 +137,10 @@ def mx_gemm(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales, b
 
 
 def mx_gemm_ex(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts, out_dtype,
-               c, ldc, workspace, workspace_bytes, stream, b_layout):
+               c, ldc, workspace, workspace_bytes, stream, a_layout, b_layout):
     return lib().mx_gemm_ex(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales,
-                            b_ts, out_dtype, c, ldc, workspace, workspace_bytes, stream, b_layout)
+                            b_ts, out_dtype, c, ldc, workspace, workspace_bytes, stream, a_layout,
+                            b_layout)
 
 
 def mx_pack(fmt, block, rows, cols, codes, scales, packed_codes, packed_scales, stream):
@@ -200,21 +202,26 @@ SCALE_RULES = {"ceil": MX_SCALE_CEIL, "oas": MX_SCALE_OAS}
 ROTATIONS = {None: MX_ROTATE_NONE, "none": MX_ROTATE_NONE, "wht32": MX_ROTATE_WHT32}
 
 
-def quantize(x, fmt, scale_rule="ceil", rotation=None):
+LAYOUTS = {"rows": MX_LAYOUT_ROWS, "kpanel": MX_LAYOUT_KPANEL}
+
+
+def quantize(x, fmt, scale_rule="ceil", rotation=None, layout="rows"):
     """Quantize a contiguous bf16 [rows][cols] device tensor. scale_rule "oas"
-    (MXFP4) and rotation "wht32" (MX formats) select mx_quantize_ex."""
+    (MXFP4), rotation "wht32" (MX formats) and layout "kpanel" (MXFP4) select
+    mx_quantize_ex."""
     import torch
     f = _fmt_id(fmt)
-    if scale_rule != "ceil" or rotation not in (None, "none"):
+    lay = LAYOUTS[layout]
+    if scale_rule != "ceil" or rotation not in (None, "none") or lay != MX_LAYOUT_ROWS:
         if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
             raise ValueError("quantize expects a contiguous 2-D bfloat16 tensor")
         rows, cols = x.shape
         codes = torch.empty((rows, code_cols(f, cols)), dtype=torch.uint8, device=x.device)
         scales = torch.empty(scale_shape(f, rows, cols), dtype=torch.uint8, device=x.device)
         _check(mx_quantize_ex(f, BLOCK[f], MX_ROUND_RNE, SCALE_RULES[scale_rule], ROTATIONS[rotation], rows,
-                              cols, _ptr(x), _ptr(codes), _ptr(scales), _stream(torch, x.device)),
+                              cols, _ptr(x), _ptr(codes), _ptr(scales), _stream(torch, x.device), lay),
                "mx_quantize_ex")
-        return QTensor(f, rows, cols, codes, scales, None)
+        return QTensor(f, rows, cols, codes, scales, None, lay)
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
         raise ValueError("quantize expects a contiguous 2-D bfloat16 tensor")
     rows, cols = x.shape
@@ -233,8 +240,10 @@ def quantize(x, fmt, scale_rule="ceil", rotation=None):
 
 
 def dequantize(q, out_dtype=None):
-    """Expand a QTensor to float32 (default) or bfloat16."""
+    """Expand a QTensor (row layout) to float32 (default) or bfloat16."""
     import torch
+    if q.layout != MX_LAYOUT_ROWS:
+        raise ValueError("dequantize takes a tensor in the row layout")
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     od = MX_OUT_F32 if out_dtype == torch.float32 else MX_OUT_BF16
     y = torch.empty((q.rows, q.cols), dtype=out_dtype, device=q.codes.device)
@@ -281,12 +290,11 @@ def gemm(a, b, out_dtype=None, out=None, workspace=None):
     wsb = mx_gemm_workspace_bytes(fa, b.fmt, M, N, K)
     if wsb and workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    if isinstance(a, QTensor) and a.layout != MX_LAYOUT_ROWS:
-        raise ValueError("the A operand must be in the row layout")
-    if b.layout != MX_LAYOUT_ROWS:
+    la = a.layout if isinstance(a, QTensor) else MX_LAYOUT_ROWS
+    if la != MX_LAYOUT_ROWS or b.layout != MX_LAYOUT_ROWS:
         _check(mx_gemm_ex(fa, b.fmt, b.block, MX_ROUND_RNE, M, N, K, pa, psa, pta, _ptr(b.codes),
                           _ptr(b.scales), _ptr(b.tensor_scale), od, _ptr(c), c.stride(0),
-                          _ptr(workspace), wsb, _stream(torch, dev), b.layout), "mx_gemm_ex")
+                          _ptr(workspace), wsb, _stream(torch, dev), la, b.layout), "mx_gemm_ex")
         return c
     _check(mx_gemm(fa, b.fmt, b.block, MX_ROUND_RNE, M, N, K, pa, psa, pta, _ptr(b.codes),
                    _ptr(b.scales), _ptr(b.tensor_scale), od, _ptr(c), c.stride(0),

@@ -210,8 +210,8 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __rest
 hipError_t gemm_mx(int fmt, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
                    const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
                    hipStream_t s) {
-  if (fmt == kMXFP4 && gemm_mxfp4_fits(M, N, K, false))
-    return gemm_mxfp4(M, N, K, a, sa, b, sb, out_dtype, c, ldc, s, false);
+  if (fmt == kMXFP4 && gemm_mxfp4_fits(M, N, K))
+    return gemm_mxfp4(M, N, K, a, sa, b, sb, out_dtype, c, ldc, s, false, false);
   const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;

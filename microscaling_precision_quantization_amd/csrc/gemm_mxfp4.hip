@@ -28,12 +28,13 @@
 //  * Workgroup ids are remapped so that each XCD (ids round-robin over 8
 //    XCDs) gets a contiguous, grouped block of output tiles and its L2 serves
 //    the shared A rows and B columns.
-//  * B may come in the K-panel layout (mx_pack): the 128 code bytes of all N
-//    rows for one super-step back to back, so a tile's loads of one
-//    super-step cover one contiguous 32 KB range instead of 256 pieces of 128
-//    bytes K / 2 bytes apart, which keeps the weights' HBM reads in open DRAM
-//    pages. The buffer view is then rebuilt per super-step to span that
-//    panel's N rows, so rows past N still fall outside its range.
+//  * A and B may come in the K-panel layout (mx_pack, or mx_quantize_ex's
+//    panel output): the 128 code bytes of all rows for one super-step back to
+//    back, so a tile's loads of one super-step cover one contiguous 32 KB
+//    range instead of 256 pieces of 128 bytes K / 2 bytes apart, which keeps
+//    the HBM reads in open DRAM pages. The buffer view is then rebuilt per
+//    super-step to span that panel's rows, so rows past M or N still fall
+//    outside its range.
 // 32x32x64 FP4 operand layout (measured): lane l = r + 32 g supplies K
 // elements [32g, 32g + 32) of row r (16 bytes, even element in the low
 // nibble) and the E8M0 scale of that K block; the output lane l holds column
@@ -79,22 +80,30 @@ struct Stage {
 // Part P (0..3) of the global loads of super-step s: code blocks 2P and 2P+1
 // of A and B, plus the A scales (P = 0) or the B scales (P = 1). Rows past M
 // or N fall outside the buffer range and load as zeros.
-// B in the K-panel layout (PANEL_B): panel s of the codes starts at byte
-// s * N * 128 of B, of the scales at s * N * 8 of SB; its buffer views span
-// the panel's N rows.
-template <int P, bool PANEL_B>
+// An operand in the K-panel layout (PANEL_A, PANEL_B): panel s of the codes
+// starts at byte s * rows * 128, of the scales at s * rows * 8; its buffer
+// views span the panel's rows.
+template <int P, bool PANEL_A, bool PANEL_B>
 __device__ __forceinline__ void load_part(Stage& st, __amdgpu_buffer_rsrc_t rA,
                                           __amdgpu_buffer_rsrc_t rB, __amdgpu_buffer_rsrc_t rSA,
                                           __amdgpu_buffer_rsrc_t rSB, int m0, int n0,
                                           uint32_t rowbytes, uint32_t scalebytes, int s, int wave,
-                                          int lane, const uint8_t* B, const uint8_t* SB, int N) {
+                                          int lane, const uint8_t* A, const uint8_t* SA, int M,
+                                          const uint8_t* B, const uint8_t* SB, int N) {
   const uint32_t kb = (uint32_t)s * kRowBytes;
 #pragma unroll
   for (int i = 2 * P; i < 2 * P + 2; i++) {
     const int row = (wave * 8 + i) * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ swz(row);  // slot lane&7 of the LDS row holds this chunk
     const uint32_t off = kb + (uint32_t)chunk * 16u;
-    st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, (uint32_t)(m0 + row) * rowbytes + off, 0, 0);
+    if (PANEL_A) {
+      const __amdgpu_buffer_rsrc_t rAp = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(A + (int64_t)s * M * kRowBytes), 0, M * kRowBytes, kRsrcFlags);
+      st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rAp, (uint32_t)(m0 + row) * (uint32_t)kRowBytes + (uint32_t)chunk * 16u, 0, 0);
+    } else {
+      st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, (uint32_t)(m0 + row) * rowbytes + off, 0, 0);
+    }
     if (PANEL_B) {
       const __amdgpu_buffer_rsrc_t rBp = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(B + (int64_t)s * N * kRowBytes), 0, N * kRowBytes, kRsrcFlags);
@@ -106,9 +115,17 @@ __device__ __forceinline__ void load_part(Stage& st, __amdgpu_buffer_rsrc_t rA,
   }
   const int srow = wave * 64 + lane;
   const uint32_t soff = (uint32_t)s * (kSuperK / 32);
-  if (P == 0)
-    st.sa = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                          rSA, (uint32_t)(m0 + srow) * scalebytes + soff, 0, 0));
+  if (P == 0) {
+    if (PANEL_A) {
+      const __amdgpu_buffer_rsrc_t rSAp = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(SA + (int64_t)s * M * (kSuperK / 32)), 0, M * (kSuperK / 32), kRsrcFlags);
+      st.sa = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                            rSAp, (uint32_t)(m0 + srow) * (uint32_t)(kSuperK / 32), 0, 0));
+    } else {
+      st.sa = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                            rSA, (uint32_t)(m0 + srow) * scalebytes + soff, 0, 0));
+    }
+  }
   if (P == 1) {
     if (PANEL_B) {
       const __amdgpu_buffer_rsrc_t rSBp = __builtin_amdgcn_make_buffer_rsrc(
@@ -201,7 +218,7 @@ __device__ __forceinline__ void interleave() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int OUT, bool PANEL_B>
+template <int OUT, bool PANEL_A, bool PANEL_B>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, void* __restrict__ C, int64_t ldc, int M, int N, int K,
@@ -236,10 +253,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
   // (s + 1) & 1 receives super-step s + 1 from registers, and the registers
   // receive super-step s + 2 from memory while the MFMAs run.
   Stage R;
-  load_part<0, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, B, SB, N);
-  load_part<1, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, B, SB, N);
-  load_part<2, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, B, SB, N);
-  load_part<3, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, B, SB, N);
+  load_part<0, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, A, SA, M, B, SB, N);
+  load_part<1, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, A, SA, M, B, SB, N);
+  load_part<2, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, A, SA, M, B, SB, N);
+  load_part<3, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, A, SA, M, B, SB, N);
   store_part<0>(R, smem, wave, lane);
   store_part<1>(R, smem, wave, lane);
   store_part<2>(R, smem, wave, lane);
@@ -250,13 +267,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
     // first LDS writes wait only for their own part.
     const int s1 = min(1, nsteps - 1);
     sched_fence();
-    load_part<0, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, B, SB, N);
+    load_part<0, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, A, SA, M, B, SB, N);
     sched_fence();
-    load_part<1, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, B, SB, N);
+    load_part<1, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, A, SA, M, B, SB, N);
     sched_fence();
-    load_part<2, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, B, SB, N);
+    load_part<2, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, A, SA, M, B, SB, N);
     sched_fence();
-    load_part<3, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, B, SB, N);
+    load_part<3, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, A, SA, M, B, SB, N);
     sched_fence();
   }
   for (int s = 0; s < nsteps; s++) {
@@ -289,21 +306,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
     sched_fence();
     load_frags<1>(As, Bs, wm, wn, r, g, f1);
     store_part<0>(R, nxt, wave, lane);
-    load_part<0, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, B, SB, N);
+    load_part<0, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
     mfma_substep<0>(f0, sa, sb, acc);
     interleave<true>();
     load_frags<2>(As, Bs, wm, wn, r, g, f0);
     store_part<1>(R, nxt, wave, lane);
-    load_part<1, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, B, SB, N);
+    load_part<1, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
     mfma_substep<1>(f1, sa, sb, acc);
     interleave<true>();
     load_frags<3>(As, Bs, wm, wn, r, g, f1);
     store_part<2>(R, nxt, wave, lane);
-    load_part<2, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, B, SB, N);
+    load_part<2, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
     mfma_substep<2>(f0, sa, sb, acc);
     interleave<true>();
     store_part<3>(R, nxt, wave, lane);
-    load_part<3, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, B, SB, N);
+    load_part<3, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
     mfma_substep<3>(f1, sa, sb, acc);
     interleave<false>();
   }
@@ -316,34 +333,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
 }  // namespace
 
 // The large-tile kernel needs whole super-steps along K and 32-bit buffer
-// offsets (including the zero-filled rows past the last tile); a K-panel B
-// also needs its whole code array within 32-bit scalar offsets.
-bool gemm_mxfp4_fits(int64_t M, int64_t N, int64_t K, bool panel_b) {
+// offsets (including the zero-filled rows past the last tile).
+bool gemm_mxfp4_fits(int64_t M, int64_t N, int64_t K) {
   if (K % kSuperK != 0) return false;
   const int64_t lim = (int64_t)1 << 31;
-  if (panel_b && N * (K / 2) >= lim) return false;
   return (M + BM) * (K / 2) < lim && (N + BN) * (K / 2) < lim;
+}
+
+template <int OUT>
+void launch(dim3 grid, hipStream_t s, bool panel_a, bool panel_b, const uint8_t* A,
+            const uint8_t* SA, const uint8_t* B, const uint8_t* SB, void* c, int64_t ldc, int m,
+            int n, int k, int tm, int tn) {
+  if (panel_a && panel_b)
+    gemm_mxfp4_kernel<OUT, true, true><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k, tm, tn);
+  else if (panel_a)
+    gemm_mxfp4_kernel<OUT, true, false><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k, tm, tn);
+  else if (panel_b)
+    gemm_mxfp4_kernel<OUT, false, true><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k, tm, tn);
+  else
+    gemm_mxfp4_kernel<OUT, false, false><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k, tm, tn);
 }
 
 hipError_t gemm_mxfp4(int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
                       const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
-                      hipStream_t s, bool panel_b) {
+                      hipStream_t s, bool panel_a, bool panel_b) {
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
   const dim3 grid((unsigned)(tm * tn));
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;
-  const int m = (int)M, n = (int)N, k = (int)K;
-  if (out_dtype == kOutF32) {
-    if (panel_b)
-      gemm_mxfp4_kernel<kOutF32, true><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k, tm, tn);
-    else
-      gemm_mxfp4_kernel<kOutF32, false><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k, tm, tn);
-  } else {
-    if (panel_b)
-      gemm_mxfp4_kernel<kOutBF16, true><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k, tm, tn);
-    else
-      gemm_mxfp4_kernel<kOutBF16, false><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k, tm, tn);
-  }
+  if (out_dtype == kOutF32)
+    launch<kOutF32>(grid, s, panel_a, panel_b, A, SA, B, SB, c, ldc, (int)M, (int)N, (int)K, tm, tn);
+  else
+    launch<kOutBF16>(grid, s, panel_a, panel_b, A, SA, B, SB, c, ldc, (int)M, (int)N, (int)K, tm, tn);
   return hipGetLastError();
 }
 

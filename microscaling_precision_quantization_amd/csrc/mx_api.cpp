@@ -36,6 +36,12 @@ mx_status hip_status(hipError_t e) {
   return MX_ERR_HIP;
 }
 
+// A K-panel MXFP4 tensor: whole 256-element panels, at most 65535 of them (a
+// grid dimension of the panel quantizer), and 32-bit byte offsets.
+bool panel_shape_ok(int64_t rows, int64_t cols) {
+  return cols % 256 == 0 && cols / 256 <= 65535 && rows < ((int64_t)1 << 31) / (cols / 2);
+}
+
 // Common checks for a [rows][cols] quantized tensor.
 mx_status check_tensor(int fmt, int block, int rnd, int64_t rows, int64_t cols) {
   if (!is_quant_fmt(fmt) || block != block_of(fmt)) return MX_ERR_UNSUPPORTED;
@@ -75,9 +81,13 @@ mx_status mx_quantize(mx_format fmt, int block, mx_round rnd, int64_t rows, int6
 
 mx_status mx_quantize_ex(mx_format fmt, int block, mx_round rnd, mx_scale_rule rule,
                          mx_rotation rot, int64_t rows, int64_t cols, const void* x,
-                         void* codes, void* scales, void* stream) {
+                         void* codes, void* scales, void* stream, mx_layout layout) {
   mx_status st = check_tensor(fmt, block, rnd, rows, cols);
   if (st != MX_OK) return st;
+  if (layout != MX_LAYOUT_ROWS && layout != MX_LAYOUT_KPANEL) return MX_ERR_UNSUPPORTED;
+  const bool panel = layout == MX_LAYOUT_KPANEL;
+  if (panel && fmt != MX_FMT_MXFP4) return MX_ERR_UNSUPPORTED;
+  if (panel && !panel_shape_ok(rows, cols)) return MX_ERR_INVALID_ARG;
   if (fmt != MX_FMT_MXFP4 && fmt != MX_FMT_MXFP8) return MX_ERR_UNSUPPORTED;
   if (rule != MX_SCALE_CEIL && !(rule == MX_SCALE_OAS && fmt == MX_FMT_MXFP4))
     return MX_ERR_UNSUPPORTED;
@@ -85,7 +95,7 @@ mx_status mx_quantize_ex(mx_format fmt, int block, mx_round rnd, mx_scale_rule r
   if (!x || !codes || !scales) return MX_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_INVALID_ARG;
   return hip_status(mx::quant_mx(fmt, rows, cols, x, codes, scales, (hipStream_t)stream,
-                                 rule == MX_SCALE_OAS, rot == MX_ROTATE_WHT32));
+                                 rule == MX_SCALE_OAS, rot == MX_ROTATE_WHT32, panel));
 }
 
 mx_status mx_dequantize(mx_format fmt, int block, mx_round rnd, int64_t rows, int64_t cols,
@@ -116,12 +126,12 @@ size_t mx_gemm_workspace_bytes(mx_format fmt_a, mx_format fmt_b, int64_t M, int6
 
 namespace {
 
-// mx_gemm and mx_gemm_ex; panel_b: B in the K-panel layout of mx_pack.
+// mx_gemm and mx_gemm_ex; panel_a / panel_b: that operand in the K-panel layout.
 mx_status gemm_impl(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int64_t M, int64_t N,
                     int64_t K, const void* a, const void* a_scales, const float* a_ts,
                     const void* b, const void* b_scales, const float* b_ts, mx_dtype out_dtype,
                     void* c, int64_t ldc, void* workspace, size_t workspace_bytes, void* stream,
-                    bool panel_b) {
+                    bool panel_a, bool panel_b) {
   const bool w4a4 = fmt_a == MX_FMT_MXFP4 && fmt_b == MX_FMT_MXFP4 && block == 32;
   const bool w8a8 = fmt_a == MX_FMT_MXFP8 && fmt_b == MX_FMT_MXFP8 && block == 32;
   const bool nv = fmt_a == MX_FMT_NVFP4 && fmt_b == MX_FMT_NVFP4 && block == 16;
@@ -130,7 +140,7 @@ mx_status gemm_impl(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, i
                    (fmt_a == MX_FMT_MXFP8_E5M2 || fmt_a == MX_FMT_MXFP6_E3M2);
   const bool mbs = fmt_a == MX_FMT_MXFP4_MBS && fmt_b == MX_FMT_MXFP4_MBS && block == 32;
   if (!(w4a4 || w8a8 || nv || w4a16 || alt || mbs)) return MX_ERR_UNSUPPORTED;
-  if (panel_b && !w4a4) return MX_ERR_UNSUPPORTED;
+  if ((panel_a || panel_b) && !w4a4) return MX_ERR_UNSUPPORTED;
   if (rnd != MX_ROUND_RNE) return MX_ERR_UNSUPPORTED;
   if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16) return MX_ERR_UNSUPPORTED;
   if (M <= 0 || N <= 0 || K <= 0 || M > kMaxExtent || N > kMaxExtent || K > kMaxExtent)
@@ -162,10 +172,13 @@ mx_status gemm_impl(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, i
   if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
     return MX_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  if (panel_b) {
-    // Only the 256 x 256-tile kernel reads a K-panel B.
-    if (!mx::gemm_mxfp4_fits(M, N, K, true)) return MX_ERR_INVALID_ARG;
-    return hip_status(mx::gemm_mxfp4(M, N, K, a, a_scales, b, b_scales, out_dtype, c, ldc, s, true));
+  if (panel_a || panel_b) {
+    // Only the 256 x 256-tile kernel reads K-panel operands.
+    if (!mx::gemm_mxfp4_fits(M, N, K)) return MX_ERR_INVALID_ARG;
+    if ((panel_a && !panel_shape_ok(M, K)) || (panel_b && !panel_shape_ok(N, K)))
+      return MX_ERR_INVALID_ARG;
+    return hip_status(mx::gemm_mxfp4(M, N, K, a, a_scales, b, b_scales, out_dtype, c, ldc, s,
+                                     panel_a, panel_b));
   }
   if (w4a4)
     return hip_status(mx::gemm_mx(fmt_a, M, N, K, a, a_scales, b, b_scales, out_dtype, c, ldc, s));
@@ -197,25 +210,25 @@ mx_status mx_gemm(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int
                   const void* b, const void* b_scales, const float* b_ts, mx_dtype out_dtype,
                   void* c, int64_t ldc, void* workspace, size_t workspace_bytes, void* stream) {
   return gemm_impl(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts,
-                   out_dtype, c, ldc, workspace, workspace_bytes, stream, false);
+                   out_dtype, c, ldc, workspace, workspace_bytes, stream, false, false);
 }
 
 mx_status mx_gemm_ex(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int64_t M,
                      int64_t N, int64_t K, const void* a, const void* a_scales, const float* a_ts,
                      const void* b, const void* b_scales, const float* b_ts, mx_dtype out_dtype,
                      void* c, int64_t ldc, void* workspace, size_t workspace_bytes, void* stream,
-                     mx_layout b_layout) {
+                     mx_layout a_layout, mx_layout b_layout) {
+  if (a_layout != MX_LAYOUT_ROWS && a_layout != MX_LAYOUT_KPANEL) return MX_ERR_UNSUPPORTED;
   if (b_layout != MX_LAYOUT_ROWS && b_layout != MX_LAYOUT_KPANEL) return MX_ERR_UNSUPPORTED;
   return gemm_impl(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts,
                    out_dtype, c, ldc, workspace, workspace_bytes, stream,
-                   b_layout == MX_LAYOUT_KPANEL);
+                   a_layout == MX_LAYOUT_KPANEL, b_layout == MX_LAYOUT_KPANEL);
 }
 
 mx_status mx_pack(mx_format fmt, int block, int64_t rows, int64_t cols, const void* codes,
                   const void* scales, void* packed_codes, void* packed_scales, void* stream) {
   if (fmt != MX_FMT_MXFP4 || block != 32) return MX_ERR_UNSUPPORTED;
-  if (rows <= 0 || cols <= 0 || cols % 256 != 0) return MX_ERR_INVALID_ARG;
-  if (rows >= ((int64_t)1 << 31) / (cols / 2)) return MX_ERR_INVALID_ARG;
+  if (rows <= 0 || cols <= 0 || !panel_shape_ok(rows, cols)) return MX_ERR_INVALID_ARG;
   if (!codes || !scales || !packed_codes || !packed_scales) return MX_ERR_INVALID_ARG;
   if (!aligned16(codes) || !aligned16(scales) || !aligned16(packed_codes) || !aligned16(packed_scales))
     return MX_ERR_INVALID_ARG;

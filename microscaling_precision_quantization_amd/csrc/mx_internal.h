@@ -13,9 +13,10 @@ enum : int { kOutF32 = 0, kOutBF16 = 1 };
 
 // ---- quantize.hip
 // oas: MXFP4's overflow-aware scale rule; rot: 32-point Walsh-Hadamard rotation first.
+// panel: MXFP4 codes and scales in the K-panel layout (cols % 256 = 0).
 hipError_t quant_mx(int fmt, int64_t rows, int64_t cols, const void* x, void* codes,
                     void* scales, hipStream_t s, bool oas = false,
-                    bool rot = false);
+                    bool rot = false, bool panel = false);
 // MXFP4 with static macro-block scaling: scales holds the E8M0 plane
 // [rows][cols/32] followed by the macro mantissa plane [rows][cols/128].
 hipError_t quant_mbs(int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
@@ -47,11 +48,12 @@ hipError_t gemm_mbs(int64_t M, int64_t N, int64_t K, const void* a, const void* 
                     hipStream_t s);
 
 // ---- gemm_mxfp4.hip (MXFP4 x MXFP4, 256 x 256 tiles, register-staged
-// pipeline); panel_b: B in the K-panel layout of mx_pack
-bool gemm_mxfp4_fits(int64_t M, int64_t N, int64_t K, bool panel_b);
+// pipeline); panel_a / panel_b: that operand in the K-panel layout (its
+// rows * K / 2 below 2^31)
+bool gemm_mxfp4_fits(int64_t M, int64_t N, int64_t K);
 hipError_t gemm_mxfp4(int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
                       const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
-                      hipStream_t s, bool panel_b);
+                      hipStream_t s, bool panel_a, bool panel_b);
 
 // ---- pack.hip (MXFP4 codes and scales into the K-panel layout)
 hipError_t pack_mxfp4(int64_t rows, int64_t cols, const void* codes, const void* scales,

@@ -126,22 +126,43 @@ __device__ __forceinline__ u32x4 wht32_chunk(u32x4 v, int lane) {
 
 // MXFP4 / MXFP8 (E4M3) / MXFP8 (E5M2); OAS: MXFP4's overflow-aware scale
 // rule; ROT: rotate every block first.
-template <int FMT, bool OAS, bool ROT>
+// PANEL (MXFP4): codes and scales in the K-panel layout ([cols/256][rows][128]
+// and [cols/256][rows][8]). The grid is then 2-D: workgroup (x, y) takes
+// rows 32 x .. 32 x + 31 of panel y, lanes 32 r' + j of a wave the 32 chunks
+// j of a row, so loads, code stores and scale stores stay contiguous and no
+// index needs a division. nchunks is then rows, cpr the chunks per row.
+template <int FMT, bool OAS, bool ROT, bool PANEL = false>
 __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restrict__ x,
                                                             void* __restrict__ codes,
                                                             uint8_t* __restrict__ scales,
-                                                            int64_t nchunks) {
+                                                            int64_t nchunks, int64_t cpr = 0) {
   const int lane = threadIdx.x & 63;
   const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+  // Source chunk, and (PANEL) destination dword of the codes, for item u.
+  auto src_of = [&](int u) -> int64_t {
+    if (!PANEL) return base + u * kThreads;
+    const int t = u * kThreads + (int)threadIdx.x;
+    const int64_t r = (int64_t)blockIdx.x * 32 + (t >> 5);
+    return r * cpr + (int64_t)blockIdx.y * 32 + (t & 31);
+  };
+  auto valid = [&](int u) -> bool {
+    if (!PANEL) return base + u * kThreads < nchunks;
+    return (int64_t)blockIdx.x * 32 + ((u * kThreads + (int)threadIdx.x) >> 5) < nchunks;
+  };
+  auto dst_of = [&](int u) -> int64_t {
+    if (!PANEL) return base + u * kThreads;
+    const int t = u * kThreads + (int)threadIdx.x;
+    const int64_t r = (int64_t)blockIdx.x * 32 + (t >> 5);
+    return ((int64_t)blockIdx.y * nchunks + r) * 32 + (t & 31);
+  };
   u32x4 v[kUnroll];
 #pragma unroll
-  for (int u = 0; u < kUnroll; u++) {
-    const int64_t c = base + u * kThreads;
-    v[u] = (c < nchunks) ? __builtin_nontemporal_load(x + c) : u32x4{0, 0, 0, 0};
-  }
+  for (int u = 0; u < kUnroll; u++)
+    v[u] = valid(u) ? __builtin_nontemporal_load(x + src_of(u)) : u32x4{0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < kUnroll; u++) {
-    const int64_t c = base + u * kThreads;
+    const int64_t c = dst_of(u);
+    const bool ok = valid(u);
     if (ROT) v[u] = wht32_chunk(v[u], lane);
     uint32_t m = chunk_absmax(v[u]);
     m = umax(m, dpp<kDppSwap1>(m));
@@ -166,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restr
       q = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(q, as_bf16x2(v[u].z), scale, 2);
       q = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(q, as_bf16x2(v[u].w), scale, 3);
       if (nonfinite) q = 0;
-      if (c < nchunks) __builtin_nontemporal_store(q, (uint32_t*)codes + c);
+      if (ok) __builtin_nontemporal_store(q, (uint32_t*)codes + c);
     } else {
       i16x2 lo = {0, 0}, hi = {0, 0};
       if (FMT == kMXFP8) {
@@ -182,19 +203,21 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restr
       }
       u32x2 q = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
       if (nonfinite) q = u32x2{0, 0};
-      if (c < nchunks) __builtin_nontemporal_store(q, (u32x2*)codes + c);
+      if (ok) __builtin_nontemporal_store(q, (u32x2*)codes + c);
     }
     // Scale bytes: lanes 3, 7, 11, 15 of each 16-lane DPP row hold 4
-    // consecutive blocks; lane 15 assembles them into one dword store.
+    // consecutive blocks; lane 15 assembles them into one dword store. (With
+    // PANEL the dword index c / 4 is (panel * rows + row) * 8 + block.)
     const uint32_t s4 = dpp<dpp_row_shr(4)>(E);
     const uint32_t s8 = dpp<dpp_row_shr(8)>(E);
     const uint32_t s12 = dpp<dpp_row_shr(12)>(E);
     const int64_t blk = c >> 2;
-    if ((lane & 15) == 15 && c < nchunks) {
+    if ((lane & 15) == 15 && ok) {
       *(uint32_t*)(scales + (blk - 3)) = s12 | (s8 << 8) | (s4 << 16) | (E << 24);
     }
-    // Ragged end: the row's lane 15 is past the end, store bytes instead.
-    if ((lane & 3) == 0 && c < nchunks && c - (lane & 15) + 15 >= nchunks) scales[blk] = (uint8_t)E;
+    // Ragged end: the row's lane 15 is past the end, store bytes instead
+    // (never with PANEL: a row's 32 chunks are all in or all out).
+    if (!PANEL && (lane & 3) == 0 && ok && c - (lane & 15) + 15 >= nchunks) scales[blk] = (uint8_t)E;
   }
 }
 
@@ -447,11 +470,25 @@ int64_t grid_for(int64_t nchunks) { return (nchunks + kThreads * kUnroll - 1) / 
 }  // namespace
 
 hipError_t quant_mx(int fmt, int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
-                    hipStream_t s, bool oas, bool rot) {
+                    hipStream_t s, bool oas, bool rot, bool panel) {
   const int64_t nchunks = rows * cols / 8;
   const dim3 grid((unsigned)grid_for(nchunks));
   const u32x4* X = (const u32x4*)x;
   uint8_t* S = (uint8_t*)scales;
+  if (panel) {
+    // MXFP4 in the K-panel layout: workgroups of 32 rows x one 256-element panel.
+    const dim3 pgrid((unsigned)((rows + 31) / 32), (unsigned)(cols / 256));
+    const int64_t cpr = cols / 8;
+    if (oas && rot)
+      quant_mx_kernel<kMXFP4, true, true, true><<<pgrid, kThreads, 0, s>>>(X, codes, S, rows, cpr);
+    else if (oas)
+      quant_mx_kernel<kMXFP4, true, false, true><<<pgrid, kThreads, 0, s>>>(X, codes, S, rows, cpr);
+    else if (rot)
+      quant_mx_kernel<kMXFP4, false, true, true><<<pgrid, kThreads, 0, s>>>(X, codes, S, rows, cpr);
+    else
+      quant_mx_kernel<kMXFP4, false, false, true><<<pgrid, kThreads, 0, s>>>(X, codes, S, rows, cpr);
+    return hipGetLastError();
+  }
   if (fmt == kMXFP4) {
     if (oas && rot)
       quant_mx_kernel<kMXFP4, true, true><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);

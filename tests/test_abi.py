@@ -70,8 +70,9 @@ def test_quantize_rejects(kw, status):
     assert q(**kw) == status
 
 
-def qx(fmt=mx.MX_FMT_MXFP4, block=32, rnd=0, rule=0, rot=0, rows=4, cols=64, x=P, codes=P, scales=P):
-    return mx.mx_quantize_ex(fmt, block, rnd, rule, rot, rows, cols, x, codes, scales, None)
+def qx(fmt=mx.MX_FMT_MXFP4, block=32, rnd=0, rule=0, rot=0, rows=4, cols=64, x=P, codes=P, scales=P,
+       layout=mx.MX_LAYOUT_ROWS):
+    return mx.mx_quantize_ex(fmt, block, rnd, rule, rot, rows, cols, x, codes, scales, None, layout)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -85,6 +86,11 @@ def qx(fmt=mx.MX_FMT_MXFP4, block=32, rnd=0, rule=0, rot=0, rows=4, cols=64, x=P
     (dict(rot=2), mx.MX_ERR_UNSUPPORTED),
     (dict(rnd=1), mx.MX_ERR_UNSUPPORTED),
     (dict(fmt=mx.MX_FMT_MXFP4_MBS, cols=128), mx.MX_ERR_UNSUPPORTED),  # MBS is its own format
+    (dict(layout=5), mx.MX_ERR_UNSUPPORTED),
+    (dict(layout=mx.MX_LAYOUT_KPANEL, fmt=mx.MX_FMT_MXFP8, cols=256), mx.MX_ERR_UNSUPPORTED),
+    (dict(layout=mx.MX_LAYOUT_KPANEL, cols=128), mx.MX_ERR_INVALID_ARG),          # cols % 256
+    (dict(layout=mx.MX_LAYOUT_KPANEL, cols=256 * 65536), mx.MX_ERR_INVALID_ARG),  # > 65535 panels
+    (dict(layout=mx.MX_LAYOUT_KPANEL, rows=1 << 23, cols=512), mx.MX_ERR_INVALID_ARG),  # 2^31 bytes
 ])
 def test_quantize_ex_rejects(kw, status):
     assert qx(**kw) == status
@@ -144,9 +150,9 @@ def test_workspace_sizes():
 
 
 def gx(layout=mx.MX_LAYOUT_KPANEL, fa=1, fb=1, block=32, rnd=0, M=64, N=64, K=256, a=P, sa=P,
-       ta=None, b=P, sb=P, tb=None, od=0, c=P2, ldc=64, ws=None, wsb=0):
+       ta=None, b=P, sb=P, tb=None, od=0, c=P2, ldc=64, ws=None, wsb=0, a_layout=mx.MX_LAYOUT_ROWS):
     return mx.mx_gemm_ex(fa, fb, block, rnd, M, N, K, a, sa, ta, b, sb, tb, od, c, ldc, ws, wsb,
-                         None, layout)
+                         None, a_layout, layout)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -160,6 +166,10 @@ def gx(layout=mx.MX_LAYOUT_KPANEL, fa=1, fb=1, block=32, rnd=0, M=64, N=64, K=25
     (dict(b=None), mx.MX_ERR_INVALID_ARG),
     (dict(sb=MIS), mx.MX_ERR_INVALID_ARG),
     (dict(layout=mx.MX_LAYOUT_ROWS, fa=1, fb=2), mx.MX_ERR_UNSUPPORTED),  # ROWS is mx_gemm
+    (dict(layout=mx.MX_LAYOUT_ROWS, a_layout=9), mx.MX_ERR_UNSUPPORTED),  # unknown A layout
+    (dict(layout=mx.MX_LAYOUT_ROWS, a_layout=mx.MX_LAYOUT_KPANEL, fa=2, fb=2), mx.MX_ERR_UNSUPPORTED),
+    (dict(layout=mx.MX_LAYOUT_ROWS, a_layout=mx.MX_LAYOUT_KPANEL, K=128), mx.MX_ERR_INVALID_ARG),
+    (dict(a_layout=mx.MX_LAYOUT_KPANEL, M=1 << 20, K=1 << 12), mx.MX_ERR_INVALID_ARG),  # M K / 2 >= 2^31
 ])
 def test_gemm_ex_rejects(kw, status):
     assert gx(**kw) == status

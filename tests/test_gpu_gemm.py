@@ -222,3 +222,24 @@ def test_gemm_kpanel_b_workload_sampled():
     ii, jj = _sample(M, N, 2000, 17)
     C, S = orc.gemm_entries(*hostops[:2], M, N, K, *hostops[2:], ii, jj)
     check_gemm(got[ii, jj], C, S, "bf16", "c4 kpanel")
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 256), (300, 520, 768), (37, 1000, 4096)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_kpanel_both(shape, out):
+    """Activations quantized straight into the K-panel layout and K-panel
+    weights: bit-for-bit the row-layout GEMM on the same codes."""
+    M, N, K = shape
+    A = synth.laplace_outlier_channels((M, K), seed=91 + M, channel_seed=92, frac=0.01, factor=50.0)
+    B = synth.normal((N, K), 0.02, 93 + N)
+    qa_rows = mx.quantize(dev_bf16(A), "mxfp4")
+    qa_panel = mx.quantize(dev_bf16(A), "mxfp4", layout="kpanel")
+    qb = mx.quantize(dev_bf16(B), "mxfp4")
+    ref = _run(qa_rows, qb, out)
+    got = _run(qa_panel, mx.pack(qb), out)
+    assert np.array_equal(ref.view(np.uint32), got.view(np.uint32))
+    got_a = _run(qa_panel, qb, out)
+    assert np.array_equal(ref.view(np.uint32), got_a.view(np.uint32))
+    C, S = orc.gemm(orc.FMT_MXFP4, orc.FMT_MXFP4, M, N, K, host(qa_rows.codes), host(qa_rows.scales), 1.0,
+                    host(qb.codes), host(qb.scales), 1.0)
+    check_gemm(got, C, S, out, f"kpanel both {shape} {out}")

@@ -97,3 +97,38 @@ def test_gemm_of_rotated_operands(fmt):
     exact = synth.bf16_to_f32(A).astype(np.float64) @ synth.bf16_to_f32(B).astype(np.float64).T
     rel = np.linalg.norm(C - exact) / np.linalg.norm(exact)
     assert rel < (0.2 if fmt == "mxfp4" else 0.05), rel
+
+
+# ---- K-panel output (mx_quantize_ex with MX_LAYOUT_KPANEL) --------------------
+
+@pytest.mark.parametrize("rule,rot", [("ceil", None), ("oas", None), ("ceil", "wht32"), ("oas", "wht32")])
+@pytest.mark.parametrize("rows,cols", [(1, 256), (37, 768), (300, 4096), (64, 12288)])
+def test_kpanel_output_is_the_packed_row_output(rows, cols, rule, rot):
+    """The quantizer's K-panel output equals the oracle's codes and scales
+    re-laid by the layout's definition, bit for bit (rows not a multiple of
+    the kernel's 32-row groups included)."""
+    bits = synth.laplace_outlier_channels((rows, cols), seed=701 + rows, channel_seed=702,
+                                          frac=0.01, factor=100.0)
+    q = mx.quantize(dev_bf16(bits), "mxfp4", scale_rule=rule, rotation=rot, layout="kpanel")
+    assert q.layout == mx.MX_LAYOUT_KPANEL
+    oc, os_ = orc.quantize_ex(orc.FMT_MXFP4, bits, RULE[rule], ROT[rot])
+    pc, ps = orc.pack_kpanel(oc, os_, rows, cols)
+    assert np.array_equal(host(q.codes).reshape(-1), pc)
+    assert np.array_equal(host(q.scales).reshape(-1), ps)
+
+
+def test_kpanel_specials():
+    """Zero, -0, subnormal, Inf and NaN blocks in the K-panel output."""
+    g = np.random.Generator(np.random.PCG64(711))
+    bits = synth.bf16_bits(g.normal(0, 1, (8, 512)))
+    bits[0, :32] = 0
+    bits[1, 32:64] = 0x8000
+    bits[2, 64:96] = g.integers(1, 0x80, 32).astype(np.uint16)
+    bits[3, 300] = 0x7F80
+    bits[4, 500] = 0xFFC0
+    bits[5, :] = 0x7F7F
+    q = mx.quantize(dev_bf16(bits), "mxfp4", layout="kpanel")
+    oc, os_, _ = orc.quantize(orc.FMT_MXFP4, bits)
+    pc, ps = orc.pack_kpanel(oc, os_, 8, 512)
+    assert np.array_equal(host(q.codes).reshape(-1), pc)
+    assert np.array_equal(host(q.scales).reshape(-1), ps)
