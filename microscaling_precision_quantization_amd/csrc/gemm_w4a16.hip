@@ -54,10 +54,6 @@ constexpr int kALoads = TM * KP / 8 / kThreads;  // 16-byte activation loads per
 constexpr uint32_t kRsrcFlags = 0x00020000u;     // raw buffer, gfx9 data format
 constexpr uint32_t kOOB = 0x80000000u;           // an offset past every buffer's range
 
-__device__ __forceinline__ float e8m0_to_float(uint32_t E) {
-  return __builtin_bit_cast(float, E == 0 ? 0x00400000u : E << 23);
-}
-
 // 8 codes (one dword) -> 8 bf16 times 2^(E-127).
 __device__ __forceinline__ bf16x8 expand8(uint32_t q, float s) {
   u32x4 o;
@@ -115,8 +111,11 @@ __device__ __forceinline__ void compute_half(const u32x4 (&q)[kHalf], const u32x
   for (int j = 0; j < 4; j++) ab[j] = arow + (((4 * g + j) ^ r) * 16);
 #pragma unroll
   for (int i = 0; i < kHalf; i++) {
+    // The scaled converts read only the exponent field of their scale, so
+    // the E8M0 byte placed in that field scales by 2^(E-127) for every E,
+    // E = 0 included (no special case for the fp32 subnormal 2^-127).
     const uint32_t E = (sc[i / 4][i % 4] >> (8 * g)) & 0xFFu;
-    const float scale = e8m0_to_float(E);
+    const float scale = __builtin_bit_cast(float, E << 23);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const bf16x8 a = *(const bf16x8*)(ab[j] + 256 * (kHalf * u + i));

@@ -125,6 +125,57 @@ def test_w4a16_nan_weight_blocks(out):
     _full_check("w4a16", A, B, out, "w4a16 nan")
 
 
+def _bottom_of_range_rows(X, rows, seed):
+    """Rows at the bottom of the E8M0 range: rows[0] all blocks at E = 0
+    (each block's maximum 1.25 * 2^-125), rows[1] blocks cycling through
+    E = 0 .. 3, rows[2] one E = 0 block among ordinary ones. Bits are bf16;
+    fp32 and bf16 subnormals included."""
+    g = synth.rng(seed)
+    K = X.shape[1]
+    X = X.copy()
+    for r, spread in ((rows[0], 0), (rows[1], 4)):
+        v = g.uniform(-1.25, 1.25, K)
+        v[::32] = 1.25
+        X[r] = synth.bf16_bits(v * 2.0 ** (-125 + (np.arange(K) // 32) % max(spread, 1)))
+    v = g.uniform(-1.25, 1.25, 32)
+    v[0] = -1.25
+    X[rows[2], 96:128] = synth.bf16_bits(v * 2.0**-125)
+    return X
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8", "w4a16"])
+def test_bottom_of_e8m0_range(fmt):
+    """Weight (and, for W4A4/W8A8, activation) blocks whose E8M0 scale is 0,
+    i.e. 2^-127, and 1 .. 3. The bound adds the underflow floor of the
+    kernel's number formats: each fp32 operation may lose up to 2^-150 in
+    the subnormal range (K * 2^-149 over a dot product), and the bf16
+    expansion of an E4M3 code times 2^-127 rounds to the bf16 subnormal grid
+    (spacing 2^-133), so the MXFP8 path may lose 2^-134 * sum_k |a_k| more."""
+    M, N, K = 40, 48, 1024
+    A = synth.normal((M, K), 1.0, 51)
+    B = _bottom_of_range_rows(synth.normal((N, K), 0.02, 52), (7, 8, 9), 53)
+    if fmt != "w4a16":
+        A = _bottom_of_range_rows(A, (5, 6, 11), 54)
+    hostops, qa, qb = _operands(fmt, A, B)
+    fa, fb, a, sa, ta, b, sb, tb = hostops
+    # The rows were built to reach the bottom of the scale range (E4M3's
+    # larger emax puts all of row 8 at E = 0 for MXFP8).
+    spread = {0} if fmt == "mxfp8" else {0, 1, 2, 3}
+    assert np.all(sb[7] == 0) and sb[9, 3] == 0 and set(np.unique(sb[8]).tolist()) == spread
+    C, S = orc.gemm(fa, fb, M, N, K, a, sa, ta, b, sb, tb)
+    got = _run(qa, qb, "f32").astype(np.float64)
+    floor = K * 2.0**-149
+    if fmt == "mxfp8":
+        asum = np.abs(orc.dequantize(fa, a, sa, 1.0, M, K).astype(np.float64)).sum(axis=1)
+        floor = floor + 2.0**-134 * asum[:, None]
+    err = np.abs(got - C)
+    tol = 2.0**-18 * S + floor
+    assert np.all(err <= tol), f"{fmt}: worst err/tol {np.max(err / tol):.3g} at {np.unravel_index(np.argmax(err / tol), err.shape)}"
+    # Columns 7 .. 9 are nonzero and, away from the tiny activation rows, far
+    # above the floor: the tiny blocks contribute rather than flush to zero.
+    assert np.all(np.abs(got[:4, 7:10]) > 0)
+
+
 # Full-size workloads: the whole output is computed on the GPU; a seeded sample
 # of entries (with every corner and the ragged last tile row/column) is checked
 # against the oracle one by one.
