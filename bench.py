@@ -293,6 +293,7 @@ def cpu_baseline(name, fmt, A_bits, qb, M, N, K, rows, variant):
     bcodes = qb.codes.cpu().numpy()
     bscales = qb.scales.cpu().numpy()
     bts = float(qb.tensor_scale.cpu().numpy()[0]) if qb.tensor_scale is not None else 1.0
+    rows = min(rows, M)
     a = np.ascontiguousarray(A_bits[:rows])
     t0 = time.perf_counter()
     if ofmt == orc.FMT_BF16:

@@ -224,24 +224,40 @@ def dequantize(fmt, codes, scales, tensor_scale, rows, cols, out=OUT_F32):
     """Returns float32 [rows][cols] (OUT_F32) or uint16 bf16 bits (OUT_BF16)."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    if cols % BLOCK[fmt] == 0:
+        _need(codes, int(np.prod(code_shape(fmt, rows, cols))), "codes")
+        _need(scales, int(np.prod(scale_shape(fmt, rows, cols))), "scales")
     y = np.zeros((rows, cols), np.float32 if out == OUT_F32 else np.uint16)
     _check(lib().mxo_dequantize(fmt, BLOCK[fmt], rows, cols, _ptr(codes), _ptr(scales),
                                 float(tensor_scale), out, _ptr(y)), "dequantize")
     return y
 
 
-def _gemm_operands(fmt, data, scales):
+def _need(arr, n, what):
+    """The C routines read exactly n elements: refuse any other size."""
+    if arr.size != n:
+        raise ValueError(f"oracle: {what} holds {arr.size} elements, the shape needs {n}")
+
+
+def _gemm_operands(fmt, data, scales, rows, K):
     if fmt == FMT_BF16:
-        return np.ascontiguousarray(data, dtype=np.uint16), None
-    return (np.ascontiguousarray(data, dtype=np.uint8),
-            np.ascontiguousarray(scales, dtype=np.uint8))
+        data = np.ascontiguousarray(data, dtype=np.uint16)
+        _need(data, rows * K, "bf16 operand")
+        return data, None
+    if K % BLOCK[fmt] != 0:
+        raise ValueError(f"oracle: K = {K} is not a multiple of the block size {BLOCK[fmt]}")
+    data = np.ascontiguousarray(data, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    _need(data, int(np.prod(code_shape(fmt, rows, K))), "code operand")
+    _need(scales, int(np.prod(scale_shape(fmt, rows, K))), "scale operand")
+    return data, scales
 
 
 def gemm(fmt_a, fmt_b, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts):
     """Exact-operand GEMM in double. Returns (C, S), each float64 [M][N], with
     S = sum_k |a_ik * b_jk|. B is stored N x K."""
-    a, a_scales = _gemm_operands(fmt_a, a, a_scales)
-    b, b_scales = _gemm_operands(fmt_b, b, b_scales)
+    a, a_scales = _gemm_operands(fmt_a, a, a_scales, M, K)
+    b, b_scales = _gemm_operands(fmt_b, b, b_scales, N, K)
     C = np.zeros((M, N), np.float64)
     S = np.zeros((M, N), np.float64)
     _check(lib().mxo_gemm(fmt_a, fmt_b, M, N, K, _ptr(a), _ptr(a_scales), float(a_ts),
@@ -251,8 +267,8 @@ def gemm(fmt_a, fmt_b, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts):
 
 def gemm_entries(fmt_a, fmt_b, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts, ii, jj):
     """As gemm(), only for output entries (ii[t], jj[t]). Returns (C, S) 1-D."""
-    a, a_scales = _gemm_operands(fmt_a, a, a_scales)
-    b, b_scales = _gemm_operands(fmt_b, b, b_scales)
+    a, a_scales = _gemm_operands(fmt_a, a, a_scales, M, K)
+    b, b_scales = _gemm_operands(fmt_b, b, b_scales, N, K)
     ii = np.ascontiguousarray(ii, dtype=np.int64)
     jj = np.ascontiguousarray(jj, dtype=np.int64)
     C = np.zeros(len(ii), np.float64)

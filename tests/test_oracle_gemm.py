@@ -112,6 +112,15 @@ def test_gemm_rejects_bad_arguments(orc):
     with pytest.raises(ValueError):
         orc.gemm_entries(orc.FMT_MXFP4, orc.FMT_MXFP4, 4, 4, 32, a, s, 1.0, a, s, 1.0,
                          np.array([4]), np.array([0]))
+    # Operands shorter than M, N, K imply are refused before the C code reads
+    # past them (here A holds 4 rows of a claimed 8; a bf16 A of 4 rows).
+    with pytest.raises(ValueError):
+        orc.gemm(orc.FMT_MXFP4, orc.FMT_MXFP4, 8, 4, 32, a, s, 1.0, a, s, 1.0)
+    with pytest.raises(ValueError):
+        orc.gemm(orc.FMT_BF16, orc.FMT_MXFP4, 8, 4, 32, np.zeros((4, 32), np.uint16), None, 1.0,
+                 a, s, 1.0)
+    with pytest.raises(ValueError):
+        orc.dequantize(orc.FMT_MXFP4, a, s, 1.0, 8, 32)
 
 
 def test_pack_kpanel_brute_force(orc):
