@@ -7,7 +7,10 @@ MXFP4 (codes + E8M0 scales) and run the block-scaled GEMM against the
 pre-quantized weights, bf16 output (MXFP4 operands in the K-panel layout:
 weights re-laid once by mx_pack, activations quantized straight into it).
 Everything in the timed region runs in
-libmx's HIP kernels; inputs are resident in HBM before timing starts.
+libmx's HIP kernels; inputs are resident in HBM before timing starts. After
+the warm-up steps the same steps are replayed, untimed, for RAMP_S seconds:
+the GPU raises its clocks only after tens of milliseconds of continuous load,
+and the timed steps should see the clocks a sustained workload runs at.
 
 Prints one JSON line. `value` is whole-step throughput, 2MNK / step time, in
 TFLOP/s. The `roofline` object is for the dominant kernel (the GEMM), timed
@@ -21,6 +24,7 @@ the headline metric is quoted on.
 import argparse
 import dataclasses
 import json
+import math
 import os
 import sys
 import time
@@ -43,6 +47,7 @@ PEAK_TFLOPS = {"mxfp4": 10100.0, "mxfp8": 5000.0, "nvfp4": 2500.0, "w4a16": 2500
 # output element per 128 K), so it is measured against this.
 PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 ROTATE_BYTES = 1 << 30  # activation copies cycled per step: > 256 MB MALL
+RAMP_S = 0.2  # seconds of untimed replays before timing (GPU clock ramp)
 WEIGHT_ROTATE_BYTES = 512 << 20  # weight copies cycled per step: > 256 MB MALL, so
                                  # every step streams its weights from HBM, as the
                                  # layers of a model would
@@ -163,6 +168,17 @@ def main():
     graph.replay()
     torch.cuda.synchronize()
     graph_out = out.clone()
+    # Clock ramp: the GPU raises its clocks only after tens of milliseconds of
+    # continuous load (measured: the c4 step takes ~122 us right after a short
+    # warm-up, ~107 us in steady state, and ~125 us again after 2 s idle), so
+    # replay the same steps, untimed, for at least RAMP_S before timing.
+    t_ramp = time.perf_counter()
+    ramp_replays = 0
+    while time.perf_counter() - t_ramp < RAMP_S:
+        graph.replay()
+        ramp_replays += 1
+        torch.cuda.synchronize()
+    ramp_s = time.perf_counter() - t_ramp
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -172,8 +188,12 @@ def main():
     ms_per_step = start.elapsed_time(end) / args.steps
 
     # Per-kernel times: the same K steps run eagerly, each launch bracketed by
-    # HIP events on the stream it runs on.
+    # HIP events on the stream it runs on. Graph replays queued first keep the
+    # GPU busy for at least 20 ms while the host enqueues those launches, so
+    # the GPU runs them back to back and no host gap lands inside a bracket.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for _ in range(max(1, math.ceil(20.0 / (ms_per_step * args.steps)))):
+        graph.replay()
     start.record(stream)
     for i in range(args.steps):
         step(i, evs[i])
@@ -240,8 +260,10 @@ def main():
                    "activation_copies_rotated": len(acts),
                    "weight_copies_rotated": len(weights)},
         "timing": {"ms_per_step": "HIP-graph replay of the timed steps",
+                   "clock_ramp": f"{ramp_replays} untimed replays of the {args.steps} steps "
+                                 f"({ramp_s * 1e3:.0f} ms) after the {args.warmup} warm-up steps",
                    "eager_ms_per_step": eager_ms_per_step,
-                   "kernel_ms": "HIP events around each launch in an eager pass of the same steps",
+                   "kernel_ms": "HIP events around each launch in an eager pass of the same steps, enqueued behind graph replays so that they run back to back",
                    "graph_output_matches_eager": graph_matches_eager},
         "roofline": roof,
         "gemm": {"TFLOP/s": gemm_tflops, "ms": g_avg, "frac_of_peak": gemm_tflops / peak},
