@@ -60,6 +60,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="c4")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--ramp-s", type=float, default=RAMP_S,
+                   help="seconds of untimed replays between the warm-up and the timed steps")
     p.add_argument("--cpu-rows", type=int, default=640,
                    help="activation rows in the oracle's CPU sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -174,7 +176,7 @@ def main():
     # replay the same steps, untimed, for at least RAMP_S before timing.
     t_ramp = time.perf_counter()
     ramp_replays = 0
-    while time.perf_counter() - t_ramp < RAMP_S:
+    while time.perf_counter() - t_ramp < args.ramp_s:
         graph.replay()
         ramp_replays += 1
         torch.cuda.synchronize()
