@@ -90,8 +90,9 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the kernels "
-              "and their measurement are single-GPU in this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the kernels "
+              "and their measurement cover one GPU's share; sharding over several GPUs is "
+              "not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
