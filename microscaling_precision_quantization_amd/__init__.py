@@ -181,11 +181,38 @@ class QTensor:
         return BLOCK[self.fmt]
 
 
+def _check_qtensor(q, what):
+    """The kernels read exactly the bytes a QTensor's shape implies: refuse
+    buffers of another size, type or layout in memory."""
+    import torch
+    if q.fmt not in BLOCK or q.fmt == MX_FMT_BF16 or q.cols % BLOCK[q.fmt] != 0:
+        raise ValueError(f"{what}: not a quantized tensor of a supported format")
+    need_c = q.rows * code_cols(q.fmt, q.cols)
+    need_s = 1
+    for d in scale_shape(q.fmt, q.rows, q.cols):
+        need_s *= d
+    for t, n, name in ((q.codes, need_c, "codes"), (q.scales, need_s, "scales")):
+        if t.dtype != torch.uint8 or not t.is_contiguous() or t.numel() != n:
+            raise ValueError(f"{what}: {name} must be a contiguous uint8 tensor of {n} bytes")
+    if q.fmt == MX_FMT_NVFP4:
+        ts = q.tensor_scale
+        if ts is None or ts.dtype != torch.float32 or ts.numel() < 1:
+            raise ValueError(f"{what}: NVFP4 needs a float32 tensor scale")
+
+
 def _fmt_id(fmt):
     return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
 
 
-def _stream(torch, device):
+def _stream(torch, device, *tensors):
+    """The current stream of `device`, after checking that the device is a GPU
+    and that every tensor handed to the kernels lives on it (a host or
+    foreign-device pointer must never reach a kernel)."""
+    if device.type != "cuda":
+        raise ValueError(f"libmx runs on GPU tensors; got a tensor on {device}")
+    for t in tensors:
+        if t is not None and t.device != device:
+            raise ValueError(f"all tensors must be on {device}; got one on {t.device}")
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
@@ -219,7 +246,7 @@ def quantize(x, fmt, scale_rule="ceil", rotation=None, layout="rows"):
         codes = torch.empty((rows, code_cols(f, cols)), dtype=torch.uint8, device=x.device)
         scales = torch.empty(scale_shape(f, rows, cols), dtype=torch.uint8, device=x.device)
         _check(mx_quantize_ex(f, BLOCK[f], MX_ROUND_RNE, SCALE_RULES[scale_rule], ROTATIONS[rotation], rows,
-                              cols, _ptr(x), _ptr(codes), _ptr(scales), _stream(torch, x.device), lay),
+                              cols, _ptr(x), _ptr(codes), _ptr(scales), _stream(torch, x.device, x), lay),
                "mx_quantize_ex")
         return QTensor(f, rows, cols, codes, scales, None, lay)
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
@@ -235,21 +262,24 @@ def quantize(x, fmt, scale_rule="ceil", rotation=None, layout="rows"):
         wsb = mx_quantize_workspace_bytes(f, rows, cols)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     _check(mx_quantize(f, BLOCK[f], MX_ROUND_RNE, rows, cols, _ptr(x), _ptr(codes), _ptr(scales),
-                       _ptr(ts), _ptr(ws), wsb, _stream(torch, dev)), "mx_quantize")
+                       _ptr(ts), _ptr(ws), wsb, _stream(torch, dev, x)), "mx_quantize")
     return QTensor(f, rows, cols, codes, scales, ts)
 
 
 def dequantize(q, out_dtype=None):
     """Expand a QTensor (row layout) to float32 (default) or bfloat16."""
     import torch
+    _check_qtensor(q, "dequantize")
     if q.layout != MX_LAYOUT_ROWS:
         raise ValueError("dequantize takes a tensor in the row layout")
     out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
     od = MX_OUT_F32 if out_dtype == torch.float32 else MX_OUT_BF16
     y = torch.empty((q.rows, q.cols), dtype=out_dtype, device=q.codes.device)
     _check(mx_dequantize(q.fmt, q.block, MX_ROUND_RNE, q.rows, q.cols, _ptr(q.codes),
                          _ptr(q.scales), _ptr(q.tensor_scale), od, _ptr(y),
-                         _stream(torch, q.codes.device)), "mx_dequantize")
+                         _stream(torch, q.codes.device, q.codes, q.scales, q.tensor_scale)), "mx_dequantize")
     return y
 
 
@@ -259,10 +289,11 @@ def pack(q):
     import torch
     if q.layout != MX_LAYOUT_ROWS:
         raise ValueError("pack() takes a tensor in the row layout")
+    _check_qtensor(q, "pack")
     codes = torch.empty_like(q.codes)
     scales = torch.empty_like(q.scales)
     _check(mx_pack(q.fmt, q.block, q.rows, q.cols, _ptr(q.codes), _ptr(q.scales), _ptr(codes),
-                   _ptr(scales), _stream(torch, q.codes.device)), "mx_pack")
+                   _ptr(scales), _stream(torch, q.codes.device, q.codes, q.scales)), "mx_pack")
     return QTensor(q.fmt, q.rows, q.cols, codes, scales, q.tensor_scale, MX_LAYOUT_KPANEL)
 
 
@@ -272,8 +303,12 @@ def gemm(a, b, out_dtype=None, out=None, workspace=None):
     K-panel layout)."""
     import torch
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
     od = MX_OUT_F32 if out_dtype == torch.float32 else MX_OUT_BF16
+    _check_qtensor(b, "gemm operand b")
     if isinstance(a, QTensor):
+        _check_qtensor(a, "gemm operand a")
         fa, M, K = a.fmt, a.rows, a.cols
         pa, psa, pta = _ptr(a.codes), _ptr(a.scales), _ptr(a.tensor_scale)
         dev = a.codes.device
@@ -286,17 +321,27 @@ def gemm(a, b, out_dtype=None, out=None, workspace=None):
     N = b.rows
     if b.cols != K:
         raise ValueError(f"K mismatch: A has {K}, B has {b.cols}")
+    if out is not None:
+        if (out.dtype != out_dtype or out.dim() != 2 or tuple(out.shape) != (M, N)
+                or out.stride(1) != 1):
+            raise ValueError(f"out must be a [{M}][{N}] {out_dtype} tensor with unit column stride")
     c = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=dev)
     wsb = mx_gemm_workspace_bytes(fa, b.fmt, M, N, K)
     if wsb and workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        wsb = workspace.numel() * workspace.element_size()  # the C call checks it is enough
     la = a.layout if isinstance(a, QTensor) else MX_LAYOUT_ROWS
+    a_parts = (a.codes, a.scales, a.tensor_scale) if isinstance(a, QTensor) else (a,)
+    stream = _stream(torch, dev, *a_parts, b.codes, b.scales, b.tensor_scale, c, workspace)
     if la != MX_LAYOUT_ROWS or b.layout != MX_LAYOUT_ROWS:
         _check(mx_gemm_ex(fa, b.fmt, b.block, MX_ROUND_RNE, M, N, K, pa, psa, pta, _ptr(b.codes),
                           _ptr(b.scales), _ptr(b.tensor_scale), od, _ptr(c), c.stride(0),
-                          _ptr(workspace), wsb, _stream(torch, dev), la, b.layout), "mx_gemm_ex")
+                          _ptr(workspace), wsb, stream, la, b.layout), "mx_gemm_ex")
         return c
     _check(mx_gemm(fa, b.fmt, b.block, MX_ROUND_RNE, M, N, K, pa, psa, pta, _ptr(b.codes),
                    _ptr(b.scales), _ptr(b.tensor_scale), od, _ptr(c), c.stride(0),
-                   _ptr(workspace), wsb, _stream(torch, dev)), "mx_gemm")
+                   _ptr(workspace), wsb, stream), "mx_gemm")
     return c
