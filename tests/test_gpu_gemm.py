@@ -275,6 +275,36 @@ def test_gemm_kpanel_b_workload_sampled():
     check_gemm(got[ii, jj], C, S, "bf16", "c4 kpanel")
 
 
+@pytest.mark.parametrize("wl", ["c4", "f1", "f4"])
+def test_bench_step_configuration_sampled(wl):
+    """The step bench.py times, at its full size and in its launch
+    configuration: the activations quantized on the GPU straight into K
+    panels (with the workload's scale rule and rotation), the weights
+    quantized (rotated the same way) and packed, bf16 output. Every code and
+    scale of both operands equals the oracle's in K-panel order; sampled
+    outputs (all corners and the last tile row and column among them) are
+    within the bound."""
+    w = synth.WORKLOADS[synth.ALIASES[wl]]
+    rule, rot = w.get("scale_rule", "ceil"), w.get("rotation")
+    A, B = workload(wl)
+    M, K = A.shape
+    N = B.shape[0]
+    qa = mx.quantize(dev_bf16(A), "mxfp4", scale_rule=rule, rotation=rot, layout="kpanel")
+    qb = mx.pack(mx.quantize(dev_bf16(B), "mxfp4", rotation=rot))
+    got = _run(qa, qb, "bf16")
+    orot = orc.ROT_WHT32 if rot == "wht32" else orc.ROT_NONE
+    a = orc.quantize_ex(orc.FMT_MXFP4, A, orc.RULE_OAS if rule == "oas" else orc.RULE_CEIL, orot)
+    b = orc.quantize_ex(orc.FMT_MXFP4, B, orc.RULE_CEIL, orot)
+    for q, (codes, scales), rows, what in ((qa, a, M, "A"), (qb, b, N, "B")):
+        pc, ps = orc.pack_kpanel(codes, scales, rows, K)
+        assert np.array_equal(host(q.codes).reshape(-1), pc), f"{wl}: {what} codes differ"
+        assert np.array_equal(host(q.scales).reshape(-1), ps), f"{wl}: {what} scales differ"
+    ii, jj = _sample(M, N, 2000, 19)
+    C, S = orc.gemm_entries(orc.FMT_MXFP4, orc.FMT_MXFP4, M, N, K, a[0], a[1], 1.0, b[0], b[1], 1.0,
+                            ii, jj)
+    check_gemm(got[ii, jj], C, S, "bf16", f"{wl} bench step")
+
+
 @pytest.mark.parametrize("shape", [(256, 256, 256), (300, 520, 768), (37, 1000, 4096)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_gemm_kpanel_both(shape, out):
