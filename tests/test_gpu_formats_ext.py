@@ -130,3 +130,28 @@ def test_quantize_then_gemm_bf16_out(fmt):
     f = ORC_FMT[fmt]
     C, S = orc.gemm(f, f, M, N, K, host(qa.codes), host(qa.scales), 1.0, host(qb.codes), host(qb.scales), 1.0)
     check_gemm(got, C, S, "bf16", f"{fmt} quantize+gemm")
+
+
+@pytest.mark.parametrize("wl,fmt", [("f2a", "mxfp8_e5m2"), ("f2b", "mxfp6_e3m2")])
+def test_bench_step_configuration_sampled(wl, fmt):
+    """The step bench.py times, at its full size (4608 x 9216 x 3072): both
+    operands quantized on the GPU, every code and scale equal to the
+    oracle's, then the GEMM with bf16 output, sampled outputs (all corners,
+    the last tile row and column) within the bound."""
+    A, B = synth.workload(wl)
+    M, K = A.shape
+    N = B.shape[0]
+    qa = mx.quantize(dev_bf16(A), fmt)
+    qb = mx.quantize(dev_bf16(B), fmt)
+    got = host(mx.gemm(qa, qb, torch.bfloat16).float())
+    f = ORC_FMT[fmt]
+    oa = orc.quantize(f, A)
+    ob = orc.quantize(f, B)
+    for q, o, what in ((qa, oa, "A"), (qb, ob, "B")):
+        assert np.array_equal(host(q.codes), o[0]), f"{wl}: {what} codes differ"
+        assert np.array_equal(host(q.scales), o[1]), f"{wl}: {what} scales differ"
+    g = np.random.Generator(np.random.PCG64(23))
+    ii = np.concatenate([g.integers(0, M, 2000), [0, 0, M - 1, M - 1], np.full(16, M - 1), g.integers(0, M, 16)])
+    jj = np.concatenate([g.integers(0, N, 2000), [0, N - 1, 0, N - 1], g.integers(0, N, 16), np.full(16, N - 1)])
+    C, S = orc.gemm_entries(f, f, M, N, K, oa[0], oa[1], 1.0, ob[0], ob[1], 1.0, ii, jj)
+    check_gemm(got[ii, jj], C, S, "bf16", f"{wl} bench step")
