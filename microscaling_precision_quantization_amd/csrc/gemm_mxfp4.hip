@@ -223,6 +223,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, void* __restrict__ C, int64_t ldc, int M, int N, int K,
     int tiles_m, int tiles_n) {
+  // Both operands in K panels (the layout of the benchmarked step): two
+  // register stages fit without spills in the loop; the other layouts keep one.
+  constexpr bool DEEP = PANEL_A && PANEL_B;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -249,34 +252,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
   const int nsteps = K / kSuperK;
-  // Three-deep pipeline: LDS buffer s & 1 feeds the MFMAs, LDS buffer
-  // (s + 1) & 1 receives super-step s + 1 from registers, and the registers
-  // receive super-step s + 2 from memory while the MFMAs run.
-  Stage R;
-  load_part<0, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, A, SA, M, B, SB, N);
-  load_part<1, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, A, SA, M, B, SB, N);
-  load_part<2, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, A, SA, M, B, SB, N);
-  load_part<3, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, A, SA, M, B, SB, N);
-  store_part<0>(R, smem, wave, lane);
-  store_part<1>(R, smem, wave, lane);
-  store_part<2>(R, smem, wave, lane);
-  store_part<3>(R, smem, wave, lane);
-  {
-    // Issued in the loop's order (the fences keep the scheduler from
-    // reordering them), so that the in-order load counter lets the loop's
-    // first LDS writes wait only for their own part.
-    const int s1 = min(1, nsteps - 1);
-    sched_fence();
-    load_part<0, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, A, SA, M, B, SB, N);
-    sched_fence();
-    load_part<1, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, A, SA, M, B, SB, N);
-    sched_fence();
-    load_part<2, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, A, SA, M, B, SB, N);
-    sched_fence();
-    load_part<3, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, A, SA, M, B, SB, N);
-    sched_fence();
-  }
-  for (int s = 0; s < nsteps; s++) {
+  // One super-step: MFMAs on LDS buffer s & 1 while the registers Rx (super-
+  // step s + 1) go to LDS buffer (s + 1) & 1 and then receive super-step
+  // s + ahead from memory.
+  auto step = [&](int s, Stage& Rx, int ahead) {
     // Every wave's LDS writes of super-step s are done and every wave is done
     // reading super-step s-1, whose buffer receives super-step s+1 below. Only
     // LDS work is waited for: the global loads stay in flight.
@@ -286,7 +265,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
     uint8_t* nxt = smem + ((s + 1) & 1) * kStage;
     // Branch-free body (a branch here lets the compiler sink the MFMAs): the
     // last iterations re-stage the final super-step into the idle buffer.
-    const int s2 = min(s + 2, nsteps - 1);
+    // The registers Rx hold super-step s + 1 and then receive s + ahead.
+    const int s2 = min(s + ahead, nsteps - 1);
     const uint8_t* As = cur;
     const uint8_t* Bs = cur + kTileBytes;
     const uint8_t* SAs = cur + 2 * kTileBytes;
@@ -305,24 +285,64 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
     load_frags<0>(As, Bs, wm, wn, r, g, f0);
     sched_fence();
     load_frags<1>(As, Bs, wm, wn, r, g, f1);
-    store_part<0>(R, nxt, wave, lane);
-    load_part<0, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
+    store_part<0>(Rx, nxt, wave, lane);
+    load_part<0, PANEL_A, PANEL_B>(Rx, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
     mfma_substep<0>(f0, sa, sb, acc);
     interleave<true>();
     load_frags<2>(As, Bs, wm, wn, r, g, f0);
-    store_part<1>(R, nxt, wave, lane);
-    load_part<1, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
+    store_part<1>(Rx, nxt, wave, lane);
+    load_part<1, PANEL_A, PANEL_B>(Rx, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
     mfma_substep<1>(f1, sa, sb, acc);
     interleave<true>();
     load_frags<3>(As, Bs, wm, wn, r, g, f1);
-    store_part<2>(R, nxt, wave, lane);
-    load_part<2, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
+    store_part<2>(Rx, nxt, wave, lane);
+    load_part<2, PANEL_A, PANEL_B>(Rx, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
     mfma_substep<2>(f0, sa, sb, acc);
     interleave<true>();
-    store_part<3>(R, nxt, wave, lane);
-    load_part<3, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
+    store_part<3>(Rx, nxt, wave, lane);
+    load_part<3, PANEL_A, PANEL_B>(Rx, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
     mfma_substep<3>(f1, sa, sb, acc);
     interleave<false>();
+  };
+  // Super-step 0 goes to LDS buffer 0 through the registers first.
+  Stage R[DEEP ? 2 : 1];
+  load_part<0, PANEL_A, PANEL_B>(R[0], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, A, SA, M, B, SB, N);
+  load_part<1, PANEL_A, PANEL_B>(R[0], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, A, SA, M, B, SB, N);
+  load_part<2, PANEL_A, PANEL_B>(R[0], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, A, SA, M, B, SB, N);
+  load_part<3, PANEL_A, PANEL_B>(R[0], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, A, SA, M, B, SB, N);
+  store_part<0>(R[0], smem, wave, lane);
+  store_part<1>(R[0], smem, wave, lane);
+  store_part<2>(R[0], smem, wave, lane);
+  store_part<3>(R[0], smem, wave, lane);
+  // Then the register stages are filled with super-steps 1 (and 2), issued in
+  // the loop's order (the fences keep the scheduler from reordering them), so
+  // that the in-order load counter lets the loop's first LDS writes wait only
+  // for their own part.
+#pragma unroll
+  for (int x = 0; x < (DEEP ? 2 : 1); x++) {
+    const int sx = min(1 + x, nsteps - 1);
+    sched_fence();
+    load_part<0, PANEL_A, PANEL_B>(R[x], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, sx, wave, lane, A, SA, M, B, SB, N);
+    sched_fence();
+    load_part<1, PANEL_A, PANEL_B>(R[x], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, sx, wave, lane, A, SA, M, B, SB, N);
+    sched_fence();
+    load_part<2, PANEL_A, PANEL_B>(R[x], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, sx, wave, lane, A, SA, M, B, SB, N);
+    sched_fence();
+    load_part<3, PANEL_A, PANEL_B>(R[x], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, sx, wave, lane, A, SA, M, B, SB, N);
+    sched_fence();
+  }
+  if (DEEP) {
+    // Four-deep pipeline: two register stages alternate, so every load has
+    // two super-steps to land.
+    int s = 0;
+    for (; s + 1 < nsteps; s += 2) {
+      step(s, R[0], 3);
+      step(s + 1, R[DEEP ? 1 : 0], 3);
+    }
+    if (s < nsteps) step(s, R[0], 3);
+  } else {
+    // Three-deep pipeline: one register stage, each load has one super-step.
+    for (int s = 0; s < nsteps; s++) step(s, R[0], 2);
   }
 
   // Epilogue: the stage buffers are free once every wave is past its loop.
