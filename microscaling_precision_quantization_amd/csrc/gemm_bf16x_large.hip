@@ -10,11 +10,11 @@
 //    one wave of a SIMD expands codes on the vector ALU, the other's MFMAs
 //    keep the matrix core busy (6% faster than 4 waves of 128 x 128 on NVFP4,
 //    2% on MXFP8).
-//  * K advances in stages of 64 elements. A stage moves through a three-deep
+//  * K advances in stages of 64 elements. A stage moves through a four-deep
 //    pipeline: global -> VGPRs (16-byte code chunks, range-checked buffer
-//    loads issued two stages ahead), VGPRs -> bf16 -> LDS (each code expanded
-//    once, one stage ahead, into the idle half of a 2 x 64 KB double buffer),
-//    LDS -> MFMA. The barrier between stages waits for LDS work only, so the
+//    loads issued three stages ahead into two alternating register stages),
+//    VGPRs -> bf16 -> LDS (each code expanded once, one stage ahead, into the
+//    idle half of a 2 x 64 KB double buffer), LDS -> MFMA. The barrier between stages waits for LDS work only, so the
 //    global loads stay in flight across it.
 //  * Expansion: MXFP8 to bf16 with v_cvt_scalef32_pk_bf16_fp8 (E4M3) or
 //    _bf8 (E5M2), MXFP6 with v_cvt_scalef32_pk32_bf16_bf6, the E8M0 scale
@@ -332,17 +332,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16x_large_kernel(
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
   const int nsteps = (K + BK - 1) / BK;
-  // Prologue: stage 0 to LDS, stage 1 in registers (issued in the loop's
-  // order so that the in-order load counter lets the loop's first expansions
-  // wait only for their own part).
-  Stage<FMT> R;
-  load_stage<FMT>(R, rA, rSA, rB, rSB, rowbytes, scalebytes, K, 0, tid);
-  store_part<FMT, 0>(R, smem, tid);
-  store_part<FMT, 1>(R, smem, tid);
-  store_part<FMT, 2>(R, smem, tid);
-  store_part<FMT, 3>(R, smem, tid);
-  load_stage<FMT>(R, rA, rSA, rB, rSB, rowbytes, scalebytes, K, min(1, nsteps - 1), tid);
-  for (int s = 0; s < nsteps; s++) {
+  // Four-deep pipeline: LDS buffer s & 1 feeds the MFMAs while one of two
+  // register stages (holding stage s + 1) is expanded into LDS buffer
+  // (s + 1) & 1 and then receives stage s + 3 from memory; the other holds
+  // s + 2. Every load has two stages to land (its few spilled registers are
+  // saved and restored outside the loop).
+  auto step = [&](int s, Stage<FMT>& Rx) {
     // Every thread's LDS writes of stage s are done and every wave is done
     // reading stage s-1, whose buffer receives stage s+1 below. Only LDS work
     // is waited for: the global loads stay in flight.
@@ -351,8 +346,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16x_large_kernel(
     const uint8_t* cur = smem + (s & 1) * kStage;
     uint8_t* nxt = smem + ((s + 1) & 1) * kStage;
     // Branch-free body (a branch lets the compiler sink the MFMAs): the last
-    // iterations re-stage the final stage into the idle buffer.
-    const int s2 = min(s + 2, nsteps - 1);
+    // iterations re-stage the final stage into the idle buffer. The registers
+    // Rx hold stage s + 1 and then receive stage s + 3.
+    const int s2 = min(s + 3, nsteps - 1);
     const uint8_t* As = cur;
     const uint8_t* Bs = cur + kTileBytes;
     // Operand elements: bf16 for the MX formats, fp16 for NVFP4.
@@ -361,27 +357,44 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16x_large_kernel(
     load_frags<0>(As, Bs, wm, wn, r, g, fa0, fb0);
     fence();
     // Sub-step 0: next fragments, expansion of chunk 0 of stage s+1, loads of
-    // chunk 0 of stage s+2, MFMAs. Likewise for the other sub-steps.
+    // chunk 0 of stage s+3, MFMAs. Likewise for the other sub-steps.
     load_frags<1>(As, Bs, wm, wn, r, g, fa1, fb1);
-    store_part<FMT, 0>(R, nxt, tid);
-    load_part<FMT, 0>(R, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
+    store_part<FMT, 0>(Rx, nxt, tid);
+    load_part<FMT, 0>(Rx, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
     mfma16(fa0, fb0, acc);
     region_order<FMT, true>();
     load_frags<2>(As, Bs, wm, wn, r, g, fa0, fb0);
-    store_part<FMT, 1>(R, nxt, tid);
-    load_part<FMT, 1>(R, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
+    store_part<FMT, 1>(Rx, nxt, tid);
+    load_part<FMT, 1>(Rx, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
     mfma16(fa1, fb1, acc);
     region_order<FMT, true>();
     load_frags<3>(As, Bs, wm, wn, r, g, fa1, fb1);
-    store_part<FMT, 2>(R, nxt, tid);
-    load_part<FMT, 2>(R, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
+    store_part<FMT, 2>(Rx, nxt, tid);
+    load_part<FMT, 2>(Rx, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
     mfma16(fa0, fb0, acc);
     region_order<FMT, true>();
-    store_part<FMT, 3>(R, nxt, tid);
-    load_part<FMT, 3>(R, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
+    store_part<FMT, 3>(Rx, nxt, tid);
+    load_part<FMT, 3>(Rx, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
     mfma16(fa1, fb1, acc);
     region_order<FMT, false>();
+  };
+  // Prologue: stage 0 to LDS, stages 1 and 2 in registers (issued in the
+  // loop's order so that the in-order load counter lets the loop's first
+  // expansions wait only for their own part).
+  Stage<FMT> R[2];
+  load_stage<FMT>(R[0], rA, rSA, rB, rSB, rowbytes, scalebytes, K, 0, tid);
+  store_part<FMT, 0>(R[0], smem, tid);
+  store_part<FMT, 1>(R[0], smem, tid);
+  store_part<FMT, 2>(R[0], smem, tid);
+  store_part<FMT, 3>(R[0], smem, tid);
+  load_stage<FMT>(R[0], rA, rSA, rB, rSB, rowbytes, scalebytes, K, min(1, nsteps - 1), tid);
+  load_stage<FMT>(R[1], rA, rSA, rB, rSB, rowbytes, scalebytes, K, min(2, nsteps - 1), tid);
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    step(s, R[0]);
+    step(s + 1, R[1]);
   }
+  if (s < nsteps) step(s, R[0]);
   __syncthreads();
   const float ts = (FMT == kNVFP4) ? TA[0] * TB[0] : 1.0f;
   tile256::store_tile<OUT, 2, kWavesN>(acc, smem, ts, C, ldc, M, N, m0, n0, wave, lane);
