@@ -14,10 +14,12 @@
 //    super-step (both code tiles and their scales, 68 KB) moves through a
 //    three-deep pipeline: global -> VGPRs (16-byte buffer loads, issued two
 //    super-steps ahead), VGPRs -> LDS (ds_write, one super-step ahead, into
-//    the idle half of a 2 x 68 KB double buffer), LDS -> MFMA. The barrier
-//    between super-steps waits for LDS work only, so global loads stay in
-//    flight across it and get a whole super-step to return. Buffer range
-//    checking returns zeros for rows past M or N.
+//    the idle half of a 2 x 68 KB double buffer), LDS -> MFMA. With both
+//    operands in K panels there are two register stages and the loads go
+//    three super-steps ahead (four-deep), which pays at sustained clocks.
+//    The barrier between super-steps waits for LDS work only, so global loads
+//    stay in flight across it. Buffer range checking returns zeros for rows
+//    past M or N.
 //  * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at slot
 //    c ^ ((r / 2) mod 8) so that the lanes reading one column of chunks hit
 //    distinct banks (measured with the LDS bank-conflict counter).
