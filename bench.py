@@ -189,6 +189,15 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
+    # Spread: four more timed replays of the same steps (reported beside the
+    # single timed pass that `value` comes from).
+    replay_ms = [ms_per_step]
+    for _ in range(4):
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        replay_ms.append(start.elapsed_time(end) / args.steps)
 
     # Per-kernel times: the same K steps run eagerly, each launch bracketed by
     # HIP events on the stream it runs on. Graph replays queued first keep the
@@ -265,6 +274,9 @@ def main():
         "timing": {"ms_per_step": "HIP-graph replay of the timed steps",
                    "clock_ramp": f"{ramp_replays} untimed replays of the {args.steps} steps "
                                  f"({ramp_s * 1e3:.0f} ms) after the {args.warmup} warm-up steps",
+                   "replays_ms_per_step": {"min": min(replay_ms),
+                                           "median": sorted(replay_ms)[len(replay_ms) // 2],
+                                           "max": max(replay_ms), "n": len(replay_ms)},
                    "eager_ms_per_step": eager_ms_per_step,
                    "kernel_ms": "HIP events around each launch in an eager pass of the same steps, enqueued behind graph replays so that they run back to back",
                    "graph_output_matches_eager": graph_matches_eager},
