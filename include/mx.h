@@ -56,12 +56,19 @@ typedef enum {
   MX_FMT_MXFP6_E3M2 = 5, /* E3M2 + E8M0 per 32; 6-bit codes, element i of a row
                             in bits 6i .. 6i+5 of the row's bytes (little-endian),
                             3 cols / 4 bytes per row */
-  MX_FMT_MXFP4_MBS = 6   /* MXFP4 with static macro-block scaling: E2M1 + E8M0
-                            per 32, plus one 8-bit macro mantissa m per 128
-                            (factor 1 + m/256); cols must be a multiple of 128.
-                            scales = two planes in one buffer: the E8M0 bytes
-                            [rows][cols/32], then the macro bytes
-                            [rows][cols/128] */
+  MX_FMT_MXFP4_MBS = 6,  /* MXFP4 with static macro-block scaling over MXFP4's
+                            own 32-element blocks (a reading: base block 32):
+                            E2M1 + E8M0 per 32, plus one 8-bit macro mantissa
+                            m per 128 (factor 1 + m/256); cols must be a
+                            multiple of 128. scales = two planes in one
+                            buffer: the E8M0 bytes [rows][cols/32], then the
+                            macro bytes [rows][cols/128] */
+  MX_FMT_MXFP4_MBS16 = 7 /* static macro-block scaling as the gist.science
+                            summary prints it (section 2.B): E2M1 codes, one
+                            E8M0 scale per 1 x 16 base block, one 8-bit macro
+                            mantissa per 1 x 128 (block 16, cols a multiple of
+                            128). scales = the E8M0 bytes [rows][cols/16],
+                            then the macro bytes [rows][cols/128] */
 } mx_format;
 
 typedef enum { MX_ROUND_RNE = 0 } mx_round; /* nearest, ties to even */
@@ -204,25 +211,43 @@ mx_status mx_dequantize(mx_format fmt, int block, mx_round rnd, int64_t rows, in
  *                       bf16 expansion on the bf16 MFMA, as for MXFP8 (these
  *                       need 256 * (bytes per code row) < 2^31, else
  *                       MX_ERR_INVALID_ARG)
- *   (MXFP4_MBS, MXFP4_MBS, 32)  K a multiple of 128: per macro block the FP4
- *                       scaled MFMA gives the E8M0-scaled partial sum P and
- *                       the vector ALU adds P * f_A * f_B (f_A f_B exact in
- *                       fp32) to the accumulator
+ *   (MXFP4_MBS, MXFP4_MBS, 32) and (MXFP4_MBS16, MXFP4_MBS16, 16)  K a
+ *                       multiple of 128: per macro block the FP4 scaled MFMA
+ *                       gives the E8M0-scaled partial sum P (for 16-element
+ *                       base blocks two MFMAs per 32 K, one per half) and the
+ *                       vector ALU adds P * f_A * f_B (f_A f_B exact in fp32)
+ *                       to the accumulator
  *   (BF16,  MXFP4, 32)  W4A16: bf16 activations times MXFP4 weights expanded
  *                       exactly to bf16 (weight-only quantization)
  * a: codes (or bf16 for MX_FMT_BF16) [M][...]; a_scales [M][K/block] (NULL for
- * BF16; for MXFP4_MBS the two-plane buffer of mx_quantize); a_ts, b_ts: NVFP4
- * tensor scales (device fp32), NULL otherwise.
- * b: codes [N][...]; b_scales [N][K/block] (two planes for MXFP4_MBS).
+ * BF16; for MXFP4_MBS / MBS16 the two-plane buffer of mx_quantize); a_ts,
+ * b_ts: NVFP4 tensor scales (device fp32), NULL otherwise.
+ * b: codes [N][...]; b_scales [N][K/block] (two planes for MXFP4_MBS / MBS16).
  * c: [M][ldc] fp32 or bf16 (rnd rounds the bf16 epilogue).
  * workspace: device scratch of at least mx_gemm_workspace_bytes(...) bytes
  * (may be NULL when that is 0).
- * K must be a multiple of 32 for every pair, and below 2^23 for W4A16 (its
- * kernel addresses a 448-row slab of weights with 32-bit offsets); larger
- * shapes return MX_ERR_INVALID_ARG. Accuracy: each fp32 output is
- * within 2^-18 * sum_k |a_ik b_jk| of the exact sum over the dequantized
- * operands (a bf16 output adds its own rounding), provided no product or
- * partial sum leaves fp32's range.
+ * K must be a multiple of 32 for every pair, and at most 65536 for W4A16;
+ * other shapes return MX_ERR_INVALID_ARG.
+ * Accuracy. With S_ij = sum_k |a_ik b_jk| over the dequantized operands, an
+ * fp32 output errs from the exact sum by at most (L + c + n - 1) * 2^-24 *
+ * S_ij: every fp32 step rounds once, the output's K is cut into n
+ * accumulator chains of at most L = 48 steps (matrix instructions; macro
+ * blocks for MBS; L = 32 and n = the K-splits of 2048 for W4A16) added in a
+ * fixed order, and c <= 4 counts the roundings inside one step (the partial
+ * sum of an MBS macro block; the NVFP4 tensor-scale product; W4A16's two
+ * chains per split). That is within 2^-18 * S_ij, the bound of the pages'
+ * target, even when every rounding goes the same way, for K <= 52224
+ * (MXFP4: chains of 3072 K), 13056 (MXFP8, E5M2, MXFP6: 768 K), 12288
+ * (NVFP4), 92160 (MBS: 6144 K), 79872 (MBS16) and 65536 (W4A16).
+ * A bf16 output rounds an fp32 value once more (within 2^-8 * |C_ij|); on the
+ * 256 x 256-tile kernels that value is one chain over all of K (K / 64 steps
+ * for MXFP4, K / 16 for the 16-bit paths, K / 128 for MBS), so before that
+ * rounding it errs by at most (steps + c) * 2^-24 * S_ij. Conditions: no
+ * product or partial sum leaves fp32's range; below 2^-126 each fp32 step may
+ * lose up to 2^-150 (K * 2^-149 in all); and for MXFP8 / E5M2 / MXFP6
+ * operands whose E8M0 byte is at most 2, e * 2^(E-127) must lie on the bf16
+ * grid (multiples of 2^-133) to be expanded exactly -- every code mx_quantize
+ * writes from bf16 input does.
  */
 mx_status mx_gemm(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd,
                   int64_t M, int64_t N, int64_t K,

@@ -62,3 +62,31 @@ def build(verbose=False):
 
 if __name__ == "__main__":
     print(build(verbose=True))
+
+
+SAN_OUT = os.path.join(BUILD, "libmx_hostsan.so")
+
+
+def build_host_sanitized():
+    """libmx with its host code (the C ABI: argument checks, dispatch, error
+    mapping) compiled by g++ under AddressSanitizer and
+    UndefinedBehaviorSanitizer, linked with the kernels' objects from build().
+    For CPU tests of the ABI only (loaded in a child process that preloads the
+    ASan runtime); written to _build/, never used by the GPU path."""
+    if not all(os.path.exists(os.path.join(BUILD, src + ".o")) for src in SOURCES):
+        build()
+    obj = os.path.join(BUILD, "mx_api_hostsan.o")
+    cxx = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-I" + os.path.join(ROOT, "include"),
+           "-c", os.path.join(CSRC, "mx_api.cpp"), "-o", obj]
+    r = subprocess.run(cxx, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("g++ failed for mx_api.cpp:\n" + r.stderr)
+    kernels = [os.path.join(BUILD, src + ".o") for src in SOURCES if src != "mx_api.cpp"]
+    link = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", obj, *kernels,
+            "-lasan", "-lubsan", "-o", SAN_OUT]
+    r = subprocess.run(link, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    return SAN_OUT

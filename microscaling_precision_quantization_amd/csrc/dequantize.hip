@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void dequant_mxfp8_kernel(const u32x2* __
 }
 
 // MXFP4-MBS: the MXFP4 value times the macro factor of its 128-element block.
-template <int OUT>
+template <int OUT, int BASE>
 __global__ __launch_bounds__(kThreads) void dequant_mbs_kernel(const uint32_t* __restrict__ codes,
                                                                const uint8_t* __restrict__ scales,
                                                                const uint8_t* __restrict__ macro,
@@ -113,7 +113,8 @@ __global__ __launch_bounds__(kThreads) void dequant_mbs_kernel(const uint32_t* _
   const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (c >= nchunks) return;
   const uint32_t q = codes[c];
-  const uint32_t E = scales[c >> 2];
+  // chunk c (8 elements) lies in base block c / 4 (BASE 32) or c / 2 (BASE 16)
+  const uint32_t E = scales[BASE == 32 ? (c >> 2) : (c >> 1)];
   const float f = (float)(256u + macro[c >> 4]) * 0x1p-8f;
   float o[8];
   if (E == 255) {
@@ -192,39 +193,45 @@ hipError_t dequant(int fmt, int64_t rows, int64_t cols, const void* codes, const
   const uint8_t* sc = (const uint8_t*)scales;
   if (fmt == kMXFP4) {
     if (out_dtype == kOutF32)
-      dequant_mxfp4_kernel<kOutF32><<<grid, kThreads, 0, s>>>((const uint32_t*)codes, sc, y, nchunks);
+      MX_TRY(launch_kernel(&dequant_mxfp4_kernel<kOutF32>, grid, kThreads, 0, s, (const uint32_t*)codes, sc, y, nchunks));
     else
-      dequant_mxfp4_kernel<kOutBF16><<<grid, kThreads, 0, s>>>((const uint32_t*)codes, sc, y, nchunks);
+      MX_TRY(launch_kernel(&dequant_mxfp4_kernel<kOutBF16>, grid, kThreads, 0, s, (const uint32_t*)codes, sc, y, nchunks));
   } else if (fmt == kMXFP8) {
     if (out_dtype == kOutF32)
-      dequant_mxfp8_kernel<kOutF32, false><<<grid, kThreads, 0, s>>>((const u32x2*)codes, sc, y, nchunks);
+      MX_TRY(launch_kernel(&dequant_mxfp8_kernel<kOutF32, false>, grid, kThreads, 0, s, (const u32x2*)codes, sc, y, nchunks));
     else
-      dequant_mxfp8_kernel<kOutBF16, false><<<grid, kThreads, 0, s>>>((const u32x2*)codes, sc, y, nchunks);
+      MX_TRY(launch_kernel(&dequant_mxfp8_kernel<kOutBF16, false>, grid, kThreads, 0, s, (const u32x2*)codes, sc, y, nchunks));
   } else if (fmt == kMXFP8E5M2) {
     if (out_dtype == kOutF32)
-      dequant_mxfp8_kernel<kOutF32, true><<<grid, kThreads, 0, s>>>((const u32x2*)codes, sc, y, nchunks);
+      MX_TRY(launch_kernel(&dequant_mxfp8_kernel<kOutF32, true>, grid, kThreads, 0, s, (const u32x2*)codes, sc, y, nchunks));
     else
-      dequant_mxfp8_kernel<kOutBF16, true><<<grid, kThreads, 0, s>>>((const u32x2*)codes, sc, y, nchunks);
+      MX_TRY(launch_kernel(&dequant_mxfp8_kernel<kOutBF16, true>, grid, kThreads, 0, s, (const u32x2*)codes, sc, y, nchunks));
   } else if (fmt == kMXFP4MBS) {
     const uint8_t* mac = sc + rows * (cols / 32);
     if (out_dtype == kOutF32)
-      dequant_mbs_kernel<kOutF32><<<grid, kThreads, 0, s>>>((const uint32_t*)codes, sc, mac, y, nchunks);
+      MX_TRY(launch_kernel(&dequant_mbs_kernel<kOutF32, 32>, grid, kThreads, 0, s, (const uint32_t*)codes, sc, mac, y, nchunks));
     else
-      dequant_mbs_kernel<kOutBF16><<<grid, kThreads, 0, s>>>((const uint32_t*)codes, sc, mac, y, nchunks);
+      MX_TRY(launch_kernel(&dequant_mbs_kernel<kOutBF16, 32>, grid, kThreads, 0, s, (const uint32_t*)codes, sc, mac, y, nchunks));
+  } else if (fmt == kMXFP4MBS16) {
+    const uint8_t* mac = sc + rows * (cols / 16);
+    if (out_dtype == kOutF32)
+      MX_TRY(launch_kernel(&dequant_mbs_kernel<kOutF32, 16>, grid, kThreads, 0, s, (const uint32_t*)codes, sc, mac, y, nchunks));
+    else
+      MX_TRY(launch_kernel(&dequant_mbs_kernel<kOutBF16, 16>, grid, kThreads, 0, s, (const uint32_t*)codes, sc, mac, y, nchunks));
   } else if (fmt == kMXFP6) {
     const int64_t nblocks = rows * cols / 32;
     const dim3 g6((unsigned)((nblocks + kThreads - 1) / kThreads));
     if (out_dtype == kOutF32)
-      dequant_mxfp6_kernel<kOutF32><<<g6, kThreads, 0, s>>>((const u32x2*)codes, sc, y, nblocks);
+      MX_TRY(launch_kernel(&dequant_mxfp6_kernel<kOutF32>, g6, kThreads, 0, s, (const u32x2*)codes, sc, y, nblocks));
     else
-      dequant_mxfp6_kernel<kOutBF16><<<g6, kThreads, 0, s>>>((const u32x2*)codes, sc, y, nblocks);
+      MX_TRY(launch_kernel(&dequant_mxfp6_kernel<kOutBF16>, g6, kThreads, 0, s, (const u32x2*)codes, sc, y, nblocks));
   } else {
     if (out_dtype == kOutF32)
-      dequant_nvfp4_kernel<kOutF32><<<grid, kThreads, 0, s>>>((const uint32_t*)codes, sc, tensor_scale, y, nchunks);
+      MX_TRY(launch_kernel(&dequant_nvfp4_kernel<kOutF32>, grid, kThreads, 0, s, (const uint32_t*)codes, sc, tensor_scale, y, nchunks));
     else
-      dequant_nvfp4_kernel<kOutBF16><<<grid, kThreads, 0, s>>>((const uint32_t*)codes, sc, tensor_scale, y, nchunks);
+      MX_TRY(launch_kernel(&dequant_nvfp4_kernel<kOutBF16>, grid, kThreads, 0, s, (const uint32_t*)codes, sc, tensor_scale, y, nchunks));
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace mx

@@ -34,6 +34,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kThreads = 256;
 constexpr int BM = 128, BN = 128, BK = 64;  // elements
 constexpr int kStride = BK * 2 + 16;         // bytes per LDS row of bf16 (padded)
+constexpr int kSegSteps = 24;                // K steps per accumulation chain (2 MFMAs each)
 
 __device__ __forceinline__ float e8m0_to_float(uint32_t E) {
   return __builtin_bit_cast(float, E == 0 ? 0x00400000u : E << 23);
@@ -130,11 +131,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16x_kernel(const uint8_t* __r
   const int srow = tid >> 1, shalf = tid & 1;
 
   Stage<FMT> sa, sb;
-  f32x4 acc[4][4];
+  f32x4 acc[4][4], tot[4][4];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0, 0, 0, 0};
+    for (int j = 0; j < 4; j++) acc[i][j] = tot[i][j] = f32x4{0, 0, 0, 0};
 
   const int r = lane & 15, g = lane >> 4;
   sa.load(A, SA, m0 + srow, M, K, 0, shalf);
@@ -162,6 +163,23 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16x_kernel(const uint8_t* __r
         for (int j = 0; j < 4; j++)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
+    // Accumulation chains of at most kSegSteps K steps (48 MFMAs), added
+    // into a running total (one fp32 rounding per segment).
+    if ((kt + 1) % kSegSteps == 0 && kt + 1 < nk) {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          tot[i][j] += acc[i][j];
+          acc[i][j] = f32x4{0, 0, 0, 0};
+        }
+    }
+  }
+  if (nk > kSegSteps) {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) acc[i][j] += tot[i][j];
   }
 
   const float ts = (FMT == kNVFP4) ? TA[0] * TB[0] : 1.0f;
@@ -185,13 +203,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16x_kernel(const uint8_t* __r
 }
 
 template <int FMT>
-void launch(const dim3& grid, hipStream_t s, const uint8_t* A, const uint8_t* SA, const float* TA,
+hipError_t launch(const dim3& grid, hipStream_t s, const uint8_t* A, const uint8_t* SA, const float* TA,
             const uint8_t* B, const uint8_t* SB, const float* TB, int out_dtype, void* c, int64_t ldc,
             int M, int N, int K) {
   if (out_dtype == kOutF32)
-    gemm_bf16x_kernel<FMT, kOutF32><<<grid, kThreads, 0, s>>>(A, SA, TA, B, SB, TB, c, ldc, M, N, K);
+    MX_TRY(launch_kernel(&gemm_bf16x_kernel<FMT, kOutF32>, grid, kThreads, 0, s, A, SA, TA, B, SB, TB, c, ldc, M, N, K));
   else
-    gemm_bf16x_kernel<FMT, kOutBF16><<<grid, kThreads, 0, s>>>(A, SA, TA, B, SB, TB, c, ldc, M, N, K);
+    MX_TRY(launch_kernel(&gemm_bf16x_kernel<FMT, kOutBF16>, grid, kThreads, 0, s, A, SA, TA, B, SB, TB, c, ldc, M, N, K));
+  return hipSuccess;
 }
 
 }  // namespace
@@ -205,10 +224,8 @@ hipError_t gemm_bf16x(int fmt, int64_t M, int64_t N, int64_t K, const void* a, c
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;
   if (fmt == kMXFP8)
-    launch<kMXFP8>(grid, s, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
-  else
-    launch<kNVFP4>(grid, s, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
-  return hipGetLastError();
+    return launch<kMXFP8>(grid, s, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
+  return launch<kNVFP4>(grid, s, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
 }
 
 }  // namespace mx

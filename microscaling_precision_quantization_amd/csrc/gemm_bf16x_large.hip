@@ -389,26 +389,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16x_large_kernel(
   store_part<FMT, 3>(R[0], smem, tid);
   load_stage<FMT>(R[0], rA, rSA, rB, rSB, rowbytes, scalebytes, K, min(1, nsteps - 1), tid);
   load_stage<FMT>(R[1], rA, rSA, rB, rSB, rowbytes, scalebytes, K, min(2, nsteps - 1), tid);
-  int s = 0;
-  for (; s + 1 < nsteps; s += 2) {
-    step(s, R[0]);
-    step(s + 1, R[1]);
-  }
-  if (s < nsteps) step(s, R[0]);
-  __syncthreads();
+  // fp32 output with more than kSeg stages: K in segments of kSeg stages (48
+  // MFMAs per chain), each folded into C (tile256::fold_tile); otherwise one
+  // chain. kSeg is even, so every segment but the last keeps the
+  // register-stage parity.
+  constexpr int kSeg = 12;
   const float ts = (FMT == kNVFP4) ? TA[0] * TB[0] : 1.0f;
+  auto run = [&](int s0, int s1) {
+    int s = s0;
+    for (; s + 1 < s1; s += 2) {
+      step(s, R[0]);
+      step(s + 1, R[1]);
+    }
+    if (s < s1) step(s, R[0]);
+  };
+  if constexpr (OUT == kOutF32) {
+    if (nsteps > kSeg) {
+      for (int s0 = 0; s0 < nsteps; s0 += kSeg) {
+        const int s1 = min(s0 + kSeg, nsteps);
+        run(s0, s1);
+        tile256::fold_tile<2, kWavesN>(acc, (float*)C, ldc, M, N, m0, n0, wave, lane, s0 == 0,
+                                       s1 == nsteps, ts);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
+      }
+      return;
+    }
+  }
+  run(0, nsteps);
+  __syncthreads();
   tile256::store_tile<OUT, 2, kWavesN>(acc, smem, ts, C, ldc, M, N, m0, n0, wave, lane);
 }
 
 template <int FMT>
-void launch(hipStream_t s, int tm, int tn, const uint8_t* A, const uint8_t* SA, const float* TA,
+hipError_t launch(hipStream_t s, int tm, int tn, const uint8_t* A, const uint8_t* SA, const float* TA,
             const uint8_t* B, const uint8_t* SB, const float* TB, int out_dtype, void* c,
             int64_t ldc, int M, int N, int K) {
   const dim3 grid((unsigned)(tm * tn));
   if (out_dtype == kOutF32)
-    gemm_bf16x_large_kernel<FMT, kOutF32><<<grid, kThreads, 0, s>>>(A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn);
+    MX_TRY(launch_kernel(&gemm_bf16x_large_kernel<FMT, kOutF32>, grid, kThreads, 0, s, A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn));
   else
-    gemm_bf16x_large_kernel<FMT, kOutBF16><<<grid, kThreads, 0, s>>>(A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn);
+    MX_TRY(launch_kernel(&gemm_bf16x_large_kernel<FMT, kOutBF16>, grid, kThreads, 0, s, A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn));
+  return hipSuccess;
 }
 
 }  // namespace
@@ -427,14 +453,12 @@ hipError_t gemm_bf16x_large(int fmt, int64_t M, int64_t N, int64_t K, const void
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;
   if (fmt == kMXFP8)
-    launch<kMXFP8>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
-  else if (fmt == kMXFP8E5M2)
-    launch<kMXFP8E5M2>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
-  else if (fmt == kMXFP6)
-    launch<kMXFP6>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
-  else
-    launch<kNVFP4>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
-  return hipGetLastError();
+    return launch<kMXFP8>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
+  if (fmt == kMXFP8E5M2)
+    return launch<kMXFP8E5M2>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
+  if (fmt == kMXFP6)
+    return launch<kMXFP6>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
+  return launch<kNVFP4>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
 }
 
 }  // namespace mx

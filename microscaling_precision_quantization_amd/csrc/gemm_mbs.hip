@@ -49,6 +49,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -58,15 +59,22 @@ constexpr int BM = 256, BN = 256;
 constexpr int kSuperK = 256;                        // elements per super-step
 constexpr int kRowBytes = kSuperK / 2;              // 128 code bytes per row
 constexpr int kOffB = BM * kRowBytes;               // 32 KB of A codes
-constexpr int kOffSA = kOffB + BN * kRowBytes;      // + 16 KB of B codes
-constexpr int kOffSB = kOffSA + BM * 8;             // + 2 KB of A scales (8 per row)
-constexpr int kOffFA = kOffSB + BN * 8;             // + 1 KB of B scales
-constexpr int kOffFB = kOffFA + 2 * BM * 4;         // + A factors / 2 [2][BM] (fp16 in a dword)
-constexpr int kStage = kOffFB + 2 * BN * 4;         // + B factors [2][BN] (fp16 in a dword)
-constexpr int kSmem = 2 * kStage;
+constexpr int kOffSA = kOffB + BN * kRowBytes;      // + 32 KB of B codes
+// Then, per stage, the E8M0 scales of A and B (kSB = 8 bytes per row and
+// super-step for 32-element base blocks, 16 for 16-element ones) and the
+// macro factors: A factors / 2 [2][BM], B factors [2][BN] (fp16 in a dword).
+template <int BASE>
+struct Lds {
+  static constexpr int kSB = kSuperK / BASE;
+  static constexpr int kOffSB = kOffSA + BM * kSB;
+  static constexpr int kOffFA = kOffSB + BN * kSB;
+  static constexpr int kOffFB = kOffFA + 2 * BM * 4;
+  static constexpr int kStage = kOffFB + 2 * BN * 4;
+  static constexpr int kSmem = 2 * kStage;
+  static_assert(kSmem >= 8 * 128 * (64 * 2 + 16), "epilogue staging must fit");
+  static_assert(kSmem <= 160 * 1024, "LDS");
+};
 constexpr uint32_t kRsrcFlags = 0x00020000u;        // raw buffer, gfx9 data format
-
-static_assert(kSmem >= 8 * 128 * (64 * 2 + 16), "epilogue staging must fit");
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
@@ -87,38 +95,49 @@ struct LaneOffsets {
   uint32_t code[2], scale;
 };
 
+template <int BASE>
 __device__ __forceinline__ LaneOffsets lane_offsets(int lane, uint32_t rowbytes, uint32_t scalebytes) {
   LaneOffsets o;
 #pragma unroll
   for (int par = 0; par < 2; par++)
     o.code[par] = (uint32_t)(lane >> 3) * rowbytes +
                   (uint32_t)(((lane & 7) ^ (((lane >> 4) + 4 * par) & 7)) * 16);
-  o.scale = (uint32_t)(lane >> 1) * scalebytes + (uint32_t)(lane & 1) * 4u;
+  // 4 bytes per lane: 2 lanes per row of 8 scale bytes, 4 per row of 16.
+  if (BASE == 32)
+    o.scale = (uint32_t)(lane >> 1) * scalebytes + (uint32_t)(lane & 1) * 4u;
+  else
+    o.scale = (uint32_t)(lane >> 2) * scalebytes + (uint32_t)(lane & 3) * 4u;
   return o;
 }
 
 // Part P (0..3) of the direct-to-LDS loads of super-step s: code block
-// 4 wave + P of A and of B (1 KB = 8 rows each), plus one 256-byte scale block
-// (32 rows x 8 bytes): A's for P = 0, B's for P = 1. `wave` is wave-uniform.
-template <int P>
+// 4 wave + P of A and of B (1 KB = 8 rows each), plus the scales of 32 rows
+// (8 or 16 bytes per row: one or two 256-byte loads of 4 bytes per lane):
+// A's for P = 0, B's for P = 1. `wave` is wave-uniform.
+template <int P, int BASE>
 __device__ __forceinline__ void issue_part(uint8_t* stage, __amdgpu_buffer_rsrc_t rA,
                                            __amdgpu_buffer_rsrc_t rB, __amdgpu_buffer_rsrc_t rSA,
                                            __amdgpu_buffer_rsrc_t rSB, const LaneOffsets& lo,
                                            uint32_t rowbytes, uint32_t scalebytes, int s, int wave) {
+  using L = Lds<BASE>;
   const uint32_t kb = (uint32_t)s * kRowBytes;
   const int b = wave * 4 + P;
   const uint32_t voff = lo.code[P & 1] + (uint32_t)(8 * b) * rowbytes;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(stage + b * 1024), 16, voff, (int)kb, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(stage + kOffB + b * 1024), 16, voff,
                                            (int)kb, 0, 0);
-  const uint32_t ks = (uint32_t)s * (kSuperK / 32);
+  const uint32_t ks = (uint32_t)s * L::kSB;
   const uint32_t soff = lo.scale + (uint32_t)(32 * wave) * scalebytes;
-  if (P == 0)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_ptr_t)(stage + kOffSA + wave * 256), 4, soff,
-                                             (int)ks, 0, 0);
-  if (P == 1)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (lds_ptr_t)(stage + kOffSB + wave * 256), 4, soff,
-                                             (int)ks, 0, 0);
+  // BASE 16: lane offsets cover 16 rows of 16 bytes per load, two loads.
+  constexpr int kLoads = L::kSB / 8;
+  if (P == 0 || P == 1) {
+    const __amdgpu_buffer_rsrc_t rS = (P == 0) ? rSA : rSB;
+    uint8_t* dst = stage + ((P == 0) ? kOffSA : L::kOffSB) + wave * 32 * L::kSB;
+#pragma unroll
+    for (int h = 0; h < kLoads; h++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(dst + h * 256), 4,
+                                               soff + (uint32_t)(16 * h) * scalebytes, (int)ks, 0, 0);
+  }
 }
 
 // Macro mantissas of super-step s (two bytes per row): waves 0..3 load A row
@@ -161,16 +180,44 @@ __device__ __forceinline__ void load_frags(const uint8_t* cur, int q, int wm, in
 }
 
 __device__ __forceinline__ i32x8 widen(i32x4 v) { return i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0}; }
+// The first 16 codes of a lane's 32 (bytes 0..7), or the last 16, the other
+// half zero.
+__device__ __forceinline__ i32x8 lo16(i32x4 v) { return i32x8{v.x, v.y, 0, 0, 0, 0, 0, 0}; }
+__device__ __forceinline__ i32x8 hi16(i32x4 v) { return i32x8{0, 0, v.z, v.w, 0, 0, 0, 0}; }
 
-// The two MFMAs of tile (i, j) in macro block Q: the block-scaled partial sum
-// over its 128 K, the first from zero.
-template <int Q>
-__device__ __forceinline__ f32x16 partial(const Frags& f, const int (&sa)[4], const int (&sb)[2],
-                                          int i, int j) {
+// A lane's E8M0 scale bytes for the super-step, byte J for sub-step J: for
+// 32-element base blocks one dword per row (a, b); for 16-element ones the
+// scale of the first 16 codes (a, b) and of the last 16 (a2, b2).
+struct Scales {
+  int a[4], b[2], a2[4], b2[2];
+};
+
+// The MFMAs of tile (i, j) in macro block Q: the block-scaled partial sum
+// over its 128 K, the first from zero. BASE 32: two MFMAs, each lane's 32
+// codes under one scale. BASE 16: the scaled MFMA takes one scale per lane's
+// 32 codes, so each 32 is split into two MFMAs over its halves (the other
+// half zero), each under its own 16-block scale -- exact, at twice the MFMAs.
+template <int Q, int BASE>
+__device__ __forceinline__ f32x16 partial(const Frags& f, const Scales& sc, int i, int j) {
+  if (BASE == 32) {
+    f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        widen(f.b[j][0]), widen(f.a[i][0]), f32x16{}, 4, 4, 2 * Q, sc.b[j], 2 * Q, sc.a[i]);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        widen(f.b[j][1]), widen(f.a[i][1]), p, 4, 4, 2 * Q + 1, sc.b[j], 2 * Q + 1, sc.a[i]);
+  }
+  // (fences: one zero-padded operand pair at a time, so the padded copies
+  // need few registers)
   f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-      widen(f.b[j][0]), widen(f.a[i][0]), f32x16{}, 4, 4, 2 * Q, sb[j], 2 * Q, sa[i]);
+      lo16(f.b[j][0]), lo16(f.a[i][0]), f32x16{}, 4, 4, 2 * Q, sc.b[j], 2 * Q, sc.a[i]);
+  sched_fence();
+  p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+      hi16(f.b[j][0]), hi16(f.a[i][0]), p, 4, 4, 2 * Q, sc.b2[j], 2 * Q, sc.a2[i]);
+  sched_fence();
+  p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+      lo16(f.b[j][1]), lo16(f.a[i][1]), p, 4, 4, 2 * Q + 1, sc.b[j], 2 * Q + 1, sc.a[i]);
+  sched_fence();
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-      widen(f.b[j][1]), widen(f.a[i][1]), p, 4, 4, 2 * Q + 1, sb[j], 2 * Q + 1, sa[i]);
+      hi16(f.b[j][1]), hi16(f.a[i][1]), p, 4, 4, 2 * Q + 1, sc.b2[j], 2 * Q + 1, sc.a2[i]);
 }
 
 // Macro block Q of the current super-step, tile by tile over the wave's 8
@@ -182,12 +229,11 @@ __device__ __forceinline__ f32x16 partial(const Frags& f, const int (&sa)[4], co
 // in flight per wave (fences keep the compiler from hoisting the next tile's
 // MFMAs, which would not fit in 256 registers); the SIMD's other wave fills
 // the wait between a tile's MFMAs and its ALU work.
-template <int Q>
-__device__ __forceinline__ void macro_step(const uint8_t* cur, const Frags& f, const int (&sa)[4],
-                                           const int (&sb)[2], int wm, int wn, int r,
-                                           f32x16 (&acc)[4][2]) {
-  const uint32_t* FA = (const uint32_t*)(cur + kOffFA) + Q * BM;
-  const uint32_t* FB = (const uint32_t*)(cur + kOffFB) + Q * BN;
+template <int Q, int BASE>
+__device__ __forceinline__ void macro_step(const uint8_t* cur, const Frags& f, const Scales& sc,
+                                           int wm, int wn, int r, f32x16 (&acc)[4][2]) {
+  const uint32_t* FA = (const uint32_t*)(cur + Lds<BASE>::kOffFA) + Q * BM;
+  const uint32_t* FB = (const uint32_t*)(cur + Lds<BASE>::kOffFB) + Q * BN;
   // The block's factor operands, read once (one dword per tile row).
   uint32_t fa[4], fb[2];
 #pragma unroll
@@ -202,7 +248,7 @@ __device__ __forceinline__ void macro_step(const uint8_t* cur, const Frags& f, c
     const f32x16 gk = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(f16x4, u32x2{fb[j], 0u}),
                                                             __builtin_bit_cast(f16x4, u32x2{fa[i], 0u}),
                                                             f32x16{}, 0, 0, 0);
-    const f32x16 p = partial<Q>(f, sa, sb, i, j);
+    const f32x16 p = partial<Q, BASE>(f, sc, i, j);
 #pragma unroll
     for (int t = 0; t < 16; t++) acc[i][j][t] = __builtin_fmaf(p[t], gk[t], acc[i][j][t]);
   }
@@ -216,12 +262,28 @@ __device__ __forceinline__ int gather_scales(const uint8_t* srow, int g) {
   return (int)__builtin_amdgcn_perm(v.y, v.x, g ? 0x07050301u : 0x06040200u);
 }
 
-template <int OUT>
+// BASE 16: the row's 16 scale bytes; sub-step J's 32 codes of lane group g
+// are 16-blocks 4 J + 2 g (first half) and 4 J + 2 g + 1 (second half), i.e.
+// byte 2 g (or 2 g + 1) of dword J.
+__device__ __forceinline__ void gather_scales16(const uint8_t* srow, int g, int& lo, int& hi) {
+  const u32x4 v = *(const u32x4*)srow;
+  const int sl = 16 * g, sh = 16 * g + 8;
+  lo = (int)(((v.x >> sl) & 0xFFu) | (((v.y >> sl) & 0xFFu) << 8) | (((v.z >> sl) & 0xFFu) << 16) |
+             (((v.w >> sl) & 0xFFu) << 24));
+  hi = (int)(((v.x >> sh) & 0xFFu) | (((v.y >> sh) & 0xFFu) << 8) | (((v.z >> sh) & 0xFFu) << 16) |
+             (((v.w >> sh) & 0xFFu) << 24));
+}
+
+// Super-steps per fp32 accumulation segment (48 macro blocks).
+constexpr int kSeg = 24;
+
+template <int OUT, int BASE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mbs_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ MA,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB, const uint8_t* __restrict__ MB,
     void* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
+  using L = Lds<BASE>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[L::kSmem];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -233,9 +295,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mbs_kernel(
   const int m0 = tm * BM, n0 = tn * BN;
 
   // Buffer views based at the tile's first rows: rows past M or N read as 0.
-  const uint32_t rowbytes = (uint32_t)(K / 2), scalebytes = (uint32_t)(K / 32);
+  const uint32_t rowbytes = (uint32_t)(K / 2), scalebytes = (uint32_t)(K / BASE);
   const uint32_t macrobytes = (uint32_t)(K / 128);
-  const LaneOffsets lo = lane_offsets(lane, rowbytes, scalebytes);
+  const LaneOffsets lo = lane_offsets<BASE>(lane, rowbytes, scalebytes);
   const int mrows = min(BM, M - m0), nrows = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * rowbytes), 0, (int)(mrows * rowbytes), kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)(B + (int64_t)n0 * rowbytes), 0, (int)(nrows * rowbytes), kRsrcFlags);
@@ -255,20 +317,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mbs_kernel(
   const int nsteps = K / kSuperK;
   const __amdgpu_buffer_rsrc_t rM = a_side ? rMA : rMB;
   uint32_t mv = load_macro(rM, macrobytes, 0, mrow);
-  issue_part<0>(smem, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, 0, wave);
-  issue_part<1>(smem, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, 0, wave);
-  issue_part<2>(smem, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, 0, wave);
-  issue_part<3>(smem, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, 0, wave);
+  issue_part<0, BASE>(smem, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, 0, wave);
+  issue_part<1, BASE>(smem, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, 0, wave);
+  issue_part<2, BASE>(smem, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, 0, wave);
+  issue_part<3, BASE>(smem, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, 0, wave);
   for (int s = 0; s < nsteps; s++) {
-    uint8_t* cur = smem + (s & 1) * kStage;
-    uint8_t* nxt = smem + ((s + 1) & 1) * kStage;
+    uint8_t* cur = smem + (s & 1) * L::kStage;
+    uint8_t* nxt = smem + ((s + 1) & 1) * L::kStage;
     // Super-step s has landed (codes, scales and the macro bytes in VGPRs);
     // its factors go to LDS, then every wave may read it -- and every wave is
     // done with super-step s - 1, whose buffer receives s + 1 below.
     wait_vmem();
     {
       // A factors are stored halved: the factor MFMA sums two K slots.
-      uint32_t* F = (uint32_t*)(cur + (a_side ? kOffFA : kOffFB));
+      uint32_t* F = (uint32_t*)(cur + (a_side ? L::kOffFA : L::kOffFB));
       const float w = a_side ? 0.5f : 1.0f;
       F[mrow] = factor_bits(mv & 0xFFu, w);
       F[BM + mrow] = factor_bits(mv >> 8, w);
@@ -278,22 +340,44 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mbs_kernel(
     // the idle buffer, which nobody reads; the wait after the loop drains it.
     const int snext = min(s + 1, nsteps - 1);
     mv = load_macro(rM, macrobytes, snext, mrow);
-    int sa[4], sb[2];
+    Scales sc;
+    if (BASE == 32) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) sa[i] = gather_scales(cur + kOffSA + (wm * 128 + i * 32 + r) * 8, g);
+      for (int i = 0; i < 4; i++) sc.a[i] = gather_scales(cur + kOffSA + (wm * 128 + i * 32 + r) * 8, g);
 #pragma unroll
-    for (int j = 0; j < 2; j++) sb[j] = gather_scales(cur + kOffSB + (wn * 64 + j * 32 + r) * 8, g);
+      for (int j = 0; j < 2; j++) sc.b[j] = gather_scales(cur + L::kOffSB + (wn * 64 + j * 32 + r) * 8, g);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        gather_scales16(cur + kOffSA + (wm * 128 + i * 32 + r) * 16, g, sc.a[i], sc.a2[i]);
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+        gather_scales16(cur + L::kOffSB + (wn * 64 + j * 32 + r) * 16, g, sc.b[j], sc.b2[j]);
+    }
     Frags f;
     load_frags(cur, 0, wm, wn, r, g, f);
-    issue_part<0>(nxt, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, snext, wave);
-    issue_part<1>(nxt, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, snext, wave);
-    macro_step<0>(cur, f, sa, sb, wm, wn, r, acc);
+    issue_part<0, BASE>(nxt, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, snext, wave);
+    issue_part<1, BASE>(nxt, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, snext, wave);
+    macro_step<0, BASE>(cur, f, sc, wm, wn, r, acc);
     load_frags(cur, 1, wm, wn, r, g, f);
-    issue_part<2>(nxt, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, snext, wave);
-    issue_part<3>(nxt, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, snext, wave);
-    macro_step<1>(cur, f, sa, sb, wm, wn, r, acc);
+    issue_part<2, BASE>(nxt, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, snext, wave);
+    issue_part<3, BASE>(nxt, rA, rB, rSA, rSB, lo, rowbytes, scalebytes, snext, wave);
+    macro_step<1, BASE>(cur, f, sc, wm, wn, r, acc);
+    // fp32 output: the fma chain into the accumulators is kept to kSeg
+    // macro blocks (2 per super-step), each segment folded into C.
+    if (OUT == kOutF32 && nsteps > kSeg && ((s + 1) % kSeg == 0 || s + 1 == nsteps)) {
+      tile256::fold_tile<2, kWavesN>(acc, (float*)C, ldc, M, N, m0, n0, wave, lane, s + 1 == kSeg,
+                                     s + 1 == nsteps, 1.0f);
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+          for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
+    }
   }
   wait_vmem();
+  if (OUT == kOutF32 && nsteps > kSeg) return;
 
   // Epilogue: every load has drained; the stage buffers are free once every
   // wave is past its loop.
@@ -310,22 +394,24 @@ bool gemm_mbs_fits(int64_t M, int64_t N, int64_t K) {
 
 hipError_t gemm_mbs(int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
                     const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
-                    hipStream_t s) {
+                    hipStream_t s, int base) {
   if (!gemm_mbs_fits(M, N, K))
-    return gemm_mbs_small(M, N, K, a, sa, b, sb, out_dtype, c, ldc, s);
+    return gemm_mbs_small(M, N, K, a, sa, b, sb, out_dtype, c, ldc, s, base);
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
   const dim3 grid((unsigned)(tm * tn));
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;
-  const uint8_t* MA = SA + M * (K / 32);  // macro planes follow the E8M0 planes
-  const uint8_t* MB = SB + N * (K / 32);
+  const uint8_t* MA = SA + M * (K / base);  // macro planes follow the E8M0 planes
+  const uint8_t* MB = SB + N * (K / base);
+  const int m = (int)M, n = (int)N, k = (int)K;
+  if (base == 16) {
+    if (out_dtype == kOutF32)
+      return launch_kernel(&gemm_mbs_kernel<kOutF32, 16>, grid, kThreads, 0, s, A, SA, MA, B, SB, MB, c, ldc, m, n, k, tm, tn);
+    return launch_kernel(&gemm_mbs_kernel<kOutBF16, 16>, grid, kThreads, 0, s, A, SA, MA, B, SB, MB, c, ldc, m, n, k, tm, tn);
+  }
   if (out_dtype == kOutF32)
-    gemm_mbs_kernel<kOutF32><<<grid, kThreads, 0, s>>>(A, SA, MA, B, SB, MB, c, ldc, (int)M,
-                                                        (int)N, (int)K, tm, tn);
-  else
-    gemm_mbs_kernel<kOutBF16><<<grid, kThreads, 0, s>>>(A, SA, MA, B, SB, MB, c, ldc, (int)M,
-                                                         (int)N, (int)K, tm, tn);
-  return hipGetLastError();
+    return launch_kernel(&gemm_mbs_kernel<kOutF32, 32>, grid, kThreads, 0, s, A, SA, MA, B, SB, MB, c, ldc, m, n, k, tm, tn);
+  return launch_kernel(&gemm_mbs_kernel<kOutBF16, 32>, grid, kThreads, 0, s, A, SA, MA, B, SB, MB, c, ldc, m, n, k, tm, tn);
 }
 
 }  // namespace mx

@@ -1,18 +1,19 @@
-// Block-scaled GEMM for MXFP4 x MXFP4 and MXFP8 x MXFP8 on gfx950's scaled
-// MFMA (v_mfma_scale_f32_16x16x128_f8f6f4). C = A * B^T, A is M x K codes,
-// B is stored N x K codes, one E8M0 scale per 32 K per row. The matrix core
-// applies both E8M0 scales inside its fp32 accumulation, so codes go to the
-// instruction unexpanded (the block-scaled dot product described in
-// "Arquitetura Blackwell SM100 e aceleracao nativa de NVFP4" on the
-// produtoramaxvision page, there for B200 tensor cores).
+// Block-scaled GEMM for MXFP4 x MXFP4 on gfx950's scaled MFMA
+// (v_mfma_scale_f32_16x16x128_f8f6f4), the 128 x 128-tile kernel for shapes
+// the 256 x 256-tile kernel (gemm_mxfp4.hip) does not take (K % 256 != 0, or
+// offsets beyond 32 bits). C = A * B^T, A is M x K codes, B is stored N x K
+// codes, one E8M0 scale per 32 K per row. The matrix core applies both E8M0
+// scales inside its fp32 accumulation, so codes go to the instruction
+// unexpanded (the block-scaled dot product described in "Arquitetura
+// Blackwell SM100 e aceleracao nativa de NVFP4" on the produtoramaxvision
+// page, there for B200 tensor cores). (MXFP8 does not come here: the FP8
+// scaled MFMA truncates within a block, see gemm_bf16x.hip.)
 //
 // Operand layout of the 16x16x128 instruction (measured on gfx950): lane
-// l = r + 16 g (r = row in the 16-row tile, g = 0..3) supplies
-//   FP4: K elements [32g, 32g + 32) of row r, 16 bytes, even element in the low
-//        nibble (the same packing as the codes in memory);
-//   FP8: K elements [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16), 32 bytes;
-// and, for both, the E8M0 scale of K block g of row r. Output: lane l holds
-// column l % 16, rows 4 (l / 16) + 0..3.
+// l = r + 16 g (r = row in the 16-row tile, g = 0..3) supplies K elements
+// [32g, 32g + 32) of row r, 16 bytes, even element in the low nibble (the same
+// packing as the codes in memory), and the E8M0 scale of K block g of row r.
+// Output: lane l holds column l % 16, rows 4 (l / 16) + 0..3.
 //
 // MXFP4-MBS (static macro-block scaling; gist.science summary of "Unveiling
 // the Potential of Quantization with MXFP4", section 2.B): a K step of 128 is
@@ -20,7 +21,9 @@
 // block-scaled partial sum P of that macro block; the vector ALU then adds
 // P * f_A(row) * f_B(col) to the accumulator (f_A f_B has 18 significant bits
 // and is exact in fp32), the factor being applied alongside the matrix core
-// as the summary describes.
+// as the summary describes. With 16-element base blocks (MXFP4-MBS16) each
+// lane's 32 codes carry two scales, so P takes two MFMAs, one per 16-element
+// half with the other half zero.
 #include "bf16.h"
 #include "mx_internal.h"
 
@@ -34,6 +37,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int BM = 128, BN = 128, BK = 128;  // tile sizes in elements
 constexpr uint32_t kUnitScale = 127u;        // 2^0 for padded blocks
+constexpr int kSegSteps = 48;                // K steps per accumulation chain
 
 template <int FMT>
 struct MxTile {
@@ -45,8 +49,9 @@ struct MxTile {
   static constexpr int kMfmaFmt = (FMT == kMXFP4) ? 4 : 0;  // cbsz / blgp selector
 };
 
-// MBS: MA / MB are the macro mantissa planes [rows][K/128] (unused otherwise).
-template <int FMT, int OUT, bool MBS>
+// MBS: MA / MB are the macro mantissa planes [rows][K/128] (unused otherwise);
+// BASE: the E8M0 block size, 32, or 16 for MXFP4-MBS16.
+template <int FMT, int OUT, bool MBS, int BASE = 32>
 __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __restrict__ A,
                                                            const uint8_t* __restrict__ SA,
                                                            const uint8_t* __restrict__ B,
@@ -60,6 +65,10 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __rest
   __shared__ __attribute__((aligned(16))) uint8_t lB[BN * T::kStride];
   __shared__ uint32_t lSA[BM];
   __shared__ uint32_t lSB[BN];
+  // BASE 16: scales of the second 16 elements of each 32 (the first 16's are
+  // in lSA / lSB).
+  __shared__ uint32_t lSA2[BASE == 16 ? BM : 1];
+  __shared__ uint32_t lSB2[BASE == 16 ? BN : 1];
   __shared__ float lFA[MBS ? BM : 1];
   __shared__ float lFB[MBS ? BN : 1];
 
@@ -67,11 +76,11 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __rest
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int64_t rowbytes = (int64_t)K * T::kBits / 8;
-  const int kblocks = K / 32;
+  const int kblocks = K / BASE;
   const int nk = (K + BK - 1) / BK;
 
   u32x4 ra[T::kLoads], rb[T::kLoads];
-  uint32_t rs = 0;
+  uint32_t rs = 0, rs2 = 0;
   float rf = 1.0f;
 
   auto gload = [&](int kt) {
@@ -91,11 +100,22 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __rest
     const int glim = isA ? M : N;
     const uint8_t* S = isA ? SA : SB;
     rs = 0;
+    rs2 = 0;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const int kbk = kt * 4 + j;
-      const uint32_t e = (grow < glim && kbk < kblocks) ? S[(int64_t)grow * kblocks + kbk] : kUnitScale;
-      rs |= e << (8 * j);
+      if (BASE == 32) {
+        const int kbk = kt * 4 + j;
+        const uint32_t e = (grow < glim && kbk < kblocks) ? S[(int64_t)grow * kblocks + kbk] : kUnitScale;
+        rs |= e << (8 * j);
+      } else {
+        // 32-element group j of the step: 16-blocks 2 j (rs) and 2 j + 1 (rs2)
+        const int kbk = kt * 8 + 2 * j;
+        const bool in = grow < glim && kbk < kblocks;
+        const uint32_t e0 = in ? S[(int64_t)grow * kblocks + kbk] : kUnitScale;
+        const uint32_t e1 = in ? S[(int64_t)grow * kblocks + kbk + 1] : kUnitScale;
+        rs |= e0 << (8 * j);
+        rs2 |= e1 << (8 * j);
+      }
     }
     if (MBS) {
       // Macro factor 1 + m / 256 of this step's macro block (K step = 128).
@@ -116,6 +136,12 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __rest
       lSA[tid] = rs;
     else
       lSB[tid - 128] = rs;
+    if (BASE == 16) {
+      if (tid < 128)
+        lSA2[tid] = rs2;
+      else
+        lSB2[tid - 128] = rs2;
+    }
     if (MBS) {
       if (tid < 128)
         lFA[tid] = rf;
@@ -124,11 +150,11 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __rest
     }
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][4], tot[4][4];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0, 0, 0, 0};
+    for (int j = 0; j < 4; j++) acc[i][j] = tot[i][j] = f32x4{0, 0, 0, 0};
 
   const int r = lane & 15, g = lane >> 4;
   gload(0);
@@ -138,26 +164,21 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __rest
     __syncthreads();
     if (kt + 1 < nk) gload(kt + 1);
     i32x8 af[4], bf[4];
-    int sa[4], sb[4];
+    int sa[4], sb[4], sa2[4], sb2[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int ra_ = wm * 64 + i * 16 + r;
       const int rb_ = wn * 64 + i * 16 + r;
-      if (FMT == kMXFP4) {
-        const u32x4 x = *(const u32x4*)(lA + ra_ * T::kStride + g * 16);
-        const u32x4 y = *(const u32x4*)(lB + rb_ * T::kStride + g * 16);
-        af[i] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        bf[i] = i32x8{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
-      } else {
-        const u32x4 x0 = *(const u32x4*)(lA + ra_ * T::kStride + g * 16);
-        const u32x4 x1 = *(const u32x4*)(lA + ra_ * T::kStride + 64 + g * 16);
-        const u32x4 y0 = *(const u32x4*)(lB + rb_ * T::kStride + g * 16);
-        const u32x4 y1 = *(const u32x4*)(lB + rb_ * T::kStride + 64 + g * 16);
-        af[i] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        bf[i] = i32x8{(int)y0.x, (int)y0.y, (int)y0.z, (int)y0.w, (int)y1.x, (int)y1.y, (int)y1.z, (int)y1.w};
-      }
+      const u32x4 x = *(const u32x4*)(lA + ra_ * T::kStride + g * 16);
+      const u32x4 y = *(const u32x4*)(lB + rb_ * T::kStride + g * 16);
+      af[i] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+      bf[i] = i32x8{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
       sa[i] = (int)((lSA[ra_] >> (8 * g)) & 0xFFu);
       sb[i] = (int)((lSB[rb_] >> (8 * g)) & 0xFFu);
+      if (BASE == 16) {
+        sa2[i] = (int)((lSA2[ra_] >> (8 * g)) & 0xFFu);
+        sb2[i] = (int)((lSB2[rb_] >> (8 * g)) & 0xFFu);
+      }
     }
     if (MBS) {
       float fa[4][4], fb[4];
@@ -171,8 +192,22 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __rest
       for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[i], bf[j], f32x4{0, 0, 0, 0}, T::kMfmaFmt, T::kMfmaFmt, 0, sa[i], 0, sb[j]);
+          f32x4 p;
+          if (BASE == 32) {
+            p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                af[i], bf[j], f32x4{0, 0, 0, 0}, T::kMfmaFmt, T::kMfmaFmt, 0, sa[i], 0, sb[j]);
+          } else {
+            // One scale per lane's 32 codes: each 32 split into its two
+            // 16-blocks (the other half zero), one MFMA under each scale.
+            const i32x8 alo = i32x8{af[i][0], af[i][1], 0, 0, 0, 0, 0, 0};
+            const i32x8 ahi = i32x8{0, 0, af[i][2], af[i][3], 0, 0, 0, 0};
+            const i32x8 blo = i32x8{bf[j][0], bf[j][1], 0, 0, 0, 0, 0, 0};
+            const i32x8 bhi = i32x8{0, 0, bf[j][2], bf[j][3], 0, 0, 0, 0};
+            p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                alo, blo, f32x4{0, 0, 0, 0}, T::kMfmaFmt, T::kMfmaFmt, 0, sa[i], 0, sb[j]);
+            p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                ahi, bhi, p, T::kMfmaFmt, T::kMfmaFmt, 0, sa2[i], 0, sb2[j]);
+          }
 #pragma unroll
           for (int t = 0; t < 4; t++)
             acc[i][j][t] = __builtin_fmaf(p[t], fa[i][t] * fb[j], acc[i][j][t]);
@@ -185,6 +220,24 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __rest
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               af[i], bf[j], acc[i][j], T::kMfmaFmt, T::kMfmaFmt, 0, sa[i], 0, sb[j]);
     }
+    // Accumulation chains of at most kSegSteps K steps (one MFMA, or one fma
+    // for MBS, per step), added into a running total (one fp32 rounding per
+    // segment).
+    if ((kt + 1) % kSegSteps == 0 && kt + 1 < nk) {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          tot[i][j] += acc[i][j];
+          acc[i][j] = f32x4{0, 0, 0, 0};
+        }
+    }
+  }
+  if (nk > kSegSteps) {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) acc[i][j] += tot[i][j];
   }
 
 #pragma unroll
@@ -207,43 +260,38 @@ __global__ __launch_bounds__(kThreads) void gemm_mx_kernel(const uint8_t* __rest
 
 }  // namespace
 
-hipError_t gemm_mx(int fmt, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
-                   const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
-                   hipStream_t s) {
-  if (fmt == kMXFP4 && gemm_mxfp4_fits(M, N, K))
+hipError_t gemm_mx(int64_t M, int64_t N, int64_t K, const void* a, const void* sa, const void* b,
+                   const void* sb, int out_dtype, void* c, int64_t ldc, hipStream_t s) {
+  if (gemm_mxfp4_fits(M, N, K))
     return gemm_mxfp4(M, N, K, a, sa, b, sb, out_dtype, c, ldc, s, false, false);
   const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (fmt == kMXFP4) {
-    if (out_dtype == kOutF32)
-      gemm_mx_kernel<kMXFP4, kOutF32, false><<<grid, kThreads, 0, s>>>(A, SA, B, SB, nullptr, nullptr, c, ldc, m, n, k);
-    else
-      gemm_mx_kernel<kMXFP4, kOutBF16, false><<<grid, kThreads, 0, s>>>(A, SA, B, SB, nullptr, nullptr, c, ldc, m, n, k);
-  } else {
-    if (out_dtype == kOutF32)
-      gemm_mx_kernel<kMXFP8, kOutF32, false><<<grid, kThreads, 0, s>>>(A, SA, B, SB, nullptr, nullptr, c, ldc, m, n, k);
-    else
-      gemm_mx_kernel<kMXFP8, kOutBF16, false><<<grid, kThreads, 0, s>>>(A, SA, B, SB, nullptr, nullptr, c, ldc, m, n, k);
-  }
-  return hipGetLastError();
+  if (out_dtype == kOutF32)
+    return launch_kernel(&gemm_mx_kernel<kMXFP4, kOutF32, false>, grid, kThreads, 0, s, A, SA, B, SB, nullptr, nullptr, c, ldc, m, n, k);
+  return launch_kernel(&gemm_mx_kernel<kMXFP4, kOutBF16, false>, grid, kThreads, 0, s, A, SA, B, SB, nullptr, nullptr, c, ldc, m, n, k);
 }
 
 hipError_t gemm_mbs_small(int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
                           const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
-                          hipStream_t s) {
+                          hipStream_t s, int base) {
   const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;
-  const uint8_t* MA = SA + M * (K / 32);  // macro planes follow the E8M0 planes
-  const uint8_t* MB = SB + N * (K / 32);
+  const uint8_t* MA = SA + M * (K / base);  // macro planes follow the E8M0 planes
+  const uint8_t* MB = SB + N * (K / base);
   const int m = (int)M, n = (int)N, k = (int)K;
+  if (base == 16) {
+    if (out_dtype == kOutF32)
+      return launch_kernel(&gemm_mx_kernel<kMXFP4, kOutF32, true, 16>, grid, kThreads, 0, s, A, SA, B, SB, MA, MB, c, ldc, m, n, k);
+    return launch_kernel(&gemm_mx_kernel<kMXFP4, kOutBF16, true, 16>, grid, kThreads, 0, s, A, SA, B, SB, MA, MB, c, ldc, m, n, k);
+  }
   if (out_dtype == kOutF32)
-    gemm_mx_kernel<kMXFP4, kOutF32, true><<<grid, kThreads, 0, s>>>(A, SA, B, SB, MA, MB, c, ldc, m, n, k);
+    MX_TRY(launch_kernel(&gemm_mx_kernel<kMXFP4, kOutF32, true>, grid, kThreads, 0, s, A, SA, B, SB, MA, MB, c, ldc, m, n, k));
   else
-    gemm_mx_kernel<kMXFP4, kOutBF16, true><<<grid, kThreads, 0, s>>>(A, SA, B, SB, MA, MB, c, ldc, m, n, k);
-  return hipGetLastError();
+    MX_TRY(launch_kernel(&gemm_mx_kernel<kMXFP4, kOutBF16, true>, grid, kThreads, 0, s, A, SA, B, SB, MA, MB, c, ldc, m, n, k));
+  return hipSuccess;
 }
 
 }  // namespace mx

@@ -333,19 +333,44 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
     load_part<3, PANEL_A, PANEL_B>(R[x], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, sx, wave, lane, A, SA, M, B, SB, N);
     sched_fence();
   }
-  if (DEEP) {
-    // Four-deep pipeline: two register stages alternate, so every load has
-    // two super-steps to land.
-    int s = 0;
-    for (; s + 1 < nsteps; s += 2) {
-      step(s, R[0], 3);
-      step(s + 1, R[DEEP ? 1 : 0], 3);
+  // fp32 output with more than kSeg super-steps: K in segments of kSeg
+  // super-steps (48 MFMAs per chain), each folded into C
+  // (tile256::fold_tile); otherwise one chain. The pipeline runs on across
+  // segment boundaries; kSeg is even, so every segment but the last starts
+  // and ends on the same register stage.
+  constexpr int kSeg = 12;
+  auto run = [&](int s0, int s1) {
+    if (DEEP) {
+      // Four-deep pipeline: two register stages alternate, so every load has
+      // two super-steps to land.
+      int s = s0;
+      for (; s + 1 < s1; s += 2) {
+        step(s, R[0], 3);
+        step(s + 1, R[DEEP ? 1 : 0], 3);
+      }
+      if (s < s1) step(s, R[0], 3);
+    } else {
+      // Three-deep pipeline: one register stage, each load has one super-step.
+      for (int s = s0; s < s1; s++) step(s, R[0], 2);
     }
-    if (s < nsteps) step(s, R[0], 3);
-  } else {
-    // Three-deep pipeline: one register stage, each load has one super-step.
-    for (int s = 0; s < nsteps; s++) step(s, R[0], 2);
+  };
+  if constexpr (OUT == kOutF32) {
+    if (nsteps > kSeg) {
+      for (int s0 = 0; s0 < nsteps; s0 += kSeg) {
+        const int s1 = min(s0 + kSeg, nsteps);
+        run(s0, s1);
+        tile256::fold_tile(acc, (float*)C, ldc, M, N, m0, n0, wave, lane, s0 == 0, s1 == nsteps, 1.0f);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
+      }
+      return;
+    }
   }
+  run(0, nsteps);
 
   // Epilogue: the stage buffers are free once every wave is past its loop.
   __syncthreads();
@@ -363,17 +388,18 @@ bool gemm_mxfp4_fits(int64_t M, int64_t N, int64_t K) {
 }
 
 template <int OUT>
-void launch(dim3 grid, hipStream_t s, bool panel_a, bool panel_b, const uint8_t* A,
+hipError_t launch(dim3 grid, hipStream_t s, bool panel_a, bool panel_b, const uint8_t* A,
             const uint8_t* SA, const uint8_t* B, const uint8_t* SB, void* c, int64_t ldc, int m,
             int n, int k, int tm, int tn) {
   if (panel_a && panel_b)
-    gemm_mxfp4_kernel<OUT, true, true><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k, tm, tn);
+    MX_TRY(launch_kernel(&gemm_mxfp4_kernel<OUT, true, true>, grid, kThreads, 0, s, A, SA, B, SB, c, ldc, m, n, k, tm, tn));
   else if (panel_a)
-    gemm_mxfp4_kernel<OUT, true, false><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k, tm, tn);
+    MX_TRY(launch_kernel(&gemm_mxfp4_kernel<OUT, true, false>, grid, kThreads, 0, s, A, SA, B, SB, c, ldc, m, n, k, tm, tn));
   else if (panel_b)
-    gemm_mxfp4_kernel<OUT, false, true><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k, tm, tn);
+    MX_TRY(launch_kernel(&gemm_mxfp4_kernel<OUT, false, true>, grid, kThreads, 0, s, A, SA, B, SB, c, ldc, m, n, k, tm, tn));
   else
-    gemm_mxfp4_kernel<OUT, false, false><<<grid, kThreads, 0, s>>>(A, SA, B, SB, c, ldc, m, n, k, tm, tn);
+    MX_TRY(launch_kernel(&gemm_mxfp4_kernel<OUT, false, false>, grid, kThreads, 0, s, A, SA, B, SB, c, ldc, m, n, k, tm, tn));
+  return hipSuccess;
 }
 
 hipError_t gemm_mxfp4(int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
@@ -384,10 +410,8 @@ hipError_t gemm_mxfp4(int64_t M, int64_t N, int64_t K, const void* a, const void
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;
   if (out_dtype == kOutF32)
-    launch<kOutF32>(grid, s, panel_a, panel_b, A, SA, B, SB, c, ldc, (int)M, (int)N, (int)K, tm, tn);
-  else
-    launch<kOutBF16>(grid, s, panel_a, panel_b, A, SA, B, SB, c, ldc, (int)M, (int)N, (int)K, tm, tn);
-  return hipGetLastError();
+    return launch<kOutF32>(grid, s, panel_a, panel_b, A, SA, B, SB, c, ldc, (int)M, (int)N, (int)K, tm, tn);
+  return launch<kOutBF16>(grid, s, panel_a, panel_b, A, SA, B, SB, c, ldc, (int)M, (int)N, (int)K, tm, tn);
 }
 
 }  // namespace mx

@@ -35,6 +35,7 @@
 #include "mx_internal.h"
 
 namespace mx {
+
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -257,18 +258,18 @@ hipError_t gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* a, const void
   const int m = (int)M, n = (int)N, k = (int)K;
   if (splits == 1) {
     if (out_dtype == kOutF32)
-      gemm_w4a16_kernel<true, kOutF32><<<grid, kThreads, 0, s>>>(A, B, SB, c, ldc, m, n, k);
+      MX_TRY(launch_kernel(&gemm_w4a16_kernel<true, kOutF32>, grid, kThreads, 0, s, A, B, SB, c, ldc, m, n, k));
     else
-      gemm_w4a16_kernel<true, kOutBF16><<<grid, kThreads, 0, s>>>(A, B, SB, c, ldc, m, n, k);
-    return hipGetLastError();
+      MX_TRY(launch_kernel(&gemm_w4a16_kernel<true, kOutBF16>, grid, kThreads, 0, s, A, B, SB, c, ldc, m, n, k));
+    return hipSuccess;
   }
-  gemm_w4a16_kernel<false, kOutF32><<<grid, kThreads, 0, s>>>(A, B, SB, workspace, 0, m, n, k);
+  MX_TRY(launch_kernel(&gemm_w4a16_kernel<false, kOutF32>, grid, kThreads, 0, s, A, B, SB, workspace, 0, m, n, k));
   const unsigned rblocks = (unsigned)((M * N + kThreads - 1) / kThreads);
   if (out_dtype == kOutF32)
-    splitk_reduce_kernel<kOutF32><<<rblocks, kThreads, 0, s>>>((const float*)workspace, c, ldc, m, n, splits);
+    MX_TRY(launch_kernel(&splitk_reduce_kernel<kOutF32>, rblocks, kThreads, 0, s, (const float*)workspace, c, ldc, m, n, splits));
   else
-    splitk_reduce_kernel<kOutBF16><<<rblocks, kThreads, 0, s>>>((const float*)workspace, c, ldc, m, n, splits);
-  return hipGetLastError();
+    MX_TRY(launch_kernel(&splitk_reduce_kernel<kOutBF16>, rblocks, kThreads, 0, s, (const float*)workspace, c, ldc, m, n, splits));
+  return hipSuccess;
 }
 
 }  // namespace mx

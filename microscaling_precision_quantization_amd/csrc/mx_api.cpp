@@ -18,17 +18,19 @@ bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 bool is_quant_fmt(int f) {
   return f == MX_FMT_MXFP4 || f == MX_FMT_MXFP8 || f == MX_FMT_NVFP4 || f == MX_FMT_MXFP8_E5M2 ||
-         f == MX_FMT_MXFP6_E3M2 || f == MX_FMT_MXFP4_MBS;
+         f == MX_FMT_MXFP6_E3M2 || f == MX_FMT_MXFP4_MBS || f == MX_FMT_MXFP4_MBS16;
 }
-int block_of(int f) { return f == MX_FMT_NVFP4 ? 16 : 32; }
+bool is_mbs(int f) { return f == MX_FMT_MXFP4_MBS || f == MX_FMT_MXFP4_MBS16; }
+int block_of(int f) { return (f == MX_FMT_NVFP4 || f == MX_FMT_MXFP4_MBS16) ? 16 : 32; }
 // cols (and K) must be a multiple of this: the block, or the 128-element macro
-// block of MXFP4-MBS.
-int granule_of(int f) { return f == MX_FMT_MXFP4_MBS ? 128 : block_of(f); }
+// block of MXFP4-MBS and MXFP4-MBS16.
+int granule_of(int f) { return is_mbs(f) ? 128 : block_of(f); }
 
 // Elements per tensor stay below 2^40 and every GEMM extent below 2^30 so that
 // the kernels' index arithmetic (int64 offsets, int extents) cannot overflow.
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
 constexpr int64_t kMaxExtent = (int64_t)1 << 30;
+constexpr int64_t kW4A16MaxK = 65536;
 
 mx_status hip_status(hipError_t e) {
   if (e == hipSuccess) return MX_OK;
@@ -75,7 +77,7 @@ mx_status mx_quantize(mx_format fmt, int block, mx_round rnd, int64_t rows, int6
     return hip_status(mx::quant_nvfp4(rows, cols, x, codes, scales, tensor_scale, workspace, s));
   }
   if (tensor_scale) return MX_ERR_INVALID_ARG;
-  if (fmt == MX_FMT_MXFP4_MBS) return hip_status(mx::quant_mbs(rows, cols, x, codes, scales, s));
+  if (is_mbs(fmt)) return hip_status(mx::quant_mbs(rows, cols, x, codes, scales, s, block));
   return hip_status(mx::quant_mx(fmt, rows, cols, x, codes, scales, s));
 }
 
@@ -117,7 +119,7 @@ mx_status mx_dequantize(mx_format fmt, int block, mx_round rnd, int64_t rows, in
 
 size_t mx_gemm_workspace_bytes(mx_format fmt_a, mx_format fmt_b, int64_t M, int64_t N, int64_t K) {
   if (fmt_a == MX_FMT_BF16 && fmt_b == MX_FMT_MXFP4 && M > 0 && N > 0 && K > 0 && K % 32 == 0 &&
-      M <= kMaxExtent && N <= kMaxExtent && K <= kMaxExtent)
+      M <= kMaxExtent && N <= kMaxExtent && K <= kW4A16MaxK)
     return mx::gemm_w4a16_workspace(M, N, K);
   return 0;
 }
@@ -138,7 +140,8 @@ mx_status gemm_impl(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, i
   const bool w4a16 = fmt_a == MX_FMT_BF16 && fmt_b == MX_FMT_MXFP4 && block == 32;
   const bool alt = fmt_a == fmt_b && block == 32 &&
                    (fmt_a == MX_FMT_MXFP8_E5M2 || fmt_a == MX_FMT_MXFP6_E3M2);
-  const bool mbs = fmt_a == MX_FMT_MXFP4_MBS && fmt_b == MX_FMT_MXFP4_MBS && block == 32;
+  const bool mbs = (fmt_a == MX_FMT_MXFP4_MBS && fmt_b == MX_FMT_MXFP4_MBS && block == 32) ||
+                   (fmt_a == MX_FMT_MXFP4_MBS16 && fmt_b == MX_FMT_MXFP4_MBS16 && block == 16);
   if (!(w4a4 || w8a8 || nv || w4a16 || alt || mbs)) return MX_ERR_UNSUPPORTED;
   if ((panel_a || panel_b) && !w4a4) return MX_ERR_UNSUPPORTED;
   if (rnd != MX_ROUND_RNE) return MX_ERR_UNSUPPORTED;
@@ -152,9 +155,10 @@ mx_status gemm_impl(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, i
   // Row tiles run along gridDim.y (at most 65535): 128 rows per tile for the
   // W4A4/W8A8 kernels, 16 for W4A16.
   if (M > (w4a16 ? 16 : 128) * (int64_t)65535) return MX_ERR_INVALID_ARG;
-  // The W4A16 kernel addresses a 448-row slab of weights (K / 2 bytes per row)
-  // with 32-bit buffer offsets.
-  if (w4a16 && K >= ((int64_t)1 << 23)) return MX_ERR_INVALID_ARG;
+  // W4A16: at most 32 K-splits of 2048, so that each output's fp32 chain (33
+  // roundings in a split, then the fixed-order sum of the splits) stays within
+  // 64 steps, the accumulation bound of mx.h.
+  if (w4a16 && K > kW4A16MaxK) return MX_ERR_INVALID_ARG;
   if (!a || !b || !b_scales || !c) return MX_ERR_INVALID_ARG;
   if (!aligned16(a) || !aligned16(b) || !aligned16(b_scales) || !aligned16(c))
     return MX_ERR_INVALID_ARG;
@@ -181,9 +185,9 @@ mx_status gemm_impl(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, i
                                      panel_a, panel_b));
   }
   if (w4a4)
-    return hip_status(mx::gemm_mx(fmt_a, M, N, K, a, a_scales, b, b_scales, out_dtype, c, ldc, s));
+    return hip_status(mx::gemm_mx(M, N, K, a, a_scales, b, b_scales, out_dtype, c, ldc, s));
   if (mbs)
-    return hip_status(mx::gemm_mbs(M, N, K, a, a_scales, b, b_scales, out_dtype, c, ldc, s));
+    return hip_status(mx::gemm_mbs(M, N, K, a, a_scales, b, b_scales, out_dtype, c, ldc, s, block));
   if (w8a8 || nv)
     return hip_status(mx::gemm_bf16x(fmt_a, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts,
                                      out_dtype, c, ldc, s));

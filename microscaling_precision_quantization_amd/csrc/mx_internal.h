@@ -4,11 +4,43 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <tuple>
+#include <utility>
 
 namespace mx {
 
+// Launches kernel<<<grid, block, shmem, stream>>>(args...) through
+// hipLaunchKernel and returns the status of that launch itself. (A status
+// read back with hipGetLastError afterwards could instead be an error that
+// an earlier HIP call of the caller left pending on this thread, and reading
+// it would also clear the caller's error.) Arguments are converted to the
+// kernel's parameter types first.
+template <typename... P, typename... A, size_t... I>
+inline hipError_t launch_impl(void (*kernel)(P...), dim3 grid, dim3 block, size_t shmem,
+                              hipStream_t stream, std::index_sequence<I...>, A&&... args) {
+  std::tuple<P...> params(static_cast<P>(std::forward<A>(args))...);
+  void* argv[] = {(void*)&std::get<I>(params)...};
+  return hipLaunchKernel((const void*)kernel, grid, block, argv, shmem, stream);
+}
+
+template <typename... P, typename... A>
+inline hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t shmem,
+                                hipStream_t stream, A&&... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  return launch_impl(kernel, grid, block, shmem, stream, std::index_sequence_for<P...>{},
+                     std::forward<A>(args)...);
+}
+
+// Returns from the enclosing launcher with the first failed launch's status.
+#define MX_TRY(launch)                     \
+  do {                                     \
+    const hipError_t mx_e_ = (launch);     \
+    if (mx_e_ != hipSuccess) return mx_e_; \
+  } while (0)
+
 // Format ids, kept equal to the public mx_format values.
-enum : int { kBF16 = 0, kMXFP4 = 1, kMXFP8 = 2, kNVFP4 = 3, kMXFP8E5M2 = 4, kMXFP6 = 5, kMXFP4MBS = 6 };
+enum : int { kBF16 = 0, kMXFP4 = 1, kMXFP8 = 2, kNVFP4 = 3, kMXFP8E5M2 = 4, kMXFP6 = 5, kMXFP4MBS = 6,
+             kMXFP4MBS16 = 7 };
 enum : int { kOutF32 = 0, kOutBF16 = 1 };
 
 // ---- quantize.hip
@@ -17,10 +49,11 @@ enum : int { kOutF32 = 0, kOutBF16 = 1 };
 hipError_t quant_mx(int fmt, int64_t rows, int64_t cols, const void* x, void* codes,
                     void* scales, hipStream_t s, bool oas = false,
                     bool rot = false, bool panel = false);
-// MXFP4 with static macro-block scaling: scales holds the E8M0 plane
-// [rows][cols/32] followed by the macro mantissa plane [rows][cols/128].
+// MXFP4 with static macro-block scaling over base blocks of `base` (16 or
+// 32) elements: scales holds the E8M0 plane [rows][cols/base] followed by the
+// macro mantissa plane [rows][cols/128].
 hipError_t quant_mbs(int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
-                     hipStream_t s);
+                     hipStream_t s, int base);
 size_t quant_nvfp4_workspace(int64_t rows, int64_t cols);
 hipError_t quant_nvfp4(int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
                        float* tensor_scale, void* workspace, hipStream_t s);
@@ -29,23 +62,23 @@ hipError_t quant_nvfp4(int64_t rows, int64_t cols, const void* x, void* codes, v
 hipError_t dequant(int fmt, int64_t rows, int64_t cols, const void* codes, const void* scales,
                    const float* tensor_scale, int out_dtype, void* y, hipStream_t s);
 
-// ---- gemm_mx.hip (MXFP4 x MXFP4 on the FP4 scaled MFMA)
-hipError_t gemm_mx(int fmt, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
-                   const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
-                   hipStream_t s);
+// ---- gemm_mx.hip (MXFP4 x MXFP4 on the FP4 scaled MFMA: the 256 x 256-tile
+// kernel when it fits, else 128 x 128 tiles)
+hipError_t gemm_mx(int64_t M, int64_t N, int64_t K, const void* a, const void* sa, const void* b,
+                   const void* sb, int out_dtype, void* c, int64_t ldc, hipStream_t s);
 
 // ---- gemm_mx.hip, MXFP4-MBS x MXFP4-MBS (128 x 128 tiles, any K % 128 = 0);
 // sa / sb are the two-plane scale buffers.
 hipError_t gemm_mbs_small(int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
                           const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
-                          hipStream_t s);
+                          hipStream_t s, int base);
 
-// ---- gemm_mbs.hip (MXFP4-MBS x MXFP4-MBS; 256 x 128 tiles when they fit,
-// else gemm_mbs_small)
+// ---- gemm_mbs.hip (MXFP4-MBS x MXFP4-MBS over base blocks of `base` = 32 or
+// 16 elements; 256 x 256 tiles when they fit, else gemm_mbs_small)
 bool gemm_mbs_fits(int64_t M, int64_t N, int64_t K);
 hipError_t gemm_mbs(int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
                     const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
-                    hipStream_t s);
+                    hipStream_t s, int base);
 
 // ---- gemm_mxfp4.hip (MXFP4 x MXFP4, 256 x 256 tiles, register-staged
 // pipeline); panel_a / panel_b: that operand in the K-panel layout (its

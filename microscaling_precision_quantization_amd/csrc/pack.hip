@@ -41,11 +41,11 @@ hipError_t pack_mxfp4(int64_t rows, int64_t cols, const void* codes, const void*
                       void* packed_codes, void* packed_scales, hipStream_t s) {
   const int64_t panels = cols / 256;
   const int64_t nchunks = rows * panels * 8, ngroups = rows * panels;
-  pack_codes_kernel<<<(unsigned)((nchunks + kThreads - 1) / kThreads), kThreads, 0, s>>>(
-      (const u32x4*)codes, (u32x4*)packed_codes, rows, panels);
-  pack_scales_kernel<<<(unsigned)((ngroups + kThreads - 1) / kThreads), kThreads, 0, s>>>(
-      (const u32x2*)scales, (u32x2*)packed_scales, rows, panels);
-  return hipGetLastError();
+  MX_TRY(launch_kernel(&pack_codes_kernel, (unsigned)((nchunks + kThreads - 1) / kThreads), kThreads, 0, s, 
+      (const u32x4*)codes, (u32x4*)packed_codes, rows, panels));
+  MX_TRY(launch_kernel(&pack_scales_kernel, (unsigned)((ngroups + kThreads - 1) / kThreads), kThreads, 0, s, 
+      (const u32x2*)scales, (u32x2*)packed_scales, rows, panels));
+  return hipSuccess;
 }
 
 }  // namespace mx

@@ -24,8 +24,9 @@
 //
 // MXFP4 with static macro-block scaling (MBS; the same gist.science summary,
 // section 2.B): a macro block of 128 elements (16 lanes, one DPP row) gets one
-// factor f = 1 + m / 256 from its amax, and each 32-block inside quantizes
-// x / f by the MX rule (details at quant_mbs_kernel).
+// factor f = 1 + m / 256 from its amax, and each base block inside (16
+// elements as the summary prints, or 32, MXFP4's own) quantizes x / f by the
+// MX rule with its own E8M0 scale (details at quant_mbs_kernel).
 //
 // Encoding uses gfx950's scaled converts. v_cvt_scalef32_pk_fp4_bf16 and
 // v_cvt_scalef32_pk_fp8_bf16 return nearest-even of x / scale (saturating for
@@ -256,9 +257,12 @@ __device__ __forceinline__ float mbs_quotient(float x, int sh, float f, float r)
 }
 
 // One lane per 16-byte chunk as in quant_mx_kernel; a DPP row of 16 lanes is
-// one macro block. Per 32-block, E is the smallest n with amax <= 6 f 2^n
-// (+127, clamped at 0): the plain MX exponent e0 of amax or e0 - 1, since
-// f is in [1, 2); the comparison with 6 f 2^(e0-128) is exact in fp32.
+// one macro block. BASE = 32: 4 lanes per base block (MXFP4's own block);
+// BASE = 16 (the summary's 1 x 16): 2 lanes per base block. Per base block,
+// E is the smallest n with amax <= 6 f 2^n (+127, clamped at 0): the plain
+// MX exponent e0 of amax or e0 - 1, since f is in [1, 2); the comparison with
+// 6 f 2^(e0-128) is exact in fp32.
+template <int BASE>
 __global__ __launch_bounds__(kThreads) void quant_mbs_kernel(const u32x4* __restrict__ x,
                                                              uint32_t* __restrict__ codes,
                                                              uint8_t* __restrict__ scales,
@@ -276,9 +280,10 @@ __global__ __launch_bounds__(kThreads) void quant_mbs_kernel(const u32x4* __rest
   for (int u = 0; u < kUnroll; u++) {
     const int64_t c = base + u * kThreads;
     uint32_t mb = chunk_absmax(v[u]);
-    mb = umax(mb, dpp<kDppSwap1>(mb));
-    mb = umax(mb, dpp<kDppSwap2>(mb));
-    uint32_t mm = umax(mb, dpp<dpp_row_ror(4)>(mb));
+    mb = umax(mb, dpp<kDppSwap1>(mb));  // the base block's amax (BASE = 16)
+    uint32_t mm = umax(mb, dpp<kDppSwap2>(mb));
+    if (BASE == 32) mb = mm;
+    mm = umax(mm, dpp<dpp_row_ror(4)>(mm));
     mm = umax(mm, dpp<dpp_row_ror(8)>(mm));
     const uint32_t mq = mbs_mantissa(mm);
     const float f = (float)(256u + mq) * 0x1p-8f;
@@ -305,11 +310,21 @@ __global__ __launch_bounds__(kThreads) void quant_mbs_kernel(const u32x4* __rest
     q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, o[6], o[7], 1.0f, 3);
     if (nonfinite) q = 0;
     if (c < nchunks) __builtin_nontemporal_store(q, codes + c);
-    const uint32_t s4 = dpp<dpp_row_shr(4)>(E);
-    const uint32_t s8 = dpp<dpp_row_shr(8)>(E);
-    const uint32_t s12 = dpp<dpp_row_shr(12)>(E);
-    if ((lane & 15) == 15 && c < nchunks)
-      *(uint32_t*)(scales + ((c >> 2) - 3)) = s12 | (s8 << 8) | (s4 << 16) | (E << 24);
+    if (BASE == 32) {
+      // Lanes 3, 7, 11, 15 of the row hold the macro block's 4 scales.
+      const uint32_t s4 = dpp<dpp_row_shr(4)>(E);
+      const uint32_t s8 = dpp<dpp_row_shr(8)>(E);
+      const uint32_t s12 = dpp<dpp_row_shr(12)>(E);
+      if ((lane & 15) == 15 && c < nchunks)
+        *(uint32_t*)(scales + ((c >> 2) - 3)) = s12 | (s8 << 8) | (s4 << 16) | (E << 24);
+    } else {
+      // Lanes 1, 3, 5, 7 (and 9 .. 15) hold 4 consecutive scales each.
+      const uint32_t s2 = dpp<dpp_row_shr(2)>(E);
+      const uint32_t s4 = dpp<dpp_row_shr(4)>(E);
+      const uint32_t s6 = dpp<dpp_row_shr(6)>(E);
+      if ((lane & 7) == 7 && c < nchunks)
+        *(uint32_t*)(scales + ((c >> 1) - 3)) = s6 | (s4 << 8) | (s2 << 16) | (E << 24);
+    }
     if ((lane & 15) == 0 && c < nchunks) macro[c >> 4] = (uint8_t)mq;
   }
 }
@@ -480,48 +495,52 @@ hipError_t quant_mx(int fmt, int64_t rows, int64_t cols, const void* x, void* co
     const dim3 pgrid((unsigned)((rows + 31) / 32), (unsigned)(cols / 256));
     const int64_t cpr = cols / 8;
     if (oas && rot)
-      quant_mx_kernel<kMXFP4, true, true, true><<<pgrid, kThreads, 0, s>>>(X, codes, S, rows, cpr);
+      MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP4, true, true, true>, pgrid, kThreads, 0, s, X, codes, S, rows, cpr));
     else if (oas)
-      quant_mx_kernel<kMXFP4, true, false, true><<<pgrid, kThreads, 0, s>>>(X, codes, S, rows, cpr);
+      MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP4, true, false, true>, pgrid, kThreads, 0, s, X, codes, S, rows, cpr));
     else if (rot)
-      quant_mx_kernel<kMXFP4, false, true, true><<<pgrid, kThreads, 0, s>>>(X, codes, S, rows, cpr);
+      MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP4, false, true, true>, pgrid, kThreads, 0, s, X, codes, S, rows, cpr));
     else
-      quant_mx_kernel<kMXFP4, false, false, true><<<pgrid, kThreads, 0, s>>>(X, codes, S, rows, cpr);
-    return hipGetLastError();
+      MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP4, false, false, true>, pgrid, kThreads, 0, s, X, codes, S, rows, cpr));
+    return hipSuccess;
   }
   if (fmt == kMXFP4) {
     if (oas && rot)
-      quant_mx_kernel<kMXFP4, true, true><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
+      MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP4, true, true>, grid, kThreads, 0, s, X, codes, S, nchunks, (int64_t)0));
     else if (oas)
-      quant_mx_kernel<kMXFP4, true, false><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
+      MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP4, true, false>, grid, kThreads, 0, s, X, codes, S, nchunks, (int64_t)0));
     else if (rot)
-      quant_mx_kernel<kMXFP4, false, true><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
+      MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP4, false, true>, grid, kThreads, 0, s, X, codes, S, nchunks, (int64_t)0));
     else
-      quant_mx_kernel<kMXFP4, false, false><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
+      MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP4, false, false>, grid, kThreads, 0, s, X, codes, S, nchunks, (int64_t)0));
   } else if (fmt == kMXFP8) {
     if (rot)
-      quant_mx_kernel<kMXFP8, false, true><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
+      MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP8, false, true>, grid, kThreads, 0, s, X, codes, S, nchunks, (int64_t)0));
     else
-      quant_mx_kernel<kMXFP8, false, false><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
+      MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP8, false, false>, grid, kThreads, 0, s, X, codes, S, nchunks, (int64_t)0));
   } else if (fmt == kMXFP8E5M2) {
-    quant_mx_kernel<kMXFP8E5M2, false, false><<<grid, kThreads, 0, s>>>(X, codes, S, nchunks);
+    MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP8E5M2, false, false>, grid, kThreads, 0, s, X, codes, S, nchunks, (int64_t)0));
   } else {
     const int64_t nblocks = rows * cols / 32;
-    quant_mxfp6_kernel<<<(unsigned)((nblocks + kThreads - 1) / kThreads), kThreads, 0, s>>>(
-        X, (u32x2*)codes, S, nblocks);
+    MX_TRY(launch_kernel(&quant_mxfp6_kernel, (unsigned)((nblocks + kThreads - 1) / kThreads), kThreads, 0, s, 
+        X, (u32x2*)codes, S, nblocks));
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 // nchunks is a multiple of 16 (cols % 128 = 0), so every DPP row is either
 // wholly inside the tensor or wholly past its end.
 hipError_t quant_mbs(int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
-                     hipStream_t s) {
+                     hipStream_t s, int base) {
   const int64_t nchunks = rows * cols / 8;
   uint8_t* S = (uint8_t*)scales;
-  quant_mbs_kernel<<<(unsigned)grid_for(nchunks), kThreads, 0, s>>>(
-      (const u32x4*)x, (uint32_t*)codes, S, S + rows * (cols / 32), nchunks);
-  return hipGetLastError();
+  if (base == 16)
+    MX_TRY(launch_kernel(&quant_mbs_kernel<16>, (unsigned)grid_for(nchunks), kThreads, 0, s,
+                         (const u32x4*)x, (uint32_t*)codes, S, S + rows * (cols / 16), nchunks));
+  else
+    MX_TRY(launch_kernel(&quant_mbs_kernel<32>, (unsigned)grid_for(nchunks), kThreads, 0, s,
+                         (const u32x4*)x, (uint32_t*)codes, S, S + rows * (cols / 32), nchunks));
+  return hipSuccess;
 }
 
 size_t quant_nvfp4_workspace(int64_t, int64_t) { return kMaxPartials * sizeof(uint32_t); }
@@ -533,10 +552,10 @@ hipError_t quant_nvfp4(int64_t rows, int64_t cols, const void* x, void* codes, v
   if (np > kMaxPartials) np = kMaxPartials;
   if (np < 1) np = 1;
   uint32_t* partial = (uint32_t*)workspace;
-  nvfp4_amax_partial<<<(unsigned)np, kThreads, 0, s>>>((const u32x4*)x, nchunks, partial);
-  quant_nvfp4_kernel<<<(unsigned)grid_for(nchunks), kThreads, 0, s>>>(
-      (const u32x4*)x, (uint32_t*)codes, (uint8_t*)scales, partial, (int)np, tensor_scale, nchunks);
-  return hipGetLastError();
+  MX_TRY(launch_kernel(&nvfp4_amax_partial, (unsigned)np, kThreads, 0, s, (const u32x4*)x, nchunks, partial));
+  MX_TRY(launch_kernel(&quant_nvfp4_kernel, (unsigned)grid_for(nchunks), kThreads, 0, s, 
+      (const u32x4*)x, (uint32_t*)codes, (uint8_t*)scales, partial, (int)np, tensor_scale, nchunks));
+  return hipSuccess;
 }
 
 }  // namespace mx

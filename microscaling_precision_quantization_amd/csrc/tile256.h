@@ -108,5 +108,70 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][NT], uint8_t* 
   }
 }
 
+// fp32 accumulation in segments. A wave's fp32 accumulator chain over K is
+// kept to at most 48 matrix instructions: after each segment the accumulators
+// are added into the wave's block of the fp32 output C (stored on the first
+// segment, one fp32 rounding per later one), then cleared. With every
+// accumulation step rounding once, an output then errs by at most
+// (48 + number of segments) * 2^-24 * sum|ab|, within 2^-18 * sum|ab| for up
+// to 16 segments, where one chain over all of K (K / 64 steps for the FP4
+// kernel, K / 16 for the 16-bit ones) could not guarantee it beyond 64 steps.
+// On the last segment the sum is multiplied by `scale` (the NVFP4 tensor
+// scales; 1 otherwise). Same element mapping as store_tile; each lane reads
+// and writes its own runs of 4 columns directly (no LDS), so the fold needs no
+// barrier. The caller zeroes the accumulators afterwards.
+template <int NT = 4, int WNW = 2>
+__device__ __forceinline__ void fold_tile(const f32x16 (&acc)[4][NT], float* __restrict__ C,
+                                          int64_t ldc, int M, int N, int m0, int n0, int wave,
+                                          int lane, bool first, bool last, float scale) {
+  const int wm = wave / WNW, wn = wave % WNW;
+  const int r = lane & 31, g = lane >> 5;
+  constexpr int kCols = 32 * NT;
+  const bool vec_ok = (ldc % 4) == 0;
+  // This lane's stores of the previous segment are complete before it reads
+  // them back (it only ever reads what it wrote itself).
+  if (!first) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int row = m0 + wm * 128 + i * 32 + r;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < NT; j++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int col = n0 + wn * kCols + j * 32 + 8 * q + 4 * g;
+        float* p = C + (int64_t)row * ldc + col;
+        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                      acc[i][j][4 * q + 3]};
+        if (vec_ok && col + 4 <= N) {
+          if (!first) {
+            const f32x4 o = *(const f32x4*)p;
+            v[0] += o.x;
+            v[1] += o.y;
+            v[2] += o.z;
+            v[3] += o.w;
+          }
+          if (last) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) v[e] *= scale;
+          }
+          *(f32x4*)p = f32x4{v[0], v[1], v[2], v[3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            if (col + e >= N) continue;
+            float w = v[e];
+            if (!first) w += p[e];
+            if (last) w *= scale;
+            p[e] = w;
+          }
+        }
+        // One run at a time: hoisting all 64 loads ahead would need 256 more
+        // VGPRs in a kernel that has none to spare.
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+}
+
 }  // namespace tile256
 }  // namespace mx

@@ -17,21 +17,23 @@ import numpy as np
 from . import build as _build
 
 FMT_BF16, FMT_MXFP4, FMT_MXFP8, FMT_NVFP4 = 0, 1, 2, 3
-FMT_MXFP8_E5M2, FMT_MXFP6_E3M2, FMT_MXFP4_MBS = 4, 5, 6
+FMT_MXFP8_E5M2, FMT_MXFP6_E3M2, FMT_MXFP4_MBS, FMT_MXFP4_MBS16 = 4, 5, 6, 7
 RULE_CEIL, RULE_OAS = 0, 1
 ROT_NONE, ROT_WHT32 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 BLOCK = {FMT_MXFP4: 32, FMT_MXFP8: 32, FMT_NVFP4: 16, FMT_MXFP8_E5M2: 32, FMT_MXFP6_E3M2: 32,
-         FMT_MXFP4_MBS: 32}
+         FMT_MXFP4_MBS: 32, FMT_MXFP4_MBS16: 16}
 
 _lib = None
 
 
 def lib():
-    """Load liboracle.so, compiling it first if it is missing or stale."""
+    """Load liboracle.so, compiling it first if it is missing or stale.
+    MX_ORACLE_LIB, if set, names another build of the same source to load
+    instead (the sanitizer build, in the sanitizer test's child process)."""
     global _lib
     if _lib is None:
-        path = _build.build(force=False)
+        path = os.environ.get("MX_ORACLE_LIB") or _build.build(force=False)
         L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i64 = ctypes.c_int64
@@ -68,8 +70,15 @@ def lib():
         L.mxo_gemm_entries.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64,
                                        P, P, ctypes.c_float, P, P, ctypes.c_float,
                                        i64, P, P, P, P]
+        L.mxo_num_threads.restype = ctypes.c_int
+        L.mxo_num_threads.argtypes = []
         _lib = L
     return _lib
+
+
+def num_threads():
+    """Host threads the GEMM routines use (OpenMP's limit)."""
+    return int(lib().mxo_num_threads())
 
 
 def _ptr(a):
@@ -148,19 +157,19 @@ def code_shape(fmt, rows, cols):
 
 
 def scale_shape(fmt, rows, cols):
-    """[rows][cols/block]; MXFP4-MBS: one flat buffer holding the E8M0 plane
-    [rows][cols/32] and then the macro plane [rows][cols/128]."""
-    if fmt == FMT_MXFP4_MBS:
-        return (rows * (cols // 32) + rows * (cols // 128),)
+    """[rows][cols/block]; MXFP4-MBS / MBS16: one flat buffer holding the E8M0
+    plane [rows][cols/block] and then the macro plane [rows][cols/128]."""
+    if fmt in (FMT_MXFP4_MBS, FMT_MXFP4_MBS16):
+        return (rows * (cols // BLOCK[fmt]) + rows * (cols // 128),)
     return (rows, cols // BLOCK[fmt])
 
 
-def mbs_planes(scales, rows, cols):
-    """Split an MXFP4-MBS scale buffer into (E8M0 [rows][cols/32],
-    macro mantissas [rows][cols/128])."""
+def mbs_planes(scales, rows, cols, block=32):
+    """Split an MXFP4-MBS (block 32) or MBS16 (block 16) scale buffer into
+    (E8M0 [rows][cols/block], macro mantissas [rows][cols/128])."""
     s = np.asarray(scales).reshape(-1)
-    n = rows * (cols // 32)
-    return s[:n].reshape(rows, cols // 32), s[n:].reshape(rows, cols // 128)
+    n = rows * (cols // block)
+    return s[:n].reshape(rows, cols // block), s[n:].reshape(rows, cols // 128)
 
 
 def pack_kpanel(codes, scales, rows, cols):

@@ -26,6 +26,9 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* ------------------------------------------------------------------------ */
 /* Element and scale formats                                                  */
@@ -213,23 +216,25 @@ static uint8_t elem_encode(int fmt, double v) {
 }
 
 static int fmt_block(int fmt) {
-  return (fmt == MXO_FMT_NVFP4) ? 16 : 32;
+  return (fmt == MXO_FMT_NVFP4 || fmt == MXO_FMT_MXFP4_MBS16) ? 16 : 32;
 }
+
+static int is_mbs(int fmt) { return fmt == MXO_FMT_MXFP4_MBS || fmt == MXO_FMT_MXFP4_MBS16; }
 
 /* Elements per row must be a multiple of this: the block, or the 128-element
  * macro block of MXFP4-MBS. */
 static int fmt_granule(int fmt) {
-  return (fmt == MXO_FMT_MXFP4_MBS) ? 128 : fmt_block(fmt);
+  return is_mbs(fmt) ? 128 : fmt_block(fmt);
 }
 
 /* 4 bits per element plus 8 bits per 32-element block is the page's
  * "4 + 8/32 = 4.25 bits per element". */
 int64_t mxo_storage_bytes(int fmt, int64_t rows, int64_t cols) {
-  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_MXFP4_MBS) return -1;
+  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_MXFP4_MBS16) return -1;
   int64_t n = rows * cols;
   int64_t code_bytes = n * elem_bits(fmt) / 8;
   int64_t scale_bytes = n / fmt_block(fmt);
-  int64_t extra = (fmt == MXO_FMT_NVFP4) ? 4 : (fmt == MXO_FMT_MXFP4_MBS) ? n / 128 : 0;
+  int64_t extra = (fmt == MXO_FMT_NVFP4) ? 4 : is_mbs(fmt) ? n / 128 : 0;
   return code_bytes + scale_bytes + extra;
 }
 
@@ -335,12 +340,14 @@ int mxo_mbs_macro_mantissa(double alpha) {
 }
 
 /* MXFP4-MBS: per macro block of 128, the factor f from the macro amax; then
- * each 32-block quantizes x / f by the MX rule. The scale search compares
- * amax_b with (6 f) 2^n and the codes compare |x| with midpoint * f * 2^(E-127):
- * every product is exact in double, so x / f is never rounded. */
-static void quantize_mbs(int64_t rows, int64_t cols, const uint16_t* x, uint8_t* codes,
+ * each base block of B elements (16, the summary's "1 x 16"; or 32, MXFP4's
+ * own block) quantizes x / f by the MX rule with its own E8M0 exponent. The
+ * scale search compares amax_b with (6 f) 2^n and the codes compare |x| with
+ * midpoint * f * 2^(E-127): every product is exact in double, so x / f is
+ * never rounded. */
+static void quantize_mbs(int64_t rows, int64_t cols, int B, const uint16_t* x, uint8_t* codes,
                          uint8_t* scales) {
-  const int64_t nb = cols / 32, nm = cols / 128;
+  const int64_t nb = cols / B, nm = cols / 128;
   uint8_t* macro = scales + rows * nb;
   for (int64_t r = 0; r < rows; r++) {
     for (int64_t q = 0; q < nm; q++) {
@@ -355,26 +362,26 @@ static void quantize_mbs(int64_t rows, int64_t cols, const uint16_t* x, uint8_t*
       const int m = finite ? mxo_mbs_macro_mantissa(alpha) : 0;
       macro[r * nm + q] = (uint8_t)m;
       const double f = 1.0 + m / 256.0;
-      for (int b = 0; b < 4; b++) {
-        const uint16_t* xb = xm + 32 * b;
-        const int64_t first = r * cols + q * 128 + 32 * b;
-        const int64_t sidx = r * nb + q * 4 + b;
+      for (int b = 0; b < 128 / B; b++) {
+        const uint16_t* xb = xm + B * b;
+        const int64_t first = r * cols + q * 128 + B * b;
+        const int64_t sidx = r * nb + q * (128 / B) + b;
         int bfinite = 1;
         double amax = 0.0;
-        for (int i = 0; i < 32; i++) {
+        for (int i = 0; i < B; i++) {
           if (!bf16_is_finite(xb[i])) bfinite = 0;
           double a = fabs(mxo_bf16_value(xb[i]));
           if (a > amax) amax = a;
         }
         if (!bfinite) {
           scales[sidx] = 255;
-          for (int i = 0; i < 32; i++) put_code(codes, MXO_FMT_MXFP4, first + i, 0);
+          for (int i = 0; i < B; i++) put_code(codes, MXO_FMT_MXFP4, first + i, 0);
           continue;
         }
         const int E = mxo_mx_scale_exponent(amax, 6.0 * f);
         scales[sidx] = (uint8_t)E;
         const double D = ldexp(f, E - 127);
-        for (int i = 0; i < 32; i++)
+        for (int i = 0; i < B; i++)
           put_code(codes, MXO_FMT_MXFP4, first + i, e2m1_nearest_scaled(mxo_bf16_value(xb[i]), D));
       }
     }
@@ -443,10 +450,10 @@ int mxo_quantize(int fmt, int block, int64_t rows, int64_t cols,
                  const uint16_t* x, uint8_t* codes, uint8_t* scales,
                  float* tensor_scale) {
   if (rows <= 0 || cols <= 0 || !x || !codes || !scales) return MXO_ERR_ARG;
-  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_MXFP4_MBS) return MXO_ERR_ARG;
+  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_MXFP4_MBS16) return MXO_ERR_ARG;
   if (block != fmt_block(fmt) || cols % fmt_granule(fmt) != 0) return MXO_ERR_ARG;
-  if (fmt == MXO_FMT_MXFP4_MBS) {
-    quantize_mbs(rows, cols, x, codes, scales);
+  if (is_mbs(fmt)) {
+    quantize_mbs(rows, cols, fmt_block(fmt), x, codes, scales);
     if (tensor_scale) *tensor_scale = 1.0f;
   } else if (is_mx(fmt)) {
     quantize_mx(fmt, rows, cols, x, codes, scales, elem_max(fmt));
@@ -472,9 +479,9 @@ int mxo_quantize_nvfp4_exact_quotient(int64_t rows, int64_t cols,
 
 /* Exact dequantized value of element idx (row-major), in double.
  * MX: element value * 2^(E-127) (x_real = S * x_elem). NVFP4: e * s_b * s_t,
- * which needs at most 2 + 4 + 24 significant bits, so it is exact. MXFP4-MBS:
- * e * 2^(E-127) * (1 + m / 256), m from the macro plane `macro`
- * ([rows][cols/128]; NULL for the other formats). */
+ * which needs at most 2 + 4 + 24 significant bits, so it is exact. MXFP4-MBS
+ * (base block 32 or 16): e * 2^(E-127) * (1 + m / 256), m from the macro plane
+ * `macro` ([rows][cols/128]; NULL for the other formats). */
 static double exact_value(int fmt, const uint8_t* codes, const uint8_t* scales,
                           const uint8_t* macro, float ts, int64_t cols, int64_t idx) {
   int block = fmt_block(fmt);
@@ -483,7 +490,7 @@ static double exact_value(int fmt, const uint8_t* codes, const uint8_t* scales,
   uint8_t code = get_code(codes, fmt, idx);
   double e = elem_value(fmt, code);
   if (fmt == MXO_FMT_NVFP4) return e * mxo_e4m3_value(sc) * (double)ts;
-  if (fmt == MXO_FMT_MXFP4_MBS)
+  if (is_mbs(fmt))
     return e * mxo_e8m0_value(sc) * (1.0 + macro[r * (cols / 128) + c / 128] / 256.0);
   return e * mxo_e8m0_value(sc);
 }
@@ -492,10 +499,10 @@ int mxo_dequantize(int fmt, int block, int64_t rows, int64_t cols,
                    const uint8_t* codes, const uint8_t* scales,
                    float tensor_scale, int out_dtype, void* y) {
   if (rows <= 0 || cols <= 0 || !codes || !scales || !y) return MXO_ERR_ARG;
-  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_MXFP4_MBS) return MXO_ERR_ARG;
+  if (fmt < MXO_FMT_MXFP4 || fmt > MXO_FMT_MXFP4_MBS16) return MXO_ERR_ARG;
   if (block != fmt_block(fmt) || cols % fmt_granule(fmt) != 0) return MXO_ERR_ARG;
   if (out_dtype != MXO_OUT_F32 && out_dtype != MXO_OUT_BF16) return MXO_ERR_ARG;
-  const uint8_t* macro = (fmt == MXO_FMT_MXFP4_MBS) ? scales + rows * (cols / 32) : NULL;
+  const uint8_t* macro = is_mbs(fmt) ? scales + rows * (cols / fmt_block(fmt)) : NULL;
   for (int64_t i = 0; i < rows * cols; i++) {
     float f;
     if (fmt == MXO_FMT_NVFP4) {
@@ -535,8 +542,8 @@ static int gemm_args_ok(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
                         const void* a, const uint8_t* a_scales, const void* b,
                         const uint8_t* b_scales) {
   if (M <= 0 || N <= 0 || K <= 0 || !a || !b) return 0;
-  if (fmt_a < MXO_FMT_BF16 || fmt_a > MXO_FMT_MXFP4_MBS) return 0;
-  if (fmt_b < MXO_FMT_MXFP4 || fmt_b > MXO_FMT_MXFP4_MBS) return 0;
+  if (fmt_a < MXO_FMT_BF16 || fmt_a > MXO_FMT_MXFP4_MBS16) return 0;
+  if (fmt_b < MXO_FMT_MXFP4 || fmt_b > MXO_FMT_MXFP4_MBS16) return 0;
   if (fmt_a != MXO_FMT_BF16 && (!a_scales || K % fmt_granule(fmt_a) != 0)) return 0;
   if (!b_scales || K % fmt_granule(fmt_b) != 0) return 0;
   return 1;
@@ -544,7 +551,7 @@ static int gemm_args_ok(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
 
 /* The macro plane of an MXFP4-MBS operand with `rows` rows, else NULL. */
 static const uint8_t* macro_plane(int fmt, const uint8_t* scales, int64_t rows, int64_t K) {
-  return (fmt == MXO_FMT_MXFP4_MBS) ? scales + rows * (K / 32) : NULL;
+  return is_mbs(fmt) ? scales + rows * (K / fmt_block(fmt)) : NULL;
 }
 
 static void dot_abs(const double* x, const double* y, int64_t K, double* c,
@@ -566,22 +573,29 @@ int mxo_gemm(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
   if (!gemm_args_ok(fmt_a, fmt_b, M, N, K, a, a_scales, b, b_scales) || !C || !S)
     return MXO_ERR_ARG;
   double* bt = (double*)malloc(sizeof(double) * (size_t)(N * K));
-  double* ar = (double*)malloc(sizeof(double) * (size_t)K);
-  if (!bt || !ar) {
-    free(bt);
-    free(ar);
-    return MXO_ERR_ARG;
-  }
+  if (!bt) return MXO_ERR_ARG;
   const uint8_t* ma = macro_plane(fmt_a, a_scales, M, K);
   const uint8_t* mb = macro_plane(fmt_b, b_scales, N, K);
+  int failed = 0;
+  /* Rows are independent: each output entry is one sequential dot product,
+   * whichever thread computes it, so the result does not depend on the
+   * thread count. */
+#pragma omp parallel for schedule(static)
   for (int64_t j = 0; j < N; j++) dequant_row(fmt_b, b, b_scales, mb, b_ts, K, j, bt + j * K);
-  for (int64_t i = 0; i < M; i++) {
-    dequant_row(fmt_a, a, a_scales, ma, a_ts, K, i, ar);
-    for (int64_t j = 0; j < N; j++) dot_abs(ar, bt + j * K, K, &C[i * N + j], &S[i * N + j]);
+#pragma omp parallel reduction(| : failed)
+  {
+    double* ar = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!ar) failed = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; i++) {
+      if (!ar) continue;
+      dequant_row(fmt_a, a, a_scales, ma, a_ts, K, i, ar);
+      for (int64_t j = 0; j < N; j++) dot_abs(ar, bt + j * K, K, &C[i * N + j], &S[i * N + j]);
+    }
+    free(ar);
   }
   free(bt);
-  free(ar);
-  return MXO_OK;
+  return failed ? MXO_ERR_ARG : MXO_OK;
 }
 
 int mxo_gemm_entries(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
@@ -594,23 +608,34 @@ int mxo_gemm_entries(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
     return MXO_ERR_ARG;
   for (int64_t t = 0; t < n_entries; t++)
     if (ii[t] < 0 || ii[t] >= M || jj[t] < 0 || jj[t] >= N) return MXO_ERR_ARG;
-  double* ar = (double*)malloc(sizeof(double) * (size_t)K);
-  double* br = (double*)malloc(sizeof(double) * (size_t)K);
-  if (!ar || !br) {
-    free(ar);
-    free(br);
-    return MXO_ERR_ARG;
-  }
   const uint8_t* ma = macro_plane(fmt_a, a_scales, M, K);
   const uint8_t* mb = macro_plane(fmt_b, b_scales, N, K);
-  for (int64_t t = 0; t < n_entries; t++) {
-    dequant_row(fmt_a, a, a_scales, ma, a_ts, K, ii[t], ar);
-    dequant_row(fmt_b, b, b_scales, mb, b_ts, K, jj[t], br);
-    dot_abs(ar, br, K, &C[t], &S[t]);
+  int failed = 0;
+#pragma omp parallel reduction(| : failed)
+  {
+    double* ar = (double*)malloc(sizeof(double) * (size_t)K);
+    double* br = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!ar || !br) failed = 1;
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t t = 0; t < n_entries; t++) {
+      if (!ar || !br) continue;
+      dequant_row(fmt_a, a, a_scales, ma, a_ts, K, ii[t], ar);
+      dequant_row(fmt_b, b, b_scales, mb, b_ts, K, jj[t], br);
+      dot_abs(ar, br, K, &C[t], &S[t]);
+    }
+    free(ar);
+    free(br);
   }
-  free(ar);
-  free(br);
-  return MXO_OK;
+  return failed ? MXO_ERR_ARG : MXO_OK;
+}
+
+/* Threads the GEMM routines use (OpenMP's limit; 1 in a build without it). */
+int mxo_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }
 
 /* ------------------------------------------------------------------------ */

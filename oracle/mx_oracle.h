@@ -51,7 +51,11 @@ enum {
   MXO_FMT_NVFP4 = 3, /* E2M1 codes, one E4M3 scale per 16, fp32 tensor scale */
   MXO_FMT_MXFP8_E5M2 = 4, /* E5M2 codes, one E8M0 scale per 32 */
   MXO_FMT_MXFP6_E3M2 = 5, /* E3M2 codes (6 bits, packed), one E8M0 scale per 32 */
-  MXO_FMT_MXFP4_MBS = 6   /* MXFP4 plus one 8-bit macro mantissa per 128 (MBS-static) */
+  MXO_FMT_MXFP4_MBS = 6,  /* MBS-static over MXFP4's 32-element E8M0 blocks (a
+                             reading: base block 32) */
+  MXO_FMT_MXFP4_MBS16 = 7 /* MBS-static as the gist.science summary prints it:
+                             E2M1 codes, one E8M0 per 16-element base block,
+                             one 8-bit macro mantissa per 128 */
 };
 enum { MXO_OUT_F32 = 0, MXO_OUT_BF16 = 1 };
 enum { MXO_OK = 0, MXO_ERR_ARG = 1 };
@@ -89,7 +93,7 @@ int mxo_mx_scale_exponent(double amax, double emax);
 int mxo_mbs_macro_mantissa(double alpha);
 
 /* Bytes of codes + scales (+4 for the NVFP4 tensor scale, + one macro byte
- * per 128 elements for MXFP4-MBS). */
+ * per 128 elements for MXFP4-MBS and MXFP4-MBS16). */
 int64_t mxo_storage_bytes(int fmt, int64_t rows, int64_t cols);
 
 /* ---- tensor operations, row-major, blocks along cols ------------------- */
@@ -97,14 +101,14 @@ int64_t mxo_storage_bytes(int fmt, int64_t rows, int64_t cols);
  * low nibble), [rows][cols] (FP8) or [rows][3 cols/4] (FP6: element i of a row
  * in bits 6i .. 6i+5 of the row's bytes, little-endian); scales: [rows][cols/block] bytes;
  * tensor_scale: NVFP4 only (written), may be NULL otherwise.
- * MXFP4-MBS (block 32, cols a multiple of 128): codes as MXFP4; scales holds
- * two planes, the E8M0 bytes [rows][cols/32] followed by the macro mantissas
- * [rows][cols/128]. Per macro block of 128: m = mxo_mbs_macro_mantissa(amax)
- * (0 if the macro block holds Inf or NaN), f = 1 + m / 256; per 32-block:
- * E = smallest n with amax_b <= 6 f 2^n, plus 127, clamped to [0, 254], and
- * each code the nearest-even E2M1 value of x / (f 2^(E-127)), saturating, sign
- * copied; a 32-block holding Inf or NaN gets E = 255 and zero codes. The
- * dequantized value is e * 2^(E-127) * f. */
+ * MXFP4-MBS16 (block 16) and MXFP4-MBS (block 32), cols a multiple of 128:
+ * codes as MXFP4; scales holds two planes, the E8M0 bytes [rows][cols/block]
+ * followed by the macro mantissas [rows][cols/128]. Per macro block of 128:
+ * m = mxo_mbs_macro_mantissa(amax) (0 if the macro block holds Inf or NaN),
+ * f = 1 + m / 256; per base block: E = smallest n with amax_b <= 6 f 2^n, plus
+ * 127, clamped to [0, 254], and each code the nearest-even E2M1 value of
+ * x / (f 2^(E-127)), saturating, sign copied; a base block holding Inf or NaN
+ * gets E = 255 and zero codes. The dequantized value is e * 2^(E-127) * f. */
 int mxo_quantize(int fmt, int block, int64_t rows, int64_t cols,
                  const uint16_t* x, uint8_t* codes, uint8_t* scales,
                  float* tensor_scale);
@@ -153,6 +157,11 @@ int mxo_gemm_entries(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
                      const void* b, const uint8_t* b_scales, float b_ts,
                      int64_t n_entries, const int64_t* ii, const int64_t* jj,
                      double* C, double* S);
+
+/* Threads the two GEMM routines above run on (OpenMP over output rows or
+ * entries; every entry is still one sequential double-precision loop, so the
+ * results do not depend on the count). */
+int mxo_num_threads(void);
 
 #ifdef __cplusplus
 }

@@ -1,5 +1,6 @@
 """Shared helpers for the GPU parity tests: moving seeded bf16 inputs to the
 device, calling libmx through its C ABI, and the GEMM acceptance bound."""
+import collections
 import functools
 
 import numpy as np
@@ -88,3 +89,20 @@ def check_gemm(got, C, S, out, what=""):
                              f"{np.unravel_index(i, err.shape)}: got {got.flat[i]!r}, oracle "
                              f"{C.flat[i]!r}, tol {tol.flat[i]!r}")
     return float(np.max(np.where(nan_ref, 0, err / np.maximum(S, 1e-300))))
+
+
+_FULL = collections.OrderedDict()
+
+
+def oracle_gemm_cached(key, *args):
+    """orc.gemm(*args), kept for the next test with the same key (the
+    full-size exact GEMMs take seconds on all host cores); at most two results
+    are held."""
+    if key in _FULL:
+        _FULL.move_to_end(key)
+        return _FULL[key]
+    r = orc.gemm(*args)
+    _FULL[key] = r
+    while len(_FULL) > 2:
+        _FULL.popitem(last=False)
+    return r

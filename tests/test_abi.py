@@ -65,6 +65,9 @@ def q(fmt=mx.MX_FMT_MXFP4, block=32, rnd=0, rows=4, cols=64, x=P, codes=P, scale
     (dict(fmt=mx.MX_FMT_MXFP4_MBS, cols=64), mx.MX_ERR_INVALID_ARG),    # macro blocks of 128
     (dict(fmt=mx.MX_FMT_MXFP4_MBS, cols=128, ts=P), mx.MX_ERR_INVALID_ARG),
     (dict(fmt=mx.MX_FMT_MXFP4_MBS, cols=128, block=16), mx.MX_ERR_UNSUPPORTED),
+    (dict(fmt=mx.MX_FMT_MXFP4_MBS16, cols=128, block=32), mx.MX_ERR_UNSUPPORTED),  # base 16
+    (dict(fmt=mx.MX_FMT_MXFP4_MBS16, cols=64, block=16), mx.MX_ERR_INVALID_ARG),
+    (dict(fmt=mx.MX_FMT_MXFP4_MBS16, cols=128, block=16, ts=P), mx.MX_ERR_INVALID_ARG),
 ])
 def test_quantize_rejects(kw, status):
     assert q(**kw) == status
@@ -86,6 +89,7 @@ def qx(fmt=mx.MX_FMT_MXFP4, block=32, rnd=0, rule=0, rot=0, rows=4, cols=64, x=P
     (dict(rot=2), mx.MX_ERR_UNSUPPORTED),
     (dict(rnd=1), mx.MX_ERR_UNSUPPORTED),
     (dict(fmt=mx.MX_FMT_MXFP4_MBS, cols=128), mx.MX_ERR_UNSUPPORTED),  # MBS is its own format
+    (dict(fmt=mx.MX_FMT_MXFP4_MBS16, block=16, cols=128), mx.MX_ERR_UNSUPPORTED),
     (dict(layout=5), mx.MX_ERR_UNSUPPORTED),
     (dict(layout=mx.MX_LAYOUT_KPANEL, fmt=mx.MX_FMT_MXFP8, cols=256), mx.MX_ERR_UNSUPPORTED),
     (dict(layout=mx.MX_LAYOUT_KPANEL, cols=128), mx.MX_ERR_INVALID_ARG),          # cols % 256
@@ -106,6 +110,8 @@ def test_dequantize_rejects():
     assert d(2, 16, 0, 4, 64, P, P, None, 0, P2, None) == mx.MX_ERR_UNSUPPORTED
     assert d(6, 32, 0, 4, 96, P, P, None, 0, P2, None) == mx.MX_ERR_INVALID_ARG  # MBS: cols % 128
     assert d(6, 32, 0, 4, 128, P, P, P, 0, P2, None) == mx.MX_ERR_INVALID_ARG  # MBS takes no ts
+    assert d(7, 32, 0, 4, 128, P, P, None, 0, P2, None) == mx.MX_ERR_UNSUPPORTED  # MBS16: block 16
+    assert d(7, 16, 0, 4, 112, P, P, None, 0, P2, None) == mx.MX_ERR_INVALID_ARG  # cols % 128
 
 
 def g(fa=1, fb=1, block=32, rnd=0, M=64, N=64, K=128, a=P, sa=P, ta=None, b=P, sb=P, tb=None,
@@ -131,11 +137,14 @@ def g(fa=1, fb=1, block=32, rnd=0, M=64, N=64, K=128, a=P, sa=P, ta=None, b=P, s
     (dict(fa=3, fb=3, block=16), mx.MX_ERR_INVALID_ARG),        # NVFP4 needs tensor scales
     (dict(fa=0, fb=1, sa=P), mx.MX_ERR_INVALID_ARG),            # bf16 A has no scales
     (dict(fa=0, fb=1, sa=None, M=16, N=28672, K=8192), mx.MX_ERR_INVALID_ARG),  # no workspace
-    (dict(fa=0, fb=1, sa=None, M=16, N=64, K=1 << 23, ws=P2, wsb=1 << 40), mx.MX_ERR_INVALID_ARG),  # W4A16 K limit
+    (dict(fa=0, fb=1, sa=None, M=16, N=64, K=65536 + 32, ws=P2, wsb=1 << 40), mx.MX_ERR_INVALID_ARG),  # W4A16 K limit
     (dict(fa=6, fb=6, K=160), mx.MX_ERR_INVALID_ARG),           # MBS: K % 128
     (dict(fa=6, fb=1), mx.MX_ERR_UNSUPPORTED),                  # MBS pairs with MBS only
     (dict(fa=6, fb=6, block=16), mx.MX_ERR_UNSUPPORTED),
     (dict(fa=6, fb=6, ta=P), mx.MX_ERR_INVALID_ARG),
+    (dict(fa=7, fb=7, block=32), mx.MX_ERR_UNSUPPORTED),        # MBS16 has block 16
+    (dict(fa=7, fb=6, block=16), mx.MX_ERR_UNSUPPORTED),        # base blocks differ
+    (dict(fa=7, fb=7, block=16, K=160), mx.MX_ERR_INVALID_ARG), # K % 128
 ])
 def test_gemm_rejects(kw, status):
     assert g(**kw) == status
@@ -194,3 +203,34 @@ def pk(fmt=mx.MX_FMT_MXFP4, block=32, rows=4, cols=256, codes=P, scales=ctypes.c
 ])
 def test_pack_rejects(kw, status):
     assert pk(**kw) == status
+
+
+def _visible_gpus():
+    """(status, count) of hipGetDeviceCount from the HIP runtime libmx links."""
+    hip = ctypes.CDLL("libamdhip64.so")
+    n = ctypes.c_int(0)
+    rc = hip.hipGetDeviceCount(ctypes.byref(n))
+    return rc, n.value
+
+
+def test_launch_failure_reports_hip_error():
+    """Valid arguments with no GPU visible: the argument checks pass, the
+    kernel launch itself fails, and the call returns MX_ERR_HIP with that
+    launch's hipError_t saved for mx_last_hip_error (per thread). Only runs
+    where no GPU is visible, so the fake pointers never reach a kernel."""
+    rc, count = _visible_gpus()
+    if rc == 0 and count > 0:
+        pytest.skip("a GPU is visible: the launch would not fail")
+    for call in (lambda: q(),
+                 lambda: mx.mx_quantize_ex(mx.MX_FMT_MXFP4, 32, 0, mx.MX_SCALE_OAS, mx.MX_ROTATE_WHT32,
+                                           4, 256, P, P, P, None, mx.MX_LAYOUT_KPANEL),
+                 lambda: mx.mx_dequantize(mx.MX_FMT_MXFP8, 32, 0, 4, 64, P, P, None, mx.MX_OUT_BF16,
+                                          P2, None),
+                 lambda: mx.mx_gemm(mx.MX_FMT_MXFP4, mx.MX_FMT_MXFP4, 32, 0, 64, 64, 256, P, P, None,
+                                    P2, P2, None, mx.MX_OUT_F32, P, 64, None, 0, None)):
+        assert call() == mx.MX_ERR_HIP
+        err = mx.mx_last_hip_error()
+        assert err != 0
+        # hipErrorNoDevice (100) or another "no usable device" code, as
+        # hipGetDeviceCount itself reported
+        assert err == rc or rc == 0, (err, rc)

@@ -9,8 +9,8 @@ import torch
 import microscaling_precision_quantization_amd as mx
 import oracle as orc
 import synth
-from gpu_helpers import (ORC_FMT, check_gemm, dev_bf16, dev_u8, host, oracle_quant,
-                         qtensor_from_host, require_gpu, workload)
+from gpu_helpers import (ORC_FMT, check_gemm, dev_bf16, dev_u8, host, oracle_gemm_cached,
+                         oracle_quant, qtensor_from_host, require_gpu, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -146,11 +146,11 @@ def _bottom_of_range_rows(X, rows, seed):
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8", "w4a16"])
 def test_bottom_of_e8m0_range(fmt):
     """Weight (and, for W4A4/W8A8, activation) blocks whose E8M0 scale is 0,
-    i.e. 2^-127, and 1 .. 3. The bound adds the underflow floor of the
-    kernel's number formats: each fp32 operation may lose up to 2^-150 in
-    the subnormal range (K * 2^-149 over a dot product), and the bf16
-    expansion of an E4M3 code times 2^-127 rounds to the bf16 subnormal grid
-    (spacing 2^-133), so the MXFP8 path may lose 2^-134 * sum_k |a_k| more."""
+    i.e. 2^-127, and 1 .. 3. The bound adds the underflow floor of fp32: each
+    fp32 operation may lose up to 2^-150 in the subnormal range (K * 2^-149
+    over a dot product). Nothing more: the MXFP8 path's bf16 expansion of
+    e * 2^(E-127) is exact here, because codes quantized from bf16 inputs
+    always land on the bf16 grid (multiples of 2^-133)."""
     M, N, K = 40, 48, 1024
     A = synth.normal((M, K), 1.0, 51)
     B = _bottom_of_range_rows(synth.normal((N, K), 0.02, 52), (7, 8, 9), 53)
@@ -166,8 +166,11 @@ def test_bottom_of_e8m0_range(fmt):
     got = _run(qa, qb, "f32").astype(np.float64)
     floor = K * 2.0**-149
     if fmt == "mxfp8":
-        asum = np.abs(orc.dequantize(fa, a, sa, 1.0, M, K).astype(np.float64)).sum(axis=1)
-        floor = floor + 2.0**-134 * asum[:, None]
+        # the premise of the exact expansion: every dequantized operand value
+        # is a multiple of 2^-133
+        for x in (orc.dequantize(fa, a, sa, 1.0, M, K), orc.dequantize(fb, b, sb, 1.0, N, K)):
+            x = x.astype(np.float64) * 2.0**133
+            assert np.array_equal(x, np.round(x))
     err = np.abs(got - C)
     tol = 2.0**-18 * S + floor
     assert np.all(err <= tol), f"{fmt}: worst err/tol {np.max(err / tol):.3g} at {np.unravel_index(np.argmax(err / tol), err.shape)}"
@@ -176,31 +179,28 @@ def test_bottom_of_e8m0_range(fmt):
     assert np.all(np.abs(got[:4, 7:10]) > 0)
 
 
-# Full-size workloads: the whole output is computed on the GPU; a seeded sample
-# of entries (with every corner and the ragged last tile row/column) is checked
-# against the oracle one by one.
+# Full-size workloads: the whole output is computed on the GPU and every
+# element is checked against the oracle's exact GEMM (double accumulation over
+# all host cores, shared by the tests of one workload).
 WL = [("c2", "mxfp8"), ("c3", "nvfp4"), ("c4", "mxfp4"), ("c5", "w4a16")]
 
 
-def _sample(M, N, n, seed):
-    g = np.random.Generator(np.random.PCG64(seed))
-    ii = np.concatenate([g.integers(0, M, n), [0, 0, M - 1, M - 1], np.full(16, M - 1), g.integers(0, M, 16)])
-    jj = np.concatenate([g.integers(0, N, n), [0, N - 1, 0, N - 1], g.integers(0, N, 16), np.full(16, N - 1)])
-    return ii, jj
+def _workload_oracle(wl, fmt, hostops, M, N, K):
+    return oracle_gemm_cached((wl, fmt, "ceil", None), *hostops[:2], M, N, K, *hostops[2:])
 
 
-@pytest.mark.parametrize("wl,fmt", WL)
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_workload_gemm_sampled(wl, fmt, out):
+@pytest.mark.parametrize("wl,fmt", WL)
+def test_workload_gemm_every_element(wl, fmt, out):
     A, B = workload(wl)
     M, K = A.shape
     N = B.shape[0]
     hostops, qa, qb = _operands(fmt, A, B, wl)
     got = _run(qa, qb, out)
-    ii, jj = _sample(M, N, 3000, 7)
-    C, S = orc.gemm_entries(*hostops[:2], M, N, K, *hostops[2:], ii, jj)
-    check_gemm(got[ii, jj], C, S, out, f"{wl} {fmt} {out}")
     assert np.all(np.isfinite(got))
+    C, S = _workload_oracle(wl, fmt, hostops, M, N, K)
+    rel = check_gemm(got, C, S, out, f"{wl} {fmt} {out}")
+    print(f"{wl} {fmt} {out}: {M * N} outputs checked, max |err| / sum|ab| = {rel:.3g}")
 
 
 def test_gemm_deterministic():
@@ -263,27 +263,25 @@ def test_gemm_kpanel_b(shape, out):
     check_gemm(panel_out, C, S, out, f"kpanel {shape} {out}")
 
 
-def test_gemm_kpanel_b_workload_sampled():
-    """The MLP-down shape with K-panel weights: sampled outputs against the oracle."""
+def test_gemm_kpanel_b_workload_every_element():
+    """The MLP-down shape with K-panel weights: every output against the oracle."""
     A, B = workload("c4")
     M, K = A.shape
     N = B.shape[0]
     hostops, qa, qb = _operands("mxfp4", A, B, "c4")
     got = _run(qa, mx.pack(qb), "bf16")
-    ii, jj = _sample(M, N, 2000, 17)
-    C, S = orc.gemm_entries(*hostops[:2], M, N, K, *hostops[2:], ii, jj)
-    check_gemm(got[ii, jj], C, S, "bf16", "c4 kpanel")
+    C, S = _workload_oracle("c4", "mxfp4", hostops, M, N, K)
+    check_gemm(got, C, S, "bf16", "c4 kpanel")
 
 
 @pytest.mark.parametrize("wl", ["c4", "f1", "f4"])
-def test_bench_step_configuration_sampled(wl):
+def test_bench_step_configuration_every_element(wl):
     """The step bench.py times, at its full size and in its launch
     configuration: the activations quantized on the GPU straight into K
     panels (with the workload's scale rule and rotation), the weights
     quantized (rotated the same way) and packed, bf16 output. Every code and
-    scale of both operands equals the oracle's in K-panel order; sampled
-    outputs (all corners and the last tile row and column among them) are
-    within the bound."""
+    scale of both operands equals the oracle's in K-panel order, and every
+    output is within the bound."""
     w = synth.WORKLOADS[synth.ALIASES[wl]]
     rule, rot = w.get("scale_rule", "ceil"), w.get("rotation")
     A, B = workload(wl)
@@ -299,10 +297,9 @@ def test_bench_step_configuration_sampled(wl):
         pc, ps = orc.pack_kpanel(codes, scales, rows, K)
         assert np.array_equal(host(q.codes).reshape(-1), pc), f"{wl}: {what} codes differ"
         assert np.array_equal(host(q.scales).reshape(-1), ps), f"{wl}: {what} scales differ"
-    ii, jj = _sample(M, N, 2000, 19)
-    C, S = orc.gemm_entries(orc.FMT_MXFP4, orc.FMT_MXFP4, M, N, K, a[0], a[1], 1.0, b[0], b[1], 1.0,
-                            ii, jj)
-    check_gemm(got[ii, jj], C, S, "bf16", f"{wl} bench step")
+    C, S = oracle_gemm_cached((wl, "mxfp4", rule, rot),
+                              orc.FMT_MXFP4, orc.FMT_MXFP4, M, N, K, a[0], a[1], 1.0, b[0], b[1], 1.0)
+    check_gemm(got, C, S, "bf16", f"{wl} bench step")
 
 
 @pytest.mark.parametrize("shape", [(256, 256, 256), (300, 520, 768), (37, 1000, 4096)])

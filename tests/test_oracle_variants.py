@@ -121,3 +121,43 @@ def test_variant_arguments_rejected():
         orc.quantize_ex(orc.FMT_MXFP8, x, orc.RULE_OAS)  # OAS is MXFP4's rule
     with pytest.raises(Exception):
         orc.quantize_ex(orc.FMT_NVFP4, x, orc.RULE_CEIL)
+
+
+def test_wht32_close_to_exact_rotation_on_outlier_blocks():
+    """The oracle's rotation against the exact one on data where fp32 sums
+    round (the MLP-down activations: Laplace with x100 outlier channels, plus
+    blocks mixing values 2^20 apart): each output y_i must lie within the
+    rounding budget of the exact (H x)_i / sqrt(32), computed in rational
+    arithmetic with 1/sqrt(32) to 80 bits. Budget, with u = 2^-24: five fp32
+    butterfly levels gamma_5 sum|x| (gamma_5 = 5u / (1 - 5u)), the rounded
+    constant and the product 2u |H x| / sqrt(32), then the bf16 rounding
+    2^-8 |t| of the fp32 value t (or 2^-134 below bf16's normal range). A
+    wrong sign, pairing or constant misses this by orders of magnitude."""
+    from fractions import Fraction
+    import math
+    A = synth.laplace_outlier_channels((8, 2048), 401, 403, 0.005, 100.0)
+    g = synth.rng(77)
+    B = synth.bf16_bits(g.normal(0, 1, (4, 2048)) * np.exp2(g.integers(-10, 11, (4, 2048))))
+    X = np.concatenate([A, B], 0)
+    Y = orc.wht32(X)
+    xv = synth.bf16_to_f32(X).astype(np.float64)
+    yv = synth.bf16_to_f32(Y).astype(np.float64)
+    H = np.array([[(-1) ** bin(i & j).count("1") for j in range(32)] for i in range(32)])
+    inv_sqrt32 = Fraction(math.isqrt(2**160 // 32), 2**80)  # 1/sqrt(32) to 80 bits
+    u = 2.0**-24
+    gamma5 = 5 * u / (1 - 5 * u)
+    worst = 0.0
+    for r in range(X.shape[0]):
+        for b in range(X.shape[1] // 32):
+            x = [Fraction(float(v)) for v in xv[r, 32 * b:32 * b + 32]]
+            s_abs = float(sum(abs(v) for v in x))
+            for i in range(32):
+                z = sum(x[j] if H[i, j] > 0 else -x[j] for j in range(32))
+                exact = float(z * inv_sqrt32)
+                t_bound = abs(exact) * (1 + 2 * u) + gamma5 * s_abs / math.sqrt(32) * (1 + u)
+                budget = (gamma5 * s_abs / math.sqrt(32) * (1 + u) + 2.0 * u * abs(exact)
+                          + max(2.0**-8 * t_bound, 2.0**-134))
+                err = abs(yv[r, 32 * b + i] - exact)
+                assert err <= budget, (r, b, i, yv[r, 32 * b + i], exact, err, budget)
+                worst = max(worst, err / budget)
+    print(f"wht32: worst error / budget = {worst:.3f}")
