@@ -113,6 +113,16 @@ WORKLOADS = {
         fmt="mxfp4_mbs", M=4608, N=3072, K=12288,
         a=("laplace_outlier_channels", 401, 403, 0.005, 100.0),
         b=("normal", 0.02, 402)),
+    "mxfp4mbs16_dit_mlp_down_4608x12288x3072": dict(
+        fmt="mxfp4_mbs16", M=4608, N=3072, K=12288,
+        a=("laplace_outlier_channels", 401, 403, 0.005, 100.0),
+        b=("normal", 0.02, 402)),
+    # The decode weights alone (28672 x 8192 bf16, 470 MB, beyond the
+    # last-level cache): their MXFP4 quantization is the largest HBM-bound
+    # quantize of the workloads.
+    "mxfp4_quantize_decode_weights_28672x8192": dict(
+        fmt="mxfp4", M=28672, N=0, K=8192, step="quantize",
+        a=("normal", 0.02, 502), b=None),
 }
 
 # Short names used on the command line and in tests.
@@ -127,6 +137,8 @@ ALIASES = {
     "f2b": "mxfp6e3m2_dit_qkv_4608x3072x9216",
     "f3": "mxfp4mbs_dit_mlp_down_4608x12288x3072",
     "f4": "mxfp4wht32_dit_mlp_down_4608x12288x3072",
+    "f3b": "mxfp4mbs16_dit_mlp_down_4608x12288x3072",
+    "c5w": "mxfp4_quantize_decode_weights_28672x8192",
 }
 
 
@@ -152,7 +164,7 @@ def workload(name, rows_a=None, rows_b=None):
     M = w["M"] if rows_a is None else rows_a
     N = w["N"] if rows_b is None else rows_b
     A = _draw(w["a"], (M, w["K"]))
-    B = _draw(w["b"], (N, w["K"]))
+    B = _draw(w["b"], (N, w["K"])) if w["b"] is not None else None
     return A, B
 
 
