@@ -195,29 +195,29 @@ struct Scales {
 // The MFMAs of tile (i, j) in macro block Q: the block-scaled partial sum
 // over its 128 K, the first from zero. BASE 32: two MFMAs, each lane's 32
 // codes under one scale. BASE 16: the scaled MFMA takes one scale per lane's
-// 32 codes, so each 32 is split into two MFMAs over its halves (the other
-// half zero), each under its own 16-block scale -- exact, at twice the MFMAs.
+// 32 codes, so each 32 is split into two MFMAs over its halves, each under
+// its own 16-block scales -- exact, at twice the MFMAs. Only the B operand
+// needs its other half zeroed (bl / bh, built once per B tile by the
+// caller): A's codes there then meet zeros, and every code times a finite
+// scale is finite (a NaN scale, 255, makes the output NaN either way, as the
+// block it belongs to does).
 template <int Q, int BASE>
-__device__ __forceinline__ f32x16 partial(const Frags& f, const Scales& sc, int i, int j) {
+__device__ __forceinline__ f32x16 partial(const Frags& f, const Scales& sc, int i, int j,
+                                          const i32x8 (&bl)[2], const i32x8 (&bh)[2]) {
   if (BASE == 32) {
     f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
         widen(f.b[j][0]), widen(f.a[i][0]), f32x16{}, 4, 4, 2 * Q, sc.b[j], 2 * Q, sc.a[i]);
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
         widen(f.b[j][1]), widen(f.a[i][1]), p, 4, 4, 2 * Q + 1, sc.b[j], 2 * Q + 1, sc.a[i]);
   }
-  // (fences: one zero-padded operand pair at a time, so the padded copies
-  // need few registers)
   f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-      lo16(f.b[j][0]), lo16(f.a[i][0]), f32x16{}, 4, 4, 2 * Q, sc.b[j], 2 * Q, sc.a[i]);
-  sched_fence();
+      bl[0], widen(f.a[i][0]), f32x16{}, 4, 4, 2 * Q, sc.b[j], 2 * Q, sc.a[i]);
   p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-      hi16(f.b[j][0]), hi16(f.a[i][0]), p, 4, 4, 2 * Q, sc.b2[j], 2 * Q, sc.a2[i]);
-  sched_fence();
+      bh[0], widen(f.a[i][0]), p, 4, 4, 2 * Q, sc.b2[j], 2 * Q, sc.a2[i]);
   p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-      lo16(f.b[j][1]), lo16(f.a[i][1]), p, 4, 4, 2 * Q + 1, sc.b[j], 2 * Q + 1, sc.a[i]);
-  sched_fence();
+      bl[1], widen(f.a[i][1]), p, 4, 4, 2 * Q + 1, sc.b[j], 2 * Q + 1, sc.a[i]);
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-      hi16(f.b[j][1]), hi16(f.a[i][1]), p, 4, 4, 2 * Q + 1, sc.b2[j], 2 * Q + 1, sc.a2[i]);
+      bh[1], widen(f.a[i][1]), p, 4, 4, 2 * Q + 1, sc.b2[j], 2 * Q + 1, sc.a2[i]);
 }
 
 // Macro block Q of the current super-step, tile by tile over the wave's 8
@@ -240,15 +240,23 @@ __device__ __forceinline__ void macro_step(const uint8_t* cur, const Frags& f, c
   for (int i = 0; i < 4; i++) fa[i] = FA[wm * 128 + i * 32 + r];
 #pragma unroll
   for (int j = 0; j < 2; j++) fb[j] = FB[wn * 64 + j * 32 + r];
+  i32x8 bl[2], bh[2];  // BASE 16: B's halves of the current j, the other half zero
 #pragma unroll
   for (int k = 0; k < 8; k++) {
     const int i = k & 3, j = k >> 2;
+    if (BASE == 16 && i == 0) {
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        bl[h] = lo16(f.b[j][h]);
+        bh[h] = hi16(f.b[j][h]);
+      }
+    }
     sched_fence();
     // The factor MFMA first: it runs while the dependent pair of P waits.
     const f32x16 gk = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(f16x4, u32x2{fb[j], 0u}),
                                                             __builtin_bit_cast(f16x4, u32x2{fa[i], 0u}),
                                                             f32x16{}, 0, 0, 0);
-    const f32x16 p = partial<Q, BASE>(f, sc, i, j);
+    const f32x16 p = partial<Q, BASE>(f, sc, i, j, bl, bh);
 #pragma unroll
     for (int t = 0; t < 16; t++) acc[i][j][t] = __builtin_fmaf(p[t], gk[t], acc[i][j][t]);
   }
