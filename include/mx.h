@@ -289,6 +289,29 @@ mx_status mx_gemm_ex(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd,
                      void* workspace, size_t workspace_bytes, void* stream,
                      mx_layout a_layout, mx_layout b_layout);
 
+/*
+ * mx_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments and results as mx_gemm without the workspace. Where mx_gemm
+ * needs one (mx_gemm_workspace_bytes > 0: the W4A16 pair's split-K partials),
+ * this call uses the library's own scratch instead: a fixed array of
+ * 8 MiB (8388608 bytes) of device memory per GPU, which each GPU the library
+ * runs on holds until the process ends (its address is looked up once per
+ * device, on the first call with that device current). A shape that would
+ * need more returns MX_ERR_INVALID_ARG; for the W4A16 pair that is
+ * 4 * M * N * ceil(K / 2048) > 8388608, so the 16-token decode shape with
+ * N = 28672 and K = 8192 (7.34 MB) fits. The call makes no hipMalloc, hipFree
+ * or other allocating call. Every call on one GPU shares that GPU's scratch:
+ * calls that overlap on one GPU (several streams or threads at once) race and
+ * must be serialized by the caller; the scratch needs no clearing, since each
+ * call writes every partial it reads.
+ */
+mx_status mx_gemm_noalloc(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd,
+                          int64_t M, int64_t N, int64_t K,
+                          const void* a, const void* a_scales, const float* a_ts,
+                          const void* b, const void* b_scales, const float* b_ts,
+                          mx_dtype out_dtype, void* c, int64_t ldc, void* stream);
+
 /* hipError_t saved by the last MX_ERR_HIP returned on the calling thread. */
 int mx_last_hip_error(void);
 

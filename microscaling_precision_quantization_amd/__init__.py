@@ -62,7 +62,7 @@ def mbs_planes(scales, rows, cols, block=32):
 # Symbols declared in include/mx.h.
 EXPORTS = ("mx_quantize", "mx_quantize_workspace_bytes", "mx_quantize_ex", "mx_dequantize",
            "mx_gemm", "mx_gemm_workspace_bytes", "mx_last_hip_error", "mx_status_string",
-           "mx_pack", "mx_gemm_ex")
+           "mx_pack", "mx_gemm_ex", "mx_gemm_noalloc")
 
 _lib = None
 
@@ -102,6 +102,9 @@ def lib():
         L.mx_gemm_ex.restype = i32
         L.mx_gemm_ex.argtypes = [i32, i32, i32, i32, i64, i64, i64, P, P, P, P, P, P, i32, P, i64,
                                  P, sz, P, i32, i32]
+        L.mx_gemm_noalloc.restype = i32
+        L.mx_gemm_noalloc.argtypes = [i32, i32, i32, i32, i64, i64, i64, P, P, P, P, P, P, i32, P,
+                                      i64, P]
         L.mx_pack.restype = i32
         L.mx_pack.argtypes = [i32, i32, i64, i64, P, P, P, P, P]
         L.mx_gemm_workspace_bytes.restype = sz
@@ -146,6 +149,12 @@ def mx_gemm_ex(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales
     return lib().mx_gemm_ex(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales,
                             b_ts, out_dtype, c, ldc, workspace, workspace_bytes, stream, a_layout,
                             b_layout)
+
+
+def mx_gemm_noalloc(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts,
+                    out_dtype, c, ldc, stream):
+    return lib().mx_gemm_noalloc(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales,
+                                 b_ts, out_dtype, c, ldc, stream)
 
 
 def mx_pack(fmt, block, rows, cols, codes, scales, packed_codes, packed_scales, stream):

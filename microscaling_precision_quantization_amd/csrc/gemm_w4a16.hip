@@ -31,10 +31,40 @@
 //  * K is split across workgroups; partial sums go to a workspace and a second
 //    kernel adds them in a fixed order (deterministic, no float atomics).
 // Two accumulator chains per row, each 32 MFMAs per split.
+#include <mutex>
+
 #include "bf16.h"
 #include "mx_internal.h"
 
+// Split-K partials of mx_gemm_noalloc's W4A16 calls: device memory of the
+// library itself, one copy per GPU, held until the process ends (for callers
+// that cannot allocate). Host code never passes this name to a kernel -- on
+// the host it is only a stand-in -- but the address hipGetSymbolAddress
+// returns for the current device.
+static __device__ __align__(256) float scratch[mx::kNoAllocScratchBytes / sizeof(float)];
+
 namespace mx {
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 namespace {
 

@@ -229,6 +229,22 @@ mx_status mx_gemm_ex(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, 
                    a_layout == MX_LAYOUT_KPANEL, b_layout == MX_LAYOUT_KPANEL);
 }
 
+mx_status mx_gemm_noalloc(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, int64_t M,
+                          int64_t N, int64_t K, const void* a, const void* a_scales,
+                          const float* a_ts, const void* b, const void* b_scales,
+                          const float* b_ts, mx_dtype out_dtype, void* c, int64_t ldc,
+                          void* stream) {
+  const size_t need = mx_gemm_workspace_bytes(fmt_a, fmt_b, M, N, K);
+  void* ws = nullptr;
+  if (need > 0) {
+    if (need > mx::kNoAllocScratchBytes) return MX_ERR_INVALID_ARG;
+    const hipError_t e = mx::noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return gemm_impl(fmt_a, fmt_b, block, rnd, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts,
+                   out_dtype, c, ldc, ws, need, stream, false, false);
+}
+
 mx_status mx_pack(mx_format fmt, int block, int64_t rows, int64_t cols, const void* codes,
                   const void* scales, void* packed_codes, void* packed_scales, void* stream) {
   if (fmt != MX_FMT_MXFP4 || block != 32) return MX_ERR_UNSUPPORTED;

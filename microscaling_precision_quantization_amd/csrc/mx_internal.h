@@ -103,6 +103,14 @@ hipError_t gemm_bf16x_large(int fmt, int64_t M, int64_t N, int64_t K, const void
                             const float* ta, const void* b, const void* sb, const float* tb,
                             int out_dtype, void* c, int64_t ldc, hipStream_t s);
 
+// ---- gemm_w4a16.hip: the library's own scratch for mx_gemm_noalloc (the
+// W4A16 split-K partials), a file-scope device array of this many bytes per
+// GPU; noalloc_scratch returns its address on the current device (looked up
+// once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(void** ptr);
+
 // ---- gemm_w4a16.hip (bf16 activations x MXFP4 weights)
 size_t gemm_w4a16_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t gemm_w4a16(int64_t M, int64_t N, int64_t K, const void* a, const void* b,

@@ -227,10 +227,27 @@ def test_launch_failure_reports_hip_error():
                  lambda: mx.mx_dequantize(mx.MX_FMT_MXFP8, 32, 0, 4, 64, P, P, None, mx.MX_OUT_BF16,
                                           P2, None),
                  lambda: mx.mx_gemm(mx.MX_FMT_MXFP4, mx.MX_FMT_MXFP4, 32, 0, 64, 64, 256, P, P, None,
-                                    P2, P2, None, mx.MX_OUT_F32, P, 64, None, 0, None)):
+                                    P2, P2, None, mx.MX_OUT_F32, P, 64, None, 0, None),
+                 # (needs the library's scratch: the device lookup itself fails)
+                 lambda: mx.mx_gemm_noalloc(mx.MX_FMT_BF16, mx.MX_FMT_MXFP4, 32, 0, 16, 4096, 8192,
+                                            P, None, None, P2, P2, None, mx.MX_OUT_BF16, P, 4096,
+                                            None)):
         assert call() == mx.MX_ERR_HIP
         err = mx.mx_last_hip_error()
         assert err != 0
         # hipErrorNoDevice (100) or another "no usable device" code, as
         # hipGetDeviceCount itself reported
         assert err == rc or rc == 0, (err, rc)
+
+
+def test_gemm_noalloc_rejects():
+    """mx_gemm_noalloc checks like mx_gemm, and refuses a W4A16 shape whose
+    split-K partials (4 M N ceil(K / 2048) bytes) exceed its 8 MiB scratch
+    before touching HIP."""
+    n = mx.mx_gemm_noalloc
+    assert n(1, 2, 32, 0, 64, 64, 128, P, P, None, P2, P2, None, 0, P, 64, None) == mx.MX_ERR_UNSUPPORTED
+    assert n(1, 1, 32, 0, 0, 64, 128, P, P, None, P2, P2, None, 0, P, 64, None) == mx.MX_ERR_INVALID_ARG
+    assert n(0, 1, 32, 0, 64, 28672, 8192, P, None, None, P2, P2, None, 1, P, 28672, None) == \
+        mx.MX_ERR_INVALID_ARG  # 29 MB of partials
+    assert n(0, 1, 32, 0, 16, 64, 65536 + 32, P, None, None, P2, P2, None, 1, P, 64, None) == \
+        mx.MX_ERR_INVALID_ARG  # W4A16 K limit
