@@ -367,29 +367,34 @@ __global__ __launch_bounds__(kThreads) void quant_mxfp6_kernel(const u32x4* __re
 // ---- NVFP4 ---------------------------------------------------------------
 
 constexpr int kMaxPartials = 1024;
+constexpr int kAmaxThreads = 1024;   // amax workgroups: 16 waves
+constexpr int kAmaxPartials = 256;   // at most one amax workgroup per CU
+constexpr int kAmaxLoads = 8;        // 16-byte loads in flight per thread
 
-// Per-workgroup partial of max |x| (as bf16 magnitude bits).
-__global__ __launch_bounds__(kThreads) void nvfp4_amax_partial(const u32x4* __restrict__ x,
-                                                               int64_t nchunks,
-                                                               uint32_t* __restrict__ partial) {
-  // Four loads in flight per thread: chunks c + i G, G the grid's width.
+// Per-workgroup partial of max |x| (as bf16 magnitude bits). Few, large
+// workgroups: the encode kernel reduces all partials in every workgroup, one
+// load per thread when there are at most 256 of them.
+__global__ __launch_bounds__(kAmaxThreads) void nvfp4_amax_partial(const u32x4* __restrict__ x,
+                                                                   int64_t nchunks,
+                                                                   uint32_t* __restrict__ partial) {
+  // kAmaxLoads loads in flight per thread: chunks c + i G, G the grid's width.
   uint32_t m = 0;
-  const int64_t G = (int64_t)gridDim.x * kThreads;
-  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nchunks; c += 4 * G) {
-    u32x4 v[4];
+  const int64_t G = (int64_t)gridDim.x * kAmaxThreads;
+  for (int64_t c = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; c < nchunks; c += kAmaxLoads * G) {
+    u32x4 v[kAmaxLoads];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < kAmaxLoads; i++)
       v[i] = (c + i * G < nchunks) ? __builtin_nontemporal_load(x + c + i * G) : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < 4; i++) m = umax(m, chunk_absmax(v[i]));
+    for (int i = 0; i < kAmaxLoads; i++) m = umax(m, chunk_absmax(v[i]));
   }
   for (int off = 32; off > 0; off >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, off));
-  __shared__ uint32_t wmax[kThreads / 64];
+  __shared__ uint32_t wmax[kAmaxThreads / 64];
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t r = 0;
-    for (int w = 0; w < kThreads / 64; w++) r = umax(r, wmax[w]);
+    for (int w = 0; w < kAmaxThreads / 64; w++) r = umax(r, wmax[w]);
     partial[blockIdx.x] = r;
   }
 }
@@ -548,11 +553,11 @@ size_t quant_nvfp4_workspace(int64_t, int64_t) { return kMaxPartials * sizeof(ui
 hipError_t quant_nvfp4(int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
                        float* tensor_scale, void* workspace, hipStream_t s) {
   const int64_t nchunks = rows * cols / 8;
-  int64_t np = (nchunks + kThreads * 8 - 1) / (kThreads * 8);
-  if (np > kMaxPartials) np = kMaxPartials;
+  int64_t np = (nchunks + kAmaxThreads * kAmaxLoads - 1) / (kAmaxThreads * kAmaxLoads);
+  if (np > kAmaxPartials) np = kAmaxPartials;
   if (np < 1) np = 1;
   uint32_t* partial = (uint32_t*)workspace;
-  MX_TRY(launch_kernel(&nvfp4_amax_partial, (unsigned)np, kThreads, 0, s, (const u32x4*)x, nchunks, partial));
+  MX_TRY(launch_kernel(&nvfp4_amax_partial, (unsigned)np, kAmaxThreads, 0, s, (const u32x4*)x, nchunks, partial));
   MX_TRY(launch_kernel(&quant_nvfp4_kernel, (unsigned)grid_for(nchunks), kThreads, 0, s, 
       (const u32x4*)x, (uint32_t*)codes, (uint8_t*)scales, partial, (int)np, tensor_scale, nchunks));
   return hipSuccess;
