@@ -96,6 +96,9 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device-to-device copy of 1 GiB, 5 times (reference "
                         "for scaling the HBM byte counters)")
+    p.add_argument("--mfma-ceiling", action="store_true",
+                   help="only measure what matrix instructions alone sustain on this device "
+                        "(FP4 scaled, bf16, fp16; include/mx_calib.h)")
     return p.parse_args()
 
 
@@ -111,6 +114,39 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_per_dispatch": n, "dispatches": 5}))
+
+
+def mfma_ceiling():
+    """The rate matrix instructions alone sustain (libmx_calib.so), on every CU
+    and on the 216 CUs that the 256 x 256 tiles of the 4608 x 3072 MLP-down
+    output occupy: the clock falls under a steady stream of them, so this, not
+    the published peak, bounds what a GEMM can reach. About 0.2 s of launches
+    per configuration: 40 launches of ~5 ms, the median of the last 20 (the
+    clock settles within the first tens of milliseconds)."""
+    import ctypes
+    import torch
+    torch.cuda.init()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    L = ctypes.CDLL(os.path.join(ROOT, "microscaling_precision_quantization_amd", "libmx_calib.so"))
+    L.mx_calib_mfma.restype = ctypes.c_int
+    L.mx_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)]
+    res = {}
+    for kind, name, peak, iters in ((0, "fp4_scaled_32x32x64", 10100.0, 15000),
+                                    (1, "bf16_32x32x16", 2500.0, 15000),
+                                    (2, "fp16_32x32x16", 2500.0, 15000)):
+        for wgs in (cus, 216):
+            ms, flop = ctypes.c_float(), ctypes.c_double()
+            rc = L.mx_calib_mfma(kind, wgs, iters, 40, ctypes.byref(ms), ctypes.byref(flop))
+            if rc != 0:
+                raise RuntimeError(f"mx_calib_mfma({kind}) failed: {rc}")
+            tf = flop.value / (ms.value * 1e-3) / 1e12
+            res[f"{name}_{wgs}cu"] = {"TFLOP/s": round(tf, 1), "frac_of_peak": round(tf / peak, 4),
+                                      "peak_TFLOP/s": peak, "ms_per_launch": round(ms.value, 3)}
+    print(json.dumps({"mfma_ceiling": res, "cus": cus,
+                      "method": "median of the last 20 of 40 back-to-back ~5 ms launches of "
+                                "MFMA-only kernels on register operands with random bits "
+                                "(include/mx_calib.h)"}))
 
 
 def graph_ms_per_step(torch, fn, nsteps, stream, ramp_s):
@@ -150,6 +186,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.mfma_ceiling:
+        mfma_ceiling()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the kernels "

@@ -1,0 +1,40 @@
+/*
+ * mx_calib.h -- roofline calibration for libmx's measurements (library
+ * libmx_calib.so, built beside libmx.so; not part of the quantize / GEMM path).
+ *
+ * The published MI355X peaks (FP4 10.1 PFLOP/s, bf16 and fp16 2.5 PFLOP/s,
+ * dense) assume the top clock. Under a steady stream of matrix instructions
+ * the chip lowers its clock to stay within its power limit, so a kernel that
+ * does nothing else sets the ceiling any real kernel can reach. This call
+ * measures it.
+ */
+#ifndef MX_CALIB_H
+#define MX_CALIB_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* mx_calib_mfma: on the current device, launch `workgroups` workgroups that
+ * issue only back-to-back matrix instructions of one kind on register
+ * operands filled with pseudo-random bits, `iters` rounds each, `reps` times in
+ * a row on a stream of its own (at most 256), and report the steady state:
+ * the median launch time of the second half, after the clock has settled.
+ *   kind 0: v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands and E8M0
+ *           scales, 4 waves per workgroup, 16 independent 32x32 tiles per
+ *           wave (the MXFP4 GEMM's shape); 131072 FLOP per instruction.
+ *   kind 1: v_mfma_f32_32x32x16_bf16, 8 waves per workgroup, 8 tiles per
+ *           wave (the bf16-expansion GEMM's shape); 32768 FLOP each.
+ *   kind 2: v_mfma_f32_32x32x16_f16, as kind 1.
+ * best_ms: that launch time in milliseconds; flop: FLOP per launch (both
+ * host pointers, written on success). The call allocates and frees its own
+ * device buffer and synchronizes; it is meant for measurement runs, not for
+ * a serving path. Returns 0, or the hipError_t of the first failing HIP call
+ * (-1 for an unknown kind or a non-positive count).
+ */
+int mx_calib_mfma(int kind, int workgroups, int iters, int reps, float* best_ms, double* flop);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MX_CALIB_H */

@@ -57,7 +57,24 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
     os.replace(tmp, OUT)
+    build_calib()
     return OUT
+
+
+CALIB_OUT = os.path.join(HERE, "libmx_calib.so")
+
+
+def build_calib():
+    """libmx_calib.so: the matrix-instruction ceiling of include/mx_calib.h
+    (measurement only; libmx.so does not use it)."""
+    obj, err = _compile("calib.hip")
+    tmp = CALIB_OUT + ".tmp"
+    r = subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", obj, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    os.replace(tmp, CALIB_OUT)
+    return CALIB_OUT
 
 
 if __name__ == "__main__":
