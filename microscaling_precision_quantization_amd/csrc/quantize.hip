@@ -338,30 +338,71 @@ typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 // One lane per 32-block: 64 bytes of bf16 in, 24 bytes of 6-bit codes out
 // (v_cvt_scalef32_pk32_bf6_bf16: nearest-even of x / scale, element i in bits
 // 6i .. 6i+5), one scale byte. emax = 28 = 1.75 * 2^4 -> E = ea - 4 + [m > 0x60].
+// MXFP6 (E3M2): one lane per 32-block, because the convert takes all 32
+// elements of a block at once (v_cvt_scalef32_pk32_bf6_bf16: 32 bf16 -> 24
+// bytes). A workgroup takes 256 consecutive blocks, and both its global
+// traffic directions go through LDS so that every load and store instruction
+// of a wave covers one contiguous range:
+//  * load: 16-byte chunk c of the workgroup's range (lane-consecutive) goes
+//    to LDS at 80 (c / 4) + 16 (c mod 4): blocks padded to 80 bytes, so the
+//    16 lanes of a quarter-wave reading their own blocks' chunk j hit 16
+//    distinct 16-byte bank groups (80 / 16 = 5 is odd);
+//  * store: each lane writes its block's 24 code bytes to LDS at 24 t, and
+//    the workgroup's 6 KB of codes leave as lane-consecutive 16-byte chunks.
+constexpr int kF6Pad = 80;                              // LDS bytes per staged block
+constexpr int kF6Codes = kThreads * 24;                 // code bytes per workgroup
+
 __global__ __launch_bounds__(kThreads) void quant_mxfp6_kernel(const u32x4* __restrict__ x,
-                                                               u32x2* __restrict__ codes,
+                                                               uint8_t* __restrict__ codes,
                                                                uint8_t* __restrict__ scales,
                                                                int64_t nblocks) {
-  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (b >= nblocks) return;
-  u32x4 v[4];
+  __shared__ __attribute__((aligned(16))) uint8_t lin[kThreads * kF6Pad];
+  __shared__ __attribute__((aligned(16))) uint8_t lout[kF6Codes];
+  const int tid = threadIdx.x;
+  const int64_t b0 = (int64_t)blockIdx.x * kThreads;              // first block of the workgroup
+  const int64_t nb = min((int64_t)kThreads, nblocks - b0);         // blocks in it
 #pragma unroll
-  for (int i = 0; i < 4; i++) v[i] = __builtin_nontemporal_load(x + 4 * b + i);
-  const uint32_t m = umax(umax(chunk_absmax(v[0]), chunk_absmax(v[1])),
-                          umax(chunk_absmax(v[2]), chunk_absmax(v[3])));
-  const int ea = (int)(m >> 7), ma = (int)(m & 0x7F);
-  int e = ea - 4 + (ma > 0x60);
-  e = e < 0 ? 0 : e;
-  const bool nonfinite = m >= 0x7F80u;
-  const u32x16 w = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w,
-                    v[2].x, v[2].y, v[2].z, v[2].w, v[3].x, v[3].y, v[3].z, v[3].w};
-  u32x6 q = __builtin_bit_cast(u32x6, __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(
-                                          __builtin_bit_cast(bf16x32, w), e8m0_to_float((uint32_t)e)));
-  if (nonfinite) q = u32x6{0, 0, 0, 0, 0, 0};
-  __builtin_nontemporal_store(u32x2{q[0], q[1]}, codes + 3 * b);
-  __builtin_nontemporal_store(u32x2{q[2], q[3]}, codes + 3 * b + 1);
-  __builtin_nontemporal_store(u32x2{q[4], q[5]}, codes + 3 * b + 2);
-  scales[b] = nonfinite ? (uint8_t)255 : (uint8_t)e;
+  for (int i = 0; i < 4; i++) {
+    const int c = i * kThreads + tid;                              // chunk within the workgroup
+    if (c < 4 * nb) {
+      const u32x4 v = __builtin_nontemporal_load(x + 4 * b0 + c);
+      *(u32x4*)(lin + (c >> 2) * kF6Pad + (c & 3) * 16) = v;
+    }
+  }
+  __syncthreads();
+  if (tid < nb) {
+    u32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) v[j] = *(const u32x4*)(lin + tid * kF6Pad + j * 16);
+    const uint32_t m = umax(umax(chunk_absmax(v[0]), chunk_absmax(v[1])),
+                            umax(chunk_absmax(v[2]), chunk_absmax(v[3])));
+    const int ea = (int)(m >> 7), ma = (int)(m & 0x7F);
+    int e = ea - 4 + (ma > 0x60);
+    e = e < 0 ? 0 : e;
+    const bool nonfinite = m >= 0x7F80u;
+    const u32x16 w = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w,
+                      v[2].x, v[2].y, v[2].z, v[2].w, v[3].x, v[3].y, v[3].z, v[3].w};
+    u32x6 q = __builtin_bit_cast(u32x6, __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(
+                                            __builtin_bit_cast(bf16x32, w), e8m0_to_float((uint32_t)e)));
+    if (nonfinite) q = u32x6{0, 0, 0, 0, 0, 0};
+    *(u32x2*)(lout + tid * 24) = u32x2{q[0], q[1]};
+    *(u32x2*)(lout + tid * 24 + 8) = u32x2{q[2], q[3]};
+    *(u32x2*)(lout + tid * 24 + 16) = u32x2{q[4], q[5]};
+    scales[b0 + tid] = nonfinite ? (uint8_t)255 : (uint8_t)e;
+  }
+  __syncthreads();
+  // 24 nb bytes of codes: 16-byte chunks while whole, then 8-byte pieces
+  // (24 nb is a multiple of 8).
+  uint8_t* out = codes + 24 * b0;
+  const int nbytes = (int)(24 * nb);
+#pragma unroll
+  for (int i = 0; i < (kF6Codes + 16 * kThreads - 1) / (16 * kThreads); i++) {
+    const int o = 16 * (i * kThreads + tid);
+    if (o + 16 <= nbytes)
+      __builtin_nontemporal_store(*(const u32x4*)(lout + o), (u32x4*)(out + o));
+    else if (o + 8 <= nbytes)
+      __builtin_nontemporal_store(*(const u32x2*)(lout + o), (u32x2*)(out + o));
+  }
 }
 
 // ---- NVFP4 ---------------------------------------------------------------
@@ -527,8 +568,8 @@ hipError_t quant_mx(int fmt, int64_t rows, int64_t cols, const void* x, void* co
     MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP8E5M2, false, false>, grid, kThreads, 0, s, X, codes, S, nchunks, (int64_t)0));
   } else {
     const int64_t nblocks = rows * cols / 32;
-    MX_TRY(launch_kernel(&quant_mxfp6_kernel, (unsigned)((nblocks + kThreads - 1) / kThreads), kThreads, 0, s, 
-        X, (u32x2*)codes, S, nblocks));
+    MX_TRY(launch_kernel(&quant_mxfp6_kernel, (unsigned)((nblocks + kThreads - 1) / kThreads), kThreads, 0, s,
+                         X, (uint8_t*)codes, S, nblocks));
   }
   return hipSuccess;
 }
