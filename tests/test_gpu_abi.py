@@ -1,5 +1,6 @@
 """The C ABI on a GPU: a HIP error that an earlier call of the caller left
-pending on the thread is not reported as a failure of a libmx launch."""
+pending on the thread is not reported as a failure of a libmx launch; the
+roofline calibration library runs."""
 import ctypes
 
 import numpy as np
@@ -34,3 +35,22 @@ def test_pending_error_is_not_charged_to_libmx():
     torch.cuda.synchronize()
     oc, os_, _ = orc.quantize(orc.FMT_MXFP4, A)
     assert np.array_equal(host(codes), oc) and np.array_equal(host(scales), os_)
+
+
+def test_mfma_ceiling_calibration_runs():
+    """libmx_calib.so (include/mx_calib.h) on the GPU: each kind launches,
+    reports its FLOP count exactly, and a rate below the published peak."""
+    require_gpu()
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    L = ctypes.CDLL(os.path.join(root, "microscaling_precision_quantization_amd", "libmx_calib.so"))
+    f = L.mx_calib_mfma
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)]
+    for kind, threads, per_wave, peak in ((0, 256, 16 * 131072, 10.1e15), (1, 512, 8 * 32768, 2.5e15),
+                                          (2, 512, 8 * 32768, 2.5e15)):
+        ms, fl = ctypes.c_float(), ctypes.c_double()
+        assert f(kind, 64, 200, 4, ctypes.byref(ms), ctypes.byref(fl)) == 0
+        assert fl.value == 64 * (threads // 64) * 200 * per_wave
+        assert ms.value > 0 and fl.value / (ms.value * 1e-3) < peak
