@@ -26,13 +26,13 @@ extern "C" {
  *   kind 1: v_mfma_f32_32x32x16_bf16, 8 waves per workgroup, 8 tiles per
  *           wave (the bf16-expansion GEMM's shape); 32768 FLOP each.
  *   kind 2: v_mfma_f32_32x32x16_f16, as kind 1.
- * best_ms: that launch time in milliseconds; flop: FLOP per launch (both
+ * steady_ms: that launch time in milliseconds; flop: FLOP per launch (both
  * host pointers, written on success). The call allocates and frees its own
  * device buffer and synchronizes; it is meant for measurement runs, not for
  * a serving path. Returns 0, or the hipError_t of the first failing HIP call
  * (-1 for an unknown kind or a non-positive count).
  */
-int mx_calib_mfma(int kind, int workgroups, int iters, int reps, float* best_ms, double* flop);
+int mx_calib_mfma(int kind, int workgroups, int iters, int reps, float* steady_ms, double* flop);
 
 #ifdef __cplusplus
 }

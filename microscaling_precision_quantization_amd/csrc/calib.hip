@@ -88,8 +88,8 @@ __global__ __launch_bounds__(512, 1) void mfma_16bit_only(float* out, int iters)
 
 }  // namespace
 
-extern "C" int mx_calib_mfma(int kind, int workgroups, int iters, int reps, float* best_ms, double* flop) {
-  if (kind < 0 || kind > 2 || workgroups <= 0 || iters <= 0 || reps <= 0 || !best_ms || !flop) return -1;
+extern "C" int mx_calib_mfma(int kind, int workgroups, int iters, int reps, float* steady_ms, double* flop) {
+  if (kind < 0 || kind > 2 || workgroups <= 0 || iters <= 0 || reps <= 0 || !steady_ms || !flop) return -1;
   const int threads = kind == 0 ? 256 : 512;
   float* out = nullptr;
   hipStream_t s = nullptr;
@@ -122,7 +122,7 @@ extern "C" int mx_calib_mfma(int kind, int workgroups, int iters, int reps, floa
   const double per_wave = kind == 0 ? 16.0 * 131072.0 : 8.0 * 32768.0;
   // steady state: the median of the second half of the launches
   std::sort(ms_all + reps / 2, ms_all + reps);
-  *best_ms = ms_all[reps / 2 + (reps - reps / 2) / 2];
+  *steady_ms = ms_all[reps / 2 + (reps - reps / 2) / 2];
   *flop = (double)workgroups * (threads / 64) * (double)iters * per_wave;
   return 0;
 }
