@@ -14,12 +14,15 @@
 //    super-step (both code tiles and their scales, 68 KB) moves through a
 //    three-deep pipeline: global -> VGPRs (16-byte buffer loads, issued two
 //    super-steps ahead), VGPRs -> LDS (ds_write, one super-step ahead, into
-//    the idle half of a 2 x 68 KB double buffer), LDS -> MFMA. With both
-//    operands in K panels there are two register stages and the loads go
-//    three super-steps ahead (four-deep), which pays at sustained clocks.
-//    The barrier between super-steps waits for LDS work only, so global loads
-//    stay in flight across it. Buffer range checking returns zeros for rows
-//    past M or N.
+//    the idle half of a 2 x 68 KB double buffer), LDS -> MFMA. The barrier
+//    between super-steps waits for LDS work only, so global loads stay in
+//    flight across it. Buffer range checking returns zeros for rows past M
+//    or N.
+//  * The barrier would leave the matrix core idle while a wave's first LDS
+//    reads of the new super-step (its scales and first fragments) come back.
+//    So the second half of each super-step's last sub-step (8 MFMAs, whose
+//    fragments are already in registers) is issued after the barrier, beside
+//    those reads. Each accumulator still sees its MFMAs in K order.
 //  * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at slot
 //    c ^ ((r / 2) mod 8) so that the lanes reading one column of chunks hit
 //    distinct banks (measured with the LDS bank-conflict counter).
@@ -43,6 +46,8 @@
 // l % 32 and rows 8 (t / 4) + 4 g + (t % 4) in accumulator t. The kernel passes
 // B as the first operand, so the output tile is C^T and each lane holds runs
 // of 4 consecutive columns of one row of C.
+#include <type_traits>
+
 #include "mx_internal.h"
 #include "tile256.h"
 
@@ -190,6 +195,23 @@ __device__ __forceinline__ void mfma_substep(const Frags& f, const int (&sa)[4],
   }
 }
 
+// Rows I0 .. I1-1 of sub-step J's MFMAs: those A fragments against all four
+// B fragments (a split sub-step).
+template <int J, int I0, int I1>
+__device__ __forceinline__ void mfma_rows(const Frags& f, const int (&sa)[4], const int (&sb)[4],
+                                          f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = I0; i < I1; i++) {
+    const i32x8 a = i32x8{f.a[i].x, f.a[i].y, f.a[i].z, f.a[i].w, 0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const i32x8 b = i32x8{f.b[j].x, f.b[j].y, f.b[j].z, f.b[j].w, 0, 0, 0, 0};
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc[i][j], 4, 4, J, sb[j],
+                                                                  J, sa[i]);
+    }
+  }
+}
+
 // Keep the compiler from moving instructions across this point.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
@@ -199,12 +221,11 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // they reach the LDS queue ahead of the other waves' staging writes and land
 // before the region ends; then the global loads, then the LDS writes of the
 // staged super-step, which are only needed by the next barrier.
-template <bool WITH_READS>
 __device__ __forceinline__ void interleave() {
 #pragma unroll
   for (int k = 0; k < 4; k++) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (WITH_READS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
 #pragma unroll
   for (int k = 0; k < 5; k++) {
@@ -220,14 +241,59 @@ __device__ __forceinline__ void interleave() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Head of a super-step: the 8 MFMAs carried over from the previous one, with
+// this super-step's 12 LDS reads (scales and sub-step 0's fragments).
+__device__ __forceinline__ void interleave_head() {
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Sub-step 2: the last sub-step's 8 fragment reads, then the LDS writes of
+// the staged super-step's last two parts (so they are complete well before
+// the barrier) and the global loads of its third part.
+__device__ __forceinline__ void interleave_third() {
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// First half of sub-step 3 (8 MFMAs) with the last part's global loads.
+__device__ __forceinline__ void interleave_last() {
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int OUT, bool PANEL_A, bool PANEL_B>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ SB, void* __restrict__ C, int64_t ldc, int M, int N, int K,
-    int tiles_m, int tiles_n) {
-  // Both operands in K panels (the layout of the benchmarked step): two
-  // register stages fit without spills in the loop; the other layouts keep one.
-  constexpr bool DEEP = PANEL_A && PANEL_B;
+    int tiles_m, int tiles_n, int s_begin, int s_end, int fold) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -253,11 +319,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
 #pragma unroll
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
-  const int nsteps = K / kSuperK;
-  // One super-step: MFMAs on LDS buffer s & 1 while the registers Rx (super-
-  // step s + 1) go to LDS buffer (s + 1) & 1 and then receive super-step
-  // s + ahead from memory.
-  auto step = [&](int s, Stage& Rx, int ahead) {
+  // Super-steps s_begin .. s_end-1 of K (all of K unless the fp32 output is
+  // accumulated over several launches, see gemm_mxfp4 below).
+  // Fragments of the odd sub-steps (f1) stay live from one super-step into
+  // the next: the second half of sub-step 3 runs after the barrier.
+  Frags f0, f1;
+  // One super-step: MFMAs on LDS buffer s & 1 while the registers R (super-
+  // step s + 1) go to LDS buffer (s + 1) & 1 and then receive super-step s + 2
+  // from memory. Its scales go to (sa, sb); (pa, pb) hold the previous
+  // super-step's, for the MFMAs carried over from it when `carry` is true.
+  auto step = [&](auto carry, int s, Stage& R, int (&sa)[4], int (&sb)[4], const int (&pa)[4],
+                  const int (&pb)[4]) __attribute__((always_inline)) {
     // Every wave's LDS writes of super-step s are done and every wave is done
     // reading super-step s-1, whose buffer receives super-step s+1 below. Only
     // LDS work is waited for: the global loads stay in flight.
@@ -267,111 +339,104 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
     uint8_t* nxt = smem + ((s + 1) & 1) * kStage;
     // Branch-free body (a branch here lets the compiler sink the MFMAs): the
     // last iterations re-stage the final super-step into the idle buffer.
-    // The registers Rx hold super-step s + 1 and then receive s + ahead.
-    const int s2 = min(s + ahead, nsteps - 1);
+    const int s2 = min(s + 2, s_end - 1);
     const uint8_t* As = cur;
     const uint8_t* Bs = cur + kTileBytes;
     const uint8_t* SAs = cur + 2 * kTileBytes;
     const uint8_t* SBs = SAs + kScaleBytes;
-    int sa[4], sb[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      sa[i] = *(const int*)(SAs + (wm * 128 + i * 32 + r) * 8 + g * 4);
       sb[i] = *(const int*)(SBs + (wn * 128 + i * 32 + r) * 8 + g * 4);
+      sa[i] = *(const int*)(SAs + (wm * 128 + i * 32 + r) * 8 + g * 4);
     }
-    // Each of the 4 regions below issues the 16 MFMAs of one sub-step, the 8
-    // LDS reads of the next sub-step's fragments, a quarter of the staged
-    // super-step's LDS writes and a quarter of the next global loads,
-    // interleaved so that each memory instruction issues in an MFMA's shadow.
-    Frags f0, f1;
     load_frags<0>(As, Bs, wm, wn, r, g, f0);
-    sched_fence();
+    if constexpr (decltype(carry)::value) {
+      mfma_rows<3, 2, 4>(f1, pa, pb, acc);
+      interleave_head();
+    } else {
+      sched_fence();
+    }
+    // Each region below issues the MFMAs of one sub-step, the LDS reads of
+    // the next sub-step's fragments, part of the staged super-step's LDS
+    // writes and part of the next global loads, interleaved so that each
+    // memory instruction issues in an MFMA's shadow.
     load_frags<1>(As, Bs, wm, wn, r, g, f1);
-    store_part<0>(Rx, nxt, wave, lane);
-    load_part<0, PANEL_A, PANEL_B>(Rx, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
+    store_part<0>(R, nxt, wave, lane);
+    load_part<0, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
     mfma_substep<0>(f0, sa, sb, acc);
-    interleave<true>();
+    interleave();
     load_frags<2>(As, Bs, wm, wn, r, g, f0);
-    store_part<1>(Rx, nxt, wave, lane);
-    load_part<1, PANEL_A, PANEL_B>(Rx, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
+    store_part<1>(R, nxt, wave, lane);
+    load_part<1, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
     mfma_substep<1>(f1, sa, sb, acc);
-    interleave<true>();
+    interleave();
     load_frags<3>(As, Bs, wm, wn, r, g, f1);
-    store_part<2>(Rx, nxt, wave, lane);
-    load_part<2, PANEL_A, PANEL_B>(Rx, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
+    store_part<2>(R, nxt, wave, lane);
+    store_part<3>(R, nxt, wave, lane);
+    load_part<2, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
     mfma_substep<2>(f0, sa, sb, acc);
-    interleave<true>();
-    store_part<3>(Rx, nxt, wave, lane);
-    load_part<3, PANEL_A, PANEL_B>(Rx, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
-    mfma_substep<3>(f1, sa, sb, acc);
-    interleave<false>();
+    interleave_third();
+    load_part<3, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
+    mfma_rows<3, 0, 2>(f1, sa, sb, acc);
+    interleave_last();
   };
-  // Super-step 0 goes to LDS buffer 0 through the registers first.
-  Stage R[DEEP ? 2 : 1];
-  load_part<0, PANEL_A, PANEL_B>(R[0], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, A, SA, M, B, SB, N);
-  load_part<1, PANEL_A, PANEL_B>(R[0], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, A, SA, M, B, SB, N);
-  load_part<2, PANEL_A, PANEL_B>(R[0], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, A, SA, M, B, SB, N);
-  load_part<3, PANEL_A, PANEL_B>(R[0], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, 0, wave, lane, A, SA, M, B, SB, N);
-  store_part<0>(R[0], smem, wave, lane);
-  store_part<1>(R[0], smem, wave, lane);
-  store_part<2>(R[0], smem, wave, lane);
-  store_part<3>(R[0], smem, wave, lane);
-  // Then the register stages are filled with super-steps 1 (and 2), issued in
-  // the loop's order (the fences keep the scheduler from reordering them), so
-  // that the in-order load counter lets the loop's first LDS writes wait only
-  // for their own part.
-#pragma unroll
-  for (int x = 0; x < (DEEP ? 2 : 1); x++) {
-    const int sx = min(1 + x, nsteps - 1);
+  // Super-step s_begin goes to its LDS buffer through the registers first;
+  // then the registers receive the next one, in the loop's order (the fences keep the
+  // scheduler from reordering the parts), so that the in-order load counter
+  // lets the loop's first LDS writes wait only for their own part.
+  Stage R;
+  load_part<0, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s_begin, wave, lane, A, SA, M, B, SB, N);
+  load_part<1, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s_begin, wave, lane, A, SA, M, B, SB, N);
+  load_part<2, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s_begin, wave, lane, A, SA, M, B, SB, N);
+  load_part<3, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s_begin, wave, lane, A, SA, M, B, SB, N);
+  uint8_t* first_buf = smem + (s_begin & 1) * kStage;
+  store_part<0>(R, first_buf, wave, lane);
+  store_part<1>(R, first_buf, wave, lane);
+  store_part<2>(R, first_buf, wave, lane);
+  store_part<3>(R, first_buf, wave, lane);
+  {
+    const int s1 = min(s_begin + 1, s_end - 1);
     sched_fence();
-    load_part<0, PANEL_A, PANEL_B>(R[x], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, sx, wave, lane, A, SA, M, B, SB, N);
+    load_part<0, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, A, SA, M, B, SB, N);
     sched_fence();
-    load_part<1, PANEL_A, PANEL_B>(R[x], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, sx, wave, lane, A, SA, M, B, SB, N);
+    load_part<1, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, A, SA, M, B, SB, N);
     sched_fence();
-    load_part<2, PANEL_A, PANEL_B>(R[x], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, sx, wave, lane, A, SA, M, B, SB, N);
+    load_part<2, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, A, SA, M, B, SB, N);
     sched_fence();
-    load_part<3, PANEL_A, PANEL_B>(R[x], rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, sx, wave, lane, A, SA, M, B, SB, N);
+    load_part<3, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, A, SA, M, B, SB, N);
     sched_fence();
   }
-  // fp32 output with more than kSeg super-steps: K in segments of kSeg
-  // super-steps (48 MFMAs per chain), each folded into C
-  // (tile256::fold_tile); otherwise one chain. The pipeline runs on across
-  // segment boundaries; kSeg is even, so every segment but the last starts
-  // and ends on the same register stage.
-  constexpr int kSeg = 12;
-  auto run = [&](int s0, int s1) {
-    if (DEEP) {
-      // Four-deep pipeline: two register stages alternate, so every load has
-      // two super-steps to land.
-      int s = s0;
-      for (; s + 1 < s1; s += 2) {
-        step(s, R[0], 3);
-        step(s + 1, R[DEEP ? 1 : 0], 3);
-      }
-      if (s < s1) step(s, R[0], 3);
+  // Super-steps s0 .. s1-1 into the accumulators: the first carries nothing
+  // over, each later one carries the previous one's last 8 MFMAs, and the
+  // last one's are issued after the loop. The two scale sets alternate.
+  int sa0[4], sb0[4], sa1[4], sb1[4];
+  auto run = [&](int s0, int s1) __attribute__((always_inline)) {
+    const std::false_type first;
+    const std::true_type carry;
+    step(first, s0, R, sa0, sb0, sa1, sb1);
+    int s = s0 + 1;
+    for (; s + 1 < s1; s += 2) {
+      step(carry, s, R, sa1, sb1, sa0, sb0);
+      step(carry, s + 1, R, sa0, sb0, sa1, sb1);
+    }
+    if (s < s1) {
+      step(carry, s, R, sa1, sb1, sa0, sb0);
+      mfma_rows<3, 2, 4>(f1, sa1, sb1, acc);
     } else {
-      // Three-deep pipeline: one register stage, each load has one super-step.
-      for (int s = s0; s < s1; s++) step(s, R[0], 2);
+      mfma_rows<3, 2, 4>(f1, sa0, sb0, acc);
     }
   };
+  run(s_begin, s_end);
+
   if constexpr (OUT == kOutF32) {
-    if (nsteps > kSeg) {
-      for (int s0 = 0; s0 < nsteps; s0 += kSeg) {
-        const int s1 = min(s0 + kSeg, nsteps);
-        run(s0, s1);
-        tile256::fold_tile(acc, (float*)C, ldc, M, N, m0, n0, wave, lane, s0 == 0, s1 == nsteps, 1.0f);
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-          for (int j = 0; j < 4; j++)
-#pragma unroll
-            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
-      }
+    // One K segment of several (bit 0 of `fold`): add this segment's sums
+    // into C (bit 1: the first segment stores them; bit 2: the last one).
+    if (fold & 1) {
+      tile256::fold_tile(acc, (float*)C, ldc, M, N, m0, n0, wave, lane, (fold & 2) != 0,
+                         (fold & 4) != 0, 1.0f);
       return;
     }
   }
-  run(0, nsteps);
-
   // Epilogue: the stage buffers are free once every wave is past its loop.
   __syncthreads();
   tile256::store_tile<OUT>(acc, smem, 1.0f, C, ldc, M, N, m0, n0, wave, lane);
@@ -390,15 +455,15 @@ bool gemm_mxfp4_fits(int64_t M, int64_t N, int64_t K) {
 template <int OUT>
 hipError_t launch(dim3 grid, hipStream_t s, bool panel_a, bool panel_b, const uint8_t* A,
             const uint8_t* SA, const uint8_t* B, const uint8_t* SB, void* c, int64_t ldc, int m,
-            int n, int k, int tm, int tn) {
+            int n, int k, int tm, int tn, int s0, int s1, int fold) {
   if (panel_a && panel_b)
-    MX_TRY(launch_kernel(&gemm_mxfp4_kernel<OUT, true, true>, grid, kThreads, 0, s, A, SA, B, SB, c, ldc, m, n, k, tm, tn));
+    MX_TRY(launch_kernel(&gemm_mxfp4_kernel<OUT, true, true>, grid, kThreads, 0, s, A, SA, B, SB, c, ldc, m, n, k, tm, tn, s0, s1, fold));
   else if (panel_a)
-    MX_TRY(launch_kernel(&gemm_mxfp4_kernel<OUT, true, false>, grid, kThreads, 0, s, A, SA, B, SB, c, ldc, m, n, k, tm, tn));
+    MX_TRY(launch_kernel(&gemm_mxfp4_kernel<OUT, true, false>, grid, kThreads, 0, s, A, SA, B, SB, c, ldc, m, n, k, tm, tn, s0, s1, fold));
   else if (panel_b)
-    MX_TRY(launch_kernel(&gemm_mxfp4_kernel<OUT, false, true>, grid, kThreads, 0, s, A, SA, B, SB, c, ldc, m, n, k, tm, tn));
+    MX_TRY(launch_kernel(&gemm_mxfp4_kernel<OUT, false, true>, grid, kThreads, 0, s, A, SA, B, SB, c, ldc, m, n, k, tm, tn, s0, s1, fold));
   else
-    MX_TRY(launch_kernel(&gemm_mxfp4_kernel<OUT, false, false>, grid, kThreads, 0, s, A, SA, B, SB, c, ldc, m, n, k, tm, tn));
+    MX_TRY(launch_kernel(&gemm_mxfp4_kernel<OUT, false, false>, grid, kThreads, 0, s, A, SA, B, SB, c, ldc, m, n, k, tm, tn, s0, s1, fold));
   return hipSuccess;
 }
 
@@ -409,9 +474,22 @@ hipError_t gemm_mxfp4(int64_t M, int64_t N, int64_t K, const void* a, const void
   const dim3 grid((unsigned)(tm * tn));
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;
-  if (out_dtype == kOutF32)
-    return launch<kOutF32>(grid, s, panel_a, panel_b, A, SA, B, SB, c, ldc, (int)M, (int)N, (int)K, tm, tn);
-  return launch<kOutBF16>(grid, s, panel_a, panel_b, A, SA, B, SB, c, ldc, (int)M, (int)N, (int)K, tm, tn);
+  const int nsteps = (int)(K / kSuperK);
+  if (out_dtype == kOutF32) {
+    // fp32 accumulation chains of at most 48 MFMAs (tile256::fold_tile): K in
+    // segments of 12 super-steps, one launch each, every launch after the
+    // first adding its sums into C (launches on one stream run in order).
+    constexpr int kSeg = 12;
+    if (nsteps <= kSeg)
+      return launch<kOutF32>(grid, s, panel_a, panel_b, A, SA, B, SB, c, ldc, (int)M, (int)N, (int)K, tm, tn, 0, nsteps, 0);
+    for (int s0 = 0; s0 < nsteps; s0 += kSeg) {
+      const int s1 = s0 + kSeg < nsteps ? s0 + kSeg : nsteps;
+      const int fold = 1 | (s0 == 0 ? 2 : 0) | (s1 == nsteps ? 4 : 0);
+      MX_TRY(launch<kOutF32>(grid, s, panel_a, panel_b, A, SA, B, SB, c, ldc, (int)M, (int)N, (int)K, tm, tn, s0, s1, fold));
+    }
+    return hipSuccess;
+  }
+  return launch<kOutBF16>(grid, s, panel_a, panel_b, A, SA, B, SB, c, ldc, (int)M, (int)N, (int)K, tm, tn, 0, nsteps, 0);
 }
 
 }  // namespace mx
