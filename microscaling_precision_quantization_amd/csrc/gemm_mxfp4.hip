@@ -84,66 +84,69 @@ struct Stage {
   u32x2 sa, sb;
 };
 
-// Part P (0..3) of the global loads of super-step s: code blocks 2P and 2P+1
-// of A and B, plus the A scales (P = 0) or the B scales (P = 1). Rows past M
-// or N fall outside the buffer range and load as zeros.
-// An operand in the K-panel layout (PANEL_A, PANEL_B): panel s of the codes
-// starts at byte s * rows * 128, of the scales at s * rows * 8; its buffer
-// views span the panel's rows.
-template <int P, bool PANEL_A, bool PANEL_B>
-__device__ __forceinline__ void load_part(Stage& st, __amdgpu_buffer_rsrc_t rA,
-                                          __amdgpu_buffer_rsrc_t rB, __amdgpu_buffer_rsrc_t rSA,
-                                          __amdgpu_buffer_rsrc_t rSB, int m0, int n0,
-                                          uint32_t rowbytes, uint32_t scalebytes, int s, int wave,
-                                          int lane, const uint8_t* A, const uint8_t* SA, int M,
+// Buffer views of one super-step s. An operand in the K-panel layout
+// (PANEL_A, PANEL_B) gets views spanning panel s: its codes start at byte
+// s * rows * 128, its scales at s * rows * 8, and rows past M or N fall
+// outside the view and load as zeros. They are made once per super-step, in
+// 32-bit offsets (a whole operand stays below 2^31 bytes, gemm_mxfp4_fits). A
+// row-layout operand keeps its whole-operand view, and the super-step's byte
+// offsets within a row are kb (codes) and ks (scales).
+struct Views {
+  __amdgpu_buffer_rsrc_t a, b, sa, sb;
+  uint32_t kb, ks;
+};
+
+template <bool PANEL_A, bool PANEL_B>
+__device__ __forceinline__ Views views_of(int s, __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB,
+                                          __amdgpu_buffer_rsrc_t rSA, __amdgpu_buffer_rsrc_t rSB,
+                                          const uint8_t* A, const uint8_t* SA, int M,
                                           const uint8_t* B, const uint8_t* SB, int N) {
-  const uint32_t kb = (uint32_t)s * kRowBytes;
+  const uint32_t us = (uint32_t)s;
+  Views v;
+  v.kb = us * kRowBytes;
+  v.ks = us * (kSuperK / 32);
+  v.a = PANEL_A ? __builtin_amdgcn_make_buffer_rsrc((void*)(A + us * (uint32_t)(M * kRowBytes)), 0,
+                                                    M * kRowBytes, kRsrcFlags)
+                : rA;
+  v.b = PANEL_B ? __builtin_amdgcn_make_buffer_rsrc((void*)(B + us * (uint32_t)(N * kRowBytes)), 0,
+                                                    N * kRowBytes, kRsrcFlags)
+                : rB;
+  v.sa = PANEL_A ? __builtin_amdgcn_make_buffer_rsrc((void*)(SA + us * (uint32_t)(M * (kSuperK / 32))),
+                                                     0, M * (kSuperK / 32), kRsrcFlags)
+                 : rSA;
+  v.sb = PANEL_B ? __builtin_amdgcn_make_buffer_rsrc((void*)(SB + us * (uint32_t)(N * (kSuperK / 32))),
+                                                     0, N * (kSuperK / 32), kRsrcFlags)
+                 : rSB;
+  return v;
+}
+
+// Part P (0..3) of the global loads of a super-step (its views v): code
+// blocks 2P and 2P+1 of A and B, plus the A scales (P = 0) or the B scales
+// (P = 1). Rows past M or N fall outside the buffer range and load as zeros.
+template <int P, bool PANEL_A, bool PANEL_B>
+__device__ __forceinline__ void load_part(Stage& st, const Views& v, int m0, int n0,
+                                          uint32_t rowbytes, uint32_t scalebytes, int wave,
+                                          int lane) {
 #pragma unroll
   for (int i = 2 * P; i < 2 * P + 2; i++) {
     const int row = (wave * 8 + i) * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ swz(row);  // slot lane&7 of the LDS row holds this chunk
-    const uint32_t off = kb + (uint32_t)chunk * 16u;
-    if (PANEL_A) {
-      const __amdgpu_buffer_rsrc_t rAp = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(A + (int64_t)s * M * kRowBytes), 0, M * kRowBytes, kRsrcFlags);
-      st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          rAp, (uint32_t)(m0 + row) * (uint32_t)kRowBytes + (uint32_t)chunk * 16u, 0, 0);
-    } else {
-      st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, (uint32_t)(m0 + row) * rowbytes + off, 0, 0);
-    }
-    if (PANEL_B) {
-      const __amdgpu_buffer_rsrc_t rBp = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(B + (int64_t)s * N * kRowBytes), 0, N * kRowBytes, kRsrcFlags);
-      st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          rBp, (uint32_t)(n0 + row) * (uint32_t)kRowBytes + (uint32_t)chunk * 16u, 0, 0);
-    } else {
-      st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, (uint32_t)(n0 + row) * rowbytes + off, 0, 0);
-    }
+    const uint32_t cb = (uint32_t)((lane & 7) ^ swz(row)) * 16u;  // slot lane&7 of the LDS row holds this chunk
+    st.a[i] = __builtin_amdgcn_raw_buffer_load_b128(
+        v.a, PANEL_A ? (uint32_t)(m0 + row) * (uint32_t)kRowBytes + cb
+                     : (uint32_t)(m0 + row) * rowbytes + v.kb + cb, 0, 0);
+    st.b[i] = __builtin_amdgcn_raw_buffer_load_b128(
+        v.b, PANEL_B ? (uint32_t)(n0 + row) * (uint32_t)kRowBytes + cb
+                     : (uint32_t)(n0 + row) * rowbytes + v.kb + cb, 0, 0);
   }
   const int srow = wave * 64 + lane;
-  const uint32_t soff = (uint32_t)s * (kSuperK / 32);
-  if (P == 0) {
-    if (PANEL_A) {
-      const __amdgpu_buffer_rsrc_t rSAp = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(SA + (int64_t)s * M * (kSuperK / 32)), 0, M * (kSuperK / 32), kRsrcFlags);
-      st.sa = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                            rSAp, (uint32_t)(m0 + srow) * (uint32_t)(kSuperK / 32), 0, 0));
-    } else {
-      st.sa = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                            rSA, (uint32_t)(m0 + srow) * scalebytes + soff, 0, 0));
-    }
-  }
-  if (P == 1) {
-    if (PANEL_B) {
-      const __amdgpu_buffer_rsrc_t rSBp = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(SB + (int64_t)s * N * (kSuperK / 32)), 0, N * (kSuperK / 32), kRsrcFlags);
-      st.sb = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                            rSBp, (uint32_t)(n0 + srow) * (uint32_t)(kSuperK / 32), 0, 0));
-    } else {
-      st.sb = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                            rSB, (uint32_t)(n0 + srow) * scalebytes + soff, 0, 0));
-    }
-  }
+  if (P == 0)
+    st.sa = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+        v.sa, PANEL_A ? (uint32_t)(m0 + srow) * (uint32_t)(kSuperK / 32)
+                      : (uint32_t)(m0 + srow) * scalebytes + v.ks, 0, 0));
+  if (P == 1)
+    st.sb = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+        v.sb, PANEL_B ? (uint32_t)(n0 + srow) * (uint32_t)(kSuperK / 32)
+                      : (uint32_t)(n0 + srow) * scalebytes + v.ks, 0, 0));
 }
 
 // Part P of the LDS writes of a staged super-step (the same pieces as
@@ -242,17 +245,20 @@ __device__ __forceinline__ void interleave() {
 }
 
 // Head of a super-step: the 8 MFMAs carried over from the previous one, with
-// this super-step's 12 LDS reads (scales and sub-step 0's fragments).
+// this super-step's 12 LDS reads (scales and sub-step 0's fragments) and the
+// scalar work that makes its load views.
 __device__ __forceinline__ void interleave_head() {
 #pragma unroll
   for (int k = 0; k < 4; k++) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x004, 3, 0);
   }
 #pragma unroll
   for (int k = 0; k < 4; k++) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x004, 3, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -340,6 +346,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
     // Branch-free body (a branch here lets the compiler sink the MFMAs): the
     // last iterations re-stage the final super-step into the idle buffer.
     const int s2 = min(s + 2, s_end - 1);
+    const Views v = views_of<PANEL_A, PANEL_B>(s2, rA, rB, rSA, rSB, A, SA, M, B, SB, N);
     const uint8_t* As = cur;
     const uint8_t* Bs = cur + kTileBytes;
     const uint8_t* SAs = cur + 2 * kTileBytes;
@@ -362,21 +369,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
     // memory instruction issues in an MFMA's shadow.
     load_frags<1>(As, Bs, wm, wn, r, g, f1);
     store_part<0>(R, nxt, wave, lane);
-    load_part<0, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
+    load_part<0, PANEL_A, PANEL_B>(R, v, m0, n0, rowbytes, scalebytes, wave, lane);
     mfma_substep<0>(f0, sa, sb, acc);
     interleave();
     load_frags<2>(As, Bs, wm, wn, r, g, f0);
     store_part<1>(R, nxt, wave, lane);
-    load_part<1, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
+    load_part<1, PANEL_A, PANEL_B>(R, v, m0, n0, rowbytes, scalebytes, wave, lane);
     mfma_substep<1>(f1, sa, sb, acc);
     interleave();
     load_frags<3>(As, Bs, wm, wn, r, g, f1);
     store_part<2>(R, nxt, wave, lane);
     store_part<3>(R, nxt, wave, lane);
-    load_part<2, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
+    load_part<2, PANEL_A, PANEL_B>(R, v, m0, n0, rowbytes, scalebytes, wave, lane);
     mfma_substep<2>(f0, sa, sb, acc);
     interleave_third();
-    load_part<3, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s2, wave, lane, A, SA, M, B, SB, N);
+    load_part<3, PANEL_A, PANEL_B>(R, v, m0, n0, rowbytes, scalebytes, wave, lane);
     mfma_rows<3, 0, 2>(f1, sa, sb, acc);
     interleave_last();
   };
@@ -385,10 +392,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
   // scheduler from reordering the parts), so that the in-order load counter
   // lets the loop's first LDS writes wait only for their own part.
   Stage R;
-  load_part<0, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s_begin, wave, lane, A, SA, M, B, SB, N);
-  load_part<1, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s_begin, wave, lane, A, SA, M, B, SB, N);
-  load_part<2, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s_begin, wave, lane, A, SA, M, B, SB, N);
-  load_part<3, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s_begin, wave, lane, A, SA, M, B, SB, N);
+  const Views v0 = views_of<PANEL_A, PANEL_B>(s_begin, rA, rB, rSA, rSB, A, SA, M, B, SB, N);
+  load_part<0, PANEL_A, PANEL_B>(R, v0, m0, n0, rowbytes, scalebytes, wave, lane);
+  load_part<1, PANEL_A, PANEL_B>(R, v0, m0, n0, rowbytes, scalebytes, wave, lane);
+  load_part<2, PANEL_A, PANEL_B>(R, v0, m0, n0, rowbytes, scalebytes, wave, lane);
+  load_part<3, PANEL_A, PANEL_B>(R, v0, m0, n0, rowbytes, scalebytes, wave, lane);
   uint8_t* first_buf = smem + (s_begin & 1) * kStage;
   store_part<0>(R, first_buf, wave, lane);
   store_part<1>(R, first_buf, wave, lane);
@@ -396,14 +404,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mxfp4_kernel(
   store_part<3>(R, first_buf, wave, lane);
   {
     const int s1 = min(s_begin + 1, s_end - 1);
+    const Views v1 = views_of<PANEL_A, PANEL_B>(s1, rA, rB, rSA, rSB, A, SA, M, B, SB, N);
     sched_fence();
-    load_part<0, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, A, SA, M, B, SB, N);
+    load_part<0, PANEL_A, PANEL_B>(R, v1, m0, n0, rowbytes, scalebytes, wave, lane);
     sched_fence();
-    load_part<1, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, A, SA, M, B, SB, N);
+    load_part<1, PANEL_A, PANEL_B>(R, v1, m0, n0, rowbytes, scalebytes, wave, lane);
     sched_fence();
-    load_part<2, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, A, SA, M, B, SB, N);
+    load_part<2, PANEL_A, PANEL_B>(R, v1, m0, n0, rowbytes, scalebytes, wave, lane);
     sched_fence();
-    load_part<3, PANEL_A, PANEL_B>(R, rA, rB, rSA, rSB, m0, n0, rowbytes, scalebytes, s1, wave, lane, A, SA, M, B, SB, N);
+    load_part<3, PANEL_A, PANEL_B>(R, v1, m0, n0, rowbytes, scalebytes, wave, lane);
     sched_fence();
   }
   // Super-steps s0 .. s1-1 into the accumulators: the first carries nothing
