@@ -10,6 +10,11 @@
 //    one wave of a SIMD expands codes on the vector ALU, the other's MFMAs
 //    keep the matrix core busy (6% faster than 4 waves of 128 x 128 on NVFP4,
 //    2% on MXFP8).
+//  * Or 224 x 256 tiles, when the tile count then fills the device's CUs in
+//    fewer rows of rounds (4608-row activations: 756 tiles in 3 rounds of 256
+//    CUs instead of 648 tiles in 3, 1008 in 4 instead of 864 in 4). The
+//    SIMD's second wave then covers 96 rows (3 x 2 MFMAs); A is still staged
+//    as 256 rows, the last 32 outside its buffer view.
 //  * K advances in stages of 64 elements. A stage moves through a four-deep
 //    pipeline: global -> VGPRs (16-byte code chunks, range-checked buffer
 //    loads issued three stages ahead into two alternating register stages),
@@ -235,12 +240,12 @@ __device__ __forceinline__ void load_stage(Stage<FMT>& st, __amdgpu_buffer_rsrc_
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Fragments of sub-step S: 4 A tiles and 2 B tiles of 32 rows, chunk 2S + g.
-template <int S, typename V>
+// Fragments of sub-step S: NI A tiles and 2 B tiles of 32 rows, chunk 2S + g.
+template <int S, int NI, typename V>
 __device__ __forceinline__ void load_frags(const uint8_t* As, const uint8_t* Bs, int wm, int wn,
                                            int r, int g, V (&fa)[4], V (&fb)[2]) {
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < NI; i++) {
     const int ra = wm * 128 + i * 32 + r;
     fa[i] = *(const V*)(As + ra * kRowBytes + (((2 * S + g) ^ swz(ra)) * 16));
   }
@@ -251,18 +256,20 @@ __device__ __forceinline__ void load_frags(const uint8_t* As, const uint8_t* Bs,
   }
 }
 
+template <int NI>
 __device__ __forceinline__ void mfma16(const bf16x8 (&fa)[4], const bf16x8 (&fb)[2], f32x16 (&acc)[4][2]) {
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < NI; i++)
 #pragma unroll
     for (int j = 0; j < 2; j++)
       // Operands swapped (B first): the result tile is C^T (see tile256.h).
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
 }
 
+template <int NI>
 __device__ __forceinline__ void mfma16(const f16x8 (&fa)[4], const f16x8 (&fb)[2], f32x16 (&acc)[4][2]) {
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < NI; i++)
 #pragma unroll
     for (int j = 0; j < 2; j++)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
@@ -300,29 +307,17 @@ __device__ __forceinline__ void region_order() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int FMT, int OUT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16x_large_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const float* __restrict__ TA,
-    const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB, const float* __restrict__ TB,
-    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / kWavesN, wn = wave % kWavesN;
-  const int r = lane & 31, g = lane >> 5;
-  int tm, tn;
-  tile256::tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  // Buffer views based at the tile's first rows: rows past M or N read as 0.
-  const uint32_t rowbytes = (uint32_t)row_bytes<FMT>(K);
-  const uint32_t scalebytes = (uint32_t)(K / Geo<FMT>::kBlock);
-  const int mrows = min(BM, M - m0), nrows = min(BN, N - n0);
-  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * rowbytes), 0, (int)(mrows * rowbytes), kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)(B + (int64_t)n0 * rowbytes), 0, (int)(nrows * rowbytes), kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc((void*)(SA + (int64_t)m0 * scalebytes), 0, (int)(mrows * scalebytes), kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t rSB = __builtin_amdgcn_make_buffer_rsrc((void*)(SB + (int64_t)n0 * scalebytes), 0, (int)(nrows * scalebytes), kRsrcFlags);
-
+// The K loop and epilogue of one tile, for a wave with NI row blocks of 32
+// (4, or 3 for the second row of waves of a 224-row tile). Mlim is the first
+// row past the tile's valid rows.
+template <int FMT, int OUT, int NI>
+__device__ __forceinline__ void tile_body(uint8_t* smem, __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rSA,
+                                          __amdgpu_buffer_rsrc_t rB, __amdgpu_buffer_rsrc_t rSB,
+                                          uint32_t rowbytes, uint32_t scalebytes, int K, int tid,
+                                          int lane, int wave, int wm, int wn, int r, int g,
+                                          const float* __restrict__ TA, const float* __restrict__ TB,
+                                          void* __restrict__ C, int64_t ldc, int Mlim, int N, int m0,
+                                          int n0, int s_begin, int s_end, int fold) {
   f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; i++)
@@ -331,110 +326,170 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16x_large_kernel(
 #pragma unroll
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
-  const int nsteps = (K + BK - 1) / BK;
+  // Stages s_begin .. s_end-1 of K (all of K unless the fp32 output is
+  // accumulated over several launches, see gemm_bf16x_large below).
   // Four-deep pipeline: LDS buffer s & 1 feeds the MFMAs while one of two
   // register stages (holding stage s + 1) is expanded into LDS buffer
   // (s + 1) & 1 and then receives stage s + 3 from memory; the other holds
-  // s + 2. Every load has two stages to land (its few spilled registers are
-  // saved and restored outside the loop).
-  auto step = [&](int s, Stage<FMT>& Rx) {
+  // s + 2. Every load has two stages to land.
+  // Stage s uses LDS buffer `par` (its position in this launch's range, mod 2:
+  // a constant in the unrolled loop, so the LDS addresses are too).
+  auto step = [&](int s, int par, Stage<FMT>& Rx) {
     // Every thread's LDS writes of stage s are done and every wave is done
     // reading stage s-1, whose buffer receives stage s+1 below. Only LDS work
     // is waited for: the global loads stay in flight.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     fence();
-    const uint8_t* cur = smem + (s & 1) * kStage;
-    uint8_t* nxt = smem + ((s + 1) & 1) * kStage;
+    const uint8_t* cur = smem + par * kStage;
+    uint8_t* nxt = smem + (par ^ 1) * kStage;
     // Branch-free body (a branch lets the compiler sink the MFMAs): the last
     // iterations re-stage the final stage into the idle buffer. The registers
     // Rx hold stage s + 1 and then receive stage s + 3.
-    const int s2 = min(s + 3, nsteps - 1);
+    const int s2 = min(s + 3, s_end - 1);
     const uint8_t* As = cur;
     const uint8_t* Bs = cur + kTileBytes;
     // Operand elements: bf16 for the MX formats, fp16 for NVFP4.
     using V = typename std::conditional<Geo<FMT>::kFp16, f16x8, bf16x8>::type;
     V fa0[4], fb0[2], fa1[4], fb1[2];
-    load_frags<0>(As, Bs, wm, wn, r, g, fa0, fb0);
+    load_frags<0, NI>(As, Bs, wm, wn, r, g, fa0, fb0);
     fence();
     // Sub-step 0: next fragments, expansion of chunk 0 of stage s+1, loads of
     // chunk 0 of stage s+3, MFMAs. Likewise for the other sub-steps.
-    load_frags<1>(As, Bs, wm, wn, r, g, fa1, fb1);
+    load_frags<1, NI>(As, Bs, wm, wn, r, g, fa1, fb1);
     store_part<FMT, 0>(Rx, nxt, tid);
     load_part<FMT, 0>(Rx, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
-    mfma16(fa0, fb0, acc);
+    mfma16<NI>(fa0, fb0, acc);
     region_order<FMT, true>();
-    load_frags<2>(As, Bs, wm, wn, r, g, fa0, fb0);
+    load_frags<2, NI>(As, Bs, wm, wn, r, g, fa0, fb0);
     store_part<FMT, 1>(Rx, nxt, tid);
     load_part<FMT, 1>(Rx, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
-    mfma16(fa1, fb1, acc);
+    mfma16<NI>(fa1, fb1, acc);
     region_order<FMT, true>();
-    load_frags<3>(As, Bs, wm, wn, r, g, fa1, fb1);
+    load_frags<3, NI>(As, Bs, wm, wn, r, g, fa1, fb1);
     store_part<FMT, 2>(Rx, nxt, tid);
     load_part<FMT, 2>(Rx, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
-    mfma16(fa0, fb0, acc);
+    mfma16<NI>(fa0, fb0, acc);
     region_order<FMT, true>();
     store_part<FMT, 3>(Rx, nxt, tid);
     load_part<FMT, 3>(Rx, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
-    mfma16(fa1, fb1, acc);
+    mfma16<NI>(fa1, fb1, acc);
     region_order<FMT, false>();
   };
-  // Prologue: stage 0 to LDS, stages 1 and 2 in registers (issued in the
-  // loop's order so that the in-order load counter lets the loop's first
-  // expansions wait only for their own part).
+  // Prologue: the first stage to LDS buffer 0, the next two in registers
+  // (issued in the loop's order so that the in-order load counter lets the
+  // loop's first expansions wait only for their own part).
   Stage<FMT> R[2];
-  load_stage<FMT>(R[0], rA, rSA, rB, rSB, rowbytes, scalebytes, K, 0, tid);
+  load_stage<FMT>(R[0], rA, rSA, rB, rSB, rowbytes, scalebytes, K, s_begin, tid);
   store_part<FMT, 0>(R[0], smem, tid);
   store_part<FMT, 1>(R[0], smem, tid);
   store_part<FMT, 2>(R[0], smem, tid);
   store_part<FMT, 3>(R[0], smem, tid);
-  load_stage<FMT>(R[0], rA, rSA, rB, rSB, rowbytes, scalebytes, K, min(1, nsteps - 1), tid);
-  load_stage<FMT>(R[1], rA, rSA, rB, rSB, rowbytes, scalebytes, K, min(2, nsteps - 1), tid);
-  // fp32 output with more than kSeg stages: K in segments of kSeg stages (48
-  // MFMAs per chain), each folded into C (tile256::fold_tile); otherwise one
-  // chain. kSeg is even, so every segment but the last keeps the
-  // register-stage parity.
-  constexpr int kSeg = 12;
+  load_stage<FMT>(R[0], rA, rSA, rB, rSB, rowbytes, scalebytes, K, min(s_begin + 1, s_end - 1), tid);
+  load_stage<FMT>(R[1], rA, rSA, rB, rSB, rowbytes, scalebytes, K, min(s_begin + 2, s_end - 1), tid);
   const float ts = (FMT == kNVFP4) ? TA[0] * TB[0] : 1.0f;
-  auto run = [&](int s0, int s1) {
-    int s = s0;
-    for (; s + 1 < s1; s += 2) {
-      step(s, R[0]);
-      step(s + 1, R[1]);
-    }
-    if (s < s1) step(s, R[0]);
-  };
+  int s = s_begin;
+  for (; s + 1 < s_end; s += 2) {
+    step(s, 0, R[0]);
+    step(s + 1, 1, R[1]);
+  }
+  if (s < s_end) step(s, 0, R[0]);
   if constexpr (OUT == kOutF32) {
-    if (nsteps > kSeg) {
-      for (int s0 = 0; s0 < nsteps; s0 += kSeg) {
-        const int s1 = min(s0 + kSeg, nsteps);
-        run(s0, s1);
-        tile256::fold_tile<2, kWavesN>(acc, (float*)C, ldc, M, N, m0, n0, wave, lane, s0 == 0,
-                                       s1 == nsteps, ts);
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-          for (int j = 0; j < 2; j++)
-#pragma unroll
-            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
-      }
+    // One K segment of several (bit 0 of `fold`): add this segment's sums
+    // into C (bit 1: the first segment stores them; bit 2: the last one,
+    // which also applies the NVFP4 tensor scales).
+    if (fold & 1) {
+      tile256::fold_tile<2, kWavesN>(acc, (float*)C, ldc, Mlim, N, m0, n0, wave, lane,
+                                     (fold & 2) != 0, (fold & 4) != 0, ts);
       return;
     }
   }
-  run(0, nsteps);
   __syncthreads();
-  tile256::store_tile<OUT, 2, kWavesN>(acc, smem, ts, C, ldc, M, N, m0, n0, wave, lane);
+  tile256::store_tile<OUT, 2, kWavesN>(acc, smem, ts, C, ldc, Mlim, N, m0, n0, wave, lane);
 }
 
-template <int FMT>
+template <int FMT, int OUT, int BMT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16x_large_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const float* __restrict__ TA,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB, const float* __restrict__ TB,
+    void* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_n, int s_begin,
+    int s_end, int fold) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+  const int r = lane & 31, g = lane >> 5;
+  int tm, tn;
+  if (!tile256::tile_of_padded(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn)) return;
+  const int m0 = tm * BMT, n0 = tn * BN;
+
+  // Buffer views based at the tile's first rows: rows past M or N read as 0.
+  const uint32_t rowbytes = (uint32_t)row_bytes<FMT>(K);
+  const uint32_t scalebytes = (uint32_t)(K / Geo<FMT>::kBlock);
+  const int mrows = min(BMT, M - m0), nrows = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * rowbytes), 0, (int)(mrows * rowbytes), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)(B + (int64_t)n0 * rowbytes), 0, (int)(nrows * rowbytes), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc((void*)(SA + (int64_t)m0 * scalebytes), 0, (int)(mrows * scalebytes), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rSB = __builtin_amdgcn_make_buffer_rsrc((void*)(SB + (int64_t)n0 * scalebytes), 0, (int)(nrows * scalebytes), kRsrcFlags);
+
+  // A 224-row tile: the first row of waves holds 128 rows (4 blocks), the
+  // second 96 (3 blocks); the staged rows 224 .. 255 lie outside A's view and
+  // are never read.
+  const int Mlim = m0 + mrows;
+  if (BMT == 256 || wm == 0)
+    tile_body<FMT, OUT, 4>(smem, rA, rSA, rB, rSB, rowbytes, scalebytes, K, tid, lane, wave, wm, wn, r, g, TA, TB, C, ldc, Mlim, N, m0, n0, s_begin, s_end, fold);
+  else
+    tile_body<FMT, OUT, 3>(smem, rA, rSA, rB, rSB, rowbytes, scalebytes, K, tid, lane, wave, wm, wn, r, g, TA, TB, C, ldc, Mlim, N, m0, n0, s_begin, s_end, fold);
+}
+
+template <int FMT, int BMT>
 hipError_t launch(hipStream_t s, int tm, int tn, const uint8_t* A, const uint8_t* SA, const float* TA,
             const uint8_t* B, const uint8_t* SB, const float* TB, int out_dtype, void* c,
             int64_t ldc, int M, int N, int K) {
-  const dim3 grid((unsigned)(tm * tn));
-  if (out_dtype == kOutF32)
-    MX_TRY(launch_kernel(&gemm_bf16x_large_kernel<FMT, kOutF32>, grid, kThreads, 0, s, A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn));
-  else
-    MX_TRY(launch_kernel(&gemm_bf16x_large_kernel<FMT, kOutBF16>, grid, kThreads, 0, s, A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn));
+  // The grid is padded to whole groups of 8 workgroups (one per XCD); the
+  // padding workgroups return at once (tile256::tile_of_padded).
+  const dim3 grid((unsigned)((tm * tn + 7) / 8 * 8));
+  const int nsteps = (K + BK - 1) / BK;
+  if (out_dtype == kOutF32) {
+    // fp32 accumulation chains of at most 48 MFMAs (tile256::fold_tile): K in
+    // segments of 12 stages, one launch each, every launch after the first
+    // adding its sums into C (launches on one stream run in order).
+    constexpr int kSeg = 12;
+    if (nsteps <= kSeg) {
+      MX_TRY(launch_kernel(&gemm_bf16x_large_kernel<FMT, kOutF32, BMT>, grid, kThreads, 0, s, A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn, 0, nsteps, 0));
+      return hipSuccess;
+    }
+    for (int s0 = 0; s0 < nsteps; s0 += kSeg) {
+      const int s1 = s0 + kSeg < nsteps ? s0 + kSeg : nsteps;
+      const int fold = 1 | (s0 == 0 ? 2 : 0) | (s1 == nsteps ? 4 : 0);
+      MX_TRY(launch_kernel(&gemm_bf16x_large_kernel<FMT, kOutF32, BMT>, grid, kThreads, 0, s, A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn, s0, s1, fold));
+    }
+    return hipSuccess;
+  }
+  MX_TRY(launch_kernel(&gemm_bf16x_large_kernel<FMT, kOutBF16, BMT>, grid, kThreads, 0, s, A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn, 0, nsteps, 0));
   return hipSuccess;
+}
+
+template <int FMT>
+hipError_t launch_rows(bool rows224, hipStream_t s, int64_t M, int tn, const uint8_t* A, const uint8_t* SA,
+                       const float* TA, const uint8_t* B, const uint8_t* SB, const float* TB,
+                       int out_dtype, void* c, int64_t ldc, int N, int K) {
+  if (rows224)
+    return launch<FMT, 224>(s, (int)((M + 223) / 224), tn, A, SA, TA, B, SB, TB, out_dtype, c, ldc, (int)M, N, K);
+  return launch<FMT, 256>(s, (int)((M + 255) / 256), tn, A, SA, TA, B, SB, TB, out_dtype, c, ldc, (int)M, N, K);
+}
+
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 }  // namespace
@@ -449,16 +504,24 @@ bool gemm_bf16x_large_fits(int fmt, int64_t M, int64_t N, int64_t K) {
 hipError_t gemm_bf16x_large(int fmt, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
                             const float* ta, const void* b, const void* sb, const float* tb,
                             int out_dtype, void* c, int64_t ldc, hipStream_t s) {
-  const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
+  const int tn = (int)((N + BN - 1) / BN);
+  // Tile height: every tile of a round of the device's CUs takes about as
+  // long as its rows, so 224-row tiles pay when they need fewer rows of
+  // rounds, rounds x tile rows, than 256-row tiles (4608 rows by 36 or 48
+  // tile columns: 3 rounds of 224 against 3 of 256, 4 of 224 against 4 of 256).
+  const int64_t cus = device_cus();
+  const int64_t r256 = ((M + 255) / 256 * tn + cus - 1) / cus;
+  const int64_t r224 = ((M + 223) / 224 * tn + cus - 1) / cus;
+  const bool rows224 = r224 * 224 < r256 * 256;
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;
   if (fmt == kMXFP8)
-    return launch<kMXFP8>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
+    return launch_rows<kMXFP8>(rows224, s, M, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)N, (int)K);
   if (fmt == kMXFP8E5M2)
-    return launch<kMXFP8E5M2>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
+    return launch_rows<kMXFP8E5M2>(rows224, s, M, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)N, (int)K);
   if (fmt == kMXFP6)
-    return launch<kMXFP6>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
-  return launch<kNVFP4>(s, tm, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)M, (int)N, (int)K);
+    return launch_rows<kMXFP6>(rows224, s, M, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)N, (int)K);
+  return launch_rows<kNVFP4>(rows224, s, M, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)N, (int)K);
 }
 
 }  // namespace mx

@@ -35,6 +35,23 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tn = (t % (GM * tiles_n)) / gsize;
 }
 
+// As tile_of, for a grid of `grid` workgroups padded to a multiple of 8: XCD
+// x gets the id range [x grid/8, (x+1) grid/8). Ids past the last tile (the
+// padding) return false.
+__device__ __forceinline__ bool tile_of_padded(int bid, int grid, int tiles_m, int tiles_n, int& tm,
+                                               int& tn) {
+  const int ntiles = tiles_m * tiles_n;
+  const int t = (grid % 8 == 0) ? (bid % 8) * (grid / 8) + bid / 8 : bid;
+  if (t >= ntiles) return false;
+  constexpr int GM = 4;
+  const int group = t / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  tm = first_m + (t % (GM * tiles_n)) % gsize;
+  tn = (t % (GM * tiles_n)) / gsize;
+  return true;
+}
+
 // Epilogue. Wave w is (wm, wn) = (w / WNW, w % WNW). With B passed as the
 // first MFMA operand, accumulator t of tile (i, j) of the wave holds
 // C[row][col] with row = m0 + 128 wm + 32 i + r (r = lane % 32) and
