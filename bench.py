@@ -4,8 +4,9 @@ Default workload: the MXFP4 W4A4 DiT MLP-down layer, M=4608 tokens, K=12288,
 N=3072, activations Laplace(0,1) with 0.5% outlier channels x100, weights
 N(0,0.02) quantized beforehand. One step = quantize the bf16 activations to
 MXFP4 (codes + E8M0 scales) and run the block-scaled GEMM against the
-pre-quantized weights, bf16 output (MXFP4 operands in the K-panel layout:
-weights re-laid once by mx_pack, activations quantized straight into it).
+pre-quantized weights, bf16 output (operands in the K-panel layout of their
+format: weights re-laid once by mx_pack, activations quantized straight into
+it).
 Everything in the timed region runs in libmx's HIP kernels; inputs are
 resident in HBM before timing starts. After the warm-up steps the same steps
 are replayed, untimed, for RAMP_S seconds: the GPU raises its clocks only
@@ -59,6 +60,10 @@ FORMAT_NAME = {"mxfp4": "fp4", "mxfp8": "fp8", "nvfp4": "fp4", "w4a16": "bf16",
 PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 ROTATE_BYTES = 1 << 30  # activation copies cycled per step: > 256 MB MALL
 RAMP_S = 0.2  # seconds of untimed replays before timing (GPU clock ramp)
+# The K-panel layout per format (include/mx.h): panel width W in elements,
+# code bytes and scale bytes of one row in one panel.
+PANEL_GEOMETRY = {"mxfp4": (256, 128, 8), "mxfp8": (64, 64, 2), "mxfp8_e5m2": (64, 64, 2),
+                  "mxfp6_e3m2": (64, 48, 2), "nvfp4": (64, 32, 4)}
 WEIGHT_ROTATE_BYTES = 512 << 20  # weight copies cycled per step: > 256 MB MALL, so
                                  # every step streams its weights from HBM, as the
                                  # layers of a model would
@@ -268,11 +273,12 @@ def bench_step(args, name, w, A_bits, B_bits, to_dev, mx, torch, np):
     # choice and W keeps the standard rule)
     qb = mx.quantize(Bx, wfmt, rotation=variant["rotation"])
     del Bx
-    # MXFP4 operands go to the GEMM in the K-panel layout: the weights re-laid
-    # once with their quantization (mx_pack), the activations quantized
-    # straight into it in the step, so each GEMM step reads one contiguous
-    # range per operand tile; qb keeps the row layout for the CPU baseline.
-    panel = fmt == "mxfp4" and K % 256 == 0
+    # Operands go to the GEMM in the K-panel layout where it has one: the
+    # weights re-laid once with their quantization (mx_pack), the activations
+    # quantized straight into it in the step, so each GEMM step reads one
+    # contiguous range per operand tile; qb keeps the row layout for the CPU
+    # baseline.
+    panel = fmt in PANEL_GEOMETRY and K % PANEL_GEOMETRY[fmt][0] == 0
     qw = mx.pack(qb) if panel else qb
     wbytes = qw.codes.numel() * qw.codes.element_size() + qw.scales.numel() * qw.scales.element_size()
     nwcopies = max(2, -(-WEIGHT_ROTATE_BYTES // wbytes))
@@ -488,9 +494,10 @@ def cpu_step_baseline(name, fmt, A_bits, B_bits, qb, out, A_dev, M, N, K, rows, 
         q = mx.quantize(A_dev, fmt, layout="kpanel" if panel else "rows", **variant)
         gc, gs = q.codes.cpu().numpy(), q.scales.cpu().numpy()
         if panel:
-            P = K // 256
-            gc = gc.reshape(P, M, 128)[:, :rows].transpose(1, 0, 2).reshape(rows, K // 2)
-            gs = gs.reshape(P, M, 8)[:, :rows].transpose(1, 0, 2).reshape(rows, K // 32)
+            W, wb, sb = PANEL_GEOMETRY[fmt]
+            P = K // W
+            gc = gc.reshape(P, M, wb)[:, :rows].transpose(1, 0, 2).reshape(rows, P * wb)
+            gs = gs.reshape(P, M, sb)[:, :rows].transpose(1, 0, 2).reshape(rows, P * sb)
         elif fmt in ("mxfp4_mbs", "mxfp4_mbs16"):
             blk = 16 if fmt == "mxfp4_mbs16" else 32
             e8, mac = orc.mbs_planes(gs, M, K, blk)

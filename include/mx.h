@@ -145,20 +145,28 @@ typedef enum {
 } mx_rotation;
 
 /*
- * Operand layout for the MXFP4 GEMM. The pages fix no memory layout; this one
- * is for HBM locality on MI355X. MX_LAYOUT_ROWS is mx_quantize's: codes
- * [rows][cols/2], scales [rows][cols/32]. MX_LAYOUT_KPANEL cuts K into panels
- * of 256 elements and stores each panel's rows back to back:
- *   codes   [cols/256][rows][128]: the 128 code bytes of row r in panel p
- *           (elements 256 p .. 256 p + 255, packed as in MX_LAYOUT_ROWS) at
- *           byte (p * rows + r) * 128;
- *   scales  [cols/256][rows][8]: byte (p * rows + r) * 8 + j is the scale of
- *           block 8 p + j of row r.
- * A GEMM step over 256 K then reads one contiguous range per operand tile
- * instead of one 128-byte piece per row spread over the whole matrix (on the
- * MXFP4 MLP-down shape the GEMM runs ~10% faster with K-panel weights, ~3%
- * more with K-panel activations). mx_pack re-lays a tensor;
- * mx_quantize_ex can write one directly.
+ * Operand layout for the GEMMs. The pages fix no memory layout; this one is
+ * for HBM and cache locality on MI355X. MX_LAYOUT_ROWS is mx_quantize's:
+ * codes [rows][cols * bits / 8], scales [rows][cols / block].
+ * MX_LAYOUT_KPANEL cuts K into panels of W elements, W = 256 for MXFP4 and
+ * W = 64 for MXFP8, MXFP8_E5M2, MXFP6_E3M2 and NVFP4 (one K step of that
+ * format's GEMM), and stores each panel's rows back to back. With
+ * wb = W * bits / 8 code bytes (MXFP4 128, MXFP8 and E5M2 64, E3M2 48,
+ * NVFP4 32) and sb = W / block scale bytes (MXFP4 8, MXFP8, E5M2 and E3M2 2,
+ * NVFP4 4) per row and panel:
+ *   codes   [cols/W][rows][wb]: the code bytes of row r in panel p (elements
+ *           W p .. W p + W - 1, packed as in MX_LAYOUT_ROWS) at byte
+ *           (p * rows + r) * wb;
+ *   scales  [cols/W][rows][sb]: byte (p * rows + r) * sb + j is the scale of
+ *           block (W / block) p + j of row r.
+ * The NVFP4 tensor scale is the same in both layouts. A GEMM step then reads
+ * one contiguous range per operand tile instead of one short piece per row
+ * spread over the whole matrix: on the MXFP4 MLP-down shape the GEMM runs
+ * ~10% faster with K-panel weights, ~3% more with K-panel activations; the
+ * MXFP8 / NVFP4 / E5M2 / E3M2 GEMMs of the QKV and MLP-up shapes 6-12%
+ * faster with both operands in K panels. mx_pack re-lays a tensor;
+ * mx_quantize_layout (any of these formats) and mx_quantize_ex (MXFP4,
+ * MXFP8) write one directly.
  */
 typedef enum {
   MX_LAYOUT_ROWS = 0,
@@ -166,19 +174,33 @@ typedef enum {
 } mx_layout;
 
 /*
- * mx_quantize with a scale rule, a rotation and an output layout: MX formats
- * (block 32) only; MX_SCALE_OAS with MXFP8, or NVFP4 with anything but
- * (MX_SCALE_CEIL, MX_ROTATE_NONE), returns MX_ERR_UNSUPPORTED. layout
- * MX_LAYOUT_ROWS gives mx_quantize's layout; MX_LAYOUT_KPANEL (MXFP4 only,
- * else MX_ERR_UNSUPPORTED) writes the same codes and scales in K panels and
- * needs cols a multiple of 256, cols / 256 <= 65535 and
- * rows * cols / 2 < 2^31 (MX_ERR_INVALID_ARG otherwise). tensor_scale is not
- * taken and no workspace is used. (MX_SCALE_CEIL, MX_ROTATE_NONE,
- * MX_LAYOUT_ROWS) is mx_quantize.
+ * mx_quantize with a scale rule, a rotation and an output layout: MXFP4 and
+ * MXFP8 (block 32) only; MX_SCALE_OAS with MXFP8, or another format, returns
+ * MX_ERR_UNSUPPORTED. layout MX_LAYOUT_ROWS gives mx_quantize's layout;
+ * MX_LAYOUT_KPANEL writes the same codes and scales in K panels and needs
+ * cols a multiple of the panel width W, cols / W <= 65535 and
+ * rows * (code bytes of a row) < 2^31 (MX_ERR_INVALID_ARG otherwise).
+ * tensor_scale is not taken and no workspace is used. (MX_SCALE_CEIL,
+ * MX_ROTATE_NONE, MX_LAYOUT_ROWS) is mx_quantize.
  */
 mx_status mx_quantize_ex(mx_format fmt, int block, mx_round rnd, mx_scale_rule rule,
                          mx_rotation rot, int64_t rows, int64_t cols, const void* x,
                          void* codes, void* scales, void* stream, mx_layout layout);
+
+/*
+ * mx_quantize with an output layout: the same arguments, results and errors
+ * as mx_quantize, with the codes and scales written in `layout`.
+ * MX_LAYOUT_KPANEL (MXFP4, MXFP8, MXFP8_E5M2, MXFP6_E3M2 and NVFP4; the MBS
+ * formats return MX_ERR_UNSUPPORTED) needs cols a multiple of the panel width
+ * W, cols / W <= 65535 and rows * (code bytes of a row) < 2^31
+ * (MX_ERR_INVALID_ARG otherwise); the codes, scales and NVFP4 tensor scale
+ * are mx_quantize's, re-laid (mx_pack of mx_quantize's output gives the same
+ * bytes). MX_LAYOUT_ROWS is mx_quantize.
+ */
+mx_status mx_quantize_layout(mx_format fmt, int block, mx_round rnd, int64_t rows, int64_t cols,
+                             const void* x, void* codes, void* scales, float* tensor_scale,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             mx_layout layout);
 
 /*
  * Dequantization (x_real = S * x_elem on the produtoramaxvision page): MX
@@ -259,11 +281,13 @@ mx_status mx_gemm(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd,
 size_t mx_gemm_workspace_bytes(mx_format fmt_a, mx_format fmt_b, int64_t M, int64_t N, int64_t K);
 
 /*
- * Re-lays an MXFP4 tensor from MX_LAYOUT_ROWS into MX_LAYOUT_KPANEL: a byte
- * permutation, no arithmetic. fmt must be MX_FMT_MXFP4 with block 32
- * (MX_ERR_UNSUPPORTED otherwise); rows > 0 and cols a positive multiple of 256
- * with cols / 256 <= 65535 and rows * cols / 2 < 2^31 (MX_ERR_INVALID_ARG
- * otherwise). codes / scales
+ * Re-lays a quantized tensor from MX_LAYOUT_ROWS into MX_LAYOUT_KPANEL: a
+ * byte permutation, no arithmetic. fmt must be MXFP4, MXFP8, MXFP8_E5M2,
+ * MXFP6_E3M2 (block 32) or NVFP4 (block 16) (MX_ERR_UNSUPPORTED otherwise);
+ * rows > 0 and cols a positive multiple of the panel width W with
+ * cols / W <= 65535 and rows * (code bytes of a row) < 2^31
+ * (MX_ERR_INVALID_ARG otherwise). The NVFP4 tensor scale needs no re-laying.
+ * codes / scales
  * are the input (sizes as in mx_quantize), packed_codes / packed_scales the
  * output of the same sizes; input and output must not overlap. All pointers
  * 16-byte aligned device pointers.
@@ -273,13 +297,17 @@ mx_status mx_pack(mx_format fmt, int block, int64_t rows, int64_t cols, const vo
 
 /*
  * mx_gemm with the layouts of the operands given. (MX_LAYOUT_ROWS,
- * MX_LAYOUT_ROWS) is exactly mx_gemm. MX_LAYOUT_KPANEL for A and / or B
- * (codes and scales as written by mx_pack or mx_quantize_ex) is supported
- * for (MXFP4, MXFP4, 32) on the 256 x 256-tile kernel: K a multiple of 256,
- * (M + 256) * K / 2 and (N + 256) * K / 2 below 2^31, and K / 256 <= 65535
- * (MX_ERR_UNSUPPORTED for other pairs, MX_ERR_INVALID_ARG for other shapes).
- * The results are bit-identical to mx_gemm on the same operands in
- * MX_LAYOUT_ROWS.
+ * MX_LAYOUT_ROWS) is exactly mx_gemm. MX_LAYOUT_KPANEL (codes and scales as
+ * written by mx_pack, mx_quantize_layout or mx_quantize_ex) is supported
+ * for A and / or B of (MXFP4, MXFP4, 32) on the 256 x 256-tile kernel: K a
+ * multiple of 256, (M + 256) * K / 2 and (N + 256) * K / 2 below 2^31, and
+ * K / 256 <= 65535; and for both A and B of (MXFP8, MXFP8, 32),
+ * (MXFP8_E5M2, MXFP8_E5M2, 32), (MXFP6_E3M2, MXFP6_E3M2, 32) and
+ * (NVFP4, NVFP4, 16) on the large-tile 16-bit kernel: K a multiple of 64,
+ * K / 64 <= 65535, M and N times the code bytes of a row below 2^31 and
+ * 256 times them below 2^31 (MX_ERR_UNSUPPORTED for other pairs or a single
+ * K-panel operand of those, MX_ERR_INVALID_ARG for other shapes). The results
+ * are bit-identical to mx_gemm on the same operands in MX_LAYOUT_ROWS.
  */
 mx_status mx_gemm_ex(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd,
                      int64_t M, int64_t N, int64_t K,

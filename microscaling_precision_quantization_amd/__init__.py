@@ -60,7 +60,8 @@ def mbs_planes(scales, rows, cols, block=32):
 
 
 # Symbols declared in include/mx.h.
-EXPORTS = ("mx_quantize", "mx_quantize_workspace_bytes", "mx_quantize_ex", "mx_dequantize",
+EXPORTS = ("mx_quantize", "mx_quantize_workspace_bytes", "mx_quantize_ex", "mx_quantize_layout",
+           "mx_dequantize",
            "mx_gemm", "mx_gemm_workspace_bytes", "mx_last_hip_error", "mx_status_string",
            "mx_pack", "mx_gemm_ex", "mx_gemm_noalloc")
 
@@ -92,6 +93,8 @@ def lib():
         L.mx_quantize.argtypes = [i32, i32, i32, i64, i64, P, P, P, P, P, sz, P]
         L.mx_quantize_ex.restype = i32
         L.mx_quantize_ex.argtypes = [i32, i32, i32, i32, i32, i64, i64, P, P, P, P, i32]
+        L.mx_quantize_layout.restype = i32
+        L.mx_quantize_layout.argtypes = [i32, i32, i32, i64, i64, P, P, P, P, P, sz, P, i32]
         L.mx_quantize_workspace_bytes.restype = sz
         L.mx_quantize_workspace_bytes.argtypes = [i32, i64, i64]
         L.mx_dequantize.restype = i32
@@ -127,6 +130,12 @@ def mx_quantize(fmt, block, rnd, rows, cols, x, codes, scales, tensor_scale, wor
 def mx_quantize_ex(fmt, block, rnd, rule, rot, rows, cols, x, codes, scales, stream, layout):
     return lib().mx_quantize_ex(fmt, block, rnd, rule, rot, rows, cols, x, codes, scales, stream,
                                 layout)
+
+
+def mx_quantize_layout(fmt, block, rnd, rows, cols, x, codes, scales, tensor_scale, workspace,
+                       workspace_bytes, stream, layout):
+    return lib().mx_quantize_layout(fmt, block, rnd, rows, cols, x, codes, scales, tensor_scale,
+                                    workspace, workspace_bytes, stream, layout)
 
 
 def mx_quantize_workspace_bytes(fmt, rows, cols):
@@ -248,12 +257,13 @@ LAYOUTS = {"rows": MX_LAYOUT_ROWS, "kpanel": MX_LAYOUT_KPANEL}
 
 def quantize(x, fmt, scale_rule="ceil", rotation=None, layout="rows"):
     """Quantize a contiguous bf16 [rows][cols] device tensor. scale_rule "oas"
-    (MXFP4), rotation "wht32" (MX formats) and layout "kpanel" (MXFP4) select
-    mx_quantize_ex."""
+    (MXFP4) and rotation "wht32" (MXFP4, MXFP8) select mx_quantize_ex, with
+    the layout given; otherwise layout "kpanel" (MXFP4, MXFP8, E5M2, E3M2,
+    NVFP4) selects mx_quantize_layout."""
     import torch
     f = _fmt_id(fmt)
     lay = LAYOUTS[layout]
-    if scale_rule != "ceil" or rotation not in (None, "none") or lay != MX_LAYOUT_ROWS:
+    if scale_rule != "ceil" or rotation not in (None, "none"):
         if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
             raise ValueError("quantize expects a contiguous 2-D bfloat16 tensor")
         rows, cols = x.shape
@@ -275,9 +285,14 @@ def quantize(x, fmt, scale_rule="ceil", rotation=None, layout="rows"):
         ts = torch.empty(1, dtype=torch.float32, device=dev)
         wsb = mx_quantize_workspace_bytes(f, rows, cols)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    _check(mx_quantize(f, BLOCK[f], MX_ROUND_RNE, rows, cols, _ptr(x), _ptr(codes), _ptr(scales),
-                       _ptr(ts), _ptr(ws), wsb, _stream(torch, dev, x)), "mx_quantize")
-    return QTensor(f, rows, cols, codes, scales, ts)
+    if lay == MX_LAYOUT_ROWS:
+        _check(mx_quantize(f, BLOCK[f], MX_ROUND_RNE, rows, cols, _ptr(x), _ptr(codes), _ptr(scales),
+                           _ptr(ts), _ptr(ws), wsb, _stream(torch, dev, x)), "mx_quantize")
+    else:
+        _check(mx_quantize_layout(f, BLOCK[f], MX_ROUND_RNE, rows, cols, _ptr(x), _ptr(codes),
+                                  _ptr(scales), _ptr(ts), _ptr(ws), wsb, _stream(torch, dev, x), lay),
+               "mx_quantize_layout")
+    return QTensor(f, rows, cols, codes, scales, ts, lay)
 
 
 def dequantize(q, out_dtype=None):
@@ -298,8 +313,8 @@ def dequantize(q, out_dtype=None):
 
 
 def pack(q):
-    """An MXFP4 QTensor re-laid into the K-panel layout (mx_pack), for use as
-    the B operand of gemm()."""
+    """A QTensor (MXFP4, MXFP8, E5M2, E3M2 or NVFP4) re-laid into the K-panel
+    layout (mx_pack), for use as a gemm() operand."""
     import torch
     if q.layout != MX_LAYOUT_ROWS:
         raise ValueError("pack() takes a tensor in the row layout")

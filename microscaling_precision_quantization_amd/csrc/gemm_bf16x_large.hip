@@ -99,50 +99,72 @@ struct Stage {
   uint32_t sa[Geo<FMT>::kChunks], sb[Geo<FMT>::kChunks];
 };
 
-template <int FMT>
+// One operand's buffer views. Row layout: views based at the tile's first
+// row, so that rows past M or N read as 0. K-panel layout (PANEL): views of
+// the whole operand, the tile's first row at row0, and stage s's panel at
+// byte s * pcodes (codes) and s * pscales (scales) -- the panel's size; the
+// tile's rows past M or N then read other rows' codes, which only reach
+// outputs that are never stored (row i of A feeds row i of C alone, row j of
+// B column j), or zeros past the operand's end.
+struct OpView {
+  __amdgpu_buffer_rsrc_t codes, scales;
+  int row0;
+  uint32_t pcodes, pscales;
+};
+
+template <int FMT, bool PANEL>
 __device__ __forceinline__ void load_op(u32x4 (&q)[Geo<FMT>::kChunks], u32x4 (&t)[Geo<FMT>::kChunks],
-                                        uint32_t (&sc)[Geo<FMT>::kChunks],
-                                        __amdgpu_buffer_rsrc_t rX, __amdgpu_buffer_rsrc_t rS,
+                                        uint32_t (&sc)[Geo<FMT>::kChunks], const OpView& v,
                                         uint32_t rowbytes, uint32_t scalebytes, int K, int s,
                                         int tid, int u) {
   using G = Geo<FMT>;
   const int row = tid / G::kChunksPerRow + G::kRowStep * u;
   const int c = tid % G::kChunksPerRow;
-  const int k = s * BK + c * G::kCodesPerChunk;  // first element of the chunk
-  const bool ok = k < K;
-  const uint32_t cb = (uint32_t)row_bytes<FMT>(k);
-  const uint32_t off = (uint32_t)row * rowbytes + cb;
-  q[u] = __builtin_amdgcn_raw_buffer_load_b128(rX, ok ? off : kOOB, 0, 0);
+  uint32_t off, so, soff = 0, ssoff = 0;
+  bool ok = true;
+  if (PANEL) {
+    // Panels of BK elements: row r's codes at r * row_bytes(BK), its scales at
+    // r * BK / kBlock (whole panels only, so every chunk is in range).
+    constexpr uint32_t kPw = (uint32_t)row_bytes<FMT>(BK), kPs = BK / G::kBlock;
+    off = (uint32_t)(v.row0 + row) * kPw + (uint32_t)row_bytes<FMT>(c * G::kCodesPerChunk);
+    so = (uint32_t)(v.row0 + row) * kPs + (uint32_t)(c * G::kCodesPerChunk / G::kBlock);
+    soff = (uint32_t)s * v.pcodes;
+    ssoff = (uint32_t)s * v.pscales;
+  } else {
+    const int k = s * BK + c * G::kCodesPerChunk;  // first element of the chunk
+    ok = k < K;
+    off = (uint32_t)row * rowbytes + (uint32_t)row_bytes<FMT>(k);
+    so = (uint32_t)row * scalebytes + (uint32_t)(k / G::kBlock);
+  }
+  q[u] = __builtin_amdgcn_raw_buffer_load_b128(v.codes, ok ? off : kOOB, soff, 0);
   if (FMT == kMXFP6) {
-    const u32x2 t2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rX, ok ? off + 16 : kOOB, 0, 0));
+    const u32x2 t2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(v.codes, ok ? off + 16 : kOOB, soff, 0));
     t[u] = u32x4{t2.x, t2.y, 0, 0};
   }
-  const uint32_t so = (uint32_t)row * scalebytes + (uint32_t)(k / G::kBlock);
   if (FMT == kNVFP4)
-    sc[u] = __builtin_amdgcn_raw_buffer_load_b16(rS, ok ? so : kOOB, 0, 0);
+    sc[u] = __builtin_amdgcn_raw_buffer_load_b16(v.scales, ok ? so : kOOB, ssoff, 0);
   else
-    sc[u] = __builtin_amdgcn_raw_buffer_load_b8(rS, ok ? so : kOOB, 0, 0);
+    sc[u] = __builtin_amdgcn_raw_buffer_load_b8(v.scales, ok ? so : kOOB, ssoff, 0);
 }
 
 // The stage's staging work is split into 4 parts, one per MFMA sub-step: an
 // item is one (operand, chunk u) pair, 2 kChunks items per stage, so a part
 // holds 1 item (8-bit codes: chunk P % 2 of A for P < 2, of B otherwise) or
 // none or one (4- and 6-bit codes: A in part 0, B in part 2).
-template <int FMT, int P>
-__device__ __forceinline__ void load_part(Stage<FMT>& st, __amdgpu_buffer_rsrc_t rA,
-                                          __amdgpu_buffer_rsrc_t rSA, __amdgpu_buffer_rsrc_t rB,
-                                          __amdgpu_buffer_rsrc_t rSB, uint32_t rowbytes,
-                                          uint32_t scalebytes, int K, int s, int tid) {
+template <int FMT, int P, bool PANEL>
+__device__ __forceinline__ void load_part(Stage<FMT>& st, const OpView& va, const OpView& vb,
+                                          uint32_t rowbytes, uint32_t scalebytes, int K, int s,
+                                          int tid) {
   if (Geo<FMT>::kChunks == 2) {
     // Part P: operand P / 2, chunk P % 2.
     if (P < 2)
-      load_op<FMT>(st.qa, st.ta, st.sa, rA, rSA, rowbytes, scalebytes, K, s, tid, P % 2);
+      load_op<FMT, PANEL>(st.qa, st.ta, st.sa, va, rowbytes, scalebytes, K, s, tid, P % 2);
     else
-      load_op<FMT>(st.qb, st.tb, st.sb, rB, rSB, rowbytes, scalebytes, K, s, tid, P % 2);
+      load_op<FMT, PANEL>(st.qb, st.tb, st.sb, vb, rowbytes, scalebytes, K, s, tid, P % 2);
   } else {
     // One chunk per operand: A in part 0, B in part 2.
-    if (P == 0) load_op<FMT>(st.qa, st.ta, st.sa, rA, rSA, rowbytes, scalebytes, K, s, tid, 0);
-    if (P == 2) load_op<FMT>(st.qb, st.tb, st.sb, rB, rSB, rowbytes, scalebytes, K, s, tid, 0);
+    if (P == 0) load_op<FMT, PANEL>(st.qa, st.ta, st.sa, va, rowbytes, scalebytes, K, s, tid, 0);
+    if (P == 2) load_op<FMT, PANEL>(st.qb, st.tb, st.sb, vb, rowbytes, scalebytes, K, s, tid, 0);
   }
 }
 
@@ -224,19 +246,18 @@ __device__ __forceinline__ void store_part(const Stage<FMT>& st, uint8_t* stage,
   }
 }
 
-template <int FMT>
-__device__ __forceinline__ void load_stage(Stage<FMT>& st, __amdgpu_buffer_rsrc_t rA,
-                                           __amdgpu_buffer_rsrc_t rSA, __amdgpu_buffer_rsrc_t rB,
-                                           __amdgpu_buffer_rsrc_t rSB, uint32_t rowbytes,
-                                           uint32_t scalebytes, int K, int s, int tid) {
+template <int FMT, bool PANEL>
+__device__ __forceinline__ void load_stage(Stage<FMT>& st, const OpView& va, const OpView& vb,
+                                           uint32_t rowbytes, uint32_t scalebytes, int K, int s,
+                                           int tid) {
   __builtin_amdgcn_sched_barrier(0);
-  load_part<FMT, 0>(st, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s, tid);
+  load_part<FMT, 0, PANEL>(st, va, vb, rowbytes, scalebytes, K, s, tid);
   __builtin_amdgcn_sched_barrier(0);
-  load_part<FMT, 1>(st, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s, tid);
+  load_part<FMT, 1, PANEL>(st, va, vb, rowbytes, scalebytes, K, s, tid);
   __builtin_amdgcn_sched_barrier(0);
-  load_part<FMT, 2>(st, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s, tid);
+  load_part<FMT, 2, PANEL>(st, va, vb, rowbytes, scalebytes, K, s, tid);
   __builtin_amdgcn_sched_barrier(0);
-  load_part<FMT, 3>(st, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s, tid);
+  load_part<FMT, 3, PANEL>(st, va, vb, rowbytes, scalebytes, K, s, tid);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -310,9 +331,8 @@ __device__ __forceinline__ void region_order() {
 // The K loop and epilogue of one tile, for a wave with NI row blocks of 32
 // (4, or 3 for the second row of waves of a 224-row tile). Mlim is the first
 // row past the tile's valid rows.
-template <int FMT, int OUT, int NI>
-__device__ __forceinline__ void tile_body(uint8_t* smem, __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rSA,
-                                          __amdgpu_buffer_rsrc_t rB, __amdgpu_buffer_rsrc_t rSB,
+template <int FMT, int OUT, int NI, bool PANEL>
+__device__ __forceinline__ void tile_body(uint8_t* smem, const OpView& va, const OpView& vb,
                                           uint32_t rowbytes, uint32_t scalebytes, int K, int tid,
                                           int lane, int wave, int wm, int wn, int r, int g,
                                           const float* __restrict__ TA, const float* __restrict__ TB,
@@ -357,21 +377,21 @@ __device__ __forceinline__ void tile_body(uint8_t* smem, __amdgpu_buffer_rsrc_t 
     // chunk 0 of stage s+3, MFMAs. Likewise for the other sub-steps.
     load_frags<1, NI>(As, Bs, wm, wn, r, g, fa1, fb1);
     store_part<FMT, 0>(Rx, nxt, tid);
-    load_part<FMT, 0>(Rx, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
+    load_part<FMT, 0, PANEL>(Rx, va, vb, rowbytes, scalebytes, K, s2, tid);
     mfma16<NI>(fa0, fb0, acc);
     region_order<FMT, true>();
     load_frags<2, NI>(As, Bs, wm, wn, r, g, fa0, fb0);
     store_part<FMT, 1>(Rx, nxt, tid);
-    load_part<FMT, 1>(Rx, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
+    load_part<FMT, 1, PANEL>(Rx, va, vb, rowbytes, scalebytes, K, s2, tid);
     mfma16<NI>(fa1, fb1, acc);
     region_order<FMT, true>();
     load_frags<3, NI>(As, Bs, wm, wn, r, g, fa1, fb1);
     store_part<FMT, 2>(Rx, nxt, tid);
-    load_part<FMT, 2>(Rx, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
+    load_part<FMT, 2, PANEL>(Rx, va, vb, rowbytes, scalebytes, K, s2, tid);
     mfma16<NI>(fa0, fb0, acc);
     region_order<FMT, true>();
     store_part<FMT, 3>(Rx, nxt, tid);
-    load_part<FMT, 3>(Rx, rA, rSA, rB, rSB, rowbytes, scalebytes, K, s2, tid);
+    load_part<FMT, 3, PANEL>(Rx, va, vb, rowbytes, scalebytes, K, s2, tid);
     mfma16<NI>(fa1, fb1, acc);
     region_order<FMT, false>();
   };
@@ -379,13 +399,13 @@ __device__ __forceinline__ void tile_body(uint8_t* smem, __amdgpu_buffer_rsrc_t 
   // (issued in the loop's order so that the in-order load counter lets the
   // loop's first expansions wait only for their own part).
   Stage<FMT> R[2];
-  load_stage<FMT>(R[0], rA, rSA, rB, rSB, rowbytes, scalebytes, K, s_begin, tid);
+  load_stage<FMT, PANEL>(R[0], va, vb, rowbytes, scalebytes, K, s_begin, tid);
   store_part<FMT, 0>(R[0], smem, tid);
   store_part<FMT, 1>(R[0], smem, tid);
   store_part<FMT, 2>(R[0], smem, tid);
   store_part<FMT, 3>(R[0], smem, tid);
-  load_stage<FMT>(R[0], rA, rSA, rB, rSB, rowbytes, scalebytes, K, min(s_begin + 1, s_end - 1), tid);
-  load_stage<FMT>(R[1], rA, rSA, rB, rSB, rowbytes, scalebytes, K, min(s_begin + 2, s_end - 1), tid);
+  load_stage<FMT, PANEL>(R[0], va, vb, rowbytes, scalebytes, K, min(s_begin + 1, s_end - 1), tid);
+  load_stage<FMT, PANEL>(R[1], va, vb, rowbytes, scalebytes, K, min(s_begin + 2, s_end - 1), tid);
   const float ts = (FMT == kNVFP4) ? TA[0] * TB[0] : 1.0f;
   int s = s_begin;
   for (; s + 1 < s_end; s += 2) {
@@ -407,7 +427,7 @@ __device__ __forceinline__ void tile_body(uint8_t* smem, __amdgpu_buffer_rsrc_t 
   tile256::store_tile<OUT, 2, kWavesN>(acc, smem, ts, C, ldc, Mlim, N, m0, n0, wave, lane);
 }
 
-template <int FMT, int OUT, int BMT>
+template <int FMT, int OUT, int BMT, bool PANEL>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16x_large_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ SA, const float* __restrict__ TA,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ SB, const float* __restrict__ TB,
@@ -422,26 +442,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16x_large_kernel(
   if (!tile256::tile_of_padded(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn)) return;
   const int m0 = tm * BMT, n0 = tn * BN;
 
-  // Buffer views based at the tile's first rows: rows past M or N read as 0.
   const uint32_t rowbytes = (uint32_t)row_bytes<FMT>(K);
   const uint32_t scalebytes = (uint32_t)(K / Geo<FMT>::kBlock);
   const int mrows = min(BMT, M - m0), nrows = min(BN, N - n0);
-  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * rowbytes), 0, (int)(mrows * rowbytes), kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)(B + (int64_t)n0 * rowbytes), 0, (int)(nrows * rowbytes), kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc((void*)(SA + (int64_t)m0 * scalebytes), 0, (int)(mrows * scalebytes), kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t rSB = __builtin_amdgcn_make_buffer_rsrc((void*)(SB + (int64_t)n0 * scalebytes), 0, (int)(nrows * scalebytes), kRsrcFlags);
+  OpView va, vb;
+  if (PANEL) {
+    va = {__builtin_amdgcn_make_buffer_rsrc((void*)A, 0, (int)(M * rowbytes), kRsrcFlags),
+          __builtin_amdgcn_make_buffer_rsrc((void*)SA, 0, (int)(M * scalebytes), kRsrcFlags), m0,
+          (uint32_t)M * (uint32_t)row_bytes<FMT>(BK), (uint32_t)M * (uint32_t)(BK / Geo<FMT>::kBlock)};
+    vb = {__builtin_amdgcn_make_buffer_rsrc((void*)B, 0, (int)(N * rowbytes), kRsrcFlags),
+          __builtin_amdgcn_make_buffer_rsrc((void*)SB, 0, (int)(N * scalebytes), kRsrcFlags), n0,
+          (uint32_t)N * (uint32_t)row_bytes<FMT>(BK), (uint32_t)N * (uint32_t)(BK / Geo<FMT>::kBlock)};
+  } else {
+    // Views based at the tile's first rows: rows past M or N read as 0.
+    va = {__builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * rowbytes), 0, (int)(mrows * rowbytes), kRsrcFlags),
+          __builtin_amdgcn_make_buffer_rsrc((void*)(SA + (int64_t)m0 * scalebytes), 0, (int)(mrows * scalebytes), kRsrcFlags),
+          0, 0u, 0u};
+    vb = {__builtin_amdgcn_make_buffer_rsrc((void*)(B + (int64_t)n0 * rowbytes), 0, (int)(nrows * rowbytes), kRsrcFlags),
+          __builtin_amdgcn_make_buffer_rsrc((void*)(SB + (int64_t)n0 * scalebytes), 0, (int)(nrows * scalebytes), kRsrcFlags),
+          0, 0u, 0u};
+  }
 
   // A 224-row tile: the first row of waves holds 128 rows (4 blocks), the
   // second 96 (3 blocks); the staged rows 224 .. 255 lie outside A's view and
   // are never read.
   const int Mlim = m0 + mrows;
   if (BMT == 256 || wm == 0)
-    tile_body<FMT, OUT, 4>(smem, rA, rSA, rB, rSB, rowbytes, scalebytes, K, tid, lane, wave, wm, wn, r, g, TA, TB, C, ldc, Mlim, N, m0, n0, s_begin, s_end, fold);
+    tile_body<FMT, OUT, 4, PANEL>(smem, va, vb, rowbytes, scalebytes, K, tid, lane, wave, wm, wn, r, g, TA, TB, C, ldc, Mlim, N, m0, n0, s_begin, s_end, fold);
   else
-    tile_body<FMT, OUT, 3>(smem, rA, rSA, rB, rSB, rowbytes, scalebytes, K, tid, lane, wave, wm, wn, r, g, TA, TB, C, ldc, Mlim, N, m0, n0, s_begin, s_end, fold);
+    tile_body<FMT, OUT, 3, PANEL>(smem, va, vb, rowbytes, scalebytes, K, tid, lane, wave, wm, wn, r, g, TA, TB, C, ldc, Mlim, N, m0, n0, s_begin, s_end, fold);
 }
 
-template <int FMT, int BMT>
+template <int FMT, int BMT, bool PANEL>
 hipError_t launch(hipStream_t s, int tm, int tn, const uint8_t* A, const uint8_t* SA, const float* TA,
             const uint8_t* B, const uint8_t* SB, const float* TB, int out_dtype, void* c,
             int64_t ldc, int M, int N, int K) {
@@ -455,27 +487,33 @@ hipError_t launch(hipStream_t s, int tm, int tn, const uint8_t* A, const uint8_t
     // adding its sums into C (launches on one stream run in order).
     constexpr int kSeg = 12;
     if (nsteps <= kSeg) {
-      MX_TRY(launch_kernel(&gemm_bf16x_large_kernel<FMT, kOutF32, BMT>, grid, kThreads, 0, s, A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn, 0, nsteps, 0));
+      MX_TRY(launch_kernel(&gemm_bf16x_large_kernel<FMT, kOutF32, BMT, PANEL>, grid, kThreads, 0, s, A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn, 0, nsteps, 0));
       return hipSuccess;
     }
     for (int s0 = 0; s0 < nsteps; s0 += kSeg) {
       const int s1 = s0 + kSeg < nsteps ? s0 + kSeg : nsteps;
       const int fold = 1 | (s0 == 0 ? 2 : 0) | (s1 == nsteps ? 4 : 0);
-      MX_TRY(launch_kernel(&gemm_bf16x_large_kernel<FMT, kOutF32, BMT>, grid, kThreads, 0, s, A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn, s0, s1, fold));
+      MX_TRY(launch_kernel(&gemm_bf16x_large_kernel<FMT, kOutF32, BMT, PANEL>, grid, kThreads, 0, s, A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn, s0, s1, fold));
     }
     return hipSuccess;
   }
-  MX_TRY(launch_kernel(&gemm_bf16x_large_kernel<FMT, kOutBF16, BMT>, grid, kThreads, 0, s, A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn, 0, nsteps, 0));
+  MX_TRY(launch_kernel(&gemm_bf16x_large_kernel<FMT, kOutBF16, BMT, PANEL>, grid, kThreads, 0, s, A, SA, TA, B, SB, TB, c, ldc, M, N, K, tm, tn, 0, nsteps, 0));
   return hipSuccess;
 }
 
 template <int FMT>
-hipError_t launch_rows(bool rows224, hipStream_t s, int64_t M, int tn, const uint8_t* A, const uint8_t* SA,
-                       const float* TA, const uint8_t* B, const uint8_t* SB, const float* TB,
-                       int out_dtype, void* c, int64_t ldc, int N, int K) {
+hipError_t launch_rows(bool rows224, bool panel, hipStream_t s, int64_t M, int tn, const uint8_t* A,
+                       const uint8_t* SA, const float* TA, const uint8_t* B, const uint8_t* SB,
+                       const float* TB, int out_dtype, void* c, int64_t ldc, int N, int K) {
+  const int tm224 = (int)((M + 223) / 224), tm256 = (int)((M + 255) / 256);
+  if (panel) {
+    if (rows224)
+      return launch<FMT, 224, true>(s, tm224, tn, A, SA, TA, B, SB, TB, out_dtype, c, ldc, (int)M, N, K);
+    return launch<FMT, 256, true>(s, tm256, tn, A, SA, TA, B, SB, TB, out_dtype, c, ldc, (int)M, N, K);
+  }
   if (rows224)
-    return launch<FMT, 224>(s, (int)((M + 223) / 224), tn, A, SA, TA, B, SB, TB, out_dtype, c, ldc, (int)M, N, K);
-  return launch<FMT, 256>(s, (int)((M + 255) / 256), tn, A, SA, TA, B, SB, TB, out_dtype, c, ldc, (int)M, N, K);
+    return launch<FMT, 224, false>(s, tm224, tn, A, SA, TA, B, SB, TB, out_dtype, c, ldc, (int)M, N, K);
+  return launch<FMT, 256, false>(s, tm256, tn, A, SA, TA, B, SB, TB, out_dtype, c, ldc, (int)M, N, K);
 }
 
 // Compute units of the current device (queried once per device).
@@ -503,7 +541,7 @@ bool gemm_bf16x_large_fits(int fmt, int64_t M, int64_t N, int64_t K) {
 
 hipError_t gemm_bf16x_large(int fmt, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
                             const float* ta, const void* b, const void* sb, const float* tb,
-                            int out_dtype, void* c, int64_t ldc, hipStream_t s) {
+                            int out_dtype, void* c, int64_t ldc, hipStream_t s, bool panel) {
   const int tn = (int)((N + BN - 1) / BN);
   // Tile height: every tile of a round of the device's CUs takes about as
   // long as its rows, so 224-row tiles pay when they need fewer rows of
@@ -516,12 +554,12 @@ hipError_t gemm_bf16x_large(int fmt, int64_t M, int64_t N, int64_t K, const void
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;
   if (fmt == kMXFP8)
-    return launch_rows<kMXFP8>(rows224, s, M, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)N, (int)K);
+    return launch_rows<kMXFP8>(rows224, panel, s, M, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)N, (int)K);
   if (fmt == kMXFP8E5M2)
-    return launch_rows<kMXFP8E5M2>(rows224, s, M, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)N, (int)K);
+    return launch_rows<kMXFP8E5M2>(rows224, panel, s, M, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)N, (int)K);
   if (fmt == kMXFP6)
-    return launch_rows<kMXFP6>(rows224, s, M, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)N, (int)K);
-  return launch_rows<kNVFP4>(rows224, s, M, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)N, (int)K);
+    return launch_rows<kMXFP6>(rows224, panel, s, M, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)N, (int)K);
+  return launch_rows<kNVFP4>(rows224, panel, s, M, tn, A, SA, ta, B, SB, tb, out_dtype, c, ldc, (int)N, (int)K);
 }
 
 }  // namespace mx

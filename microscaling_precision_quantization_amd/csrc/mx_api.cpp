@@ -38,10 +38,28 @@ mx_status hip_status(hipError_t e) {
   return MX_ERR_HIP;
 }
 
-// A K-panel MXFP4 tensor: whole 256-element panels, at most 65535 of them (a
-// grid dimension of the panel quantizer), and 32-bit byte offsets.
-bool panel_shape_ok(int64_t rows, int64_t cols) {
-  return cols % 256 == 0 && cols / 256 <= 65535 && rows < ((int64_t)1 << 31) / (cols / 2);
+// Elements per K panel of a K-panel tensor: 256 for MXFP4 (one step of its
+// GEMM), 64 for MXFP8, E5M2, E3M2 and NVFP4 (one stage of theirs).
+int panel_width(int fmt) { return fmt == MX_FMT_MXFP4 ? 256 : 64; }
+
+// Code bytes of a row of cols elements.
+int64_t code_bytes(int fmt, int64_t cols) {
+  if (fmt == MX_FMT_MXFP8 || fmt == MX_FMT_MXFP8_E5M2) return cols;
+  if (fmt == MX_FMT_MXFP6_E3M2) return cols * 3 / 4;
+  return cols / 2;
+}
+
+// Formats with a K-panel layout.
+bool has_panel(int fmt) {
+  return fmt == MX_FMT_MXFP4 || fmt == MX_FMT_MXFP8 || fmt == MX_FMT_MXFP8_E5M2 ||
+         fmt == MX_FMT_MXFP6_E3M2 || fmt == MX_FMT_NVFP4;
+}
+
+// A K-panel tensor: whole panels, at most 65535 of them (a grid dimension of
+// the panel quantizer), and 32-bit byte offsets.
+bool panel_shape_ok(int fmt, int64_t rows, int64_t cols) {
+  const int w = panel_width(fmt);
+  return cols % w == 0 && cols / w <= 65535 && rows < ((int64_t)1 << 31) / code_bytes(fmt, cols);
 }
 
 // Common checks for a [rows][cols] quantized tensor.
@@ -62,11 +80,16 @@ size_t mx_quantize_workspace_bytes(mx_format fmt, int64_t rows, int64_t cols) {
   return mx::quant_nvfp4_workspace(rows, cols);
 }
 
-mx_status mx_quantize(mx_format fmt, int block, mx_round rnd, int64_t rows, int64_t cols,
-                      const void* x, void* codes, void* scales, float* tensor_scale,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+mx_status mx_quantize_layout(mx_format fmt, int block, mx_round rnd, int64_t rows, int64_t cols,
+                             const void* x, void* codes, void* scales, float* tensor_scale,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             mx_layout layout) {
   mx_status st = check_tensor(fmt, block, rnd, rows, cols);
   if (st != MX_OK) return st;
+  if (layout != MX_LAYOUT_ROWS && layout != MX_LAYOUT_KPANEL) return MX_ERR_UNSUPPORTED;
+  const bool panel = layout == MX_LAYOUT_KPANEL;
+  if (panel && !has_panel(fmt)) return MX_ERR_UNSUPPORTED;
+  if (panel && !panel_shape_ok(fmt, rows, cols)) return MX_ERR_INVALID_ARG;
   if (!x || !codes || !scales) return MX_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
@@ -74,11 +97,18 @@ mx_status mx_quantize(mx_format fmt, int block, mx_round rnd, int64_t rows, int6
     if (!tensor_scale || !aligned4(tensor_scale)) return MX_ERR_INVALID_ARG;
     if (!workspace || !aligned16(workspace)) return MX_ERR_INVALID_ARG;
     if (workspace_bytes < mx::quant_nvfp4_workspace(rows, cols)) return MX_ERR_INVALID_ARG;
-    return hip_status(mx::quant_nvfp4(rows, cols, x, codes, scales, tensor_scale, workspace, s));
+    return hip_status(mx::quant_nvfp4(rows, cols, x, codes, scales, tensor_scale, workspace, s, panel));
   }
   if (tensor_scale) return MX_ERR_INVALID_ARG;
   if (is_mbs(fmt)) return hip_status(mx::quant_mbs(rows, cols, x, codes, scales, s, block));
-  return hip_status(mx::quant_mx(fmt, rows, cols, x, codes, scales, s));
+  return hip_status(mx::quant_mx(fmt, rows, cols, x, codes, scales, s, false, false, panel));
+}
+
+mx_status mx_quantize(mx_format fmt, int block, mx_round rnd, int64_t rows, int64_t cols,
+                      const void* x, void* codes, void* scales, float* tensor_scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return mx_quantize_layout(fmt, block, rnd, rows, cols, x, codes, scales, tensor_scale, workspace,
+                            workspace_bytes, stream, MX_LAYOUT_ROWS);
 }
 
 mx_status mx_quantize_ex(mx_format fmt, int block, mx_round rnd, mx_scale_rule rule,
@@ -88,9 +118,8 @@ mx_status mx_quantize_ex(mx_format fmt, int block, mx_round rnd, mx_scale_rule r
   if (st != MX_OK) return st;
   if (layout != MX_LAYOUT_ROWS && layout != MX_LAYOUT_KPANEL) return MX_ERR_UNSUPPORTED;
   const bool panel = layout == MX_LAYOUT_KPANEL;
-  if (panel && fmt != MX_FMT_MXFP4) return MX_ERR_UNSUPPORTED;
-  if (panel && !panel_shape_ok(rows, cols)) return MX_ERR_INVALID_ARG;
   if (fmt != MX_FMT_MXFP4 && fmt != MX_FMT_MXFP8) return MX_ERR_UNSUPPORTED;
+  if (panel && !panel_shape_ok(fmt, rows, cols)) return MX_ERR_INVALID_ARG;
   if (rule != MX_SCALE_CEIL && !(rule == MX_SCALE_OAS && fmt == MX_FMT_MXFP4))
     return MX_ERR_UNSUPPORTED;
   if (rot != MX_ROTATE_NONE && rot != MX_ROTATE_WHT32) return MX_ERR_UNSUPPORTED;
@@ -143,7 +172,10 @@ mx_status gemm_impl(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, i
   const bool mbs = (fmt_a == MX_FMT_MXFP4_MBS && fmt_b == MX_FMT_MXFP4_MBS && block == 32) ||
                    (fmt_a == MX_FMT_MXFP4_MBS16 && fmt_b == MX_FMT_MXFP4_MBS16 && block == 16);
   if (!(w4a4 || w8a8 || nv || w4a16 || alt || mbs)) return MX_ERR_UNSUPPORTED;
-  if ((panel_a || panel_b) && !w4a4) return MX_ERR_UNSUPPORTED;
+  // K-panel operands: the MXFP4 pair (either operand or both), or both
+  // operands of the pairs on the 16-bit MFMAs.
+  if ((panel_a || panel_b) && !w4a4 && !((w8a8 || nv || alt) && panel_a && panel_b))
+    return MX_ERR_UNSUPPORTED;
   if (rnd != MX_ROUND_RNE) return MX_ERR_UNSUPPORTED;
   if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16) return MX_ERR_UNSUPPORTED;
   if (M <= 0 || N <= 0 || K <= 0 || M > kMaxExtent || N > kMaxExtent || K > kMaxExtent)
@@ -177,10 +209,16 @@ mx_status gemm_impl(mx_format fmt_a, mx_format fmt_b, int block, mx_round rnd, i
     return MX_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   if (panel_a || panel_b) {
-    // Only the 256 x 256-tile kernel reads K-panel operands.
-    if (!mx::gemm_mxfp4_fits(M, N, K)) return MX_ERR_INVALID_ARG;
-    if ((panel_a && !panel_shape_ok(M, K)) || (panel_b && !panel_shape_ok(N, K)))
+    if ((panel_a && !panel_shape_ok(fmt_a, M, K)) || (panel_b && !panel_shape_ok(fmt_b, N, K)))
       return MX_ERR_INVALID_ARG;
+    if (!w4a4) {
+      // The large-tile kernel of the 16-bit MFMAs reads K-panel operands.
+      if (!mx::gemm_bf16x_large_fits(fmt_a, M, N, K)) return MX_ERR_INVALID_ARG;
+      return hip_status(mx::gemm_bf16x_large(fmt_a, M, N, K, a, a_scales, a_ts, b, b_scales, b_ts,
+                                             out_dtype, c, ldc, s, true));
+    }
+    // Only the 256 x 256-tile kernel reads K-panel MXFP4 operands.
+    if (!mx::gemm_mxfp4_fits(M, N, K)) return MX_ERR_INVALID_ARG;
     return hip_status(mx::gemm_mxfp4(M, N, K, a, a_scales, b, b_scales, out_dtype, c, ldc, s,
                                      panel_a, panel_b));
   }
@@ -247,17 +285,19 @@ mx_status mx_gemm_noalloc(mx_format fmt_a, mx_format fmt_b, int block, mx_round 
 
 mx_status mx_pack(mx_format fmt, int block, int64_t rows, int64_t cols, const void* codes,
                   const void* scales, void* packed_codes, void* packed_scales, void* stream) {
-  if (fmt != MX_FMT_MXFP4 || block != 32) return MX_ERR_UNSUPPORTED;
-  if (rows <= 0 || cols <= 0 || !panel_shape_ok(rows, cols)) return MX_ERR_INVALID_ARG;
+  if (!has_panel(fmt) || block != block_of(fmt)) return MX_ERR_UNSUPPORTED;
+  if (rows <= 0 || cols <= 0 || !panel_shape_ok(fmt, rows, cols)) return MX_ERR_INVALID_ARG;
   if (!codes || !scales || !packed_codes || !packed_scales) return MX_ERR_INVALID_ARG;
   if (!aligned16(codes) || !aligned16(scales) || !aligned16(packed_codes) || !aligned16(packed_scales))
     return MX_ERR_INVALID_ARG;
-  const size_t cb = (size_t)rows * (size_t)(cols / 2), sb = (size_t)rows * (size_t)(cols / 32);
+  const size_t cb = (size_t)rows * (size_t)code_bytes(fmt, cols),
+               sb = (size_t)rows * (size_t)(cols / block);
   if (overlap(codes, cb, packed_codes, cb) || overlap(codes, cb, packed_scales, sb) ||
       overlap(scales, sb, packed_codes, cb) || overlap(scales, sb, packed_scales, sb))
     return MX_ERR_INVALID_ARG;
-  return hip_status(mx::pack_mxfp4(rows, cols, codes, scales, packed_codes, packed_scales,
-                                   (hipStream_t)stream));
+  const int w = panel_width(fmt);
+  return hip_status(mx::pack_kpanel(rows, cols / w, (int)code_bytes(fmt, w), w / block, codes, scales,
+                                    packed_codes, packed_scales, (hipStream_t)stream));
 }
 
 int mx_last_hip_error(void) { return g_last_hip_error; }

@@ -45,7 +45,8 @@ enum : int { kOutF32 = 0, kOutBF16 = 1 };
 
 // ---- quantize.hip
 // oas: MXFP4's overflow-aware scale rule; rot: 32-point Walsh-Hadamard rotation first.
-// panel: MXFP4 codes and scales in the K-panel layout (cols % 256 = 0).
+// panel: codes and scales in the K-panel layout (panels of 256 elements for
+// MXFP4, of 64 for MXFP8, E5M2 and E3M2; cols a multiple of that).
 hipError_t quant_mx(int fmt, int64_t rows, int64_t cols, const void* x, void* codes,
                     void* scales, hipStream_t s, bool oas = false,
                     bool rot = false, bool panel = false);
@@ -55,8 +56,9 @@ hipError_t quant_mx(int fmt, int64_t rows, int64_t cols, const void* x, void* co
 hipError_t quant_mbs(int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
                      hipStream_t s, int base);
 size_t quant_nvfp4_workspace(int64_t rows, int64_t cols);
+// panel: codes and scales in the K-panel layout with 64-element panels.
 hipError_t quant_nvfp4(int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
-                       float* tensor_scale, void* workspace, hipStream_t s);
+                       float* tensor_scale, void* workspace, hipStream_t s, bool panel = false);
 
 // ---- dequantize.hip
 hipError_t dequant(int fmt, int64_t rows, int64_t cols, const void* codes, const void* scales,
@@ -88,9 +90,11 @@ hipError_t gemm_mxfp4(int64_t M, int64_t N, int64_t K, const void* a, const void
                       const void* b, const void* sb, int out_dtype, void* c, int64_t ldc,
                       hipStream_t s, bool panel_a, bool panel_b);
 
-// ---- pack.hip (MXFP4 codes and scales into the K-panel layout)
-hipError_t pack_mxfp4(int64_t rows, int64_t cols, const void* codes, const void* scales,
-                      void* packed_codes, void* packed_scales, hipStream_t s);
+// ---- pack.hip (codes and scales into the K-panel layout): `panels` panels,
+// wb code bytes (a multiple of 16) and sb scale bytes (8, 4 or 2) per row
+// and panel.
+hipError_t pack_kpanel(int64_t rows, int64_t panels, int wb, int sb, const void* codes,
+                       const void* scales, void* packed_codes, void* packed_scales, hipStream_t s);
 
 // ---- gemm_bf16x.hip (MXFP8 x MXFP8 and NVFP4 x NVFP4, expanded exactly to bf16)
 hipError_t gemm_bf16x(int fmt, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
@@ -99,9 +103,10 @@ hipError_t gemm_bf16x(int fmt, int64_t M, int64_t N, int64_t K, const void* a, c
 
 // ---- gemm_bf16x_large.hip (256 x 256 or 224 x 256 tiles; MXFP8 / NVFP4 on the bf16 MFMA)
 bool gemm_bf16x_large_fits(int fmt, int64_t M, int64_t N, int64_t K);
+// panel: both operands in the K-panel layout (64-element panels).
 hipError_t gemm_bf16x_large(int fmt, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
                             const float* ta, const void* b, const void* sb, const float* tb,
-                            int out_dtype, void* c, int64_t ldc, hipStream_t s);
+                            int out_dtype, void* c, int64_t ldc, hipStream_t s, bool panel = false);
 
 // ---- gemm_w4a16.hip: the library's own scratch for mx_gemm_noalloc (the
 // W4A16 split-K partials), a file-scope device array of this many bytes per

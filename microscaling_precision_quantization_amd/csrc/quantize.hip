@@ -127,11 +127,21 @@ __device__ __forceinline__ u32x4 wht32_chunk(u32x4 v, int lane) {
 
 // MXFP4 / MXFP8 (E4M3) / MXFP8 (E5M2); OAS: MXFP4's overflow-aware scale
 // rule; ROT: rotate every block first.
-// PANEL (MXFP4): codes and scales in the K-panel layout ([cols/256][rows][128]
-// and [cols/256][rows][8]). The grid is then 2-D: workgroup (x, y) takes
-// rows 32 x .. 32 x + 31 of panel y, lanes 32 r' + j of a wave the 32 chunks
-// j of a row, so loads, code stores and scale stores stay contiguous and no
-// index needs a division. nchunks is then rows, cpr the chunks per row.
+// PANEL: codes and scales in the K-panel layout, panels of kPanel elements
+// (MXFP4 256: [cols/256][rows][128] and [cols/256][rows][8]; MXFP8 64:
+// [cols/64][rows][64] and [cols/64][rows][2]), i.e. kCpp 16-byte input
+// chunks per row and panel. The grid is then 2-D: workgroup (x, y) takes
+// rows kRpw x .. kRpw x + kRpw - 1 of panel y, consecutive lanes the chunks
+// of a row, so loads, code stores and scale stores stay contiguous and no
+// index needs a division by a runtime value. nchunks is then rows, cpr the
+// chunks per row.
+template <int FMT>
+struct PanelGeo {
+  static constexpr int kPanel = (FMT == kMXFP4) ? 256 : 64;
+  static constexpr int kCpp = kPanel / 8;                    // chunks per row and panel
+  static constexpr int kRpw = kThreads * kUnroll / kCpp;      // rows per workgroup
+};
+
 template <int FMT, bool OAS, bool ROT, bool PANEL = false>
 __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restrict__ x,
                                                             void* __restrict__ codes,
@@ -140,21 +150,25 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restr
   const int lane = threadIdx.x & 63;
   const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
   // Source chunk, and (PANEL) destination dword of the codes, for item u.
+  using PG = PanelGeo<FMT>;
   auto src_of = [&](int u) -> int64_t {
     if (!PANEL) return base + u * kThreads;
     const int t = u * kThreads + (int)threadIdx.x;
-    const int64_t r = (int64_t)blockIdx.x * 32 + (t >> 5);
-    return r * cpr + (int64_t)blockIdx.y * 32 + (t & 31);
+    const int64_t r = (int64_t)blockIdx.x * PG::kRpw + t / PG::kCpp;
+    return r * cpr + (int64_t)blockIdx.y * PG::kCpp + t % PG::kCpp;
+  };
+  // Row of item u of this thread, or of the same item of lane t (PANEL).
+  auto prow = [&](int u, int t) -> int64_t {
+    return (int64_t)blockIdx.x * PG::kRpw + (u * kThreads + t) / PG::kCpp;
   };
   auto valid = [&](int u) -> bool {
     if (!PANEL) return base + u * kThreads < nchunks;
-    return (int64_t)blockIdx.x * 32 + ((u * kThreads + (int)threadIdx.x) >> 5) < nchunks;
+    return prow(u, (int)threadIdx.x) < nchunks;
   };
   auto dst_of = [&](int u) -> int64_t {
     if (!PANEL) return base + u * kThreads;
     const int t = u * kThreads + (int)threadIdx.x;
-    const int64_t r = (int64_t)blockIdx.x * 32 + (t >> 5);
-    return ((int64_t)blockIdx.y * nchunks + r) * 32 + (t & 31);
+    return ((int64_t)blockIdx.y * nchunks + prow(u, (int)threadIdx.x)) * PG::kCpp + t % PG::kCpp;
   };
   u32x4 v[kUnroll];
 #pragma unroll
@@ -208,7 +222,8 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restr
     }
     // Scale bytes: lanes 3, 7, 11, 15 of each 16-lane DPP row hold 4
     // consecutive blocks; lane 15 assembles them into one dword store. (With
-    // PANEL the dword index c / 4 is (panel * rows + row) * 8 + block.)
+    // PANEL the byte index c / 4 is (panel * rows + row) * kPanel / 32 +
+    // block, so a DPP row's 4 blocks are consecutive there too.)
     const uint32_t s4 = dpp<dpp_row_shr(4)>(E);
     const uint32_t s8 = dpp<dpp_row_shr(8)>(E);
     const uint32_t s12 = dpp<dpp_row_shr(12)>(E);
@@ -216,9 +231,13 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restr
     if ((lane & 15) == 15 && ok) {
       *(uint32_t*)(scales + (blk - 3)) = s12 | (s8 << 8) | (s4 << 16) | (E << 24);
     }
-    // Ragged end: the row's lane 15 is past the end, store bytes instead
-    // (never with PANEL: a row's 32 chunks are all in or all out).
-    if (!PANEL && (lane & 3) == 0 && ok && c - (lane & 15) + 15 >= nchunks) scales[blk] = (uint8_t)E;
+    // Ragged end: the DPP row's lane 15 is past the end, store bytes instead.
+    // Row layout: past the tensor's last chunk. PANEL: a row's chunks are all
+    // in or all out, so this only happens where a DPP row spans two rows of
+    // 8 chunks (64-element panels) and the second is past the last row.
+    const bool last_out = PANEL ? prow(u, ((int)threadIdx.x & ~15) | 15) >= nchunks
+                                : c - (lane & 15) + 15 >= nchunks;
+    if ((lane & 3) == 0 && ok && last_out) scales[blk] = (uint8_t)E;
   }
 }
 
@@ -349,23 +368,40 @@ typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 //    distinct 16-byte bank groups (80 / 16 = 5 is odd);
 //  * store: each lane writes its block's 24 code bytes to LDS at 24 t, and
 //    the workgroup's 6 KB of codes leave as lane-consecutive 16-byte chunks.
+// PANEL: the K-panel layout with 64-element panels ([cols/64][rows][48] and
+// [cols/64][rows][2]). Workgroup (x, y) then takes the two blocks of rows
+// 128 x .. 128 x + 127 in panel y: 8 chunks of 128 contiguous input bytes per
+// row, and its output is again one contiguous range of codes and of scales.
+// nblocks is then the row count and cpr the input chunks per row.
 constexpr int kF6Pad = 80;                              // LDS bytes per staged block
 constexpr int kF6Codes = kThreads * 24;                 // code bytes per workgroup
 
+template <bool PANEL>
 __global__ __launch_bounds__(kThreads) void quant_mxfp6_kernel(const u32x4* __restrict__ x,
                                                                uint8_t* __restrict__ codes,
                                                                uint8_t* __restrict__ scales,
-                                                               int64_t nblocks) {
+                                                               int64_t nblocks, int64_t cpr) {
   __shared__ __attribute__((aligned(16))) uint8_t lin[kThreads * kF6Pad];
   __shared__ __attribute__((aligned(16))) uint8_t lout[kF6Codes];
   const int tid = threadIdx.x;
-  const int64_t b0 = (int64_t)blockIdx.x * kThreads;              // first block of the workgroup
-  const int64_t nb = min((int64_t)kThreads, nblocks - b0);         // blocks in it
+  // b0: first output block of the workgroup (row layout: also its first
+  // input block); nb: blocks in it.
+  int64_t b0, nb, r0 = 0;
+  if (PANEL) {
+    r0 = (int64_t)blockIdx.x * (kThreads / 2);
+    b0 = ((int64_t)blockIdx.y * nblocks + r0) * 2;
+    nb = 2 * min((int64_t)(kThreads / 2), nblocks - r0);
+  } else {
+    b0 = (int64_t)blockIdx.x * kThreads;
+    nb = min((int64_t)kThreads, nblocks - b0);
+  }
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int c = i * kThreads + tid;                              // chunk within the workgroup
     if (c < 4 * nb) {
-      const u32x4 v = __builtin_nontemporal_load(x + 4 * b0 + c);
+      const int64_t src = PANEL ? (r0 + (c >> 3)) * cpr + (int64_t)blockIdx.y * 8 + (c & 7)
+                                : 4 * b0 + c;
+      const u32x4 v = __builtin_nontemporal_load(x + src);
       *(u32x4*)(lin + (c >> 2) * kF6Pad + (c & 3) * 16) = v;
     }
   }
@@ -470,28 +506,48 @@ __device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast
 // x * (1/D), with x = +-0 kept as is (no 0 * Inf) and D = 0 giving +-0.
 __device__ __forceinline__ float nv_scaled(float xv, float rz) { return xv == 0.0f ? xv : xv * rz; }
 
+// PANEL: codes and scales in the K-panel layout with 64-element panels
+// ([cols/64][rows][32] and [cols/64][rows][4]). The grid is then 2-D:
+// workgroup (x, y) takes rows 128 x .. 128 x + 127 of panel y, each group of
+// 8 lanes the 8 chunks of one row; nchunks is then the row count and cpr the
+// chunks per row.
+template <bool PANEL>
 __global__ __launch_bounds__(kThreads) void quant_nvfp4_kernel(const u32x4* __restrict__ x,
                                                                uint32_t* __restrict__ codes,
                                                                uint8_t* __restrict__ scales,
                                                                const uint32_t* __restrict__ partial,
                                                                int npartial,
                                                                float* __restrict__ tensor_scale,
-                                                               int64_t nchunks) {
+                                                               int64_t nchunks, int64_t cpr) {
   const int lane = threadIdx.x & 63;
   const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+  // Input chunk, output chunk and validity of item u.
+  auto row_of = [&](int u) -> int64_t {
+    return (int64_t)blockIdx.x * (kThreads * kUnroll / 8) + (u * kThreads + (int)threadIdx.x) / 8;
+  };
+  auto src_of = [&](int u) -> int64_t {
+    if (!PANEL) return base + u * kThreads;
+    return row_of(u) * cpr + (int64_t)blockIdx.y * 8 + (threadIdx.x & 7);
+  };
+  auto dst_of = [&](int u) -> int64_t {
+    if (!PANEL) return base + u * kThreads;
+    return ((int64_t)blockIdx.y * nchunks + row_of(u)) * 8 + (threadIdx.x & 7);
+  };
+  auto valid = [&](int u) -> bool {
+    return PANEL ? row_of(u) < nchunks : base + u * kThreads < nchunks;
+  };
   // The element loads go out first; the tensor scale is reduced meanwhile.
   u32x4 v[kUnroll];
 #pragma unroll
-  for (int u = 0; u < kUnroll; u++) {
-    const int64_t c = base + u * kThreads;
-    v[u] = (c < nchunks) ? __builtin_nontemporal_load(x + c) : u32x4{0, 0, 0, 0};
-  }
+  for (int u = 0; u < kUnroll; u++)
+    v[u] = valid(u) ? __builtin_nontemporal_load(x + src_of(u)) : u32x4{0, 0, 0, 0};
   const float st = nvfp4_tensor_scale(partial, npartial, tensor_scale);
   const bool bad = __builtin_isnan(st);
   const float d6 = 6.0f * st;
 #pragma unroll
   for (int u = 0; u < kUnroll; u++) {
-    const int64_t c = base + u * kThreads;
+    const int64_t c = dst_of(u);
+    const bool ok = valid(u);
     uint32_t m = chunk_absmax(v[u]);
     m = umax(m, dpp<kDppSwap1>(m));  // the partner lane holds the other half
     const float bamax = __builtin_bit_cast(float, m << 16);
@@ -513,16 +569,18 @@ __global__ __launch_bounds__(kThreads) void quant_nvfp4_kernel(const u32x4* __re
       q = 0;
       sbc = 0x7F;
     }
-    if (c < nchunks) __builtin_nontemporal_store(q, codes + c);
-    // Lanes 1, 3, 5, 7 of each group of 8 hold 4 consecutive block scales.
+    if (ok) __builtin_nontemporal_store(q, codes + c);
+    // Lanes 1, 3, 5, 7 of each group of 8 hold 4 consecutive block scales
+    // (with PANEL, the 4 scales of one row's panel).
     const uint32_t s2 = dpp<dpp_row_shr(2)>(sbc);
     const uint32_t s4 = dpp<dpp_row_shr(4)>(sbc);
     const uint32_t s6 = dpp<dpp_row_shr(6)>(sbc);
     const int64_t blk = c >> 1;
-    if ((lane & 7) == 7 && c < nchunks) {
+    if ((lane & 7) == 7 && ok) {
       *(uint32_t*)(scales + (blk - 3)) = s6 | (s4 << 8) | (s2 << 16) | (sbc << 24);
     }
-    if ((lane & 1) == 0 && c < nchunks && c - (lane & 7) + 7 >= nchunks) scales[blk] = (uint8_t)sbc;
+    // Ragged end of the row layout (with PANEL a row's 8 lanes are all in or out).
+    if (!PANEL && (lane & 1) == 0 && ok && c - (lane & 7) + 7 >= nchunks) scales[blk] = (uint8_t)sbc;
   }
 }
 
@@ -536,7 +594,25 @@ hipError_t quant_mx(int fmt, int64_t rows, int64_t cols, const void* x, void* co
   const dim3 grid((unsigned)grid_for(nchunks));
   const u32x4* X = (const u32x4*)x;
   uint8_t* S = (uint8_t*)scales;
-  if (panel) {
+  if (panel && fmt != kMXFP4) {
+    // MXFP8 / E5M2 in the K-panel layout: workgroups of 128 rows x one
+    // 64-element panel (MXFP6 below).
+    const int64_t cpr = cols / 8;
+    if (fmt == kMXFP8) {
+      const dim3 pgrid((unsigned)((rows + PanelGeo<kMXFP8>::kRpw - 1) / PanelGeo<kMXFP8>::kRpw), (unsigned)(cols / 64));
+      if (rot)
+        MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP8, false, true, true>, pgrid, kThreads, 0, s, X, codes, S, rows, cpr));
+      else
+        MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP8, false, false, true>, pgrid, kThreads, 0, s, X, codes, S, rows, cpr));
+      return hipSuccess;
+    }
+    if (fmt == kMXFP8E5M2) {
+      const dim3 pgrid((unsigned)((rows + PanelGeo<kMXFP8E5M2>::kRpw - 1) / PanelGeo<kMXFP8E5M2>::kRpw), (unsigned)(cols / 64));
+      MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP8E5M2, false, false, true>, pgrid, kThreads, 0, s, X, codes, S, rows, cpr));
+      return hipSuccess;
+    }
+  }
+  if (panel && fmt == kMXFP4) {
     // MXFP4 in the K-panel layout: workgroups of 32 rows x one 256-element panel.
     const dim3 pgrid((unsigned)((rows + 31) / 32), (unsigned)(cols / 256));
     const int64_t cpr = cols / 8;
@@ -566,10 +642,15 @@ hipError_t quant_mx(int fmt, int64_t rows, int64_t cols, const void* x, void* co
       MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP8, false, false>, grid, kThreads, 0, s, X, codes, S, nchunks, (int64_t)0));
   } else if (fmt == kMXFP8E5M2) {
     MX_TRY(launch_kernel(&quant_mx_kernel<kMXFP8E5M2, false, false>, grid, kThreads, 0, s, X, codes, S, nchunks, (int64_t)0));
+  } else if (panel) {
+    // MXFP6 in the K-panel layout: workgroups of 128 rows x one 64-element panel.
+    const dim3 pgrid((unsigned)((rows + kThreads / 2 - 1) / (kThreads / 2)), (unsigned)(cols / 64));
+    MX_TRY(launch_kernel(&quant_mxfp6_kernel<true>, pgrid, kThreads, 0, s, X, (uint8_t*)codes, S, rows,
+                         cols / 8));
   } else {
     const int64_t nblocks = rows * cols / 32;
-    MX_TRY(launch_kernel(&quant_mxfp6_kernel, (unsigned)((nblocks + kThreads - 1) / kThreads), kThreads, 0, s,
-                         X, (uint8_t*)codes, S, nblocks));
+    MX_TRY(launch_kernel(&quant_mxfp6_kernel<false>, (unsigned)((nblocks + kThreads - 1) / kThreads), kThreads, 0, s,
+                         X, (uint8_t*)codes, S, nblocks, (int64_t)0));
   }
   return hipSuccess;
 }
@@ -592,15 +673,23 @@ hipError_t quant_mbs(int64_t rows, int64_t cols, const void* x, void* codes, voi
 size_t quant_nvfp4_workspace(int64_t, int64_t) { return kMaxPartials * sizeof(uint32_t); }
 
 hipError_t quant_nvfp4(int64_t rows, int64_t cols, const void* x, void* codes, void* scales,
-                       float* tensor_scale, void* workspace, hipStream_t s) {
+                       float* tensor_scale, void* workspace, hipStream_t s, bool panel) {
   const int64_t nchunks = rows * cols / 8;
   int64_t np = (nchunks + kAmaxThreads * kAmaxLoads - 1) / (kAmaxThreads * kAmaxLoads);
   if (np > kAmaxPartials) np = kAmaxPartials;
   if (np < 1) np = 1;
   uint32_t* partial = (uint32_t*)workspace;
   MX_TRY(launch_kernel(&nvfp4_amax_partial, (unsigned)np, kAmaxThreads, 0, s, (const u32x4*)x, nchunks, partial));
-  MX_TRY(launch_kernel(&quant_nvfp4_kernel, (unsigned)grid_for(nchunks), kThreads, 0, s, 
-      (const u32x4*)x, (uint32_t*)codes, (uint8_t*)scales, partial, (int)np, tensor_scale, nchunks));
+  if (panel) {
+    // Workgroups of 128 rows x one 64-element panel.
+    const dim3 pgrid((unsigned)((rows + 127) / 128), (unsigned)(cols / 64));
+    MX_TRY(launch_kernel(&quant_nvfp4_kernel<true>, pgrid, kThreads, 0, s, (const u32x4*)x,
+                         (uint32_t*)codes, (uint8_t*)scales, partial, (int)np, tensor_scale, rows, cols / 8));
+  } else {
+    MX_TRY(launch_kernel(&quant_nvfp4_kernel<false>, (unsigned)grid_for(nchunks), kThreads, 0, s,
+                         (const u32x4*)x, (uint32_t*)codes, (uint8_t*)scales, partial, (int)np,
+                         tensor_scale, nchunks, (int64_t)0));
+  }
   return hipSuccess;
 }
 

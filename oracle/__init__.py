@@ -172,14 +172,22 @@ def mbs_planes(scales, rows, cols, block=32):
     return s[:n].reshape(rows, cols // block), s[n:].reshape(rows, cols // 128)
 
 
-def pack_kpanel(codes, scales, rows, cols):
-    """The K-panel layout of an MXFP4 tensor (a byte permutation, no
-    arithmetic): codes [cols/256][rows][128], scales [cols/256][rows][8], from
-    the row layout [rows][cols/2] and [rows][cols/32]."""
-    assert cols % 256 == 0
-    p = cols // 256
-    c = np.asarray(codes, np.uint8).reshape(rows, p, 128).transpose(1, 0, 2).reshape(-1)
-    s = np.asarray(scales, np.uint8).reshape(rows, p, 8).transpose(1, 0, 2).reshape(-1)
+# K-panel geometry per format: panel width W in elements, code bytes and
+# scale bytes of one row in one panel (W * bits / 8 and W / block).
+KPANEL = {FMT_MXFP4: (256, 128, 8), FMT_MXFP8: (64, 64, 2), FMT_MXFP8_E5M2: (64, 64, 2),
+          FMT_MXFP6_E3M2: (64, 48, 2), FMT_NVFP4: (64, 32, 4)}
+
+
+def pack_kpanel(codes, scales, rows, cols, fmt=FMT_MXFP4):
+    """The K-panel layout of a quantized tensor (a byte permutation, no
+    arithmetic): codes [cols/W][rows][wb], scales [cols/W][rows][sb], from
+    the row layout [rows][cols * bits / 8] and [rows][cols / block], with W,
+    wb and sb from KPANEL (MXFP4: 256, 128, 8)."""
+    W, wb, sb = KPANEL[fmt]
+    assert cols % W == 0
+    p = cols // W
+    c = np.asarray(codes, np.uint8).reshape(rows, p, wb).transpose(1, 0, 2).reshape(-1)
+    s = np.asarray(scales, np.uint8).reshape(rows, p, sb).transpose(1, 0, 2).reshape(-1)
     return c.copy(), s.copy()
 
 

@@ -91,13 +91,39 @@ def qx(fmt=mx.MX_FMT_MXFP4, block=32, rnd=0, rule=0, rot=0, rows=4, cols=64, x=P
     (dict(fmt=mx.MX_FMT_MXFP4_MBS, cols=128), mx.MX_ERR_UNSUPPORTED),  # MBS is its own format
     (dict(fmt=mx.MX_FMT_MXFP4_MBS16, block=16, cols=128), mx.MX_ERR_UNSUPPORTED),
     (dict(layout=5), mx.MX_ERR_UNSUPPORTED),
-    (dict(layout=mx.MX_LAYOUT_KPANEL, fmt=mx.MX_FMT_MXFP8, cols=256), mx.MX_ERR_UNSUPPORTED),
+    (dict(layout=mx.MX_LAYOUT_KPANEL, fmt=mx.MX_FMT_MXFP8_E5M2, cols=256), mx.MX_ERR_UNSUPPORTED),
+    (dict(layout=mx.MX_LAYOUT_KPANEL, fmt=mx.MX_FMT_MXFP8, cols=96), mx.MX_ERR_INVALID_ARG),  # cols % 64
     (dict(layout=mx.MX_LAYOUT_KPANEL, cols=128), mx.MX_ERR_INVALID_ARG),          # cols % 256
     (dict(layout=mx.MX_LAYOUT_KPANEL, cols=256 * 65536), mx.MX_ERR_INVALID_ARG),  # > 65535 panels
     (dict(layout=mx.MX_LAYOUT_KPANEL, rows=1 << 23, cols=512), mx.MX_ERR_INVALID_ARG),  # 2^31 bytes
 ])
 def test_quantize_ex_rejects(kw, status):
     assert qx(**kw) == status
+
+
+def ql(fmt=mx.MX_FMT_MXFP8, block=32, rnd=0, rows=4, cols=256, x=P, codes=P, scales=P, ts=None,
+       ws=None, wsb=0, layout=mx.MX_LAYOUT_KPANEL):
+    return mx.mx_quantize_layout(fmt, block, rnd, rows, cols, x, codes, scales, ts, ws, wsb, None,
+                                 layout)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=5), mx.MX_ERR_UNSUPPORTED),
+    (dict(fmt=mx.MX_FMT_MXFP4_MBS, cols=256), mx.MX_ERR_UNSUPPORTED),             # no K panels
+    (dict(fmt=mx.MX_FMT_MXFP4_MBS16, block=16, cols=256), mx.MX_ERR_UNSUPPORTED),
+    (dict(fmt=mx.MX_FMT_MXFP8, block=16), mx.MX_ERR_UNSUPPORTED),
+    (dict(cols=96), mx.MX_ERR_INVALID_ARG),                                         # cols % 64
+    (dict(fmt=mx.MX_FMT_MXFP4, cols=192), mx.MX_ERR_INVALID_ARG),                   # cols % 256
+    (dict(fmt=mx.MX_FMT_MXFP6_E3M2, cols=64 * 65536), mx.MX_ERR_INVALID_ARG),       # > 65535 panels
+    (dict(rows=1 << 24, cols=128), mx.MX_ERR_INVALID_ARG),                          # 2^31 code bytes
+    (dict(fmt=mx.MX_FMT_NVFP4, block=16), mx.MX_ERR_INVALID_ARG),                   # no tensor scale
+    (dict(fmt=mx.MX_FMT_NVFP4, block=16, ts=P2), mx.MX_ERR_INVALID_ARG),            # no workspace
+    (dict(ts=P2), mx.MX_ERR_INVALID_ARG),                                           # MX takes none
+    (dict(x=None), mx.MX_ERR_INVALID_ARG),
+    (dict(scales=MIS), mx.MX_ERR_INVALID_ARG),
+])
+def test_quantize_layout_rejects(kw, status):
+    assert ql(**kw) == status
 
 
 def test_dequantize_rejects():
@@ -166,7 +192,9 @@ def gx(layout=mx.MX_LAYOUT_KPANEL, fa=1, fb=1, block=32, rnd=0, M=64, N=64, K=25
 
 @pytest.mark.parametrize("kw,status", [
     (dict(layout=7), mx.MX_ERR_UNSUPPORTED),                    # unknown layout
-    (dict(fa=2, fb=2), mx.MX_ERR_UNSUPPORTED),                  # K-panel B is MXFP4 only
+    (dict(fa=2, fb=2), mx.MX_ERR_UNSUPPORTED),                  # MXFP8: both K-panel or neither
+    (dict(fa=3, fb=3, block=16, ta=P2, tb=P2), mx.MX_ERR_UNSUPPORTED),  # NVFP4 likewise
+    (dict(fa=2, fb=2, a_layout=mx.MX_LAYOUT_KPANEL, K=96), mx.MX_ERR_INVALID_ARG),  # K % 64
     (dict(fa=0, fb=1, sa=None, M=16), mx.MX_ERR_UNSUPPORTED),   # not for W4A16
     (dict(fa=6, fb=6), mx.MX_ERR_UNSUPPORTED),                  # not for MBS
     (dict(K=128 + 32), mx.MX_ERR_INVALID_ARG),                  # K % 256
@@ -190,9 +218,10 @@ def pk(fmt=mx.MX_FMT_MXFP4, block=32, rows=4, cols=256, codes=P, scales=ctypes.c
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(fmt=mx.MX_FMT_MXFP8), mx.MX_ERR_UNSUPPORTED),
-    (dict(fmt=mx.MX_FMT_NVFP4, block=16), mx.MX_ERR_UNSUPPORTED),
+    (dict(fmt=mx.MX_FMT_MXFP4_MBS), mx.MX_ERR_UNSUPPORTED),     # no K panels
+    (dict(fmt=mx.MX_FMT_NVFP4, block=32), mx.MX_ERR_UNSUPPORTED),
     (dict(block=16), mx.MX_ERR_UNSUPPORTED),
+    (dict(fmt=mx.MX_FMT_MXFP8, cols=96), mx.MX_ERR_INVALID_ARG),   # cols % 64
     (dict(rows=0), mx.MX_ERR_INVALID_ARG),
     (dict(cols=128), mx.MX_ERR_INVALID_ARG),                    # cols % 256
     (dict(rows=1 << 23, cols=1 << 9), mx.MX_ERR_INVALID_ARG),    # rows * cols / 2 >= 2^31

@@ -123,19 +123,26 @@ def test_gemm_rejects_bad_arguments(orc):
         orc.dequantize(orc.FMT_MXFP4, a, s, 1.0, 8, 32)
 
 
-def test_pack_kpanel_brute_force(orc):
-    """The K-panel layout by its definition, byte by byte: code byte
-    (p * rows + r) * 128 + j is byte 128 p + j of row r, scale byte
-    (p * rows + r) * 8 + j is the scale of block 8 p + j of row r."""
-    rows, cols = 5, 768
+@pytest.mark.parametrize("fmt,bits,W", [("FMT_MXFP4", 4, 256), ("FMT_MXFP8", 8, 64),
+                                         ("FMT_MXFP8_E5M2", 8, 64), ("FMT_MXFP6_E3M2", 6, 64),
+                                         ("FMT_NVFP4", 4, 64)])
+def test_pack_kpanel_brute_force(orc, fmt, bits, W):
+    """The K-panel layout by its definition, byte by byte, panels of W
+    elements: code byte (p * rows + r) * wb + j is byte wb p + j of row r
+    (wb = W * bits / 8), scale byte (p * rows + r) * sb + j is the scale of
+    block sb p + j of row r (sb = W / block)."""
+    f = getattr(orc, fmt)
+    blk = orc.BLOCK[f]
+    rows, cols = 5, 3 * W
+    wb, sb = W * bits // 8, W // blk
     g = np.random.Generator(np.random.PCG64(71))
-    codes = g.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
-    scales = g.integers(0, 256, (rows, cols // 32), dtype=np.uint8)
-    pc, ps = orc.pack_kpanel(codes, scales, rows, cols)
+    codes = g.integers(0, 256, (rows, cols * bits // 8), dtype=np.uint8)
+    scales = g.integers(0, 256, (rows, cols // blk), dtype=np.uint8)
+    pc, ps = orc.pack_kpanel(codes, scales, rows, cols, f)
     assert pc.size == codes.size and ps.size == scales.size
-    for p in range(cols // 256):
+    for p in range(cols // W):
         for r in range(rows):
-            for j in range(128):
-                assert pc[(p * rows + r) * 128 + j] == codes[r, 128 * p + j]
-            for j in range(8):
-                assert ps[(p * rows + r) * 8 + j] == scales[r, 8 * p + j]
+            for j in range(wb):
+                assert pc[(p * rows + r) * wb + j] == codes[r, wb * p + j]
+            for j in range(sb):
+                assert ps[(p * rows + r) * sb + j] == scales[r, sb * p + j]
