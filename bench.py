@@ -104,6 +104,9 @@ def parse():
     p.add_argument("--mfma-ceiling", action="store_true",
                    help="only measure what matrix instructions alone sustain on this device "
                         "(FP4 scaled, bf16, fp16; include/mx_calib.h)")
+    p.add_argument("--hbm-ceiling", action="store_true",
+                   help="only measure what plain 16-byte streams of loads and stores sustain "
+                        "from HBM (read, write, copy, 4:1 read:write; include/mx_calib.h)")
     return p.parse_args()
 
 
@@ -154,6 +157,45 @@ def mfma_ceiling():
                                 "(include/mx_calib.h)"}))
 
 
+def hbm_ceiling():
+    """What plain streams of 16-byte loads and stores sustain from HBM
+    (libmx_calib.so): 1 GiB per launch, four times the last-level cache, 20
+    launches per configuration (the median of the last 10). Configurations:
+    one pass over the data with 1 to 8 chunks per thread (each workgroup a
+    contiguous run, as the quantizers are laid out), or a grid-stride loop
+    over 1 to 8 workgroups per CU; plain or non-temporal accesses. The best
+    configuration per kind is the ceiling."""
+    import ctypes
+    import torch
+    torch.cuda.init()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    L = ctypes.CDLL(os.path.join(ROOT, "microscaling_precision_quantization_amd", "libmx_calib.so"))
+    L.mx_calib_stream.restype = ctypes.c_int
+    L.mx_calib_stream.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)]
+    nbytes = 1 << 30
+    res = {}
+    for kind, name in ((0, "read"), (1, "write"), (2, "copy"), (3, "read4_write1")):
+        runs = {}
+        for nt in (0, 1):
+            for per_cu in (0, 1, 2, 4, 8):
+                for unroll in (1, 2, 4, 8):
+                    ms, moved = ctypes.c_float(), ctypes.c_double()
+                    rc = L.mx_calib_stream(kind, nbytes, cus * per_cu, unroll, nt, 20, ctypes.byref(ms),
+                                           ctypes.byref(moved))
+                    if rc != 0:
+                        raise RuntimeError(f"mx_calib_stream({kind}) failed: {rc}")
+                    grid = "one_pass" if per_cu == 0 else f"{per_cu}_per_cu"
+                    runs[f"{grid}_x{unroll}{'_nt' if nt else ''}"] = {
+                        "GB/s": round(moved.value / (ms.value * 1e-3) / 1e9, 1), "ms_per_launch": round(ms.value, 4)}
+        best = max(runs, key=lambda k: runs[k]["GB/s"])
+        res[name] = {"best_GB/s": runs[best]["GB/s"], "frac_of_peak": round(runs[best]["GB/s"] / PEAK_HBM_GBPS, 4),
+                     "best": best, "runs": runs}
+    print(json.dumps({"hbm_ceiling": res, "cus": cus, "bytes_per_launch": nbytes, "peak_GB/s": PEAK_HBM_GBPS,
+                      "method": "median of the last 10 of 20 back-to-back launches of 16-byte stream "
+                                "kernels (include/mx_calib.h)"}))
+
+
 def graph_ms_per_step(torch, fn, nsteps, stream, ramp_s):
     """fn(i) for i < nsteps captured once as a HIP graph; after ramp_s of
     untimed replays, five timed replays. Returns (ms per step of the first
@@ -194,6 +236,9 @@ def main():
         return
     if args.mfma_ceiling:
         mfma_ceiling()
+        return
+    if args.hbm_ceiling:
+        hbm_ceiling()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the kernels "

@@ -287,7 +287,7 @@ def test_calib_library_exports_and_rejects():
     declares, and refuses bad arguments before any HIP call."""
     src = open(os.path.join(ROOT, "include", "mx_calib.h")).read()
     declared = set(re.findall(r"^\s*int\s+(mx_\w+)\s*\(", src, re.M))
-    assert declared == {"mx_calib_mfma"}
+    assert declared == {"mx_calib_mfma", "mx_calib_stream"}
     L = ctypes.CDLL(os.path.join(ROOT, "microscaling_precision_quantization_amd", "libmx_calib.so"))
     f = L.mx_calib_mfma
     f.restype = ctypes.c_int
@@ -297,3 +297,15 @@ def test_calib_library_exports_and_rejects():
     assert f(3, 1, 1, 1, ctypes.byref(ms), ctypes.byref(fl)) == -1
     assert f(0, 0, 1, 1, ctypes.byref(ms), ctypes.byref(fl)) == -1
     assert f(0, 1, 1, 1, None, ctypes.byref(fl)) == -1
+    g = L.mx_calib_stream
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)]
+    ok = (0, 1 << 20, 64, 4, 0, 2)
+    for bad in ((4, 1 << 20, 64, 4, 0, 2), (-1, 1 << 20, 64, 4, 0, 2), (0, 4000, 64, 4, 0, 2),
+                (0, (1 << 20) + 16, 64, 4, 0, 2), (0, (1 << 36) + 64, 64, 4, 0, 2),
+                (0, 1 << 20, -1, 4, 0, 2), (0, 1 << 20, 65536, 4, 0, 2), (0, 1 << 20, 64, 3, 0, 2),
+                (0, 1 << 20, 64, 16, 0, 2), (0, 1 << 20, 64, 4, 2, 2), (0, 1 << 20, 64, 4, 0, 0)):
+        assert g(*bad, ctypes.byref(ms), ctypes.byref(fl)) == -1, bad
+    assert g(*ok, None, ctypes.byref(fl)) == -1
+    assert g(*ok, ctypes.byref(ms), None) == -1

@@ -54,3 +54,25 @@ def test_mfma_ceiling_calibration_runs():
         assert f(kind, 64, 200, 4, ctypes.byref(ms), ctypes.byref(fl)) == 0
         assert fl.value == 64 * (threads // 64) * 200 * per_wave
         assert ms.value > 0 and fl.value / (ms.value * 1e-3) < peak
+
+
+def test_hbm_stream_calibration_runs():
+    """mx_calib_stream on the GPU: each kind launches and reports exactly the
+    bytes it moves per launch and a plausible rate."""
+    require_gpu()
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    L = ctypes.CDLL(os.path.join(root, "microscaling_precision_quantization_amd", "libmx_calib.so"))
+    g = L.mx_calib_stream
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)]
+    nbytes = (64 << 20) + 64     # not a whole number of 256-thread blocks
+    for kind, moved in ((0, nbytes), (1, nbytes), (2, 2 * nbytes), (3, nbytes + nbytes // 4)):
+        # one pass and grid-stride grids (one workgroup, ragged, large);
+        # every unroll depth; plain and non-temporal accesses
+        for wgs, unroll, nt in ((0, 1, 0), (0, 8, 1), (1, 8, 0), (333, 1, 1), (333, 2, 0), (2048, 4, 1)):
+            ms, mv = ctypes.c_float(), ctypes.c_double()
+            assert g(kind, nbytes, wgs, unroll, nt, 3, ctypes.byref(ms), ctypes.byref(mv)) == 0
+            assert mv.value == moved
+            assert ms.value > 0 and mv.value / (ms.value * 1e-3) < 50e12
