@@ -56,8 +56,8 @@ def lib():
         L.mxo_storage_bytes.argtypes = [ctypes.c_int, i64, i64]
         L.mxo_quantize.restype = ctypes.c_int
         L.mxo_quantize.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, P, P, P, P]
-        L.mxo_quantize_nvfp4_exact_quotient.restype = ctypes.c_int
-        L.mxo_quantize_nvfp4_exact_quotient.argtypes = [i64, i64, P, P, P, P]
+        L.mxo_quantize_nvfp4_reciprocal.restype = ctypes.c_int
+        L.mxo_quantize_nvfp4_reciprocal.argtypes = [i64, i64, P, P, P, P]
         L.mxo_quantize_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, P, P, P]
         L.mxo_wht32.argtypes = [i64, i64, P, P]
         L.mxo_dequantize.restype = ctypes.c_int
@@ -226,14 +226,14 @@ def wht32(x_bits):
     return y
 
 
-def quantize_nvfp4_exact_quotient(x_bits):
+def quantize_nvfp4_reciprocal(x_bits):
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
     rows, cols = x.shape
     codes = np.zeros((rows, cols // 2), np.uint8)
     scales = np.zeros((rows, cols // 16), np.uint8)
     ts = np.zeros(1, np.float32)
-    _check(lib().mxo_quantize_nvfp4_exact_quotient(rows, cols, _ptr(x), _ptr(codes),
-                                                   _ptr(scales), _ptr(ts)), "quantize")
+    _check(lib().mxo_quantize_nvfp4_reciprocal(rows, cols, _ptr(x), _ptr(codes),
+                                               _ptr(scales), _ptr(ts)), "quantize")
     return codes, scales, float(ts[0])
 
 

@@ -388,18 +388,23 @@ static void quantize_mbs(int64_t rows, int64_t cols, int B, const uint16_t* x, u
   }
 }
 
-/* NVFP4, fp32 throughout (one rounding per operation):
+/* NVFP4. The scales in fp32, one rounding per operation; the codes from the
+ * exact quotient:
  *  1. T = max |x| over the tensor.
  *  2. s_t = T / 2688 (2688 = 6 * 448 maps T onto the largest E2M1 value times
  *     the largest E4M3 scale); T = 0 gives s_t = 1.
  *  3. per 16-block: s_b = E4M3 nearest-even, saturating, of amax_b / (6 s_t).
- *  4. D = s_b * s_t; D = 0 gives sign-only zero codes.
- *  5. code = E2M1 nearest-even, saturating, of x * (1 / D); x = +-0 gives +-0.
+ *  4. s_b = 0 gives sign-only zero codes for the block.
+ *  5. code = E2M1 nearest-even, saturating, of the exact quotient
+ *     x / (s_b s_t) (the product is exact in double, and so is each midpoint
+ *     times it); x = +-0 gives +-0.
  * A non-finite T gives s_t = NaN, NaN block scales and zero codes.
- * exact_quotient != 0 replaces step 5 by the exact quotient x / (s_b s_t). */
+ * reciprocal != 0 replaces steps 4-5 by the fp32 sequence D = fl(s_b s_t),
+ * D = 0 -> sign-only zeros, code = E2M1 of fl(x * fl(1 / D)) (information:
+ * how often that cheaper form decides a code differently). */
 static void quantize_nvfp4(int64_t rows, int64_t cols, const uint16_t* x,
                            uint8_t* codes, uint8_t* scales, float* tensor_scale,
-                           int exact_quotient) {
+                           int reciprocal) {
   const int B = 16;
   const int64_t n = rows * cols;
   float T = 0.0f;
@@ -428,15 +433,16 @@ static void quantize_nvfp4(int64_t rows, int64_t cols, const uint16_t* x,
     float r = bamax / d6;
     uint8_t sb = mxo_encode_e4m3((double)r);
     scales[b] = sb;
-    float D = (float)mxo_e4m3_value(sb) * s_t;
-    float R = 1.0f / D;
+    const double sbv = mxo_e4m3_value(sb);
+    const float D = (float)sbv * s_t;
+    const float R = 1.0f / D;
     for (int i = 0; i < B; i++) {
       float xi = (float)mxo_bf16_value(xb[i]);
       uint8_t c;
-      if (D == 0.0f || xi == 0.0f) {
+      if (xi == 0.0f || (reciprocal ? D == 0.0f : sbv == 0.0)) {
         c = signbit(xi) ? 0x8 : 0x0;
-      } else if (exact_quotient) {
-        c = e2m1_nearest_scaled((double)xi, (double)mxo_e4m3_value(sb) * (double)s_t);
+      } else if (!reciprocal) {
+        c = e2m1_nearest_scaled((double)xi, sbv * (double)s_t);
       } else {
         float q = xi * R;
         c = mxo_encode_e2m1((double)q);
@@ -464,9 +470,9 @@ int mxo_quantize(int fmt, int block, int64_t rows, int64_t cols,
   return MXO_OK;
 }
 
-int mxo_quantize_nvfp4_exact_quotient(int64_t rows, int64_t cols,
-                                      const uint16_t* x, uint8_t* codes,
-                                      uint8_t* scales, float* tensor_scale) {
+int mxo_quantize_nvfp4_reciprocal(int64_t rows, int64_t cols,
+                                  const uint16_t* x, uint8_t* codes,
+                                  uint8_t* scales, float* tensor_scale) {
   if (rows <= 0 || cols <= 0 || cols % 16 != 0 || !x || !codes || !scales)
     return MXO_ERR_ARG;
   quantize_nvfp4(rows, cols, x, codes, scales, tensor_scale, 1);

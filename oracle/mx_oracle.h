@@ -6,8 +6,9 @@
  * CPU-baseline leg of the benchmark may load or call this library. The GPU
  * library shares no code, header, table or constant with it, and never calls it.
  *
- * Every routine works on host memory, computes in double unless the method
- * fixes fp32 (the NVFP4 sequence), and is written for clarity, not speed.
+ * Every routine works on host memory, computes in double unless a reading
+ * fixes fp32 (the NVFP4 tensor and block scales), and is written for
+ * clarity, not speed.
  *
  * Sources (web pages on microscaling formats):
  *  - "Microscaling MXFP4/NVFP4 on Blackwell for reasoning LLMs"
@@ -101,6 +102,11 @@ int64_t mxo_storage_bytes(int fmt, int64_t rows, int64_t cols);
  * low nibble), [rows][cols] (FP8) or [rows][3 cols/4] (FP6: element i of a row
  * in bits 6i .. 6i+5 of the row's bytes, little-endian); scales: [rows][cols/block] bytes;
  * tensor_scale: NVFP4 only (written), may be NULL otherwise.
+ * NVFP4 (block 16): s_t = fl(T / 2688) for the tensor amax T (T = 0 -> 1);
+ * s_b = E4M3 nearest-even, saturating, of fl(amax_b / fl(6 s_t)); each code
+ * the nearest-even E2M1 value of the exact quotient x / (s_b s_t),
+ * saturating, sign copied (s_b = 0: sign-only zeros); a non-finite T gives
+ * s_t = NaN, every scale 0x7F and every code 0.
  * MXFP4-MBS16 (block 16) and MXFP4-MBS (block 32), cols a multiple of 128:
  * codes as MXFP4; scales holds two planes, the E8M0 bytes [rows][cols/block]
  * followed by the macro mantissas [rows][cols/128]. Per macro block of 128:
@@ -132,11 +138,12 @@ int mxo_quantize_ex(int fmt, int block, int rule, int rot, int64_t rows, int64_t
  * (x_i + x_{i+h}, x_i - x_{i+h}). */
 int mxo_wht32(int64_t rows, int64_t cols, const uint16_t* x, uint16_t* y);
 
-/* NVFP4 only, information: codes from the exact quotient x / (s_b * s_t)
- * instead of the fp32 reciprocal sequence; scales are as mxo_quantize's. */
-int mxo_quantize_nvfp4_exact_quotient(int64_t rows, int64_t cols,
-                                      const uint16_t* x, uint8_t* codes,
-                                      uint8_t* scales, float* tensor_scale);
+/* NVFP4 only, information: codes from the fp32 sequence D = fl(s_b * s_t),
+ * code = E2M1(fl(x * fl(1 / D))) instead of the exact quotient
+ * x / (s_b * s_t); scales are as mxo_quantize's. */
+int mxo_quantize_nvfp4_reciprocal(int64_t rows, int64_t cols,
+                                  const uint16_t* x, uint8_t* codes,
+                                  uint8_t* scales, float* tensor_scale);
 
 /* y: float [rows][cols] (MXO_OUT_F32) or bf16 bits (MXO_OUT_BF16). */
 int mxo_dequantize(int fmt, int block, int64_t rows, int64_t cols,

@@ -248,10 +248,66 @@ def test_nvfp4_zero_tensor_and_signed_zero(orc):
     assert c[1, 3] == 8 and np.count_nonzero(c) == 1
 
 
-def test_nvfp4_exact_quotient_rarely_differs(orc):
+def test_nvfp4_reciprocal_form_rarely_differs(orc):
+    """The cheaper fp32 form fl(x * fl(1 / fl(s_b s_t))) decides a handful of
+    codes differently from the exact quotient; the scales are the same."""
     x = synth.student_t((128, 512), 4.0, 13)
     c1, s1, t1 = orc.quantize(orc.FMT_NVFP4, x)
-    c2, s2, t2 = orc.quantize_nvfp4_exact_quotient(x)
+    c2, s2, t2 = orc.quantize_nvfp4_reciprocal(x)
     assert t1 == t2 and np.array_equal(s1, s2)
     diff = np.count_nonzero(_unpack_fp4(c1) != _unpack_fp4(c2))
     assert diff <= 0.001 * x.size
+
+
+def _nvfp4_pin_tensors():
+    """Student-t rows, an outlier row, a block that s_b rounds to zero, and
+    whole tensors at the bottom and top of the bf16 range (where fl(s_b s_t)
+    underflows or 1 / fl(s_b s_t) overflows in fp32)."""
+    base = synth.student_t((6, 128), 4.0, 31)
+    base[1, 5] = synth.bf16_bits(np.array([300.0]))[0]
+    base[2, 16:32] = synth.bf16_bits(np.full(16, 1e-6))
+    base[3, 32:48] = 0x8000
+    f = synth.bf16_to_f32(synth.student_t((4, 128), 4.0, 32)).astype(np.float64)
+    out = [base]
+    for scale in (2.0**-100, 2.0**-126, 2.0**-131, 1e37):
+        out.append(synth.bf16_bits(f * scale))
+    return out
+
+
+def test_nvfp4_codes_nearest_to_exact_quotient(orc):
+    """Each NVFP4 code is the E2M1 value nearest the exact rational
+    x / (s_b s_t), ties to the even code, saturating at 6, sign copied; a
+    zero block scale gives sign-only zeros. Brute force with Fractions over
+    every magnitude, for the oracle's own s_b and s_t."""
+    from fractions import Fraction
+    for x in _nvfp4_pin_tensors():
+        codes, scales, ts = orc.quantize(orc.FMT_NVFP4, x)
+        c = _unpack_fp4(codes)
+        xf = synth.bf16_to_f32(x).astype(np.float64)
+        st = Fraction(float(ts))
+        for r in range(x.shape[0]):
+            for j in range(x.shape[1]):
+                v = float(xf[r, j])
+                sign = 8 if math.copysign(1.0, v) < 0 else 0
+                sb = Fraction(orc.e4m3_value(int(scales[r, j // 16])))
+                if v == 0.0 or sb == 0:
+                    assert c[r, j] == sign, (r, j)
+                    continue
+                q = abs(Fraction(v)) / (sb * st)
+                best = min(range(8), key=lambda k: (abs(q - Fraction(FP4_VALUES[k])), k & 1))
+                assert c[r, j] == sign | best, (r, j, v, float(q), c[r, j], best)
+
+
+def test_nvfp4_block_scales_match_torch_e4m3(orc):
+    """s_b is torch's float8_e4m3fn rounding (nearest-even) of the fp32 value
+    amax_b / (6 s_t), clamped at 448 first; s_t = T / 2688 in fp32."""
+    import torch
+    for x in _nvfp4_pin_tensors():
+        codes, scales, ts = orc.quantize(orc.FMT_NVFP4, x)
+        xf = synth.bf16_to_f32(x)
+        T = np.float32(np.abs(xf).max())
+        assert np.float32(ts) == (np.float32(1.0) if T == 0 else T / np.float32(2688.0))
+        bamax = np.abs(xf).reshape(x.shape[0], -1, 16).max(axis=2).astype(np.float32)
+        r = np.minimum(bamax / (np.float32(6.0) * np.float32(ts)), np.float32(448.0))
+        want = torch.from_numpy(r).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(scales, want)
