@@ -102,12 +102,13 @@ typedef enum {
  *     and codes = nearest-even E2M1 of x / (f 2^(E-127)) with saturation, the
  *     sign copied; a 32-block holding Inf/NaN gets 255 and zero codes. The
  *     element's value is e * 2^(E-127) * f.
- *   NVFP4 (block 16), fp32 arithmetic, one rounding per step:
+ *   NVFP4 (block 16), the scales in fp32 with one rounding per step:
  *     T = max|x| over the tensor; s_t = T / 2688 (1 if T = 0);
  *     s_b = E4M3(amax_b / (6 s_t)) nearest-even, saturating at 448;
- *     D = s_b * s_t; code = E2M1(x * (1/D)) nearest-even, saturating; a zero
- *     x or D = 0 gives a signed zero code. Non-finite T: s_t = NaN, every
- *     block scale 0x7F (E4M3 NaN), every code 0.
+ *     code = the E2M1 value nearest the exact quotient x / (s_b * s_t), ties
+ *     to the even code, saturating; a zero x or s_b = 0 gives a signed zero
+ *     code. Non-finite T: s_t = NaN, every block scale 0x7F (E4M3 NaN),
+ *     every code 0.
  * x: bf16 [rows][cols]; codes, scales: outputs as in the layout above.
  * tensor_scale: NVFP4 only, one device fp32 written with s_t; NULL otherwise.
  * workspace: NVFP4 only, device scratch of at least

@@ -479,8 +479,13 @@ __global__ __launch_bounds__(kAmaxThreads) void nvfp4_amax_partial(const u32x4* 
 // The tensor scale from the amax partials, in every workgroup of the encode
 // kernel (the maximum does not depend on the order): s_t = T / 2688
 // (T = 0 -> 1, non-finite T -> NaN). Workgroup 0 writes it out.
+// fdir (see nv_codes): 1 - 2^-19 where s_t > T / 2688, 1 + 2^-19 where
+// s_t < T / 2688 (the sign of the exact fma s_t 2688 - T), both for a normal
+// s_t; 1 for T = 0; 0 (the bracketing path) for s_t = T / 2688 exactly or a
+// subnormal s_t.
 __device__ __forceinline__ float nvfp4_tensor_scale(const uint32_t* __restrict__ partial,
-                                                    int npartial, float* __restrict__ tensor_scale) {
+                                                    int npartial, float* __restrict__ tensor_scale,
+                                                    float& fdir) {
   uint32_t m = 0;
   for (int i = threadIdx.x; i < npartial; i += kThreads) m = umax(m, partial[i]);
   for (int off = 32; off > 0; off >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, off));
@@ -490,11 +495,17 @@ __device__ __forceinline__ float nvfp4_tensor_scale(const uint32_t* __restrict__
   uint32_t r = 0;
   for (int w = 0; w < kThreads / 64; w++) r = umax(r, wmax[w]);
   float st;
+  fdir = 0.0f;
   if (r >= 0x7F80u) {
     st = __builtin_nanf("");
   } else {
     const float T = __builtin_bit_cast(float, r << 16);
     st = (T == 0.0f) ? 1.0f : T / 2688.0f;  // 2688 = 6 * 448
+    const float e = __builtin_fmaf(st, 2688.0f, -T);
+    if (T == 0.0f)
+      fdir = 1.0f;
+    else if (st >= 0x1p-126f && e != 0.0f)
+      fdir = e > 0.0f ? 1.0f - 0x1p-19f : 1.0f + 0x1p-19f;
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) tensor_scale[0] = st;
   return st;
@@ -503,8 +514,87 @@ __device__ __forceinline__ float nvfp4_tensor_scale(const uint32_t* __restrict__
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
 
-// x * (1/D), with x = +-0 kept as is (no 0 * Inf) and D = 0 giving +-0.
-__device__ __forceinline__ float nv_scaled(float xv, float rz) { return xv == 0.0f ? xv : xv * rz; }
+// NVFP4 codes are the nearest-even E2M1 values of the exact quotient
+// Q = x / (s_b s_t). x and s_t are both taken times xs = 2^64 when
+// s_t < 2^-60 (exact), so that D = s_b s_t xs and R = rcp(fl(D)) (v_rcp_f32,
+// within 1 ulp) are normal fp32 numbers; fl(x xs fl(R f)) is then within
+// 5 2^-24 relative of Q f.
+//
+// Fast path (nv_codes), for a normal s_t = (T / 2688)(1 + eps) that is not
+// exact: 2688 |x| and m s_b T (m an E2M1 midpoint) are integers below 2^13
+// and 2^17 times powers of two, so Q0 = 2688 |x| / (s_b T) either equals m
+// or lies 2^-17 or more (relative) away from it, and Q = Q0 / (1 + eps)
+// with |eps| <= 2^-24. Where Q0 = m, Q falls below m exactly when eps > 0.
+// So the code of fl(x xs fl(R f)) with f = 1 - 2^-19 (eps > 0) or 1 + 2^-19
+// (eps < 0) is Q's: the 2^-19 pushes the quotients that sit on a midpoint in
+// Q0 to the side eps puts them on, and moves no other across one.
+//
+// Bracketing path (nv_bracket + nv_resolve), for s_t exact or subnormal:
+// x xs R (1 -+ 2^-18), each product rounded, lie on either side of Q.
+// Rounding to E2M1 is monotone, so where the codes of the two agree that is
+// Q's code; the lower one's magnitude is never above the upper one's.
+__device__ __forceinline__ float nv_elem(const u32x4& v, int j) {
+  const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
+  return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+template <int P, bool SCALED>
+__device__ __forceinline__ uint32_t nv_pair(const u32x4& v, float rf, uint32_t c) {
+  const float e0 = SCALED ? nv_elem(v, 2 * P) * 0x1p64f : nv_elem(v, 2 * P);
+  const float e1 = SCALED ? nv_elem(v, 2 * P + 1) * 0x1p64f : nv_elem(v, 2 * P + 1);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, e0 * rf, e1 * rf, 1.0f, P);
+}
+
+template <bool SCALED>
+__device__ __forceinline__ uint32_t nv_codes(const u32x4& v, float rf) {
+  uint32_t c = 0;
+  c = nv_pair<0, SCALED>(v, rf, c);
+  c = nv_pair<1, SCALED>(v, rf, c);
+  c = nv_pair<2, SCALED>(v, rf, c);
+  return nv_pair<3, SCALED>(v, rf, c);
+}
+
+template <int P, bool SCALED>
+__device__ __forceinline__ void nv_bracket_pair(const u32x4& v, float rlo, float rhi, uint32_t& cl,
+                                                uint32_t& ch) {
+  cl = nv_pair<P, SCALED>(v, rlo, cl);
+  ch = nv_pair<P, SCALED>(v, rhi, ch);
+}
+
+template <bool SCALED>
+__device__ __forceinline__ void nv_bracket(const u32x4& v, float rlo, float rhi, uint32_t& cl, uint32_t& ch) {
+  cl = 0;
+  ch = 0;
+  nv_bracket_pair<0, SCALED>(v, rlo, rhi, cl, ch);
+  nv_bracket_pair<1, SCALED>(v, rlo, rhi, cl, ch);
+  nv_bracket_pair<2, SCALED>(v, rlo, rhi, cl, ch);
+  nv_bracket_pair<3, SCALED>(v, rlo, rhi, cl, ch);
+}
+
+// Where the two codes differ, exactly one E2M1 midpoint m lies between them
+// (the window is 2^-17 wide, midpoints are 29% or more apart): the one above
+// the lower code's magnitude k. The sign of fma(m s_b, s_t xs, -|x xs|) then
+// places the quotient below, above or on it (ties to the even code). m s_b is
+// exact; the exact difference is 0 or a multiple of 2^-133 (2^-96 when
+// scaled), so its sign survives the rounding. Branch-free over the 8 codes:
+// where the two agree, either choice gives the same code. 4 m for k = 0..6 is
+// 1, 3, 5, 7, 10, 14, 20.
+__device__ __forceinline__ uint32_t nv_resolve(const u32x4& v, uint32_t cl, uint32_t ch, float xs,
+                                               float sb, float stx) {
+  constexpr uint64_t kMid4 = 0x00140E0A07050301ull;
+  const float sbq = sb * 0.25f;
+  uint32_t out = 0;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const uint32_t a = (cl >> (4 * j)) & 0xFu, b = (ch >> (4 * j)) & 0xFu;
+    const uint32_t k = a & 7u;
+    const float m4 = (float)(uint32_t)((kMid4 >> (8 * k)) & 0xFFu);
+    const float d = __builtin_fmaf(m4 * sbq, stx, -__builtin_fabsf(nv_elem(v, j) * xs));
+    const bool up = d < 0.0f || (d == 0.0f && (k & 1u));
+    out |= (up ? b : a) << (4 * j);
+  }
+  return out;
+}
 
 // PANEL: codes and scales in the K-panel layout with 64-element panels
 // ([cols/64][rows][32] and [cols/64][rows][4]). The grid is then 2-D:
@@ -541,9 +631,12 @@ __global__ __launch_bounds__(kThreads) void quant_nvfp4_kernel(const u32x4* __re
 #pragma unroll
   for (int u = 0; u < kUnroll; u++)
     v[u] = valid(u) ? __builtin_nontemporal_load(x + src_of(u)) : u32x4{0, 0, 0, 0};
-  const float st = nvfp4_tensor_scale(partial, npartial, tensor_scale);
+  float fdir;
+  const float st = nvfp4_tensor_scale(partial, npartial, tensor_scale, fdir);
   const bool bad = __builtin_isnan(st);
   const float d6 = 6.0f * st;
+  const float xs = st < 0x1p-60f ? 0x1p64f : 1.0f;  // see nv_bracket
+  const float stx = st * xs;
 #pragma unroll
   for (int u = 0; u < kUnroll; u++) {
     const int64_t c = dst_of(u);
@@ -557,14 +650,26 @@ __global__ __launch_bounds__(kThreads) void quant_nvfp4_kernel(const u32x4* __re
     const float rs = r < 448.0f ? r : 448.0f;
     uint32_t sbc = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(rs, rs, 0, false) & 0xFFu;
     const float sb = __builtin_amdgcn_cvt_f32_fp8((int)sbc, 0);
-    const float D = sb * st;
-    const float R = 1.0f / D;
-    const float rz = (D == 0.0f) ? 0.0f : R;
-    uint32_t q = 0;
-    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, nv_scaled(bf16_lo(v[u].x), rz), nv_scaled(bf16_hi(v[u].x), rz), 1.0f, 0);
-    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, nv_scaled(bf16_lo(v[u].y), rz), nv_scaled(bf16_hi(v[u].y), rz), 1.0f, 1);
-    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, nv_scaled(bf16_lo(v[u].z), rz), nv_scaled(bf16_hi(v[u].z), rz), 1.0f, 2);
-    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, nv_scaled(bf16_lo(v[u].w), rz), nv_scaled(bf16_hi(v[u].w), rz), 1.0f, 3);
+    // s_b = 0: sign-only zeros (x * 0). Otherwise D is normal (s_b >= 2^-9,
+    // s_t xs >= 2^-85) and so is R.
+    const float D = sb * stx;
+    const float rz = (sb == 0.0f) ? 0.0f : __builtin_amdgcn_rcpf(D);
+    uint32_t q;
+    if (fdir != 0.0f) {
+      const float rf = rz * fdir;
+      if (xs == 1.0f)
+        q = nv_codes<false>(v[u], rf);
+      else
+        q = nv_codes<true>(v[u], rf);
+    } else {
+      const float rlo = rz * (1.0f - 0x1p-18f), rhi = rz * (1.0f + 0x1p-18f);
+      uint32_t qh;
+      if (xs == 1.0f)
+        nv_bracket<false>(v[u], rlo, rhi, q, qh);
+      else
+        nv_bracket<true>(v[u], rlo, rhi, q, qh);
+      if (q != qh) q = nv_resolve(v[u], q, qh, xs, sb, stx);
+    }
     if (bad) {
       q = 0;
       sbc = 0x7F;

@@ -97,6 +97,37 @@ def test_special_tensors_nvfp4():
     assert np.isnan(t) and np.all(s == 0x7F)
 
 
+@pytest.mark.parametrize("scale", [1.0, 2.0**-100, 2.0**-126, 2.0**-131, 1e37])
+def test_nvfp4_exact_quotient_across_magnitudes(scale):
+    """NVFP4 codes are decided on the exact quotient x / (s_b s_t) at every
+    tensor magnitude, also where fl(s_b s_t) would underflow or its fp32
+    reciprocal overflow (tensor amax near the bottom of the bf16 range) and
+    near the top. Student-t data also puts many quotients within 2^-24 of an
+    E2M1 midpoint (s_t = T / 2688 carries a factor 1/21)."""
+    f = synth.bf16_to_f32(synth.student_t((64, 512), 4.0, 33)).astype(np.float64)
+    x = synth.bf16_bits(f * scale)
+    _assert_quant_equal(x, "nvfp4")
+    # At each scale the cheaper fp32 form fl(x * fl(1 / fl(s_b s_t))) would
+    # decide some codes differently.
+    c1, _, _ = orc.quantize(orc.FMT_NVFP4, x)
+    c2, _, _ = orc.quantize_nvfp4_reciprocal(x)
+    assert not np.array_equal(c1, c2)
+
+
+@pytest.mark.parametrize("sig,ex", [(168, 0), (147, -40), (252, 30), (210, -100), (200, 0)])
+def test_nvfp4_exact_tensor_scale(sig, ex):
+    """Tensor amax T = sig/128 * 2^ex. A significand that is a multiple of 21
+    makes s_t = T / 2688 exact in fp32, so quotients can sit exactly on an
+    E2M1 midpoint (ties to the even code); 200 is a control with a rounded
+    s_t."""
+    f = synth.bf16_to_f32(synth.student_t((64, 512), 4.0, 44)).astype(np.float64)
+    x = synth.bf16_bits(f / np.abs(f).max() * (sig / 128.0) * 2.0**ex)
+    T = float(np.abs(synth.bf16_to_f32(x)).max())
+    assert T == sig / 128.0 * 2.0**ex
+    _, _, ts = _assert_quant_equal(x, "nvfp4")
+    assert (float(np.float32(ts)) * 2688 == T) == (sig % 21 == 0)
+
+
 # Full-size quantization of every workload's operands.
 QUANT_CASES = [("c1", "A", "mxfp4"), ("c1", "B", "mxfp4"), ("c2", "A", "mxfp8"),
                ("c2", "B", "mxfp8"), ("c3", "A", "nvfp4"), ("c3", "B", "nvfp4"),
