@@ -458,7 +458,8 @@ def measured_traffic(workload):
     """HBM bytes per dispatch of the dominant kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by the copy calibration),
     or None when there is none for this workload or the kernel source changed
-    since it was taken."""
+    since it was taken: the record's hash covers its source file followed by
+    the headers it lists (shared kernel code such as the epilogue)."""
     import glob
     import hashlib
     import re
@@ -471,10 +472,10 @@ def measured_traffic(workload):
                 continue
             if rec.get("workload") != workload or "traffic_bytes" not in rec:
                 continue
-            src = os.path.join(ROOT, rec["source"])
-            if not os.path.exists(src):
+            paths = [os.path.join(ROOT, f) for f in [rec["source"], *rec.get("headers", [])]]
+            if not all(os.path.exists(f) for f in paths):
                 return None
-            sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+            sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in paths)).hexdigest()[:16]
             return rec["traffic_bytes"] if sha == rec["source_sha256_16"] else None
     return None
 
