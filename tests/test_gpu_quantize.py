@@ -128,6 +128,21 @@ def test_nvfp4_exact_tensor_scale(sig, ex):
     assert (float(np.float32(ts)) * 2688 == T) == (sig % 21 == 0)
 
 
+def test_nvfp4_random_tensor_scales():
+    """96 tensors whose amax has a random bf16 significand (a sixth of them a
+    multiple of 21, so that s_t is exact) and a random binade from 2^-140 to
+    2^120: the codes follow the exact quotient on both of the encoder's paths
+    (rounded normal s_t; exact or subnormal s_t)."""
+    g = np.random.Generator(np.random.PCG64(97))
+    base = synth.bf16_to_f32(synth.student_t((16, 256), 4.0, 98)).astype(np.float64)
+    base = base / np.abs(base).max()
+    for t in range(96):
+        sig = int(g.choice([147, 168, 189, 210, 231, 252])) if t % 6 == 0 else int(g.integers(128, 256))
+        ex = int(g.integers(-140, 121))
+        x = synth.bf16_bits(base * (sig / 128.0) * 2.0**ex)
+        _assert_quant_equal(x, "nvfp4")
+
+
 # Full-size quantization of every workload's operands.
 QUANT_CASES = [("c1", "A", "mxfp4"), ("c1", "B", "mxfp4"), ("c2", "A", "mxfp8"),
                ("c2", "B", "mxfp8"), ("c3", "A", "nvfp4"), ("c3", "B", "nvfp4"),
