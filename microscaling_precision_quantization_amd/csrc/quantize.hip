@@ -455,13 +455,14 @@ __global__ __launch_bounds__(kAmaxThreads) void nvfp4_amax_partial(const u32x4* 
                                                                    int64_t nchunks,
                                                                    uint32_t* __restrict__ partial) {
   // kAmaxLoads loads in flight per thread: chunks c + i G, G the grid's width.
+  // Plain loads, so that the encode kernel finds x in the caches.
   uint32_t m = 0;
   const int64_t G = (int64_t)gridDim.x * kAmaxThreads;
   for (int64_t c = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; c < nchunks; c += kAmaxLoads * G) {
     u32x4 v[kAmaxLoads];
 #pragma unroll
     for (int i = 0; i < kAmaxLoads; i++)
-      v[i] = (c + i * G < nchunks) ? __builtin_nontemporal_load(x + c + i * G) : u32x4{0, 0, 0, 0};
+      v[i] = (c + i * G < nchunks) ? x[c + i * G] : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < kAmaxLoads; i++) m = umax(m, chunk_absmax(v[i]));
   }
@@ -627,10 +628,12 @@ __global__ __launch_bounds__(kThreads) void quant_nvfp4_kernel(const u32x4* __re
     return PANEL ? row_of(u) < nchunks : base + u * kThreads < nchunks;
   };
   // The element loads go out first; the tensor scale is reduced meanwhile.
+  // Plain loads here and in the amax pass (not non-temporal): the second
+  // read of x then comes from the caches, 4% faster over both kernels.
   u32x4 v[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; u++)
-    v[u] = valid(u) ? __builtin_nontemporal_load(x + src_of(u)) : u32x4{0, 0, 0, 0};
+    v[u] = valid(u) ? x[src_of(u)] : u32x4{0, 0, 0, 0};
   float fdir;
   const float st = nvfp4_tensor_scale(partial, npartial, tensor_scale, fdir);
   const bool bad = __builtin_isnan(st);
