@@ -202,7 +202,10 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restr
       q = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(q, as_bf16x2(v[u].z), scale, 2);
       q = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(q, as_bf16x2(v[u].w), scale, 3);
       if (nonfinite) q = 0;
-      if (ok) __builtin_nontemporal_store(q, (uint32_t*)codes + c);
+      // K-panel codes are activations that a GEMM reads next: plain stores
+      // leave them in the caches (the MLP-down step 0.6-0.8 us faster).
+      if (ok && PANEL) ((uint32_t*)codes)[c] = q;
+      if (ok && !PANEL) __builtin_nontemporal_store(q, (uint32_t*)codes + c);
     } else {
       i16x2 lo = {0, 0}, hi = {0, 0};
       if (FMT == kMXFP8) {
@@ -218,7 +221,8 @@ __global__ __launch_bounds__(kThreads) void quant_mx_kernel(const u32x4* __restr
       }
       u32x2 q = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
       if (nonfinite) q = u32x2{0, 0};
-      if (ok) __builtin_nontemporal_store(q, (u32x2*)codes + c);
+      if (ok && PANEL) ((u32x2*)codes)[c] = q;
+      if (ok && !PANEL) __builtin_nontemporal_store(q, (u32x2*)codes + c);
     }
     // Scale bytes: lanes 3, 7, 11, 15 of each 16-lane DPP row hold 4
     // consecutive blocks; lane 15 assembles them into one dword store. (With
