@@ -332,7 +332,9 @@ __global__ __launch_bounds__(kThreads) void quant_mbs_kernel(const u32x4* __rest
     q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, o[4], o[5], 1.0f, 2);
     q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, o[6], o[7], 1.0f, 3);
     if (nonfinite) q = 0;
-    if (c < nchunks) __builtin_nontemporal_store(q, codes + c);
+    // Plain stores: the GEMM that reads the activation codes next finds them
+    // in the caches (MBS step ~2.5% faster; the quantize alone ~7% slower).
+    if (c < nchunks) codes[c] = q;
     if (BASE == 32) {
       // Lanes 3, 7, 11, 15 of the row hold the macro block's 4 scales.
       const uint32_t s4 = dpp<dpp_row_shr(4)>(E);
